@@ -1,0 +1,299 @@
+/*
+ * rc.h — C ABI of the prefix-shared KV attention library (gfx950 / MI355X).
+ *
+ * The operations follow two pages:
+ *   [PC]  "Prompt Caching" glossary (Ultralytics): the problem statement.
+ *         Section "How prompt caching works": prefill computes one key and one
+ *         value per prompt token per layer; every decoded token attends to all
+ *         of them; because attention is causal the K/V of an identical prefix
+ *         are identical, so a cached copy replaces the recompute and only the
+ *         new tokens run.  Opening paragraph: reuse needs an exactly identical
+ *         prefix.  Closing list: a hit leaves next-token scores unchanged up to
+ *         floating-point rounding.
+ *   [SG]  "SGLang: Efficient Execution of Structured Language Model Programs"
+ *         summary (unite.ai): section "SGLang: programming model", RadixAttention
+ *         bullet (KV kept in a radix tree used for match / insert / evict, LRU
+ *         policy), the `fork` primitive, and the nine-step radix tree example
+ *         (new turns inserted as nodes; nodes split so sessions share a prompt).
+ *
+ * Conventions for every call
+ *   - Tensors are dense, row-major, caller-owned.  "device" pointers are HIP
+ *     device memory, "host" pointers are ordinary host memory.  The library
+ *     never allocates or frees device memory; it borrows pointers for the call.
+ *   - GPU calls only enqueue work on `stream` (a hipStream_t passed as void*,
+ *     NULL = the null stream) and return; the caller keeps buffers alive until
+ *     that work completes.
+ *   - Arguments are validated on the host before anything is launched; a
+ *     failing call returns a non-zero rc_status, launches nothing, changes
+ *     nothing, and rc_last_error() describes the failure (thread-local).
+ *   - Indices read from device memory (slots, table entries, plan entries) are
+ *     bounds-checked inside the kernels: an invalid one is never dereferenced;
+ *     the affected key is treated as absent and a bit is OR-ed into the device
+ *     error word if one was registered with rc_set_error_word().
+ *   - Layouts: q, o            [tokens, Hq, D]
+ *              k_new, v_new    [tokens, Hkv, D]
+ *              k_pool, v_pool  [pool_slots, Hkv, D]   (page size: one token)
+ *              req_to_token    [rows, stride] int32   (slot of position j of a
+ *                                                      request's context)
+ *   - Grouped-query attention: query head h reads kv head h / (Hq / Hkv).
+ *   - Causal alignment is by absolute position: new token i of a request with
+ *     a cached prefix of P tokens is at position P+i and sees keys 0..P+i.
+ */
+#ifndef RC_H
+#define RC_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum rc_status {
+  RC_OK = 0,
+  RC_ERR_ARG = 1,      /* null pointer, negative size, malformed argument        */
+  RC_ERR_SHAPE = 2,    /* head counts / head_dim not supported or inconsistent  */
+  RC_ERR_DTYPE = 3,    /* unsupported dtype                                     */
+  RC_ERR_RANGE = 4,    /* an index or length outside its documented range       */
+  RC_ERR_NOMEM = 5,    /* the KV pool has too few free slots (host tree calls)  */
+  RC_ERR_HIP = 6,      /* a HIP runtime call or kernel launch failed            */
+  RC_ERR_INTERNAL = 7
+} rc_status;
+
+typedef enum rc_dtype { RC_F32 = 0, RC_BF16 = 1 } rc_dtype;
+
+/* Model-side shape shared by the KV pool and the attention calls.
+ * num_q_heads % num_kv_heads == 0, group = num_q_heads / num_kv_heads <= 128,
+ * head_dim in {64, 128}. */
+typedef struct rc_shape {
+  int32_t dtype;        /* rc_dtype of q, k, v, pools and o                     */
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int64_t pool_slots;   /* rows of k_pool / v_pool                              */
+} rc_shape;
+
+/* Bits OR-ed into the device error word. */
+#define RC_DEVERR_SLOT 1    /* a slot outside [0, pool_slots)                    */
+#define RC_DEVERR_TABLE 2   /* a table position outside [0, stride)              */
+#define RC_DEVERR_LENGTH 4  /* extend_len > max_extend or a negative length      */
+#define RC_DEVERR_PLAN 8    /* a malformed plan entry                            */
+
+const char* rc_last_error(void);
+const char* rc_version(void);
+
+/* Register a device int32 that kernels OR RC_DEVERR_* bits into (NULL = off).
+ * Process-wide; not thread-safe against concurrent GPU calls. */
+rc_status rc_set_error_word(int32_t* device_word);
+
+/* ------------------------------------------------------------------------ */
+/* KV-pool scatter  [PC] "How prompt caching works": K and V of every token   */
+/* are stored and kept for later use.                                         */
+/*   k_pool[slots[i], h, :] = k_new[i, h, :] and the same for V, i < n.       */
+/* A bit copy (no conversion).  Slots must be distinct within one call (else */
+/* which row lands is unspecified); out-of-range slots are skipped and       */
+/* flagged.  Every other pool row is left unchanged.                          */
+/*   k_pool, v_pool : device, [pool_slots, Hkv, D] of shape->dtype            */
+/*   k_new, v_new   : device, [n, Hkv, D]                                     */
+/*   slots          : device int32 [n]                                        */
+/* ------------------------------------------------------------------------ */
+rc_status rc_kv_store(const rc_shape* shape, void* k_pool, void* v_pool, const void* k_new,
+                      const void* v_new, const int32_t* slots, int64_t n, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Extend attention  [PC] worked example: only the new tokens of a request    */
+/* run, over the cached prefix, and give the scores of a full recompute.     */
+/* For request b (table row rows[b], or b when rows is NULL), new token i <  */
+/* E_b = extend_lens[b] at absolute position p = P_b + i, P_b = prefix_lens[b]*/
+/*   o[s_b+i, h] = sum_{j<=p} softmax_j(sm_scale * q[s_b+i,h] . k_j) v_j,     */
+/* s_b = extend_start[b]; keys j < P_b are read from the pool at slot         */
+/* req_to_token[row, j]; keys P_b <= j <= p from k_new/v_new[s_b + j - P_b].   */
+/*   o               : device [total_extend, Hq, D], shape->dtype             */
+/*   q               : device [total_extend, Hq, D]                            */
+/*   k_new, v_new    : device [total_extend, Hkv, D]                           */
+/*   req_to_token    : device int32 [table_rows, stride]; only entries j < P_b */
+/*                     are read                                               */
+/*   rows            : device int32 [batch] or NULL; rows[b] < table_rows      */
+/*   prefix_lens, extend_lens, extend_start : device int32 [batch]             */
+/*   max_extend      : host bound on extend_lens (sets the grid)               */
+/* Requests with E_b = 0 write nothing.  Outputs are rounded once, from fp32, */
+/* to shape->dtype (round to nearest even for bf16).  Device-side checks:    */
+/* P_b <= stride, row < table_rows, s_b + E_b <= total_extend (else the      */
+/* request is skipped and RC_DEVERR_TABLE / RC_DEVERR_LENGTH raised).         */
+/* ------------------------------------------------------------------------ */
+rc_status rc_extend_attention(const rc_shape* shape, void* o, const void* q, const void* k_new,
+                              const void* v_new, const void* k_pool, const void* v_pool,
+                              const int32_t* req_to_token, int32_t table_rows, int64_t stride,
+                              const int32_t* rows, const int32_t* prefix_lens, const int32_t* extend_lens,
+                              const int32_t* extend_start, int32_t batch, int64_t total_extend,
+                              int32_t max_extend, float sm_scale, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Decode work plan.  A plan lists work items; each item is a range of KV     */
+/* positions [pos_begin, pos_end) read through one table row (rep_row) and   */
+/* the set of requests ("members") whose contexts contain exactly those      */
+/* slots at those positions.  The decode kernel loads each item's K/V once   */
+/* and computes it for every member and every query head of the group: a     */
+/* prefix shared by many branches is read from HBM once per step.            */
+/* Layout of the int32 plan buffer (copy it to the device as is):            */
+/*   [0..8)      header {RC_PLAN_MAGIC, n_items, n_members, max_splits,        */
+/*                        batch, group, chunk, max_cols}                      */
+/*   items       n_items x 8 {rep_row, pos_begin, pos_end, split, member_off, */
+/*                            member_cnt, 0, 0}                               */
+/*   members     n_members batch indices                                       */
+/*   n_splits    batch entries: partial results per request                    */
+/* The kernel clamps pos_end to seq_lens[first member]; the planners only    */
+/* put a range in a shared item when it lies inside every member's context.  */
+/* ------------------------------------------------------------------------ */
+#define RC_PLAN_MAGIC 0x52435031 /* "RCP1" */
+#define RC_PLAN_HEADER 8
+#define RC_PLAN_ITEM 8
+
+typedef struct rc_plan_info {
+  int32_t n_items;
+  int32_t n_members;
+  int32_t max_splits;
+  int32_t batch;
+  int32_t group;       /* Hq / Hkv the plan was built for                       */
+  int32_t chunk;       /* max positions per item                               */
+  int32_t max_cols;    /* max members*group per item                           */
+  int32_t shared_items;/* items with more than one member                       */
+  int64_t plan_ints;   /* length of the plan buffer in int32                    */
+  int64_t unique_positions; /* sum over items of (pos_end - pos_begin)         */
+  int64_t logical_positions;/* sum over requests of their context length       */
+} rc_plan_info;
+
+/* A plan without sharing: one chain of chunks per request over positions   */
+/* [0, max_seq_lens[b]) of table row rows[b] (NULL rows: b).                 */
+/* plan (host) receives plan_ints int32; if capacity is too small the call   */
+/* returns RC_ERR_RANGE with info->plan_ints set to the size needed.         */
+rc_status rc_plan_decode_unshared(int32_t batch, const int32_t* rows, const int32_t* max_seq_lens,
+                                  int32_t group, int32_t chunk, int32_t* plan, int64_t capacity,
+                                  rc_plan_info* info);
+
+/* Workspace bytes rc_decode_attention needs for a plan (fp32 partials).     */
+int64_t rc_decode_workspace_bytes(const rc_shape* shape, const rc_plan_info* info);
+
+/* ------------------------------------------------------------------------ */
+/* Decode attention  [PC] "How prompt caching works": each new token attends */
+/* to all cached keys and values.  One query token per request b:            */
+/*   o[b, h] = sum_{j < L_b} softmax_j(sm_scale * q[b,h] . k_j) v_j,          */
+/* L_b = seq_lens[b] includes the current token (store its K/V first).       */
+/* Keys come from the pool through the plan's table rows.  Split-K: each     */
+/* item writes fp32 partial (max, sum, unnormalised output) per member and   */
+/* head; a merge kernel combines each request's partials in split order      */
+/* (deterministic, no float atomics).                                         */
+/*   o, q          : device [batch, Hq, D]                                    */
+/*   req_to_token  : device int32 [table_rows, stride]                        */
+/*   seq_lens      : device int32 [batch]                                     */
+/*   plan_dev      : device copy of the plan buffer (info->plan_ints int32);  */
+/*                   info: the summary the planner returned with it          */
+/*   workspace     : device, >= rc_decode_workspace_bytes() bytes             */
+/* ------------------------------------------------------------------------ */
+rc_status rc_decode_attention(const rc_shape* shape, void* o, const void* q, const void* k_pool,
+                              const void* v_pool, const int32_t* req_to_token, int32_t table_rows,
+                              int64_t stride,
+                              const int32_t* seq_lens, int32_t batch, const int32_t* plan_dev,
+                              const rc_plan_info* info, float sm_scale, void* workspace,
+                              int64_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Radix tree over token ids, with the KV-pool slot allocator  ([SG]         */
+/* RadixAttention bullet and nine-step example; [PC] exact-prefix reuse).    */
+/* Host only; a handle is not thread-safe, separate handles are independent. */
+/* Every call is atomic: on failure the tree and allocator are unchanged.    */
+/* ------------------------------------------------------------------------ */
+typedef struct rc_radix rc_radix;
+
+typedef struct rc_radix_stats {
+  int64_t nodes;           /* live nodes, root excluded                        */
+  int64_t cached_tokens;   /* tokens held by the tree                          */
+  int64_t free_slots;
+  int64_t pool_slots;
+  int64_t splits;          /* edge splits so far                               */
+  int64_t matches;         /* match calls (including those inside emit_rows)   */
+  int64_t matched_tokens;  /* sum of matched lengths                           */
+  int64_t inserted_tokens; /* tokens newly stored by insert                    */
+  int64_t duplicate_slots; /* slots freed because their prefix was already stored */
+  int64_t evicted_tokens;
+} rc_radix_stats;
+
+/* free_order (host, nullable): the initial order in which slots are handed   */
+/* out, a permutation of [0, pool_slots); NULL means 0, 1, 2, ...            */
+rc_status rc_radix_create(int64_t pool_slots, const int32_t* free_order, rc_radix** out);
+void rc_radix_destroy(rc_radix* tree);
+
+/* Longest cached prefix of tokens[0..n), capped at n-1 (a request always     */
+/* runs at least one token).  out_slots (host, capacity n, nullable) gets    */
+/* the slots of the matched tokens.  Marks the matched nodes as used now.    */
+rc_status rc_radix_match(rc_radix* tree, const int32_t* tokens, int64_t n, int32_t* out_slots,
+                         int64_t* matched);
+
+/* Take n slots first-in first-out from the free list (all or nothing).      */
+rc_status rc_radix_alloc(rc_radix* tree, int64_t n, int32_t* out_slots);
+
+/* Return slots to the back of the free list.  Slots already free, out of    */
+/* range or repeated are rejected (RC_ERR_ARG) and nothing is freed.         */
+rc_status rc_radix_free(rc_radix* tree, const int32_t* slots, int64_t n);
+
+/* Store tokens[0..n) with their slots.  An edge is split at the first       */
+/* divergence.  Where a prefix is already stored its stored slots win: the   */
+/* caller's different slots for those positions are freed (ascending         */
+/* position order) and slots_inout is overwritten with the stored ones, so   */
+/* the caller can rewrite its table row.  n_new (nullable): tokens stored.   */
+rc_status rc_radix_insert(rc_radix* tree, const int32_t* tokens, int32_t* slots_inout, int64_t n,
+                          int64_t* n_new);
+
+/* Rows of the request -> slot table for a batch.  Request b has tokens      */
+/* tokens[tok_off[b] .. tok_off[b+1]) (host, CSR).  Row rows[b] of the host   */
+/* table req_to_token [*, stride] receives [matched prefix slots | new slots */
+/* for the n_b - P_b uncached tokens | `reserve` more slots for decoding];   */
+/* prefix_lens[b] = P_b, extend_lens[b] = n_b - P_b.  Allocation for the     */
+/* whole batch is all or nothing, in request order.  Entries after the row's */
+/* end are not touched.  table_rows bounds rows[b]; each row must fit in     */
+/* stride (n_b + reserve <= stride) or the call fails with RC_ERR_RANGE.     */
+rc_status rc_radix_emit_rows(rc_radix* tree, int32_t batch, const int32_t* tokens,
+                             const int64_t* tok_off, int32_t reserve, const int32_t* rows,
+                             int32_t* req_to_token, int32_t table_rows, int64_t stride,
+                             int32_t* prefix_lens, int32_t* extend_lens);
+
+/* fork ([SG] primitive list: parallel copies of a prompt state): store the  */
+/* parent's first n tokens with their slots (parent_slots, from its row) and */
+/* copy those n slots into rows child_rows[0..n_children) of req_to_token.   */
+/* The children then extend from the shared prefix without copying KV.       */
+rc_status rc_radix_fork(rc_radix* tree, const int32_t* tokens, const int32_t* parent_slots, int64_t n,
+                        int32_t n_children, const int32_t* child_rows, int32_t* req_to_token,
+                        int32_t table_rows, int64_t stride);
+
+/* Shared decode plan from the tree: request b's committed tokens            */
+/* tokens[tok_off[b]..tok_off[b+1]) are walked through the tree; every node  */
+/* range is one item whose members are all batch requests passing through    */
+/* it (split into items of at most max(1, 128 / group) members); positions   */
+/* past the walked prefix up to max_seq_lens[b] form the request's own tail. */
+/* Ranges are cut into chunks of at most `chunk` positions.  Table rows must */
+/* hold the tree's slots over the walked prefix (emit_rows + insert give     */
+/* that).  Output as rc_plan_decode_unshared.                                */
+rc_status rc_radix_plan_decode(rc_radix* tree, int32_t batch, const int32_t* tokens,
+                               const int64_t* tok_off, const int32_t* rows,
+                               const int32_t* max_seq_lens, int32_t group, int32_t chunk,
+                               int32_t* plan, int64_t capacity, rc_plan_info* info);
+
+rc_status rc_radix_stats_get(const rc_radix* tree, rc_radix_stats* out);
+
+/* ------------------------------------------------------------------------ */
+/* Kernel timing.  While enabled, every kernel the library launches is       */
+/* bracketed by HIP events on its own stream.  rc_prof_collect waits for the */
+/* recorded events, returns per-kernel totals and clears them.               */
+/* ------------------------------------------------------------------------ */
+typedef struct rc_prof_entry {
+  char name[48];
+  int64_t launches;
+  double total_ms;
+} rc_prof_entry;
+
+rc_status rc_prof_enable(int32_t on);
+rc_status rc_prof_collect(rc_prof_entry* out, int32_t capacity, int32_t* n_out);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* RC_H */

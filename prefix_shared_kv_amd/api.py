@@ -1,0 +1,291 @@
+"""Python binding of the C ABI (include/rc.h).
+
+Argument marshalling only: tensors are checked for device, dtype and layout,
+then their device pointers and the current HIP stream are handed to the
+library.  Every computation runs in the library's HIP kernels (GPU calls) or
+its C++ radix tree (host calls).  PyTorch provides device memory and streams.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import dataclasses
+from typing import List, Optional, Sequence, Tuple
+
+import numpy as np
+import torch
+
+from . import _native as N
+from ._native import RcPlanInfo, RcProfEntry, RcRadixStats, RcShape, check, lib
+
+_DT = {torch.float32: N.RC_F32, torch.bfloat16: N.RC_BF16}
+
+
+def _vp(t: Optional[torch.Tensor]):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _np_ptr(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(C.c_void_p)
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return C.c_void_p(s.cuda_stream)
+
+
+@dataclasses.dataclass(frozen=True)
+class KVShape:
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    dtype: torch.dtype
+    pool_slots: int
+
+    @property
+    def group(self) -> int:
+        return self.num_q_heads // self.num_kv_heads
+
+    def c(self) -> RcShape:
+        if self.dtype not in _DT:
+            raise TypeError(f"dtype {self.dtype} not supported")
+        return RcShape(_DT[self.dtype], self.num_q_heads, self.num_kv_heads, self.head_dim, self.pool_slots)
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if shape is not None:
+        for i, (a, b) in enumerate(zip(t.shape, shape)):
+            if b is not None and a != b:
+                raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {shape}")
+        if len(t.shape) != len(shape):
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {shape}")
+    return t
+
+
+def set_error_word(word: Optional[torch.Tensor]) -> None:
+    """Register a device int32 tensor (1 element) that kernels OR error bits into."""
+    if word is not None:
+        _dev(word, "error word", torch.int32)
+    check(lib.rc_set_error_word(_vp(word)))
+
+
+def kv_store(shape: KVShape, k_pool, v_pool, k_new, v_new, slots, stream=None) -> None:
+    """pool[slots[i]] = new[i] for K and V (see rc_kv_store)."""
+    H, D, S = shape.num_kv_heads, shape.head_dim, shape.pool_slots
+    _dev(k_pool, "k_pool", shape.dtype, (S, H, D))
+    _dev(v_pool, "v_pool", shape.dtype, (S, H, D))
+    n = slots.numel()
+    _dev(k_new, "k_new", shape.dtype, (n, H, D))
+    _dev(v_new, "v_new", shape.dtype, (n, H, D))
+    _dev(slots, "slots", torch.int32)
+    sh = shape.c()
+    check(lib.rc_kv_store(C.byref(sh), _vp(k_pool), _vp(v_pool), _vp(k_new), _vp(v_new), _vp(slots), n, _stream(stream)))
+
+
+def extend_attention(shape: KVShape, o, q, k_new, v_new, k_pool, v_pool, req_to_token, prefix_lens, extend_lens,
+                     extend_start, max_extend: int, sm_scale: float, rows=None, stream=None) -> None:
+    """Causal attention of each request's new tokens over its cached prefix plus themselves (rc_extend_attention)."""
+    Hq, Hkv, D, S = shape.num_q_heads, shape.num_kv_heads, shape.head_dim, shape.pool_slots
+    T = q.shape[0]
+    _dev(q, "q", shape.dtype, (T, Hq, D))
+    _dev(o, "o", shape.dtype, (T, Hq, D))
+    _dev(k_new, "k_new", shape.dtype, (T, Hkv, D))
+    _dev(v_new, "v_new", shape.dtype, (T, Hkv, D))
+    _dev(k_pool, "k_pool", shape.dtype, (S, Hkv, D))
+    _dev(v_pool, "v_pool", shape.dtype, (S, Hkv, D))
+    _dev(req_to_token, "req_to_token", torch.int32)
+    if req_to_token.dim() != 2:
+        raise ValueError("req_to_token must be [rows, stride]")
+    B = prefix_lens.numel()
+    for t, nm in ((prefix_lens, "prefix_lens"), (extend_lens, "extend_lens"), (extend_start, "extend_start")):
+        _dev(t, nm, torch.int32, (B,))
+    if rows is not None:
+        _dev(rows, "rows", torch.int32, (B,))
+    sh = shape.c()
+    check(lib.rc_extend_attention(C.byref(sh), _vp(o), _vp(q), _vp(k_new), _vp(v_new), _vp(k_pool), _vp(v_pool),
+                                  _vp(req_to_token), req_to_token.shape[0], req_to_token.shape[1], _vp(rows),
+                                  _vp(prefix_lens), _vp(extend_lens), _vp(extend_start), B, T, int(max_extend),
+                                  float(sm_scale), _stream(stream)))
+
+
+class DecodePlan:
+    """A decode work plan: the host int32 buffer, its summary, and a device copy."""
+
+    def __init__(self, buf: np.ndarray, info: RcPlanInfo):
+        self.host = buf
+        self.info = info
+        self.dev: Optional[torch.Tensor] = None
+
+    def to(self, device) -> "DecodePlan":
+        self.dev = torch.from_numpy(self.host).to(device)
+        return self
+
+    @property
+    def summary(self) -> dict:
+        return {f: getattr(self.info, f) for f, _ in RcPlanInfo._fields_}
+
+    def items(self) -> np.ndarray:
+        n = self.info.n_items
+        return self.host[N.RC_PLAN_HEADER:N.RC_PLAN_HEADER + n * N.RC_PLAN_ITEM].reshape(n, N.RC_PLAN_ITEM)
+
+    def members(self) -> np.ndarray:
+        o = N.RC_PLAN_HEADER + self.info.n_items * N.RC_PLAN_ITEM
+        return self.host[o:o + self.info.n_members]
+
+    def n_splits(self) -> np.ndarray:
+        o = N.RC_PLAN_HEADER + self.info.n_items * N.RC_PLAN_ITEM + self.info.n_members
+        return self.host[o:o + self.info.batch]
+
+
+def _run_planner(call) -> DecodePlan:
+    info = RcPlanInfo()
+    st = call(None, 0, info)
+    if st not in (N.RC_OK, N.RC_ERR_RANGE) or info.plan_ints <= 0:
+        check(st)
+    buf = np.zeros(info.plan_ints, np.int32)
+    check(call(_np_ptr(buf), buf.size, info))
+    return DecodePlan(buf, info)
+
+
+def plan_decode_unshared(max_seq_lens: Sequence[int], group: int, chunk: int = 512,
+                         rows: Optional[Sequence[int]] = None) -> DecodePlan:
+    ms = np.ascontiguousarray(max_seq_lens, np.int32)
+    rw = None if rows is None else np.ascontiguousarray(rows, np.int32)
+    return _run_planner(lambda p, cap, info: lib.rc_plan_decode_unshared(
+        ms.size, _np_ptr(rw), _np_ptr(ms), group, chunk, p, cap, C.byref(info)))
+
+
+def decode_workspace_bytes(shape: KVShape, plan: DecodePlan) -> int:
+    sh = shape.c()
+    return int(lib.rc_decode_workspace_bytes(C.byref(sh), C.byref(plan.info)))
+
+
+def decode_attention(shape: KVShape, o, q, k_pool, v_pool, req_to_token, seq_lens, plan: DecodePlan, sm_scale: float,
+                     workspace, stream=None) -> None:
+    """One query token per request over its whole context, through a share plan (rc_decode_attention)."""
+    Hq, Hkv, D, S = shape.num_q_heads, shape.num_kv_heads, shape.head_dim, shape.pool_slots
+    B = q.shape[0]
+    _dev(q, "q", shape.dtype, (B, Hq, D))
+    _dev(o, "o", shape.dtype, (B, Hq, D))
+    _dev(k_pool, "k_pool", shape.dtype, (S, Hkv, D))
+    _dev(v_pool, "v_pool", shape.dtype, (S, Hkv, D))
+    _dev(req_to_token, "req_to_token", torch.int32)
+    _dev(seq_lens, "seq_lens", torch.int32, (B,))
+    if plan.dev is None:
+        raise ValueError("plan has no device copy; call plan.to(device)")
+    _dev(workspace, "workspace")
+    sh = shape.c()
+    check(lib.rc_decode_attention(C.byref(sh), _vp(o), _vp(q), _vp(k_pool), _vp(v_pool), _vp(req_to_token),
+                                  req_to_token.shape[0], req_to_token.shape[1], _vp(seq_lens), B, _vp(plan.dev),
+                                  C.byref(plan.info), float(sm_scale), _vp(workspace),
+                                  workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def _csr(batch: Sequence[Sequence[int]]) -> Tuple[np.ndarray, np.ndarray]:
+    lens = np.array([len(t) for t in batch], np.int64)
+    off = np.zeros(len(batch) + 1, np.int64)
+    np.cumsum(lens, out=off[1:])
+    flat = np.concatenate([np.asarray(t, np.int32) for t in batch]) if len(batch) else np.zeros(0, np.int32)
+    return np.ascontiguousarray(flat, np.int32), off
+
+
+class RadixTree:
+    """Host radix tree over token ids with the pool's slot allocator (rc_radix_*)."""
+
+    def __init__(self, pool_slots: int, free_order: Optional[np.ndarray] = None):
+        self._h = C.c_void_p()
+        fo = None if free_order is None else np.ascontiguousarray(free_order, np.int32)
+        if fo is not None and fo.size != pool_slots:
+            raise ValueError("free_order must have pool_slots entries")
+        check(lib.rc_radix_create(pool_slots, _np_ptr(fo), C.byref(self._h)))
+        self.pool_slots = pool_slots
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value:
+            lib.rc_radix_destroy(h)
+            self._h = None
+
+    def match(self, tokens) -> Tuple[int, np.ndarray]:
+        t = np.ascontiguousarray(tokens, np.int32)
+        out = np.zeros(max(t.size, 1), np.int32)
+        m = C.c_int64()
+        check(lib.rc_radix_match(self._h, _np_ptr(t), t.size, _np_ptr(out), C.byref(m)))
+        return m.value, out[:m.value].copy()
+
+    def alloc(self, n: int) -> np.ndarray:
+        out = np.zeros(max(n, 1), np.int32)
+        check(lib.rc_radix_alloc(self._h, n, _np_ptr(out)))
+        return out[:n].copy()
+
+    def free(self, slots) -> None:
+        s = np.ascontiguousarray(slots, np.int32)
+        check(lib.rc_radix_free(self._h, _np_ptr(s), s.size))
+
+    def insert(self, tokens, slots) -> Tuple[np.ndarray, int]:
+        t = np.ascontiguousarray(tokens, np.int32)
+        s = np.array(slots, np.int32, copy=True)
+        if s.size != t.size:
+            raise ValueError("tokens and slots differ in length")
+        n_new = C.c_int64()
+        check(lib.rc_radix_insert(self._h, _np_ptr(t), _np_ptr(s), t.size, C.byref(n_new)))
+        return s, n_new.value
+
+    def emit_rows(self, batch: Sequence[Sequence[int]], table: np.ndarray, rows: Optional[Sequence[int]] = None,
+                  reserve: int = 0) -> Tuple[np.ndarray, np.ndarray]:
+        """Fill rows of a host table [R, stride]; returns (prefix_lens, extend_lens)."""
+        if table.dtype != np.int32 or table.ndim != 2 or not table.flags.c_contiguous:
+            raise ValueError("table must be a C-contiguous int32 [rows, stride] array")
+        flat, off = _csr(batch)
+        B = len(batch)
+        rw = np.arange(B, dtype=np.int32) if rows is None else np.ascontiguousarray(rows, np.int32)
+        P = np.zeros(B, np.int32)
+        E = np.zeros(B, np.int32)
+        check(lib.rc_radix_emit_rows(self._h, B, _np_ptr(flat), _np_ptr(off), reserve, _np_ptr(rw), _np_ptr(table),
+                                     table.shape[0], table.shape[1], _np_ptr(P), _np_ptr(E)))
+        return P, E
+
+    def fork(self, tokens, parent_slots, child_rows: Sequence[int], table: np.ndarray) -> None:
+        t = np.ascontiguousarray(tokens, np.int32)
+        s = np.ascontiguousarray(parent_slots, np.int32)
+        cr = np.ascontiguousarray(child_rows, np.int32)
+        check(lib.rc_radix_fork(self._h, _np_ptr(t), _np_ptr(s), t.size, cr.size, _np_ptr(cr), _np_ptr(table),
+                                table.shape[0], table.shape[1]))
+
+    def plan_decode(self, batch: Sequence[Sequence[int]], max_seq_lens: Sequence[int], group: int, chunk: int = 512,
+                    rows: Optional[Sequence[int]] = None) -> DecodePlan:
+        flat, off = _csr(batch)
+        B = len(batch)
+        rw = np.arange(B, dtype=np.int32) if rows is None else np.ascontiguousarray(rows, np.int32)
+        ms = np.ascontiguousarray(max_seq_lens, np.int32)
+        return _run_planner(lambda p, cap, info: lib.rc_radix_plan_decode(
+            self._h, B, _np_ptr(flat), _np_ptr(off), _np_ptr(rw), _np_ptr(ms), group, chunk, p, cap, C.byref(info)))
+
+    def stats(self) -> dict:
+        st = RcRadixStats()
+        check(lib.rc_radix_stats_get(self._h, C.byref(st)))
+        return {f: getattr(st, f) for f, _ in RcRadixStats._fields_}
+
+
+def prof_enable(on: bool = True) -> None:
+    check(lib.rc_prof_enable(1 if on else 0))
+
+
+def prof_collect() -> dict:
+    """{kernel name: (launches, total ms)} since the last collect; waits for the recorded events."""
+    cap = 64
+    arr = (RcProfEntry * cap)()
+    n = C.c_int32()
+    check(lib.rc_prof_collect(arr, cap, C.byref(n)))
+    return {arr[i].name.decode(): (arr[i].launches, arr[i].total_ms) for i in range(min(n.value, cap))}
+
+
+def version() -> str:
+    return lib.rc_version().decode()

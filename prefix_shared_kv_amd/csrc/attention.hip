@@ -1,0 +1,635 @@
+// Attention over a prefix-shared KV pool: extend (new tokens over their cached
+// prefix plus themselves) and split-K decode (one token per request), gfx950.
+//
+// What is computed follows the "Prompt Caching" glossary, section "How prompt
+// caching works" and its GPT-2 example: a request's new tokens attend causally,
+// by absolute position, over the cached K/V of its prefix and over their own
+// K/V; a decode token attends over the whole context.  The result equals a full
+// recompute up to floating-point rounding (the page's closing "related terms").
+//
+// One MFMA kernel serves both.  A workgroup (4 waves) owns up to 128 query
+// "columns" that read the same kv head over the same key positions:
+//   extend : columns = (new token, q head of the kv head's group) of one request
+//   decode : columns = (member request, q head) of one plan item, i.e. every
+//            request whose context holds this range of slots — a prefix shared
+//            by many branches is loaded from HBM once for all of them.
+// Keys are processed in stages of 64.  Each stage is gathered from the pool
+// through the request->slot table (or read from k_new/v_new for the extend's
+// own tokens), staged in LDS — K row-major, V transposed — and consumed by
+//   S^T = K Q^T    (v_mfma_f32_32x32x16_bf16, rows = keys, columns = queries)
+//   O^T += V^T P^T (same instruction, rows = head dims)
+// Computing S transposed puts one query column per lane: the softmax max and
+// the rescale of O are in-lane, plus one exchange between lanes l and l^32
+// per stage.  The 16 keys a lane holds for one PV step come straight from the
+// S^T accumulator; V^T is stored in LDS with the matching key permutation so
+// each MFMA operand is one 16-byte LDS read.  Online softmax runs in base 2
+// with log2(e) folded into the scale.
+#include <cfloat>
+#include <cmath>
+
+#include "hip_common.h"
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int BN = 64;     // keys per stage
+constexpr int NCOL = 128;  // query columns per workgroup (4 waves x 32)
+constexpr int NT = 256;
+constexpr float LOG2E = 1.4426950408889634f;
+
+enum Mode { EXTEND = 0, DECODE = 1 };
+
+struct Args {
+  const void* q;
+  void* o;
+  const void* k_new;
+  const void* v_new;
+  const void* k_pool;
+  const void* v_pool;
+  const int32_t* table;
+  int32_t table_rows;
+  int64_t stride;
+  int64_t pool_slots;
+  int32_t Hq, Hkv, g;
+  float scale_log2;  // sm_scale * log2(e)
+  int32_t* err;
+  int32_t n_work;    // workgroups in the grid
+  // extend
+  const int32_t* rows;
+  const int32_t* prefix_lens;
+  const int32_t* extend_lens;
+  const int32_t* extend_start;
+  int32_t batch;
+  int32_t max_extend;
+  int64_t total_extend;
+  int32_t tiles;     // tiles per (request, kv head)
+  int32_t tok_per_tile;
+  // decode
+  const int32_t* plan;
+  int32_t n_items, n_members;  // from the planner's host summary
+  const int32_t* seq_lens;
+  float* ws_o;
+  float* ws_ml;
+  int32_t max_splits;
+};
+
+// What one workgroup computes, resolved from the grid position.
+struct Work {
+  bool valid;
+  int32_t hk;
+  int64_t row;         // table row for positions < ext_begin
+  int32_t key_begin, key_end;
+  int32_t ext_begin;   // positions >= ext_begin come from k_new/v_new
+  int64_t ext_base;    // token index in k_new of position ext_begin
+  int32_t ncols;
+  int32_t min_limit;   // smallest causal limit over the columns
+  // extend
+  int32_t t0, E, P;
+  // decode
+  int32_t split, moff, mcnt;
+};
+
+__device__ __forceinline__ void flag(int32_t* err, int32_t bit) {
+  if (err) atomicOr(err, bit);
+}
+
+__device__ Work resolve(const Args& a, int mode, int L) {
+  Work w{};
+  w.valid = false;
+  if (mode == EXTEND) {
+    const int tile = L % a.tiles;
+    const int bh = L / a.tiles;
+    const int b = bh / a.Hkv;
+    w.hk = bh - b * a.Hkv;
+    const int P = a.prefix_lens[b], E = a.extend_lens[b];
+    if (P < 0 || E < 0) {
+      if (tile == 0 && threadIdx.x == 0) flag(a.err, RC_DEVERR_LENGTH);
+      return w;
+    }
+    if (E > a.max_extend && tile == 0 && w.hk == 0 && threadIdx.x == 0) flag(a.err, RC_DEVERR_LENGTH);
+    if ((int64_t)P > a.stride) {
+      if (tile == 0 && threadIdx.x == 0) flag(a.err, RC_DEVERR_TABLE);
+      return w;
+    }
+    const int t0 = tile * a.tok_per_tile;
+    const int Ec = E < a.max_extend ? E : a.max_extend;
+    if (t0 >= Ec) return w;
+    const int nt = min(a.tok_per_tile, Ec - t0);
+    const int64_t s0 = a.extend_start[b];
+    if (s0 < 0 || s0 + Ec > a.total_extend) {
+      if (tile == 0 && threadIdx.x == 0) flag(a.err, RC_DEVERR_LENGTH);
+      return w;
+    }
+    w.row = a.rows ? a.rows[b] : b;
+    if (w.row < 0 || w.row >= a.table_rows) {
+      if (threadIdx.x == 0) flag(a.err, RC_DEVERR_TABLE);
+      return w;
+    }
+    w.key_begin = 0;
+    w.key_end = P + t0 + nt;
+    w.ext_begin = P;
+    w.ext_base = s0;
+    w.ncols = nt * a.g;
+    w.min_limit = P + t0;
+    w.t0 = t0;
+    w.E = Ec;
+    w.P = P;
+    w.valid = true;
+  } else {
+    const int item = L / a.Hkv;
+    w.hk = L - item * a.Hkv;
+    const int32_t* it = a.plan + RC_PLAN_HEADER + (int64_t)item * RC_PLAN_ITEM;
+    const int32_t n_members = a.n_members;
+    const int32_t rep = it[0], pb = it[1], pe = it[2];
+    w.split = it[3];
+    w.moff = it[4];
+    w.mcnt = it[5];
+    if (rep < 0 || rep >= a.table_rows || pb < 0 || pe < pb || (int64_t)pe > a.stride || w.split < 0 || w.split >= a.max_splits ||
+        w.moff < 0 || w.mcnt < 1 || w.mcnt * a.g > NCOL || w.moff + w.mcnt > n_members) {
+      if (threadIdx.x == 0) flag(a.err, RC_DEVERR_PLAN);
+      return w;
+    }
+    const int32_t* mem = a.plan + RC_PLAN_HEADER + (int64_t)a.n_items * RC_PLAN_ITEM + w.moff;
+    for (int i = 0; i < w.mcnt; ++i)
+      if (mem[i] < 0 || mem[i] >= a.batch) {
+        if (threadIdx.x == 0) flag(a.err, RC_DEVERR_PLAN);
+        return w;
+      }
+    const int sl = a.seq_lens[mem[0]];
+    w.row = rep;
+    w.key_begin = pb;
+    w.key_end = pe < sl ? pe : sl;
+    if (w.key_end < w.key_begin) w.key_end = w.key_begin;
+    w.ext_begin = INT_MAX;
+    w.ext_base = 0;
+    w.ncols = w.mcnt * a.g;
+    w.min_limit = INT_MAX;
+    w.valid = true;
+  }
+  return w;
+}
+
+// Per-column (query) information.
+struct Col {
+  int64_t qoff;   // element offset of the query row (token, head)
+  int32_t limit;  // last visible key position
+  int32_t head;
+  int32_t b;      // decode: batch index
+  bool real;
+};
+
+__device__ __forceinline__ Col column(const Args& a, int mode, const Work& w, int c) {
+  Col k;
+  k.real = c < w.ncols;
+  const int cc = k.real ? c : w.ncols - 1;
+  const int u = cc / a.g, j = cc - (cc / a.g) * a.g;
+  k.head = w.hk * a.g + j;
+  if (mode == EXTEND) {
+    const int t = w.t0 + u;
+    k.qoff = (w.ext_base + t) * (int64_t)a.Hq + k.head;
+    k.limit = w.P + t;
+    k.b = -1;
+  } else {
+    const int32_t* mem = a.plan + RC_PLAN_HEADER + (int64_t)a.n_items * RC_PLAN_ITEM + w.moff;
+    k.b = mem[u];
+    k.qoff = (int64_t)k.b * a.Hq + k.head;
+    k.limit = INT_MAX;
+  }
+  return k;
+}
+
+// Position of key r (0..15) of a 16-key block inside the transposed V tile:
+// swaps bits 2 and 3 so a lane's 8 PV-operand keys are contiguous.
+__device__ __forceinline__ int vperm(int r) { return (((r >> 2) & 1) << 3) | (((r >> 3) & 1) << 2) | (r & 3); }
+
+__device__ __forceinline__ uint32_t pack2(uint32_t lo16, uint32_t hi16) { return (lo16 & 0xffffu) | (hi16 << 16); }
+
+template <int D>
+__global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(Args a, int mode) {
+  constexpr int KST = D + 8;      // K row stride in LDS (elements)
+  constexpr int VST = BN + 8;     // V^T row stride in LDS (elements)
+  constexpr int CH = D / 8;       // 16-byte chunks per key row
+  constexpr int KPT = BN * CH / NT;  // keys per thread per stage (4 for D=128, 2 for D=64)
+  constexpr int NKS = D / 16;     // MFMA k-steps over D
+  constexpr int NDB = D / 32;     // 32-row blocks of O^T
+  __shared__ __attribute__((aligned(16))) uint16_t sK[BN * KST];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[D * VST];
+
+  const int L = xcd_remap(blockIdx.x, a.n_work);
+  const Work w = resolve(a, mode, L);
+  if (!w.valid) return;  // uniform over the workgroup
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int hi = lane >> 5;  // which half of the wave
+  const int c = wave * 32 + (lane & 31);
+  const bool active = wave * 32 < w.ncols;
+  const Col col = column(a, mode, w, c);
+
+  const uint16_t* q = (const uint16_t*)a.q;
+  bf16x8 qf[NKS];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) qf[ks] = *(const bf16x8*)(q + col.qoff * D + ks * 16 + 8 * hi);
+
+  f32x16 acc[NDB];
+#pragma unroll
+  for (int i = 0; i < NDB; ++i) acc[i] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  // loader: thread -> (chunk lc of D, keys lk0 .. lk0+KPT-1 of the stage)
+  const int lc = tid % CH;
+  const int lk0 = (tid / CH) * KPT;
+  const uint16_t* kpool = (const uint16_t*)a.k_pool;
+  const uint16_t* vpool = (const uint16_t*)a.v_pool;
+  const uint16_t* knew = (const uint16_t*)a.k_new;
+  const uint16_t* vnew = (const uint16_t*)a.v_new;
+  const int64_t rowHD = (int64_t)a.Hkv * D;
+  uint4 kr[KPT], vr[KPT];
+
+  auto load_stage = [&](int kt) {
+#pragma unroll
+    for (int r = 0; r < KPT; ++r) {
+      const int j = kt + lk0 + r;
+      kr[r] = make_uint4(0, 0, 0, 0);
+      vr[r] = make_uint4(0, 0, 0, 0);
+      if (j < w.key_end) {
+        if (j >= w.ext_begin) {
+          const int64_t off = (w.ext_base + (j - w.ext_begin)) * rowHD + (int64_t)w.hk * D + lc * 8;
+          kr[r] = *(const uint4*)(knew + off);
+          vr[r] = *(const uint4*)(vnew + off);
+        } else {
+          const int32_t s = a.table[w.row * a.stride + j];
+          if (s >= 0 && (int64_t)s < a.pool_slots) {
+            const int64_t off = (int64_t)s * rowHD + (int64_t)w.hk * D + lc * 8;
+            kr[r] = *(const uint4*)(kpool + off);
+            vr[r] = *(const uint4*)(vpool + off);
+          } else {
+            flag(a.err, RC_DEVERR_SLOT);
+          }
+        }
+      }
+    }
+  };
+
+  auto store_stage = [&]() {
+#pragma unroll
+    for (int r = 0; r < KPT; ++r) *(uint4*)(sK + (lk0 + r) * KST + lc * 8) = kr[r];
+    const int vbase = (lk0 & ~15) + vperm(lk0 & 15);
+    uint32_t e[KPT][8];
+#pragma unroll
+    for (int r = 0; r < KPT; ++r) {
+      e[r][0] = vr[r].x & 0xffffu; e[r][1] = vr[r].x >> 16;
+      e[r][2] = vr[r].y & 0xffffu; e[r][3] = vr[r].y >> 16;
+      e[r][4] = vr[r].z & 0xffffu; e[r][5] = vr[r].z >> 16;
+      e[r][6] = vr[r].w & 0xffffu; e[r][7] = vr[r].w >> 16;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      uint16_t* dst = sV + (lc * 8 + i) * VST + vbase;
+      if constexpr (KPT == 4) {
+        *(uint2*)dst = make_uint2(pack2(e[0][i], e[1][i]), pack2(e[2][i], e[3][i]));
+      } else {
+        *(uint32_t*)dst = pack2(e[0][i], e[1][i]);
+      }
+    }
+  };
+
+  int kt = w.key_begin;
+  if (kt < w.key_end) load_stage(kt);
+  for (; kt < w.key_end; kt += BN) {
+    __syncthreads();
+    store_stage();
+    __syncthreads();
+    if (kt + BN < w.key_end) load_stage(kt + BN);
+    if (!active) continue;
+
+    // S^T = K Q^T over two 32-key blocks
+    f32x16 s[2];
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      s[m] = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        const bf16x8 kf = *(const bf16x8*)(sK + (m * 32 + (lane & 31)) * KST + ks * 16 + 8 * hi);
+        s[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s[m], 0, 0, 0);
+      }
+    }
+    const bool need_mask = (kt + BN > w.key_end) || ((int64_t)kt + BN - 1 > (int64_t)w.min_limit);
+    float mx = -INFINITY;
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        float x = s[m][v] * a.scale_log2;
+        if (need_mask) {
+          const int key = kt + m * 32 + (v >> 2) * 8 + hi * 4 + (v & 3);
+          if (key >= w.key_end || key > col.limit) x = -INFINITY;
+        }
+        s[m][v] = x;
+        mx = fmaxf(mx, x);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = exp2f(m_run - m_use);
+    float psum = 0.f;
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const float p = exp2f(s[m][v] - m_use);
+        s[m][v] = p;
+        psum += p;
+      }
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) acc[db] *= alpha;
+
+    // O^T += V^T P^T, four 16-key steps
+#pragma unroll
+    for (int k2 = 0; k2 < 4; ++k2) {
+      const int m = k2 >> 1, h = k2 & 1;
+      bf16x8 pf;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) pf[i] = (__bf16)s[m][8 * h + i];
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const bf16x8 vf = *(const bf16x8*)(sV + (db * 32 + (lane & 31)) * VST + k2 * 16 + 8 * hi);
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, acc[db], 0, 0, 0);
+      }
+    }
+  }
+
+  if (!active || !col.real) return;
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  if (mode == EXTEND) {
+    const float inv = 1.f / l_tot;
+    {
+      uint16_t* o = (uint16_t*)a.o + col.qoff * D;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int d = db * 32 + g4 * 8 + hi * 4;
+          __bf16 b0 = (__bf16)(acc[db][4 * g4 + 0] * inv), b1 = (__bf16)(acc[db][4 * g4 + 1] * inv);
+          __bf16 b2 = (__bf16)(acc[db][4 * g4 + 2] * inv), b3 = (__bf16)(acc[db][4 * g4 + 3] * inv);
+          uint2 pk;
+          pk.x = pack2(__builtin_bit_cast(uint16_t, b0), __builtin_bit_cast(uint16_t, b1));
+          pk.y = pack2(__builtin_bit_cast(uint16_t, b2), __builtin_bit_cast(uint16_t, b3));
+          *(uint2*)(o + d) = pk;
+        }
+    }
+  } else {
+    const int64_t pidx = ((int64_t)col.b * a.Hq + col.head) * a.max_splits + w.split;
+    float* wo = a.ws_o + pidx * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d = db * 32 + g4 * 8 + hi * 4;
+        *(float4*)(wo + d) = make_float4(acc[db][4 * g4], acc[db][4 * g4 + 1], acc[db][4 * g4 + 2], acc[db][4 * g4 + 3]);
+      }
+    if (hi == 0) *(float2*)(a.ws_ml + pidx * 2) = make_float2(m_run, l_tot);
+  }
+}
+
+// fp32 path: one wave per column, lanes over head dims, keys one at a time.
+// Same work decomposition and outputs as the MFMA kernel; used for fp32 data.
+template <int D>
+__global__ __launch_bounds__(NT) void attn_f32_kernel(Args a, int mode) {
+  constexpr int PER = D / 64;
+  const int L = xcd_remap(blockIdx.x, a.n_work);
+  const Work w = resolve(a, mode, L);
+  if (!w.valid) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const float* q = (const float*)a.q;
+  const float* kpool = (const float*)a.k_pool;
+  const float* vpool = (const float*)a.v_pool;
+  const float* knew = (const float*)a.k_new;
+  const float* vnew = (const float*)a.v_new;
+  const int64_t rowHD = (int64_t)a.Hkv * D;
+  for (int c = wave; c < w.ncols; c += NT / 64) {
+    const Col col = column(a, mode, w, c);
+    float qv[PER], ov[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      qv[i] = q[col.qoff * D + lane + 64 * i];
+      ov[i] = 0.f;
+    }
+    float m_run = -INFINITY, l_run = 0.f;
+    const int end = min(w.key_end, col.limit == INT_MAX ? w.key_end : col.limit + 1);
+    for (int j = w.key_begin; j < end; ++j) {
+      const float *kp, *vp;
+      if (j >= w.ext_begin) {
+        const int64_t off = (w.ext_base + (j - w.ext_begin)) * rowHD + (int64_t)w.hk * D;
+        kp = knew + off;
+        vp = vnew + off;
+      } else {
+        const int32_t s = a.table[w.row * a.stride + j];
+        if (s < 0 || (int64_t)s >= a.pool_slots) {
+          if (lane == 0) flag(a.err, RC_DEVERR_SLOT);
+          continue;
+        }
+        const int64_t off = (int64_t)s * rowHD + (int64_t)w.hk * D;
+        kp = kpool + off;
+        vp = vpool + off;
+      }
+      float dot = 0.f;
+#pragma unroll
+      for (int i = 0; i < PER; ++i) dot += qv[i] * kp[lane + 64 * i];
+#pragma unroll
+      for (int sh = 32; sh >= 1; sh >>= 1) dot += __shfl_xor(dot, sh);
+      const float x = dot * a.scale_log2;
+      const float m_new = fmaxf(m_run, x);
+      const float alpha = exp2f(m_run - m_new);
+      const float p = exp2f(x - m_new);
+      l_run = l_run * alpha + p;
+#pragma unroll
+      for (int i = 0; i < PER; ++i) ov[i] = ov[i] * alpha + p * vp[lane + 64 * i];
+      m_run = m_new;
+    }
+    if (!col.real) continue;
+    if (mode == EXTEND) {
+      float* o = (float*)a.o + col.qoff * D;
+#pragma unroll
+      for (int i = 0; i < PER; ++i) o[lane + 64 * i] = ov[i] / l_run;
+    } else {
+      const int64_t pidx = ((int64_t)col.b * a.Hq + col.head) * a.max_splits + w.split;
+#pragma unroll
+      for (int i = 0; i < PER; ++i) a.ws_o[pidx * D + lane + 64 * i] = ov[i];
+      if (lane == 0) *(float2*)(a.ws_ml + pidx * 2) = make_float2(m_run, l_run);
+    }
+  }
+}
+
+// Split merge: for each (request, q head), combine its partials k = 0..n-1 in
+// order: M = max m_k, l = sum l_k 2^(m_k - M), o = sum o_k 2^(m_k - M) / l.
+template <int D, bool BF16>
+__global__ __launch_bounds__(256) void merge_kernel(void* out, const float* __restrict__ ws_o,
+                                                    const float* __restrict__ ws_ml, const int32_t* nsplit,
+                                                    int32_t batch, int32_t Hq, int32_t max_splits) {
+  constexpr int PER = D / 64;
+  const int pair = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (pair >= batch * Hq) return;
+  const int lane = threadIdx.x & 63;
+  const int b = pair / Hq;
+  int ns = nsplit[b];
+  ns = ns < 0 ? 0 : (ns < max_splits ? ns : max_splits);
+  const float* ml = ws_ml + (int64_t)pair * max_splits * 2;
+  float M = -INFINITY;
+  for (int k = 0; k < ns; ++k) M = fmaxf(M, ml[2 * k]);
+  float l = 0.f, acc[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) acc[i] = 0.f;
+  const float* po = ws_o + (int64_t)pair * max_splits * D;
+  for (int k = 0; k < ns; ++k) {
+    const float mk = ml[2 * k];
+    if (mk == -INFINITY) continue;
+    const float wgt = exp2f(mk - M);
+    l += ml[2 * k + 1] * wgt;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) acc[i] += po[(int64_t)k * D + lane + 64 * i] * wgt;
+  }
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const float r = acc[i] * inv;
+    if (BF16)
+      ((__bf16*)out)[(int64_t)pair * D + lane + 64 * i] = (__bf16)r;
+    else
+      ((float*)out)[(int64_t)pair * D + lane + 64 * i] = r;
+  }
+}
+
+template <int D>
+void launch_attn(const Args& a, int mode, int n_work, bool bf16, hipStream_t s, const char* name) {
+  rc::ProfScope p(name, s);
+  if (bf16)
+    hipLaunchKernelGGL(attn_bf16_kernel<D>, dim3(n_work), dim3(NT), 0, s, a, mode);
+  else
+    hipLaunchKernelGGL(attn_f32_kernel<D>, dim3(n_work), dim3(NT), 0, s, a, mode);
+}
+
+rc_status check_common(const rc_shape* shape, float sm_scale) {
+  rc_status st = rc::check_shape(shape);
+  if (st != RC_OK) return st;
+  if (!std::isfinite(sm_scale)) return rc::fail(RC_ERR_ARG, "sm_scale is not finite");
+  return RC_OK;
+}
+
+}  // namespace
+
+extern "C" rc_status rc_extend_attention(const rc_shape* shape, void* o, const void* q, const void* k_new,
+                                         const void* v_new, const void* k_pool, const void* v_pool,
+                                         const int32_t* req_to_token, int32_t table_rows, int64_t stride,
+                                         const int32_t* rows, const int32_t* prefix_lens, const int32_t* extend_lens,
+                                         const int32_t* extend_start, int32_t batch, int64_t total_extend,
+                                         int32_t max_extend, float sm_scale, void* stream) {
+  using namespace rc;
+  rc_status st = check_common(shape, sm_scale);
+  if (st != RC_OK) return st;
+  if (batch < 0 || total_extend < 0 || max_extend < 0 || stride <= 0 || table_rows < 0)
+    return fail(RC_ERR_ARG, "negative size (batch=%d total_extend=%lld max_extend=%d) or stride <= 0", batch,
+                (long long)total_extend, max_extend);
+  if (batch == 0 || max_extend == 0 || total_extend == 0) return RC_OK;
+  if (!o || !q || !k_new || !v_new || !k_pool || !v_pool || !req_to_token || !prefix_lens || !extend_lens ||
+      !extend_start)
+    return fail(RC_ERR_ARG, "NULL device pointer in rc_extend_attention");
+  const int g = shape->num_q_heads / shape->num_kv_heads;
+  Args a{};
+  a.q = q; a.o = o; a.k_new = k_new; a.v_new = v_new; a.k_pool = k_pool; a.v_pool = v_pool;
+  a.table = req_to_token; a.table_rows = table_rows; a.stride = stride; a.pool_slots = shape->pool_slots;
+  a.Hq = shape->num_q_heads; a.Hkv = shape->num_kv_heads; a.g = g;
+  a.scale_log2 = sm_scale * LOG2E;
+  a.err = error_word();
+  a.total_extend = total_extend;
+  a.rows = rows; a.prefix_lens = prefix_lens; a.extend_lens = extend_lens; a.extend_start = extend_start;
+  a.batch = batch; a.max_extend = max_extend;
+  a.tok_per_tile = NCOL / g;
+  a.tiles = (max_extend + a.tok_per_tile - 1) / a.tok_per_tile;
+  const int64_t n_work = (int64_t)batch * a.Hkv * a.tiles;
+  if (n_work > INT32_MAX) return fail(RC_ERR_RANGE, "grid of %lld workgroups too large", (long long)n_work);
+  a.n_work = (int32_t)n_work;
+  hipStream_t s = (hipStream_t)stream;
+  const bool bf16 = shape->dtype == RC_BF16;
+  if (shape->head_dim == 128)
+    launch_attn<128>(a, EXTEND, a.n_work, bf16, s, bf16 ? "extend_bf16_d128" : "extend_f32_d128");
+  else
+    launch_attn<64>(a, EXTEND, a.n_work, bf16, s, bf16 ? "extend_bf16_d64" : "extend_f32_d64");
+  return check_launch("extend attention");
+}
+
+extern "C" int64_t rc_decode_workspace_bytes(const rc_shape* shape, const rc_plan_info* info) {
+  if (!shape || !info || shape->head_dim <= 0) return -1;
+  const int64_t parts = (int64_t)info->batch * shape->num_q_heads * (info->max_splits > 0 ? info->max_splits : 1);
+  return parts * shape->head_dim * 4 + parts * 2 * 4;
+}
+
+extern "C" rc_status rc_decode_attention(const rc_shape* shape, void* o, const void* q, const void* k_pool,
+                                         const void* v_pool, const int32_t* req_to_token, int32_t table_rows,
+                                         int64_t stride, const int32_t* seq_lens, int32_t batch, const int32_t* plan_dev,
+                                         const rc_plan_info* info, float sm_scale, void* workspace,
+                                         int64_t ws_bytes, void* stream) {
+  using namespace rc;
+  rc_status st = check_common(shape, sm_scale);
+  if (st != RC_OK) return st;
+  if (batch < 0 || stride <= 0 || table_rows < 0) return fail(RC_ERR_ARG, "batch < 0, stride <= 0 or table_rows < 0");
+  if (batch == 0) return RC_OK;
+  if (!info) return fail(RC_ERR_ARG, "plan info is NULL");
+  if (!o || !q || !k_pool || !v_pool || !req_to_token || !seq_lens || !plan_dev || !workspace)
+    return fail(RC_ERR_ARG, "NULL device pointer in rc_decode_attention");
+  const int g = shape->num_q_heads / shape->num_kv_heads;
+  if (info->batch != batch) return fail(RC_ERR_ARG, "plan built for batch %d, called with %d", info->batch, batch);
+  if (info->group != g) return fail(RC_ERR_SHAPE, "plan built for group %d, shape has %d", info->group, g);
+  if (info->max_cols > NCOL || info->n_items < 0 || info->n_members < 0 || info->max_splits < 1 ||
+      info->plan_ints != RC_PLAN_HEADER + (int64_t)info->n_items * RC_PLAN_ITEM + info->n_members + batch)
+    return fail(RC_ERR_ARG, "plan summary out of range");
+  const int64_t need = rc_decode_workspace_bytes(shape, info);
+  if (ws_bytes < need) return fail(RC_ERR_RANGE, "workspace of %lld bytes, %lld needed", (long long)ws_bytes, (long long)need);
+  const int64_t parts = (int64_t)batch * shape->num_q_heads * info->max_splits;
+  Args a{};
+  a.q = q; a.o = o; a.k_pool = k_pool; a.v_pool = v_pool;
+  a.table = req_to_token; a.table_rows = table_rows; a.stride = stride; a.pool_slots = shape->pool_slots;
+  a.Hq = shape->num_q_heads; a.Hkv = shape->num_kv_heads; a.g = g;
+  a.scale_log2 = sm_scale * LOG2E;
+  a.err = error_word();
+  a.batch = batch;
+  a.plan = plan_dev; a.seq_lens = seq_lens;
+  a.n_items = info->n_items; a.n_members = info->n_members;
+  a.ws_o = (float*)workspace;
+  a.ws_ml = (float*)workspace + parts * shape->head_dim;
+  a.max_splits = info->max_splits;
+  const int64_t n_work = (int64_t)info->n_items * a.Hkv;
+  if (n_work > INT32_MAX) return fail(RC_ERR_RANGE, "grid too large");
+  a.n_work = (int32_t)n_work;
+  hipStream_t s = (hipStream_t)stream;
+  const bool bf16 = shape->dtype == RC_BF16;
+  if (n_work > 0) {
+    if (shape->head_dim == 128)
+      launch_attn<128>(a, DECODE, a.n_work, bf16, s, bf16 ? "decode_bf16_d128" : "decode_f32_d128");
+    else
+      launch_attn<64>(a, DECODE, a.n_work, bf16, s, bf16 ? "decode_bf16_d64" : "decode_f32_d64");
+    st = check_launch("decode attention");
+    if (st != RC_OK) return st;
+  }
+  const int32_t* nsplit = plan_dev + RC_PLAN_HEADER + (int64_t)info->n_items * RC_PLAN_ITEM + info->n_members;
+  const int pairs = batch * shape->num_q_heads;
+  const dim3 grid((pairs + 3) / 4);
+  {
+    ProfScope p("decode_merge", s);
+    if (shape->head_dim == 128) {
+      if (bf16)
+        hipLaunchKernelGGL((merge_kernel<128, true>), grid, dim3(256), 0, s, o, a.ws_o, a.ws_ml, nsplit, batch, a.Hq, a.max_splits);
+      else
+        hipLaunchKernelGGL((merge_kernel<128, false>), grid, dim3(256), 0, s, o, a.ws_o, a.ws_ml, nsplit, batch, a.Hq, a.max_splits);
+    } else {
+      if (bf16)
+        hipLaunchKernelGGL((merge_kernel<64, true>), grid, dim3(256), 0, s, o, a.ws_o, a.ws_ml, nsplit, batch, a.Hq, a.max_splits);
+      else
+        hipLaunchKernelGGL((merge_kernel<64, false>), grid, dim3(256), 0, s, o, a.ws_o, a.ws_ml, nsplit, batch, a.Hq, a.max_splits);
+    }
+  }
+  return check_launch("decode merge");
+}

@@ -1,0 +1,550 @@
+// Host-side radix tree over token ids with the KV-pool slot allocator, and the
+// decode work planners.
+//
+// The tree follows the RadixAttention description in the SGLang summary
+// (unite.ai), section "SGLang: programming model": KV kept in a radix tree used
+// for matching, inserting and evicting; every edge carries a token sequence;
+// the nine-step example inserts new turns as nodes and splits a node when two
+// sessions (or few-shot queries) share only part of it.  Reuse requires an
+// exactly identical prefix ("Prompt Caching" glossary, opening paragraph).
+//
+// Plain C++17; no HIP.  Every public call validates first and mutates after,
+// so a failing call leaves the tree and the allocator unchanged.
+#include <algorithm>
+#include <cstring>
+#include <deque>
+#include <new>
+#include <unordered_map>
+#include <vector>
+
+#include "rc_internal.h"
+
+using rc::fail;
+
+namespace {
+
+struct Node {
+  int32_t parent = -1;
+  int64_t start = 0;  // absolute position of the edge's first token
+  std::vector<int32_t> tok, slot;
+  std::unordered_map<int32_t, int32_t> kids;  // first token of child edge -> child
+  int64_t last_use = 0;
+  int32_t lock = 0;
+  bool alive = true;
+};
+
+}  // namespace
+
+struct rc_radix {
+  std::vector<Node> nodes;  // nodes[0] is the root; its edge is empty
+  std::vector<int32_t> dead_ids;
+  std::deque<int32_t> free_q;
+  std::vector<uint8_t> is_free;  // slot is in free_q
+  std::vector<uint8_t> in_tree;  // slot is owned by a tree node
+  int64_t pool = 0;
+  int64_t clock = 0;
+  rc_radix_stats st{};
+};
+
+namespace {
+
+// Walk tokens[0..n) down the tree; visit(node, k) for each edge entered with k
+// matched tokens (k >= 1).  Returns the matched length.
+template <class F>
+int64_t walk(const rc_radix& t, const int32_t* tok, int64_t n, F&& visit) {
+  int32_t cur = 0;
+  int64_t pos = 0;
+  while (pos < n) {
+    auto it = t.nodes[cur].kids.find(tok[pos]);
+    if (it == t.nodes[cur].kids.end()) break;
+    const Node& c = t.nodes[it->second];
+    const int64_t len = (int64_t)c.tok.size();
+    const int64_t lim = std::min(len, n - pos);
+    int64_t k = 0;
+    while (k < lim && c.tok[k] == tok[pos + k]) ++k;
+    visit(it->second, k);
+    pos += k;
+    if (k < len) break;
+    cur = it->second;
+  }
+  return pos;
+}
+
+int32_t new_node(rc_radix& t) {
+  if (!t.dead_ids.empty()) {
+    int32_t id = t.dead_ids.back();
+    t.dead_ids.pop_back();
+    t.nodes[id] = Node();
+    return id;
+  }
+  t.nodes.emplace_back();
+  return (int32_t)t.nodes.size() - 1;
+}
+
+// Split node c so that its first k tokens become a new parent node.  Returns the new node.
+int32_t split(rc_radix& t, int32_t c, int64_t k) {
+  int32_t u = new_node(t);  // may reallocate: index only from here on
+  Node& cn = t.nodes[c];
+  Node& un = t.nodes[u];
+  un.parent = cn.parent;
+  un.start = cn.start;
+  un.tok.assign(cn.tok.begin(), cn.tok.begin() + k);
+  un.slot.assign(cn.slot.begin(), cn.slot.begin() + k);
+  un.last_use = cn.last_use;
+  un.lock = cn.lock;
+  cn.tok.erase(cn.tok.begin(), cn.tok.begin() + k);
+  cn.slot.erase(cn.slot.begin(), cn.slot.begin() + k);
+  cn.start += k;
+  cn.parent = u;
+  un.kids[cn.tok[0]] = c;
+  t.nodes[un.parent].kids[un.tok[0]] = u;
+  t.st.splits++;
+  t.st.nodes++;
+  return u;
+}
+
+bool slot_ok(const rc_radix& t, int32_t s) { return s >= 0 && s < t.pool; }
+
+}  // namespace
+
+extern "C" {
+
+rc_status rc_radix_create(int64_t pool_slots, const int32_t* free_order, rc_radix** out) {
+  if (!out) return fail(RC_ERR_ARG, "out is NULL");
+  if (pool_slots < 0 || pool_slots > INT32_MAX) return fail(RC_ERR_RANGE, "pool_slots %lld out of range", (long long)pool_slots);
+  rc_radix* t = nullptr;
+  try {
+    t = new rc_radix();
+    t->pool = pool_slots;
+    t->is_free.assign(pool_slots, 0);
+    t->in_tree.assign(pool_slots, 0);
+    if (free_order) {
+      for (int64_t i = 0; i < pool_slots; ++i) {
+        int32_t s = free_order[i];
+        if (s < 0 || s >= pool_slots || t->is_free[s]) {
+          delete t;
+          return fail(RC_ERR_ARG, "free_order is not a permutation of [0, %lld) (entry %lld = %d)", (long long)pool_slots, (long long)i, s);
+        }
+        t->is_free[s] = 1;
+        t->free_q.push_back(s);
+      }
+    } else {
+      for (int64_t i = 0; i < pool_slots; ++i) {
+        t->is_free[i] = 1;
+        t->free_q.push_back((int32_t)i);
+      }
+    }
+    t->nodes.emplace_back();  // root
+    t->st.pool_slots = pool_slots;
+  } catch (const std::bad_alloc&) {
+    delete t;
+    return fail(RC_ERR_NOMEM, "host allocation failed");
+  }
+  *out = t;
+  return RC_OK;
+}
+
+void rc_radix_destroy(rc_radix* tree) { delete tree; }
+
+rc_status rc_radix_match(rc_radix* t, const int32_t* tokens, int64_t n, int32_t* out_slots, int64_t* matched) {
+  if (!t || !matched || n < 0 || (n > 0 && !tokens)) return fail(RC_ERR_ARG, "bad argument to rc_radix_match");
+  std::vector<int32_t> touched;
+  int64_t w = 0;
+  const int64_t cap = n > 0 ? n - 1 : 0;
+  walk(*t, tokens, n, [&](int32_t id, int64_t k) {
+    touched.push_back(id);
+    const Node& c = t->nodes[id];
+    for (int64_t i = 0; i < k && w < cap; ++i, ++w)
+      if (out_slots) out_slots[w] = c.slot[i];
+  });
+  *matched = w;
+  int64_t now = ++t->clock;
+  for (int32_t id : touched) t->nodes[id].last_use = now;
+  t->st.matches++;
+  t->st.matched_tokens += w;
+  return RC_OK;
+}
+
+rc_status rc_radix_alloc(rc_radix* t, int64_t n, int32_t* out_slots) {
+  if (!t || n < 0 || (n > 0 && !out_slots)) return fail(RC_ERR_ARG, "bad argument to rc_radix_alloc");
+  if (n > (int64_t)t->free_q.size())
+    return fail(RC_ERR_NOMEM, "need %lld slots, %zu free", (long long)n, t->free_q.size());
+  for (int64_t i = 0; i < n; ++i) {
+    int32_t s = t->free_q.front();
+    t->free_q.pop_front();
+    t->is_free[s] = 0;
+    out_slots[i] = s;
+  }
+  return RC_OK;
+}
+
+rc_status rc_radix_free(rc_radix* t, const int32_t* slots, int64_t n) {
+  if (!t || n < 0 || (n > 0 && !slots)) return fail(RC_ERR_ARG, "bad argument to rc_radix_free");
+  std::vector<uint8_t> seen;
+  for (int64_t i = 0; i < n; ++i) {
+    int32_t s = slots[i];
+    if (!slot_ok(*t, s)) return fail(RC_ERR_ARG, "slot %d out of range", s);
+    if (t->is_free[s]) return fail(RC_ERR_ARG, "slot %d is already free", s);
+    if (t->in_tree[s]) return fail(RC_ERR_ARG, "slot %d is held by the tree", s);
+  }
+  // repeated entries
+  {
+    std::vector<int32_t> v(slots, slots + n);
+    std::sort(v.begin(), v.end());
+    if (std::adjacent_find(v.begin(), v.end()) != v.end()) return fail(RC_ERR_ARG, "repeated slot in free list");
+  }
+  for (int64_t i = 0; i < n; ++i) {
+    t->is_free[slots[i]] = 1;
+    t->free_q.push_back(slots[i]);
+  }
+  return RC_OK;
+}
+
+rc_status rc_radix_insert(rc_radix* t, const int32_t* tokens, int32_t* slots, int64_t n, int64_t* n_new) {
+  if (!t || n < 0 || (n > 0 && (!tokens || !slots))) return fail(RC_ERR_ARG, "bad argument to rc_radix_insert");
+  // pass 1 (read only): how much is stored already, and validate every slot
+  std::vector<int32_t> stored;
+  const int64_t m = walk(*t, tokens, n, [&](int32_t id, int64_t k) {
+    const Node& c = t->nodes[id];
+    stored.insert(stored.end(), c.slot.begin(), c.slot.begin() + k);
+  });
+  {
+    std::vector<int32_t> mine;
+    for (int64_t i = 0; i < n; ++i) {
+      int32_t s = slots[i];
+      if (!slot_ok(*t, s)) return fail(RC_ERR_ARG, "slot %d (position %lld) out of range", s, (long long)i);
+      if (i < m && s == stored[i]) continue;  // the caller already uses the stored slot
+      if (t->is_free[s]) return fail(RC_ERR_ARG, "slot %d (position %lld) is free, not allocated", s, (long long)i);
+      if (t->in_tree[s]) return fail(RC_ERR_ARG, "slot %d (position %lld) already belongs to the tree", s, (long long)i);
+      mine.push_back(s);
+    }
+    std::sort(mine.begin(), mine.end());
+    if (std::adjacent_find(mine.begin(), mine.end()) != mine.end()) return fail(RC_ERR_ARG, "repeated slot in insert");
+  }
+  try {
+    // pass 2: mutate
+    int32_t cur = 0;
+    int64_t pos = 0;
+    const int64_t now = ++t->clock;
+    while (pos < n) {
+      auto it = t->nodes[cur].kids.find(tokens[pos]);
+      if (it == t->nodes[cur].kids.end()) {
+        int32_t id = new_node(*t);
+        Node& nn = t->nodes[id];
+        nn.parent = cur;
+        nn.start = pos;
+        nn.tok.assign(tokens + pos, tokens + n);
+        nn.slot.assign(slots + pos, slots + n);
+        nn.last_use = now;
+        for (int64_t i = pos; i < n; ++i) t->in_tree[slots[i]] = 1;
+        t->nodes[cur].kids[tokens[pos]] = id;
+        t->st.nodes++;
+        t->st.cached_tokens += n - pos;
+        t->st.inserted_tokens += n - pos;
+        pos = n;
+        break;
+      }
+      int32_t c = it->second;
+      const int64_t len = (int64_t)t->nodes[c].tok.size();
+      const int64_t lim = std::min(len, n - pos);
+      int64_t k = 0;
+      while (k < lim && t->nodes[c].tok[k] == tokens[pos + k]) ++k;
+      for (int64_t i = 0; i < k; ++i) {
+        int32_t have = t->nodes[c].slot[i];
+        if (slots[pos + i] != have) {
+          t->is_free[slots[pos + i]] = 1;
+          t->free_q.push_back(slots[pos + i]);
+          t->st.duplicate_slots++;
+          slots[pos + i] = have;
+        }
+      }
+      t->nodes[c].last_use = now;
+      pos += k;
+      if (k < len) {
+        if (pos < n) {
+          int32_t u = split(*t, c, k);
+          t->nodes[u].last_use = now;
+          cur = u;
+          continue;  // next lookup adds the new leaf under u
+        }
+        break;  // the sequence ends inside this edge: nothing new to store
+      }
+      cur = c;
+    }
+    if (n_new) *n_new = n - m;
+  } catch (const std::bad_alloc&) {
+    return fail(RC_ERR_INTERNAL, "host allocation failed during insert (tree may be inconsistent)");
+  }
+  return RC_OK;
+}
+
+rc_status rc_radix_emit_rows(rc_radix* t, int32_t batch, const int32_t* tokens, const int64_t* tok_off,
+                             int32_t reserve, const int32_t* rows, int32_t* table, int32_t table_rows,
+                             int64_t stride, int32_t* prefix_lens, int32_t* extend_lens) {
+  if (!t || batch < 0 || reserve < 0 || stride <= 0 || table_rows < 0) return fail(RC_ERR_ARG, "bad argument to rc_radix_emit_rows");
+  if (batch > 0 && (!tok_off || !rows || !table || !prefix_lens || !extend_lens)) return fail(RC_ERR_ARG, "NULL array in rc_radix_emit_rows");
+  std::vector<int64_t> P(batch);
+  std::vector<std::vector<int32_t>> pre(batch);
+  std::vector<std::vector<int32_t>> touched(batch);
+  int64_t need = 0;
+  for (int32_t b = 0; b < batch; ++b) {
+    const int64_t n = tok_off[b + 1] - tok_off[b];
+    if (n < 0 || tok_off[b] < 0) return fail(RC_ERR_ARG, "tok_off not non-decreasing at %d", b);
+    if (n > 0 && !tokens) return fail(RC_ERR_ARG, "tokens is NULL");
+    if (rows[b] < 0 || rows[b] >= table_rows) return fail(RC_ERR_RANGE, "row %d of request %d outside [0, %d)", rows[b], b, table_rows);
+    if (n + reserve > stride) return fail(RC_ERR_RANGE, "request %d needs %lld table entries, stride is %lld", b, (long long)(n + reserve), (long long)stride);
+    const int64_t cap = n > 0 ? n - 1 : 0;
+    walk(*t, tokens + tok_off[b], n, [&](int32_t id, int64_t k) {
+      touched[b].push_back(id);
+      const Node& c = t->nodes[id];
+      for (int64_t i = 0; i < k && (int64_t)pre[b].size() < cap; ++i) pre[b].push_back(c.slot[i]);
+    });
+    P[b] = (int64_t)pre[b].size();
+    need += n - P[b] + reserve;
+  }
+  for (int32_t b = 0; b < batch; ++b)
+    for (int32_t b2 = 0; b2 < b; ++b2)
+      if (rows[b] == rows[b2] && batch <= 4096) return fail(RC_ERR_ARG, "requests %d and %d share table row %d", b2, b, rows[b]);
+  if (need > (int64_t)t->free_q.size())
+    return fail(RC_ERR_NOMEM, "batch needs %lld slots, %zu free", (long long)need, t->free_q.size());
+  const int64_t now = ++t->clock;
+  for (int32_t b = 0; b < batch; ++b) {
+    const int64_t n = tok_off[b + 1] - tok_off[b];
+    int32_t* row = table + (int64_t)rows[b] * stride;
+    std::copy(pre[b].begin(), pre[b].end(), row);
+    for (int64_t i = P[b]; i < n + reserve; ++i) {
+      int32_t s = t->free_q.front();
+      t->free_q.pop_front();
+      t->is_free[s] = 0;
+      row[i] = s;
+    }
+    prefix_lens[b] = (int32_t)P[b];
+    extend_lens[b] = (int32_t)(n - P[b]);
+    for (int32_t id : touched[b]) t->nodes[id].last_use = now;
+    t->st.matches++;
+    t->st.matched_tokens += P[b];
+  }
+  return RC_OK;
+}
+
+rc_status rc_radix_fork(rc_radix* t, const int32_t* tokens, const int32_t* parent_slots, int64_t n, int32_t n_children,
+                        const int32_t* child_rows, int32_t* table, int32_t table_rows, int64_t stride) {
+  if (!t || n < 0 || n_children < 0 || stride <= 0) return fail(RC_ERR_ARG, "bad argument to rc_radix_fork");
+  if (n > stride) return fail(RC_ERR_RANGE, "prefix of %lld tokens exceeds stride %lld", (long long)n, (long long)stride);
+  if (n_children > 0 && (!child_rows || !table)) return fail(RC_ERR_ARG, "NULL child rows or table");
+  for (int32_t c = 0; c < n_children; ++c)
+    if (child_rows[c] < 0 || child_rows[c] >= table_rows) return fail(RC_ERR_RANGE, "child row %d outside [0, %d)", child_rows[c], table_rows);
+  std::vector<int32_t> s(parent_slots, parent_slots + n);
+  rc_status st = rc_radix_insert(t, tokens, s.data(), n, nullptr);
+  if (st != RC_OK) return st;
+  for (int32_t c = 0; c < n_children; ++c) std::copy(s.begin(), s.end(), table + (int64_t)child_rows[c] * stride);
+  return RC_OK;
+}
+
+rc_status rc_radix_stats_get(const rc_radix* t, rc_radix_stats* out) {
+  if (!t || !out) return fail(RC_ERR_ARG, "NULL argument");
+  *out = t->st;
+  out->free_slots = (int64_t)t->free_q.size();
+  return RC_OK;
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Decode planners.
+//
+// A work item is a range of positions read through one table row, computed
+// for every member request.  Ranges shared by several requests come from tree
+// nodes; all requests passing through a node read its slots, so the item loads
+// that KV once per step for all of them.
+// ---------------------------------------------------------------------------
+namespace {
+
+struct Range {
+  int64_t begin, end;
+  std::vector<int32_t> members;
+};
+
+struct PlanBuilder {
+  int32_t batch, group, chunk, max_m;
+  const int32_t* rows;
+  std::vector<Range> ranges;
+  std::vector<std::vector<int32_t>> path;  // per request: range ids in order
+  std::vector<int32_t> item_rows;          // built items, 8 ints each
+  std::vector<int32_t> members;
+  std::vector<int32_t> nsplit;
+  int32_t shared_items = 0;
+  int64_t unique_pos = 0;
+
+  int32_t row_of(int32_t b) const { return rows ? rows[b] : b; }
+
+  void build() {
+    nsplit.assign(batch, 0);
+    // split index of each range: chunks of the ranges before it on any member's path
+    std::vector<int32_t> first_split(ranges.size(), -1);
+    for (int32_t b = 0; b < batch; ++b) {
+      int32_t acc = 0;
+      for (int32_t r : path[b]) {
+        if (first_split[r] < 0) first_split[r] = acc;
+        const int64_t len = ranges[r].end - ranges[r].begin;
+        acc += (int32_t)((len + chunk - 1) / chunk);
+      }
+      nsplit[b] = acc;
+    }
+    // items, longest member lists first (more columns = more compute per item)
+    std::vector<int32_t> order(ranges.size());
+    for (size_t i = 0; i < order.size(); ++i) order[i] = (int32_t)i;
+    std::stable_sort(order.begin(), order.end(), [&](int32_t a, int32_t b) {
+      return ranges[a].members.size() > ranges[b].members.size();
+    });
+    for (int32_t r : order) {
+      const Range& R = ranges[r];
+      if (R.end <= R.begin) continue;
+      unique_pos += R.end - R.begin;
+      int32_t sp = first_split[r];
+      for (int64_t p = R.begin; p < R.end; p += chunk, ++sp) {
+        const int64_t pe = std::min<int64_t>(p + chunk, R.end);
+        for (size_t g0 = 0; g0 < R.members.size(); g0 += max_m) {
+          const size_t cnt = std::min<size_t>(max_m, R.members.size() - g0);
+          const int32_t off = (int32_t)members.size();
+          members.insert(members.end(), R.members.begin() + g0, R.members.begin() + g0 + cnt);
+          int32_t it[RC_PLAN_ITEM] = {row_of(R.members[g0]), (int32_t)p, (int32_t)pe, sp, off, (int32_t)cnt, 0, 0};
+          item_rows.insert(item_rows.end(), it, it + RC_PLAN_ITEM);
+          if (R.members.size() > 1) shared_items++;
+        }
+      }
+    }
+  }
+
+  rc_status emit(int32_t* plan, int64_t cap, rc_plan_info* info, int64_t logical) {
+    const int32_t n_items = (int32_t)(item_rows.size() / RC_PLAN_ITEM);
+    int32_t max_splits = 0;
+    for (int32_t v : nsplit) max_splits = std::max(max_splits, v);
+    const int64_t need = RC_PLAN_HEADER + (int64_t)item_rows.size() + (int64_t)members.size() + batch;
+    info->n_items = n_items;
+    info->n_members = (int32_t)members.size();
+    info->max_splits = max_splits;
+    info->batch = batch;
+    info->group = group;
+    info->chunk = chunk;
+    info->max_cols = max_m * group;
+    info->shared_items = shared_items;
+    info->plan_ints = need;
+    info->unique_positions = unique_pos;
+    info->logical_positions = logical;
+    if (!plan || cap < need) return fail(RC_ERR_RANGE, "plan needs %lld int32, capacity %lld", (long long)need, (long long)cap);
+    int32_t hdr[RC_PLAN_HEADER] = {(int32_t)RC_PLAN_MAGIC, n_items, (int32_t)members.size(), max_splits, batch, group, chunk, max_m * group};
+    int32_t* w = plan;
+    w = std::copy(hdr, hdr + RC_PLAN_HEADER, w);
+    w = std::copy(item_rows.begin(), item_rows.end(), w);
+    w = std::copy(members.begin(), members.end(), w);
+    std::copy(nsplit.begin(), nsplit.end(), w);
+    return RC_OK;
+  }
+};
+
+rc_status plan_args(int32_t batch, const int32_t* max_seq, int32_t group, int32_t chunk, rc_plan_info* info) {
+  if (batch < 0 || !info || (batch > 0 && !max_seq)) return fail(RC_ERR_ARG, "bad planner argument");
+  if (group < 1 || group > 128) return fail(RC_ERR_SHAPE, "group %d outside [1, 128]", group);
+  if (chunk < 1) return fail(RC_ERR_ARG, "chunk must be positive");
+  for (int32_t b = 0; b < batch; ++b)
+    if (max_seq[b] < 1) return fail(RC_ERR_RANGE, "max_seq_lens[%d] = %d < 1", b, max_seq[b]);
+  return RC_OK;
+}
+
+}  // namespace
+
+extern "C" rc_status rc_plan_decode_unshared(int32_t batch, const int32_t* rows, const int32_t* max_seq, int32_t group,
+                                             int32_t chunk, int32_t* plan, int64_t cap, rc_plan_info* info) {
+  rc_status st = plan_args(batch, max_seq, group, chunk, info);
+  if (st != RC_OK) return st;
+  PlanBuilder pb{batch, group, chunk, std::max(1, 128 / group), rows, {}, {}, {}, {}, {}};
+  pb.path.resize(batch);
+  int64_t logical = 0;
+  for (int32_t b = 0; b < batch; ++b) {
+    pb.ranges.push_back(Range{0, max_seq[b], {b}});
+    pb.path[b].push_back((int32_t)pb.ranges.size() - 1);
+    logical += max_seq[b];
+  }
+  pb.build();
+  return pb.emit(plan, cap, info, logical);
+}
+
+extern "C" rc_status rc_radix_plan_decode(rc_radix* t, int32_t batch, const int32_t* tokens, const int64_t* tok_off,
+                                          const int32_t* rows, const int32_t* max_seq, int32_t group, int32_t chunk,
+                                          int32_t* plan, int64_t cap, rc_plan_info* info) {
+  if (!t) return fail(RC_ERR_ARG, "tree is NULL");
+  rc_status st = plan_args(batch, max_seq, group, chunk, info);
+  if (st != RC_OK) return st;
+  if (batch > 0 && !tok_off) return fail(RC_ERR_ARG, "tok_off is NULL");
+  // walk every request; per node, the members and how far into the node each goes
+  struct Visit { int32_t node; int64_t end; };
+  std::vector<std::vector<Visit>> walks(batch);
+  std::unordered_map<int32_t, std::vector<std::pair<int64_t, int32_t>>> by_node;  // node -> (end, b)
+  std::vector<int64_t> walked(batch);
+  for (int32_t b = 0; b < batch; ++b) {
+    const int64_t n = tok_off[b + 1] - tok_off[b];
+    if (n < 0) return fail(RC_ERR_ARG, "tok_off not non-decreasing at %d", b);
+    if (n > 0 && !tokens) return fail(RC_ERR_ARG, "tokens is NULL");
+    walked[b] = walk(*t, tokens + tok_off[b], n, [&](int32_t id, int64_t k) {
+      const int64_t e = t->nodes[id].start + k;
+      walks[b].push_back({id, e});
+      by_node[id].push_back({e, b});
+    });
+    if (max_seq[b] < walked[b]) return fail(RC_ERR_RANGE, "max_seq_lens[%d] = %d shorter than its cached prefix %lld", b, max_seq[b], (long long)walked[b]);
+  }
+  PlanBuilder pb{batch, group, chunk, std::max(1, 128 / group), rows, {}, {}, {}, {}, {}};
+  pb.path.resize(batch);
+  // node -> list of (sub-range id, sub-range end); members of a sub-range reach at least its end
+  std::unordered_map<int32_t, std::vector<std::pair<int32_t, int64_t>>> subs;
+  for (auto& kv : by_node) {
+    auto v = kv.second;
+    std::sort(v.begin(), v.end());
+    int64_t prev = t->nodes[kv.first].start;
+    size_t i = 0;
+    auto& out = subs[kv.first];
+    while (i < v.size()) {
+      const int64_t e = v[i].first;
+      if (e > prev) {
+        Range R{prev, e, {}};
+        for (size_t j = i; j < v.size(); ++j) R.members.push_back(v[j].second);
+        std::sort(R.members.begin(), R.members.end());
+        pb.ranges.push_back(std::move(R));
+        out.push_back({(int32_t)pb.ranges.size() - 1, e});
+        prev = e;
+      }
+      while (i < v.size() && v[i].first == e) ++i;
+    }
+  }
+  const size_t n_node_ranges = pb.ranges.size();
+  int64_t logical = 0;
+  for (int32_t b = 0; b < batch; ++b) {
+    logical += max_seq[b];
+    // shared part of the path, then everything this request alone reads as one range
+    int64_t own_begin = 0;
+    bool own = false;
+    for (const Visit& v : walks[b]) {
+      for (auto& sr : subs[v.node]) {
+        if (sr.second > v.end) break;
+        const Range& R = pb.ranges[sr.first];
+        if (R.members.size() > 1) {
+          pb.path[b].push_back(sr.first);
+          own_begin = R.end;
+        } else {
+          own = true;
+          break;
+        }
+      }
+      if (own) break;
+    }
+    if (max_seq[b] > own_begin) {
+      pb.ranges.push_back(Range{own_begin, max_seq[b], {b}});
+      pb.path[b].push_back((int32_t)pb.ranges.size() - 1);
+    }
+  }
+  // drop the single-member node ranges: each request's own range covers them
+  for (size_t r = 0; r < n_node_ranges; ++r)
+    if (pb.ranges[r].members.size() == 1) pb.ranges[r].end = pb.ranges[r].begin;
+  pb.build();
+  return pb.emit(plan, cap, info, logical);
+}

@@ -1,0 +1,94 @@
+// Kernel timing with HIP events and the device error word.
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "hip_common.h"
+
+namespace rc {
+
+static int32_t* g_err_word = nullptr;
+int32_t* error_word() { return g_err_word; }
+
+namespace {
+struct Rec {
+  const char* name;
+  hipEvent_t a, b;
+};
+bool g_on = false;
+std::vector<Rec> g_recs;
+std::vector<hipEvent_t> g_pool;
+
+hipEvent_t get_event() {
+  if (!g_pool.empty()) {
+    hipEvent_t e = g_pool.back();
+    g_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+}  // namespace
+
+ProfScope::ProfScope(const char* name, hipStream_t stream) : stream_(stream) {
+  if (!g_on) return;
+  hipEvent_t a = get_event(), b = get_event();
+  if (!a || !b) return;
+  hipEventRecord(a, stream);
+  g_recs.push_back({name, a, b});
+  idx_ = (int)g_recs.size() - 1;
+}
+
+ProfScope::~ProfScope() {
+  if (idx_ >= 0) hipEventRecord(g_recs[idx_].b, stream_);
+}
+
+rc_status check_launch(const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(RC_ERR_HIP, "%s launch failed: %s", what, hipGetErrorString(e));
+  return RC_OK;
+}
+
+}  // namespace rc
+
+extern "C" rc_status rc_set_error_word(int32_t* device_word) {
+  rc::g_err_word = device_word;
+  return RC_OK;
+}
+
+extern "C" rc_status rc_prof_enable(int32_t on) {
+  rc::g_on = on != 0;
+  return RC_OK;
+}
+
+extern "C" rc_status rc_prof_collect(rc_prof_entry* out, int32_t capacity, int32_t* n_out) {
+  using namespace rc;
+  if (!n_out || capacity < 0 || (capacity > 0 && !out)) return fail(RC_ERR_ARG, "bad argument to rc_prof_collect");
+  std::vector<rc_prof_entry> agg;
+  rc_status st = RC_OK;
+  for (auto& r : g_recs) {
+    float ms = 0.f;
+    if (hipEventSynchronize(r.b) != hipSuccess || hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess) {
+      st = fail(RC_ERR_HIP, "event timing failed for %s", r.name);
+      ms = 0.f;
+    }
+    size_t i = 0;
+    for (; i < agg.size(); ++i)
+      if (!strncmp(agg[i].name, r.name, sizeof(agg[i].name))) break;
+    if (i == agg.size()) {
+      rc_prof_entry e{};
+      strncpy(e.name, r.name, sizeof(e.name) - 1);
+      agg.push_back(e);
+    }
+    agg[i].launches++;
+    agg[i].total_ms += ms;
+    g_pool.push_back(r.a);
+    g_pool.push_back(r.b);
+  }
+  g_recs.clear();
+  int32_t n = (int32_t)agg.size();
+  for (int32_t i = 0; i < n && i < capacity; ++i) out[i] = agg[i];
+  *n_out = n;
+  return st;
+}

@@ -1,0 +1,197 @@
+"""Host-side sequencing of the hot path for one attention layer.
+
+Owns the KV pool (two device tensors), the request->slot table (host copy and
+device copy) and the radix tree.  Each method issues library calls only: the
+tree and planners run in the C++ host library, K/V movement and attention in
+the HIP kernels.  Host->device copies of integer metadata (table rows, slot
+lists, lengths, plans) are the only other device traffic.
+
+Flow of one batch ("Prompt Caching" glossary, GPT-2 example; SGLang summary,
+RadixAttention and `fork`):
+  schedule   longest cached prefix per request, slots for the new tokens and
+             for the decode steps, table rows            (host, C++)
+  extend     store new K/V in the pool, attend            (kv_store, extend)
+  commit     insert prompts into the tree; rows get the tree's slots
+  prepare_decode  share plan from the tree (who reads which node), per-step
+             slot and length tables uploaded once
+  decode_step  store the token's K/V, split-K attention over shared nodes,
+             merge                                        (kv_store, decode)
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import List, Optional, Sequence
+
+import numpy as np
+import torch
+
+from . import api
+from .api import DecodePlan, KVShape, RadixTree
+
+
+@dataclasses.dataclass
+class Batch:
+    tokens: List[np.ndarray]
+    rows: np.ndarray           # table row of each request
+    prefix_lens: np.ndarray    # P_b
+    extend_lens: np.ndarray    # E_b
+    reserve: int
+    dev: dict = dataclasses.field(default_factory=dict)
+
+    @property
+    def size(self) -> int:
+        return len(self.tokens)
+
+    @property
+    def total_extend(self) -> int:
+        return int(self.extend_lens.sum())
+
+
+@dataclasses.dataclass
+class DecodeState:
+    plan: DecodePlan
+    base_lens: np.ndarray      # position of decode step 0 per request
+    n_steps: int
+    slots: torch.Tensor        # [n_steps, B] int32: slot of each step's token
+    seq_lens: torch.Tensor     # [n_steps, B] int32: keys attended at each step
+    workspace: torch.Tensor
+
+
+class Engine:
+    def __init__(self, shape: KVShape, stride: int, max_rows: int, device="cuda",
+                 free_order: Optional[np.ndarray] = None, k_pool: Optional[torch.Tensor] = None,
+                 v_pool: Optional[torch.Tensor] = None):
+        self.shape = shape
+        self.device = torch.device(device)
+        S, H, D = shape.pool_slots, shape.num_kv_heads, shape.head_dim
+        self.k_pool = k_pool if k_pool is not None else torch.zeros((S, H, D), dtype=shape.dtype, device=self.device)
+        self.v_pool = v_pool if v_pool is not None else torch.zeros((S, H, D), dtype=shape.dtype, device=self.device)
+        self.tree = RadixTree(S, free_order)
+        self.stride = stride
+        self.table_h = np.full((max_rows, stride), -1, np.int32)
+        self.table_d = torch.full((max_rows, stride), -1, dtype=torch.int32, device=self.device)
+        self.free_rows = list(range(max_rows))
+
+    # -- helpers ------------------------------------------------------------
+    def _i32(self, a) -> torch.Tensor:
+        return torch.from_numpy(np.ascontiguousarray(a, np.int32)).to(self.device, non_blocking=False)
+
+    def _upload_rows(self, rows: np.ndarray) -> None:
+        if len(rows) == 0:
+            return
+        r = np.asarray(rows, np.int64)
+        if np.all(np.diff(r) == 1):
+            self.table_d[int(r[0]):int(r[-1]) + 1].copy_(torch.from_numpy(self.table_h[int(r[0]):int(r[-1]) + 1]))
+        else:
+            self.table_d[torch.from_numpy(r).to(self.device)] = torch.from_numpy(self.table_h[r]).to(self.device)
+
+    # -- cache population (a sequence whose K/V are already known) -----------
+    def populate(self, tokens: Sequence[int], k: torch.Tensor, v: torch.Tensor, expect_cached: Optional[int] = None) -> int:
+        """Store K/V for the uncached tail of `tokens` and insert the sequence.
+        k, v hold rows for positions [cached, n).  Returns the cached length found."""
+        t = np.ascontiguousarray(tokens, np.int32)
+        probe = np.concatenate([t, np.array([-1], np.int32)])  # no stored edge starts with -1: full match allowed
+        m, pre = self.tree.match(probe)
+        if expect_cached is not None and m != expect_cached:
+            raise RuntimeError(f"expected {expect_cached} cached tokens, found {m}")
+        n_new = len(t) - m
+        if k.shape[0] != n_new or v.shape[0] != n_new:
+            raise ValueError(f"need K/V for {n_new} uncached tokens, got {k.shape[0]}")
+        new = self.tree.alloc(n_new)
+        if n_new:
+            api.kv_store(self.shape, self.k_pool, self.v_pool, k, v, self._i32(new))
+        self.tree.insert(t, np.concatenate([pre, new]).astype(np.int32))
+        return m
+
+    # -- a batch of requests --------------------------------------------------
+    def schedule(self, batch_tokens: Sequence[Sequence[int]], reserve: int = 0) -> Batch:
+        B = len(batch_tokens)
+        if B > len(self.free_rows):
+            raise RuntimeError("no free table rows")
+        rows = np.array(self.free_rows[:B], np.int32)
+        toks = [np.ascontiguousarray(t, np.int32) for t in batch_tokens]
+        P, E = self.tree.emit_rows(toks, self.table_h, rows=rows, reserve=reserve)
+        del self.free_rows[:B]
+        self._upload_rows(rows)
+        b = Batch(toks, rows, P, E, reserve)
+        start = np.zeros(B, np.int32)
+        if B:
+            start[1:] = np.cumsum(E)[:-1]
+        b.dev = {"rows": self._i32(rows), "P": self._i32(P), "E": self._i32(E), "start": self._i32(start)}
+        return b
+
+    def new_token_slots(self, b: Batch) -> np.ndarray:
+        return np.concatenate([self.table_h[r, p:p + e] for r, p, e in zip(b.rows, b.prefix_lens, b.extend_lens)]
+                              ).astype(np.int32)
+
+    def extend(self, b: Batch, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, sm_scale: float,
+               o: Optional[torch.Tensor] = None, store: bool = True) -> torch.Tensor:
+        """Store the new tokens' K/V in their slots, then attend (new tokens over prefix + themselves)."""
+        T = b.total_extend
+        if q.shape[0] != T:
+            raise ValueError(f"q has {q.shape[0]} rows, the batch has {T} new tokens")
+        if store:
+            if "slots" not in b.dev:
+                b.dev["slots"] = self._i32(self.new_token_slots(b))
+            api.kv_store(self.shape, self.k_pool, self.v_pool, k_new, v_new, b.dev["slots"])
+        if o is None:
+            o = torch.empty_like(q)
+        api.extend_attention(self.shape, o, q, k_new, v_new, self.k_pool, self.v_pool, self.table_d, b.dev["P"],
+                             b.dev["E"], b.dev["start"], int(b.extend_lens.max()) if b.size else 0, sm_scale,
+                             rows=b.dev["rows"])
+        return o
+
+    def commit(self, b: Batch, lengths: Optional[Sequence[int]] = None) -> None:
+        """Insert each request's first `lengths[i]` tokens (default: all) into the tree.
+        Where the tree already held them, the row is rewritten to the tree's slots."""
+        dirty = []
+        for i, (t, r) in enumerate(zip(b.tokens, b.rows)):
+            n = len(t) if lengths is None else int(lengths[i])
+            canon, _ = self.tree.insert(t[:n], self.table_h[r, :n])
+            if not np.array_equal(canon, self.table_h[r, :n]):
+                self.table_h[r, :n] = canon
+                dirty.append(r)
+        self._upload_rows(np.array(sorted(dirty), np.int32))
+
+    def prepare_decode(self, b: Batch, base_lens: Sequence[int], n_steps: int, chunk: int = 512,
+                       shared: bool = True, committed: Optional[Sequence[int]] = None) -> DecodeState:
+        """Plan decode steps t = 0..n_steps-1; step t's token sits at position base_lens[i] + t.
+        `committed[i]` tokens of request i are in the tree (default: base_lens)."""
+        base = np.asarray(base_lens, np.int32)
+        if np.any(base + n_steps > np.array([len(t) for t in b.tokens]) + b.reserve):
+            raise ValueError("decode steps run past the reserved slots")
+        max_seq = base + n_steps
+        g = self.shape.group
+        com = base if committed is None else np.asarray(committed, np.int32)
+        if shared:
+            plan = self.tree.plan_decode([t[:c] for t, c in zip(b.tokens, com)], max_seq, g, chunk, rows=b.rows)
+        else:
+            plan = api.plan_decode_unshared(max_seq, g, chunk, rows=b.rows)
+        plan.to(self.device)
+        steps = np.arange(n_steps, dtype=np.int32)[:, None]
+        pos = base[None, :] + steps                                    # [T, B]
+        slots = self.table_h[b.rows[None, :].repeat(n_steps, 0), pos]  # [T, B]
+        seq = pos + 1
+        ws = torch.empty(api.decode_workspace_bytes(self.shape, plan), dtype=torch.uint8, device=self.device)
+        return DecodeState(plan, base, n_steps, self._i32(slots), self._i32(seq), ws)
+
+    def decode_step(self, st: DecodeState, t: int, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                    sm_scale: float, o: Optional[torch.Tensor] = None) -> torch.Tensor:
+        """Store step t's K/V, then attend over each request's whole context."""
+        api.kv_store(self.shape, self.k_pool, self.v_pool, k, v, st.slots[t])
+        if o is None:
+            o = torch.empty_like(q)
+        api.decode_attention(self.shape, o, q, self.k_pool, self.v_pool, self.table_d, st.seq_lens[t], st.plan,
+                             sm_scale, st.workspace)
+        return o
+
+    def release(self, b: Batch, keep: Optional[Sequence[int]] = None) -> None:
+        """Return the batch's table rows; slots past `keep[i]` (default: tokens given) go back to the pool
+        unless the tree holds them."""
+        for i, (t, r) in enumerate(zip(b.tokens, b.rows)):
+            n = len(t) if keep is None else int(keep[i])
+            tail = self.table_h[r, n:len(t) + b.reserve]
+            if tail.size:
+                self.tree.free(tail)
+            self.table_h[r, :] = -1
+            self.free_rows.append(int(r))

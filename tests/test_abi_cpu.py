@@ -1,0 +1,124 @@
+"""The C ABI on the CPU: the library loads, exports every function rc.h
+declares, and rejects bad arguments with the documented status before
+launching anything (so no GPU is needed)."""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+from prefix_shared_kv_amd import _native as N
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "rc.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(rc_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert len(names) >= 20
+    for n in names:
+        assert hasattr(N.lib, n), n
+    assert set(names) == set(N._SIGS), "binding and header disagree"
+
+
+def test_version():
+    assert "gfx950" in N.lib.rc_version().decode()
+
+
+def shape(dtype=N.RC_BF16, hq=8, hkv=2, d=128, slots=16):
+    return N.RcShape(dtype, hq, hkv, d, slots)
+
+
+FAKE = C.c_void_p(0x1000)  # never dereferenced: validation fails first, or n == 0
+
+
+@pytest.mark.parametrize("sh,code", [
+    (shape(dtype=7), N.RC_ERR_DTYPE),
+    (shape(d=96), N.RC_ERR_SHAPE),
+    (shape(hq=6, hkv=4), N.RC_ERR_SHAPE),
+    (shape(hq=0), N.RC_ERR_SHAPE),
+    (shape(hq=512, hkv=2), N.RC_ERR_SHAPE),
+])
+def test_kv_store_rejects_bad_shapes(sh, code):
+    st = N.lib.rc_kv_store(C.byref(sh), FAKE, FAKE, FAKE, FAKE, FAKE, 4, None)
+    assert st == code
+    assert N.last_error()
+
+
+def test_kv_store_argument_checks():
+    sh = shape()
+    assert N.lib.rc_kv_store(None, FAKE, FAKE, FAKE, FAKE, FAKE, 4, None) == N.RC_ERR_ARG
+    assert N.lib.rc_kv_store(C.byref(sh), FAKE, FAKE, FAKE, FAKE, FAKE, -1, None) == N.RC_ERR_ARG
+    assert N.lib.rc_kv_store(C.byref(sh), None, FAKE, FAKE, FAKE, FAKE, 4, None) == N.RC_ERR_ARG
+    assert N.lib.rc_kv_store(C.byref(sh), FAKE, FAKE, FAKE, FAKE, FAKE, 0, None) == N.RC_OK  # nothing to do
+
+
+def test_extend_argument_checks():
+    sh = shape()
+    args = [C.byref(sh), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 64, None, FAKE, FAKE, FAKE]
+    assert N.lib.rc_extend_attention(*args, -1, 10, 8, 0.1, None) == N.RC_ERR_ARG
+    assert N.lib.rc_extend_attention(*args, 2, 10, 8, float("nan"), None) == N.RC_ERR_ARG
+    assert N.lib.rc_extend_attention(*args, 0, 0, 0, 0.1, None) == N.RC_OK
+    bad = list(args)
+    bad[1] = None
+    assert N.lib.rc_extend_attention(*bad, 2, 10, 8, 0.1, None) == N.RC_ERR_ARG
+    bad = list(args)
+    bad[9] = 0  # stride
+    assert N.lib.rc_extend_attention(*bad, 2, 10, 8, 0.1, None) == N.RC_ERR_ARG
+
+
+def _plan(max_seq, group, chunk=64):
+    info = N.RcPlanInfo()
+    ms = np.ascontiguousarray(max_seq, np.int32)
+    st = N.lib.rc_plan_decode_unshared(ms.size, None, ms.ctypes.data_as(C.c_void_p), group, chunk, None, 0, C.byref(info))
+    assert st == N.RC_ERR_RANGE and info.plan_ints > 0
+    buf = np.zeros(info.plan_ints, np.int32)
+    N.check(N.lib.rc_plan_decode_unshared(ms.size, None, ms.ctypes.data_as(C.c_void_p), group, chunk,
+                                          buf.ctypes.data_as(C.c_void_p), buf.size, C.byref(info)))
+    return buf, info
+
+
+def test_decode_argument_checks():
+    sh = shape()  # group 4
+    buf, info = _plan([100, 70], 4)
+    need = N.lib.rc_decode_workspace_bytes(C.byref(sh), C.byref(info))
+    assert need == 2 * 8 * info.max_splits * (128 + 2) * 4
+
+    def call(sh_, batch, ws):
+        return N.lib.rc_decode_attention(C.byref(sh_), FAKE, FAKE, FAKE, FAKE, FAKE, 2, 128, FAKE, batch, FAKE,
+                                         C.byref(info), 0.1, FAKE, ws, None)
+
+    assert call(sh, 2, need - 1) == N.RC_ERR_RANGE
+    assert call(sh, 3, need) == N.RC_ERR_ARG  # plan built for batch 2
+    assert call(shape(hq=8, hkv=8), 2, need) == N.RC_ERR_SHAPE  # plan built for group 4
+    assert call(sh, 0, need) == N.RC_OK
+
+
+def test_unshared_plan_layout():
+    buf, info = _plan([100, 70, 1], 4, chunk=64)
+    assert buf[0] == N.RC_PLAN_MAGIC
+    assert info.n_items == 2 + 2 + 1
+    assert info.max_splits == 2
+    items = buf[8:8 + 8 * info.n_items].reshape(-1, 8)
+    cover = {}
+    for rep, pb, pe, sp, mo, mc, _, _ in items:
+        assert mc == 1
+        b = buf[8 + 8 * info.n_items + mo]
+        cover.setdefault(int(b), []).append((int(pb), int(pe), int(sp)))
+    assert sorted(cover[0]) == [(0, 64, 0), (64, 100, 1)]
+    assert sorted(cover[1]) == [(0, 64, 0), (64, 70, 1)]
+    assert sorted(cover[2]) == [(0, 1, 0)]
+    nsplit = buf[8 + 8 * info.n_items + info.n_members:]
+    assert nsplit.tolist() == [2, 2, 1]
+
+
+def test_error_text_is_thread_local_and_set():
+    sh = shape(d=96)
+    N.lib.rc_kv_store(C.byref(sh), FAKE, FAKE, FAKE, FAKE, FAKE, 4, None)
+    assert "head_dim" in N.last_error()

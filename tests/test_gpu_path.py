@@ -1,0 +1,213 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Bars: KV scatter bit-exact over the whole pool; attention within max-abs 1e-4
+for fp32 inputs and 2e-2 for bf16 inputs of the float64 oracle."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import attention as A
+from prefix_shared_kv_amd import KVShape, api
+from synth import drive
+from synth import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+DT = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+
+def host(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def check(got, want, tol, what):
+    err = float(np.max(np.abs(got - want))) if got.size else 0.0
+    assert err <= tol, f"{what}: max abs error {err:.3e} > {tol}"
+    return err
+
+
+# ---------------------------------------------------------------- KV scatter
+@pytest.mark.parametrize("dtype,H,D", [("bf16", 8, 128), ("f32", 4, 64), ("bf16", 12, 64)])
+def test_kv_store_bit_exact_whole_pool(gpu, dtype, H, D):
+    S, n = 1000, 333
+    g = np.random.default_rng(0)
+    shape = KVShape(H, H, D, DT[dtype], S)
+    pool_k = torch.randn(S, H, D, device=gpu).to(DT[dtype])
+    pool_v = torch.randn(S, H, D, device=gpu).to(DT[dtype])
+    new_k = torch.randn(n, H, D, device=gpu).to(DT[dtype])
+    new_v = torch.randn(n, H, D, device=gpu).to(DT[dtype])
+    slots = g.choice(S, n, replace=False).astype(np.int32)
+    ibits = torch.int16 if dtype == "bf16" else torch.int32
+    before_k, before_v = pool_k.view(ibits).cpu().numpy(), pool_v.view(ibits).cpu().numpy()
+    api.kv_store(shape, pool_k, pool_v, new_k, new_v, torch.from_numpy(slots).to(gpu))
+    torch.cuda.synchronize()
+    want_k = A.kv_store(before_k, new_k.view(ibits).cpu().numpy(), slots)
+    want_v = A.kv_store(before_v, new_v.view(ibits).cpu().numpy(), slots)
+    assert np.array_equal(pool_k.view(ibits).cpu().numpy(), want_k)
+    assert np.array_equal(pool_v.view(ibits).cpu().numpy(), want_v)
+
+
+def test_kv_store_flags_out_of_range_slot(gpu):
+    shape = KVShape(2, 2, 64, torch.bfloat16, 8)
+    pool = torch.zeros(8, 2, 64, device=gpu, dtype=torch.bfloat16)
+    pool_v = torch.zeros_like(pool)
+    new = torch.ones(2, 2, 64, device=gpu, dtype=torch.bfloat16)
+    err = torch.zeros(1, dtype=torch.int32, device=gpu)
+    api.set_error_word(err)
+    try:
+        api.kv_store(shape, pool, pool_v, new, new, torch.tensor([3, 8], dtype=torch.int32, device=gpu))
+        torch.cuda.synchronize()
+    finally:
+        api.set_error_word(None)
+    assert int(err.item()) & 1
+    assert float(pool[3].float().sum()) == 128.0 and float(pool.float().sum()) == 128.0
+
+
+# ---------------------------------------------------------------- extend, direct API
+def _extend_case(gpu, dtype, Hq, Hkv, D, P_list, E_list, seed=0, shuffled=True):
+    g = np.random.default_rng(seed)
+    B = len(P_list)
+    S = sum(P_list) + 64
+    shape = KVShape(Hq, Hkv, D, DT[dtype], S)
+    std = 1.0
+
+    def rnd(*s):
+        x = g.standard_normal(s).astype(np.float32) * std
+        return W.round_bf16(x) if dtype == "bf16" else x
+
+    pk = [rnd(p, Hkv, D) for p in P_list]
+    pv = [rnd(p, Hkv, D) for p in P_list]
+    T = sum(E_list)
+    q, kn, vn = rnd(T, Hq, D), rnd(T, Hkv, D), rnd(T, Hkv, D)
+    order = g.permutation(S).astype(np.int32) if shuffled else np.arange(S, dtype=np.int32)
+    stride = max(P_list) + 3
+    table = np.full((B + 2, stride), -1, np.int32)
+    pool_k = torch.zeros(S, Hkv, D, device=gpu, dtype=DT[dtype])
+    pool_v = torch.zeros_like(pool_k)
+    used = 0
+    rows = (np.arange(B) + 1).astype(np.int32)  # not the identity mapping
+    for b, p in enumerate(P_list):
+        sl = order[used:used + p]
+        used += p
+        table[rows[b], :p] = sl
+        if p:
+            idx = torch.from_numpy(sl.astype(np.int64)).to(gpu)
+            pool_k[idx] = torch.from_numpy(pk[b]).to(gpu).to(DT[dtype])
+            pool_v[idx] = torch.from_numpy(pv[b]).to(gpu).to(DT[dtype])
+    start = np.concatenate([[0], np.cumsum(E_list)[:-1]]).astype(np.int32)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(gpu)
+    to = lambda a: torch.from_numpy(a).to(gpu).to(DT[dtype])
+    o = torch.full((T, Hq, D), 7.0, device=gpu, dtype=DT[dtype])
+    err = torch.zeros(1, dtype=torch.int32, device=gpu)
+    api.set_error_word(err)
+    try:
+        api.extend_attention(shape, o, to(q), to(kn), to(vn), pool_k, pool_v, dev(table),
+                             dev(np.array(P_list, np.int32)), dev(np.array(E_list, np.int32)), dev(start),
+                             max(E_list) if E_list else 0, 1.0 / np.sqrt(D), rows=dev(rows))
+        torch.cuda.synchronize()
+    finally:
+        api.set_error_word(None)
+    assert int(err.item()) == 0
+    got = host(o)
+    worst = 0.0
+    for b in range(B):
+        E = E_list[b]
+        if E == 0:
+            continue
+        s0 = start[b]
+        K = np.concatenate([pk[b], kn[s0:s0 + E]])
+        V = np.concatenate([pv[b], vn[s0:s0 + E]])
+        want = A.extend(q[s0:s0 + E], K, V, P_list[b], 1.0 / np.sqrt(D))
+        worst = max(worst, check(got[s0:s0 + E], want, TOL[dtype], f"request {b} (P={P_list[b]}, E={E})"))
+    return worst
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("Hq,Hkv,D", [(4, 4, 64), (8, 2, 128), (32, 8, 128), (16, 1, 64), (12, 4, 128), (24, 3, 64)])
+def test_extend_ragged_against_oracle(gpu, dtype, Hq, Hkv, D):
+    P_list = [0, 1, 63, 64, 130, 300, 5]
+    E_list = [70, 1, 65, 0, 33, 129, 8]
+    _extend_case(gpu, dtype, Hq, Hkv, D, P_list, E_list, seed=Hq * 100 + D)
+
+
+def test_extend_single_token_prefill_is_value(gpu):
+    # first token of an empty-prefix prefill sees only itself: o = v (after bf16 rounding of v: exact)
+    _extend_case(gpu, "bf16", 8, 8, 128, [0], [1])
+
+
+# ---------------------------------------------------------------- whole workloads
+def _run_workload(gpu, w, shared=True, chunk=512, decode_steps=None):
+    tol = TOL[w.shape.dtype]
+    eng = drive.make_engine(w, device=gpu)
+    errs = []
+    outs = drive.prefill_nodes(eng, w, device=gpu)
+    for nid, o in outs.items():
+        k, v = w.node_kv(nid)
+        want = A.extend(w.node_prefill_q(nid), k, v, 0, w.sm_scale)
+        errs.append(check(host(o), want, tol, f"prefill node {nid}"))
+    rest = [n for n in drive.node_order(w) if n not in w.prefill_nodes]
+    drive.populate(eng, w, rest, device=gpu)
+    rids = list(range(len(w.requests)))
+    has_ext = any(len(r.ext_tokens) for r in w.requests)
+    if has_ext:
+        b, o = drive.extend_requests(eng, w, rids, device=gpu)
+        got = host(o)
+        s = 0
+        for i in rids:
+            q, _, _ = w.ext_qkv(i)
+            K, V = w.context_kv(i, 0)
+            P = len(w.prefix_tokens(w.requests[i]))
+            want = A.extend(q, K, V, P, w.sm_scale)
+            errs.append(check(got[s:s + len(q)], want, tol, f"extend request {i}"))
+            s += len(q)
+        base = [len(w.prompt_tokens(w.requests[i])) for i in rids]
+    else:
+        b = drive.schedule_decode_only(eng, w, rids)
+        base = [len(w.prompt_tokens(w.requests[i])) for i in rids]
+    n_steps = decode_steps if decode_steps is not None else max(r.n_decode for r in w.requests)
+    if n_steps:
+        st = eng.prepare_decode(b, base, n_steps, chunk=chunk, shared=shared)
+        for t in range(n_steps):
+            q, k, v = drive.decode_inputs(w, rids, t, device=gpu)
+            o = host(eng.decode_step(st, t, q, k, v, w.sm_scale))
+            for j, i in enumerate(rids):
+                K, V = w.context_kv(i, t + 1)
+                want = A.decode(w.dec_qkv(i, t)[0], K, V, w.sm_scale)
+                errs.append(check(o[j], want, tol, f"decode step {t} request {i}"))
+    return eng, b, max(errs)
+
+
+def test_tiny_fp32_workload(gpu):
+    _run_workload(gpu, W.tiny_fp32())
+
+
+@pytest.mark.parametrize("shared,chunk", [(True, 512), (False, 512), (True, 64), (False, 4096)])
+def test_gpt2_system_prompt_workload(gpu, shared, chunk):
+    w = W.gpt2_system_prompt()
+    eng, b, err = _run_workload(gpu, w, shared=shared, chunk=chunk)
+    # the glossary's bookkeeping: 8 of 417 and 7 of 416 tokens computed
+    assert [(int(e), int(p + e)) for p, e in zip(b.prefix_lens, b.extend_lens)] == [(8, 417), (7, 416)]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_small_radix_tree_workload_shared_vs_unshared(gpu, dtype):
+    w = W.multi_turn_tree(depth=3, fanout=3, seg_lo=5, seg_hi=90, ext=9, n_decode=3)
+    if dtype == "f32":
+        w.shape.dtype = "f32"
+    for shared, chunk in [(True, 32), (True, 4096), (False, 64)]:
+        _run_workload(gpu, w, shared=shared, chunk=chunk)
+
+
+def test_decode_is_deterministic(gpu):
+    w = W.few_shot(n_req=6, prefix=200, ext=5, n_decode=2)
+    outs = []
+    for _ in range(2):
+        eng = drive.make_engine(w, device=gpu)
+        drive.prefill_nodes(eng, w, device=gpu)
+        b, o = drive.extend_requests(eng, w, device=gpu)
+        st = eng.prepare_decode(b, [len(w.prompt_tokens(r)) for r in w.requests], 2, chunk=64)
+        q, k, v = drive.decode_inputs(w, range(6), 0, device=gpu)
+        d = eng.decode_step(st, 0, q, k, v, w.sm_scale)
+        outs.append((o.view(torch.int16).cpu(), d.view(torch.int16).cpu()))
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])

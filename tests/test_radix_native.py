@@ -1,0 +1,150 @@
+"""The C++ radix tree and slot allocator against the brute-force model in
+oracle/radix_ref.py: matched lengths, slot lists, table rows and the free
+list must agree exactly on random operation sequences.  Tree shapes may
+differ; only observable outputs are compared."""
+import numpy as np
+import pytest
+from hypothesis import HealthCheck, given, settings
+from hypothesis import strategies as st
+
+from oracle.radix_ref import OutOfSlots, RadixRef
+from prefix_shared_kv_amd import RadixTree, RcError
+from prefix_shared_kv_amd import _native as N
+
+
+def _seq(draw, base, vocab):
+    # sequences built from a few shared stems so prefixes collide often
+    stem = draw(st.sampled_from(base))
+    tail = draw(st.lists(st.integers(0, vocab - 1), min_size=0, max_size=6))
+    cut = draw(st.integers(0, len(stem)))
+    return stem[:cut] + tail
+
+
+@st.composite
+def scenarios(draw):
+    vocab = draw(st.sampled_from([3, 5, 50]))
+    base = [draw(st.lists(st.integers(0, vocab - 1), min_size=1, max_size=10)) for _ in range(3)]
+    ops = []
+    for _ in range(draw(st.integers(1, 25))):
+        kind = draw(st.sampled_from(["match", "emit_insert", "emit_insert", "alloc_free"]))
+        if kind == "emit_insert":
+            batch = [_seq(draw, base, vocab) or [0] for _ in range(draw(st.integers(1, 3)))]
+            reserve = draw(st.integers(0, 2))
+            ops.append((kind, batch, reserve))
+        elif kind == "match":
+            ops.append((kind, _seq(draw, base, vocab)))
+        else:
+            ops.append((kind, draw(st.integers(0, 4))))
+    perm = draw(st.booleans())
+    return ops, perm
+
+
+@settings(max_examples=150, deadline=None, suppress_health_check=[HealthCheck.too_slow])
+@given(scenarios())
+def test_tree_matches_bruteforce(sc):
+    ops, perm = sc
+    S = 120
+    order = np.random.default_rng(len(ops)).permutation(S).astype(np.int32) if perm else None
+    tree, ref = RadixTree(S, order), RadixRef(S, order)
+    table = np.full((4, 64), -1, np.int32)
+    for op in ops:
+        if op[0] == "match":
+            got = tree.match(op[1])
+            want = ref.match(op[1])
+            assert got[0] == want[0]
+            assert got[1].tolist() == want[1]
+        elif op[0] == "alloc_free":
+            n = op[1]
+            try:
+                want = ref.alloc(n)
+            except OutOfSlots:
+                with pytest.raises(RcError):
+                    tree.alloc(n)
+                continue
+            got = tree.alloc(n)
+            assert got.tolist() == want
+            tree.free(got)
+            ref.free_slots(want)
+        else:
+            _, batch, reserve = op
+            try:
+                rows_w, P_w, E_w = ref.emit_rows(batch, reserve)
+            except OutOfSlots:
+                before = tree.stats()["free_slots"]
+                with pytest.raises(RcError) as ei:
+                    tree.emit_rows(batch, table, reserve=reserve)
+                assert ei.value.status == N.RC_ERR_NOMEM
+                assert tree.stats()["free_slots"] == before
+                continue
+            P, E = tree.emit_rows(batch, table, reserve=reserve)
+            assert P.tolist() == P_w and E.tolist() == E_w
+            for b, toks in enumerate(batch):
+                n = len(toks) + reserve
+                assert table[b, :n].tolist() == rows_w[b]
+            # commit each request's prompt; rows get the tree's slots back
+            for b, toks in enumerate(batch):
+                canon, n_new = tree.insert(toks, table[b, :len(toks)])
+                canon_w, n_new_w = ref.insert(toks, rows_w[b][:len(toks)])
+                assert canon.tolist() == canon_w and n_new == n_new_w
+                # reserved decode slots are not used here: give them back
+                if reserve:
+                    tree.free(table[b, len(toks):len(toks) + reserve])
+                    ref.free_slots(rows_w[b][len(toks):len(toks) + reserve])
+        assert tree.stats()["free_slots"] == ref.num_free()
+    assert list(ref.free)[:5] == tree.alloc(min(5, ref.num_free())).tolist()
+
+
+def test_split_and_stats():
+    t = RadixTree(64)
+    a = t.alloc(6)
+    t.insert([1, 2, 3, 4, 5, 6], a)
+    b = t.alloc(3)
+    canon, n_new = t.insert([1, 2, 3, 9, 9, 9], np.concatenate([a[:3], b]))
+    assert n_new == 3 and canon.tolist() == a[:3].tolist() + b.tolist()
+    s = t.stats()
+    assert s["splits"] == 1 and s["nodes"] == 3 and s["cached_tokens"] == 9
+    m, sl = t.match([1, 2, 3, 9, 9, 9, 7])
+    assert m == 6 and sl.tolist() == canon.tolist()
+
+
+def test_insert_rejects_bad_slots_atomically():
+    t = RadixTree(16)
+    a = t.alloc(3)
+    t.insert([1, 2, 3], a)
+    free_before = t.stats()["free_slots"]
+    with pytest.raises(RcError):
+        t.insert([1, 2, 3, 4], [a[0], a[1], a[2], 15])  # slot 15 is still free
+    with pytest.raises(RcError):
+        t.insert([5, 6], [a[0], a[1]])  # slots already held by the tree
+    with pytest.raises(RcError):
+        t.free([a[0]])  # held by the tree
+    assert t.stats()["free_slots"] == free_before
+    assert t.match([1, 2, 3, 4])[0] == 3
+
+
+def test_free_order_must_be_a_permutation():
+    with pytest.raises(RcError):
+        RadixTree(4, np.array([0, 1, 1, 3], np.int32))
+
+
+def test_fork_shares_the_prefix_rows():
+    t = RadixTree(32)
+    table = np.full((4, 16), -1, np.int32)
+    parent = t.alloc(5)
+    t.fork([7, 7, 8, 9, 1], parent, [1, 2, 3], table)
+    for r in (1, 2, 3):
+        assert table[r, :5].tolist() == parent.tolist()
+    # a child extending the forked prefix matches all of it
+    P, E = t.emit_rows([[7, 7, 8, 9, 1, 4, 4]], table, rows=[1])
+    assert P.tolist() == [5] and E.tolist() == [2]
+
+
+def test_gpt2_bookkeeping_through_the_native_tree():
+    t = RadixTree(1024)
+    prefix = list(range(100, 509))
+    table = np.full((3, 512), -1, np.int32)
+    P, E = t.emit_rows([prefix], table)
+    assert (P[0], E[0]) == (0, 409)
+    t.insert(prefix, table[0, :409])
+    P, E = t.emit_rows([prefix + list(range(9000, 9008)), prefix + list(range(9100, 9107))], table, rows=[1, 2])
+    assert [(int(p), int(e), int(p + e)) for p, e in zip(P, E)] == [(409, 8, 417), (409, 7, 416)]
