@@ -48,6 +48,7 @@ def parse():
     ap.add_argument("--cpu-sample", type=int, default=8, help="requests in the oracle sample")
     ap.add_argument("--cpu-decode-steps", type=int, default=16, help="decode steps per request in the oracle sample")
     ap.add_argument("--seed", type=int, default=4)
+    ap.add_argument("--no-shuffle", action="store_true", help="hand out pool slots in order (no gather scatter)")
     return ap.parse_args()
 
 
@@ -77,7 +78,7 @@ def main():
     pool = cached + n_steps_total * B * E + B * (E + T) + 1024
     kvs = pk.KVShape(sh.num_q_heads, sh.num_kv_heads, sh.head_dim, torch.bfloat16, pool)
     stride = max(len(w.prompt_tokens(r)) for r in w.requests) + T + 8
-    order = np.random.default_rng(args.seed).permutation(pool).astype(np.int32)
+    order = None if args.no_shuffle else np.random.default_rng(args.seed).permutation(pool).astype(np.int32)
     eng = Engine(kvs, stride, B + 8, dev, free_order=order)
     gen = torch.Generator(device=dev)
     gen.manual_seed(args.seed)
@@ -181,6 +182,7 @@ def main():
                         "per leaf then 256 decode steps, shuffled pool slots",
             "batch": B, "new_tokens_per_request": E, "decode_steps": T, "cached_tokens": cached,
             "mean_prefix": round(float(P.mean()), 1), "decode_chunk": args.chunk,
+            "slot_order": "in order" if args.no_shuffle else "shuffled",
         },
         "roofline": {
             "bound": "hbm", "kernel": dec_name,

@@ -26,6 +26,7 @@
 // with log2(e) folded into the scale.
 #include <cfloat>
 #include <cmath>
+#include <type_traits>
 
 #include "hip_common.h"
 
@@ -200,22 +201,41 @@ __device__ __forceinline__ Col column(const Args& a, int mode, const Work& w, in
   return k;
 }
 
-// Position of key r (0..15) of a 16-key block inside the transposed V tile:
-// swaps bits 2 and 3 so a lane's 8 PV-operand keys are contiguous.
-__device__ __forceinline__ int vperm(int r) { return (((r >> 2) & 1) << 3) | (((r >> 3) & 1) << 2) | (r & 3); }
+// LDS tiles hold K and V row-major, [key][head dim], with the 16-byte chunks
+// of each row XOR-swizzled by a function of the key.  For D = 128 the swizzle
+// is a bijection of the key's low 4 bits chosen so that both access patterns
+// are free of bank conflicts: 16 consecutive keys reading one chunk (the K
+// operand, ds_read_b128) and 8 consecutive keys x 4 chunks (the transposing
+// V reads, ds_read_b64_tr_b16).
+template <int D>
+__device__ __forceinline__ int swz(int key) {
+  if constexpr (D == 128)
+    return ((key & 7) << 1) | ((key >> 3) & 1);
+  else
+    return key & 7;
+}
 
 __device__ __forceinline__ uint32_t pack2(uint32_t lo16, uint32_t hi16) { return (lo16 & 0xffffu) | (hi16 << 16); }
 
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+
+// Transposing LDS read (gfx950): within each 16-lane group, lane j receives
+// element j%4 of the 8-byte blocks addressed by lanes j/4, 4+j/4, 8+j/4 and
+// 12+j/4.  Lanes addressing 4 keys x 4 column blocks therefore receive a
+// 16 (head dims) x 4 (keys) tile: one lane per head dim, 4 keys each.
+__device__ __forceinline__ i16x4 lds_read_tr(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p));
+}
+
 template <int D>
-__global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(Args a, int mode) {
-  constexpr int KST = D + 8;      // K row stride in LDS (elements)
-  constexpr int VST = BN + 8;     // V^T row stride in LDS (elements)
-  constexpr int CH = D / 8;       // 16-byte chunks per key row
+__device__ __forceinline__ void attn_bf16_body(const Args& a, const int mode) {
+  constexpr int CH = D / 8;          // 16-byte chunks per key row
   constexpr int KPT = BN * CH / NT;  // keys per thread per stage (4 for D=128, 2 for D=64)
-  constexpr int NKS = D / 16;     // MFMA k-steps over D
-  constexpr int NDB = D / 32;     // 32-row blocks of O^T
-  __shared__ __attribute__((aligned(16))) uint16_t sK[BN * KST];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[D * VST];
+  constexpr int NKS = D / 16;        // MFMA k-steps over D
+  constexpr int NDB = D / 32;        // 32-row blocks of O^T
+  __shared__ __attribute__((aligned(16))) uint16_t sK[2][BN * D];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[2][BN * D];
 
   const int L = xcd_remap(blockIdx.x, a.n_work);
   const Work w = resolve(a, mode, L);
@@ -237,7 +257,7 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(Args a, int mode) {
   for (int i = 0; i < NDB; ++i) acc[i] = f32x16{};
   float m_run = -INFINITY, l_run = 0.f;
 
-  // loader: thread -> (chunk lc of D, keys lk0 .. lk0+KPT-1 of the stage)
+  // loader: thread -> (chunk lc of the row, keys lk0 .. lk0+KPT-1 of the stage)
   const int lc = tid % CH;
   const int lk0 = (tid / CH) * KPT;
   const uint16_t* kpool = (const uint16_t*)a.k_pool;
@@ -245,73 +265,78 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(Args a, int mode) {
   const uint16_t* knew = (const uint16_t*)a.k_new;
   const uint16_t* vnew = (const uint16_t*)a.v_new;
   const int64_t rowHD = (int64_t)a.Hkv * D;
+  const int32_t* trow = a.table + w.row * a.stride;
+  int32_t slot[2][KPT];
   uint4 kr[KPT], vr[KPT];
 
-  auto load_stage = [&](int kt) {
+  // slots of stage st (pool positions only)
+  auto load_slots = [&](int (&sl)[KPT], int kt) {
 #pragma unroll
     for (int r = 0; r < KPT; ++r) {
       const int j = kt + lk0 + r;
-      kr[r] = make_uint4(0, 0, 0, 0);
-      vr[r] = make_uint4(0, 0, 0, 0);
+      sl[r] = (j < w.key_end && j < w.ext_begin) ? trow[j] : -1;
+    }
+  };
+  int bad_slot = 0;  // an out-of-range slot was met (reported once, at the end)
+  auto load_kv = [&](uint4 (&kk)[KPT], uint4 (&vv)[KPT], const int (&sl)[KPT], int kt) {
+    if (kt + BN <= w.key_end && kt + BN <= w.ext_begin) {
+      // every key of the stage is a cached prefix key: no branches
+#pragma unroll
+      for (int r = 0; r < KPT; ++r) {
+        const int32_t s = sl[r];
+        const bool ok = (uint32_t)s < (uint32_t)a.pool_slots;
+        bad_slot |= !ok;
+        const int64_t off = (int64_t)(ok ? s : 0) * rowHD + (int64_t)w.hk * D + lc * 8;
+        kk[r] = *(const uint4*)(kpool + off);
+        vv[r] = *(const uint4*)(vpool + off);
+      }
+      return;
+    }
+#pragma unroll
+    for (int r = 0; r < KPT; ++r) {
+      const int j = kt + lk0 + r;
+      kk[r] = make_uint4(0, 0, 0, 0);
+      vv[r] = make_uint4(0, 0, 0, 0);
       if (j < w.key_end) {
         if (j >= w.ext_begin) {
           const int64_t off = (w.ext_base + (j - w.ext_begin)) * rowHD + (int64_t)w.hk * D + lc * 8;
-          kr[r] = *(const uint4*)(knew + off);
-          vr[r] = *(const uint4*)(vnew + off);
+          kk[r] = *(const uint4*)(knew + off);
+          vv[r] = *(const uint4*)(vnew + off);
         } else {
-          const int32_t s = a.table[w.row * a.stride + j];
-          if (s >= 0 && (int64_t)s < a.pool_slots) {
+          const int32_t s = sl[r];
+          const bool ok = (uint32_t)s < (uint32_t)a.pool_slots;
+          bad_slot |= !ok;
+          if (ok) {
             const int64_t off = (int64_t)s * rowHD + (int64_t)w.hk * D + lc * 8;
-            kr[r] = *(const uint4*)(kpool + off);
-            vr[r] = *(const uint4*)(vpool + off);
-          } else {
-            flag(a.err, RC_DEVERR_SLOT);
+            kk[r] = *(const uint4*)(kpool + off);
+            vv[r] = *(const uint4*)(vpool + off);
           }
         }
       }
     }
   };
-
-  auto store_stage = [&]() {
-#pragma unroll
-    for (int r = 0; r < KPT; ++r) *(uint4*)(sK + (lk0 + r) * KST + lc * 8) = kr[r];
-    const int vbase = (lk0 & ~15) + vperm(lk0 & 15);
-    uint32_t e[KPT][8];
+  auto store = [&](uint16_t* dk, uint16_t* dv, const uint4 (&kk)[KPT], const uint4 (&vv)[KPT]) {
 #pragma unroll
     for (int r = 0; r < KPT; ++r) {
-      e[r][0] = vr[r].x & 0xffffu; e[r][1] = vr[r].x >> 16;
-      e[r][2] = vr[r].y & 0xffffu; e[r][3] = vr[r].y >> 16;
-      e[r][4] = vr[r].z & 0xffffu; e[r][5] = vr[r].z >> 16;
-      e[r][6] = vr[r].w & 0xffffu; e[r][7] = vr[r].w >> 16;
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      uint16_t* dst = sV + (lc * 8 + i) * VST + vbase;
-      if constexpr (KPT == 4) {
-        *(uint2*)dst = make_uint2(pack2(e[0][i], e[1][i]), pack2(e[2][i], e[3][i]));
-      } else {
-        *(uint32_t*)dst = pack2(e[0][i], e[1][i]);
-      }
+      const int key = lk0 + r;
+      const int o = key * D + ((lc ^ swz<D>(key)) << 3);
+      *(uint4*)(dk + o) = kk[r];
+      *(uint4*)(dv + o) = vv[r];
     }
   };
 
-  int kt = w.key_begin;
-  if (kt < w.key_end) load_stage(kt);
-  for (; kt < w.key_end; kt += BN) {
-    __syncthreads();
-    store_stage();
-    __syncthreads();
-    if (kt + BN < w.key_end) load_stage(kt + BN);
-    if (!active) continue;
-
+  auto compute = [&](const uint16_t* tk, const uint16_t* tv, int kt) {
     // S^T = K Q^T over two 32-key blocks
     f32x16 s[2];
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
       s[m] = f32x16{};
+      const int key = m * 32 + (lane & 31);
+      const uint16_t* row = tk + key * D;
+      const int sw = swz<D>(key);
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
-        const bf16x8 kf = *(const bf16x8*)(sK + (m * 32 + (lane & 31)) * KST + ks * 16 + 8 * hi);
+        const bf16x8 kf = *(const bf16x8*)(row + (((2 * ks + hi) ^ sw) << 3));
         s[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s[m], 0, 0, 0);
       }
     }
@@ -321,7 +346,7 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(Args a, int mode) {
     for (int m = 0; m < 2; ++m)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        float x = s[m][v] * a.scale_log2;
+        float x = s[m][v];
         if (need_mask) {
           const int key = kt + m * 32 + (v >> 2) * 8 + hi * 4 + (v & 3);
           if (key >= w.key_end || key > col.limit) x = -INFINITY;
@@ -329,39 +354,75 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(Args a, int mode) {
         s[m][v] = x;
         mx = fmaxf(mx, x);
       }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = fmaxf(mx, __shfl_xor(mx, 32)) * a.scale_log2;
     const float m_new = fmaxf(m_run, mx);
     const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = exp2f(m_run - m_use);
     float psum = 0.f;
 #pragma unroll
     for (int m = 0; m < 2; ++m)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const float p = exp2f(s[m][v] - m_use);
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[m][v], a.scale_log2, -m_use));
         s[m][v] = p;
         psum += p;
       }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
+    // rescale only when some running max moved (alpha == 1 exactly otherwise)
+    if (__any(m_new != m_run)) {
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+      l_run *= alpha;
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) acc[db] *= alpha;
+      for (int db = 0; db < NDB; ++db) acc[db] *= alpha;
+    }
+    l_run += psum;
+    m_run = m_new;
 
-    // O^T += V^T P^T, four 16-key steps
+    // O^T += V^T P^T, four 16-key steps; V^T fragments by transposing reads
+    const int g = lane >> 4, r = lane & 15;
+    const int dsub = 16 * (g & 1) + 4 * (r & 3);
 #pragma unroll
     for (int k2 = 0; k2 < 4; ++k2) {
       const int m = k2 >> 1, h = k2 & 1;
       bf16x8 pf;
 #pragma unroll
       for (int i = 0; i < 8; ++i) pf[i] = (__bf16)s[m][8 * h + i];
+      const int key0 = 16 * k2 + 4 * (g >> 1) + (r >> 2);
+      const int key1 = key0 + 8;
+      const int sw0 = swz<D>(key0), sw1 = swz<D>(key1);
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
-        const bf16x8 vf = *(const bf16x8*)(sV + (db * 32 + (lane & 31)) * VST + k2 * 16 + 8 * hi);
-        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, acc[db], 0, 0, 0);
+        const int d = db * 32 + dsub;
+        const i16x4 lo = lds_read_tr(tv + key0 * D + (((d >> 3) ^ sw0) << 3) + (d & 7));
+        const i16x4 up = lds_read_tr(tv + key1 * D + (((d >> 3) ^ sw1) << 3) + (d & 7));
+        const i16x8 both = __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7);
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, both), pf, acc[db], 0, 0, 0);
       }
     }
+  };
+
+  // Pipeline: LDS double buffer (one barrier per stage), the next stage's K/V
+  // in registers while this one is computed, slot indices one stage ahead of
+  // the loads that use them.
+  const int kb = w.key_begin;
+  const int n_st = (w.key_end - kb + BN - 1) / BN;
+  if (n_st > 0) load_slots(slot[0], kb);
+  if (n_st > 1) load_slots(slot[1], kb + BN);
+  if (n_st > 0) load_kv(kr, vr, slot[0], kb);
+
+  auto step = [&](auto bufc, int i) {
+    constexpr int b = decltype(bufc)::value;
+    const int kt = kb + i * BN;
+    store(sK[b], sV[b], kr, vr);
+    __syncthreads();
+    if (i + 1 < n_st) load_kv(kr, vr, slot[b ^ 1], kt + BN);
+    if (i + 2 < n_st) load_slots(slot[b], kt + 2 * BN);
+    if (active) compute(sK[b], sV[b], kt);
+  };
+  for (int i = 0; i < n_st; i += 2) {
+    step(std::integral_constant<int, 0>{}, i);
+    if (i + 1 < n_st) step(std::integral_constant<int, 1>{}, i + 1);
   }
 
+  if (bad_slot) flag(a.err, RC_DEVERR_SLOT);
   if (!active || !col.real) return;
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   if (mode == EXTEND) {
@@ -395,10 +456,20 @@ __global__ __launch_bounds__(NT, 2) void attn_bf16_kernel(Args a, int mode) {
   }
 }
 
+template <int D>
+__global__ __launch_bounds__(NT, 2) void extend_attn_bf16(Args a) {
+  attn_bf16_body<D>(a, EXTEND);
+}
+
+template <int D>
+__global__ __launch_bounds__(NT, 2) void decode_attn_bf16(Args a) {
+  attn_bf16_body<D>(a, DECODE);
+}
+
 // fp32 path: one wave per column, lanes over head dims, keys one at a time.
 // Same work decomposition and outputs as the MFMA kernel; used for fp32 data.
 template <int D>
-__global__ __launch_bounds__(NT) void attn_f32_kernel(Args a, int mode) {
+__device__ __forceinline__ void attn_f32_body(const Args& a, const int mode) {
   constexpr int PER = D / 64;
   const int L = xcd_remap(blockIdx.x, a.n_work);
   const Work w = resolve(a, mode, L);
@@ -464,6 +535,16 @@ __global__ __launch_bounds__(NT) void attn_f32_kernel(Args a, int mode) {
   }
 }
 
+template <int D>
+__global__ __launch_bounds__(NT) void extend_attn_f32(Args a) {
+  attn_f32_body<D>(a, EXTEND);
+}
+
+template <int D>
+__global__ __launch_bounds__(NT) void decode_attn_f32(Args a) {
+  attn_f32_body<D>(a, DECODE);
+}
+
 // Split merge: for each (request, q head), combine its partials k = 0..n-1 in
 // order: M = max m_k, l = sum l_k 2^(m_k - M), o = sum o_k 2^(m_k - M) / l.
 template <int D, bool BF16>
@@ -506,10 +587,17 @@ __global__ __launch_bounds__(256) void merge_kernel(void* out, const float* __re
 template <int D>
 void launch_attn(const Args& a, int mode, int n_work, bool bf16, hipStream_t s, const char* name) {
   rc::ProfScope p(name, s);
-  if (bf16)
-    hipLaunchKernelGGL(attn_bf16_kernel<D>, dim3(n_work), dim3(NT), 0, s, a, mode);
-  else
-    hipLaunchKernelGGL(attn_f32_kernel<D>, dim3(n_work), dim3(NT), 0, s, a, mode);
+  if (mode == EXTEND) {
+    if (bf16)
+      hipLaunchKernelGGL(extend_attn_bf16<D>, dim3(n_work), dim3(NT), 0, s, a);
+    else
+      hipLaunchKernelGGL(extend_attn_f32<D>, dim3(n_work), dim3(NT), 0, s, a);
+  } else {
+    if (bf16)
+      hipLaunchKernelGGL(decode_attn_bf16<D>, dim3(n_work), dim3(NT), 0, s, a);
+    else
+      hipLaunchKernelGGL(decode_attn_f32<D>, dim3(n_work), dim3(NT), 0, s, a);
+  }
 }
 
 rc_status check_common(const rc_shape* shape, float sm_scale) {
