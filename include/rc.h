@@ -141,6 +141,7 @@ rc_status rc_extend_attention(const rc_shape* shape, void* o, const void* q, con
 /*                            member_cnt, 0, 0}                               */
 /*   members     n_members batch indices                                       */
 /*   n_splits    batch entries: partial results per request                    */
+/* Items with members*group > 16 come first, then the narrow ones.           */
 /* The kernel clamps pos_end to seq_lens[first member]; the planners only    */
 /* put a range in a shared item when it lies inside every member's context.  */
 /* ------------------------------------------------------------------------ */
@@ -157,6 +158,9 @@ typedef struct rc_plan_info {
   int32_t chunk;       /* max positions per item                               */
   int32_t max_cols;    /* max members*group per item                           */
   int32_t shared_items;/* items with more than one member                       */
+  int32_t narrow_begin;/* items from here on have members*group <= 16 (the plan */
+                       /* lists wider items first)                              */
+  int32_t reserved;
   int64_t plan_ints;   /* length of the plan buffer in int32                    */
   int64_t unique_positions; /* sum over items of (pos_end - pos_begin)         */
   int64_t logical_positions;/* sum over requests of their context length       */

@@ -34,6 +34,8 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int BN = 64;     // keys per stage
 constexpr int NCOL = 128;  // query columns per workgroup (4 waves x 32)
@@ -70,6 +72,9 @@ struct Args {
   // decode
   const int32_t* plan;
   int32_t n_items, n_members;  // from the planner's host summary
+  int32_t narrow_begin;        // first item with members*group <= 16
+  int32_t n_wide_blocks;       // workgroups that run wide items
+  int32_t n_narrow_units;      // (narrow item, kv head) pairs, one wave each
   const int32_t* seq_lens;
   float* ws_o;
   float* ws_ml;
@@ -96,7 +101,7 @@ __device__ __forceinline__ void flag(int32_t* err, int32_t bit) {
   if (err) atomicOr(err, bit);
 }
 
-__device__ Work resolve(const Args& a, int mode, int L) {
+__device__ Work resolve(const Args& a, int mode, int L, bool leader) {
   Work w{};
   w.valid = false;
   if (mode == EXTEND) {
@@ -106,12 +111,12 @@ __device__ Work resolve(const Args& a, int mode, int L) {
     w.hk = bh - b * a.Hkv;
     const int P = a.prefix_lens[b], E = a.extend_lens[b];
     if (P < 0 || E < 0) {
-      if (tile == 0 && threadIdx.x == 0) flag(a.err, RC_DEVERR_LENGTH);
+      if (tile == 0 && leader) flag(a.err, RC_DEVERR_LENGTH);
       return w;
     }
-    if (E > a.max_extend && tile == 0 && w.hk == 0 && threadIdx.x == 0) flag(a.err, RC_DEVERR_LENGTH);
+    if (E > a.max_extend && tile == 0 && w.hk == 0 && leader) flag(a.err, RC_DEVERR_LENGTH);
     if ((int64_t)P > a.stride) {
-      if (tile == 0 && threadIdx.x == 0) flag(a.err, RC_DEVERR_TABLE);
+      if (tile == 0 && leader) flag(a.err, RC_DEVERR_TABLE);
       return w;
     }
     const int t0 = tile * a.tok_per_tile;
@@ -120,12 +125,12 @@ __device__ Work resolve(const Args& a, int mode, int L) {
     const int nt = min(a.tok_per_tile, Ec - t0);
     const int64_t s0 = a.extend_start[b];
     if (s0 < 0 || s0 + Ec > a.total_extend) {
-      if (tile == 0 && threadIdx.x == 0) flag(a.err, RC_DEVERR_LENGTH);
+      if (tile == 0 && leader) flag(a.err, RC_DEVERR_LENGTH);
       return w;
     }
     w.row = a.rows ? a.rows[b] : b;
     if (w.row < 0 || w.row >= a.table_rows) {
-      if (threadIdx.x == 0) flag(a.err, RC_DEVERR_TABLE);
+      if (leader) flag(a.err, RC_DEVERR_TABLE);
       return w;
     }
     w.key_begin = 0;
@@ -149,13 +154,13 @@ __device__ Work resolve(const Args& a, int mode, int L) {
     w.mcnt = it[5];
     if (rep < 0 || rep >= a.table_rows || pb < 0 || pe < pb || (int64_t)pe > a.stride || w.split < 0 || w.split >= a.max_splits ||
         w.moff < 0 || w.mcnt < 1 || w.mcnt * a.g > NCOL || w.moff + w.mcnt > n_members) {
-      if (threadIdx.x == 0) flag(a.err, RC_DEVERR_PLAN);
+      if (leader) flag(a.err, RC_DEVERR_PLAN);
       return w;
     }
     const int32_t* mem = a.plan + RC_PLAN_HEADER + (int64_t)a.n_items * RC_PLAN_ITEM + w.moff;
     for (int i = 0; i < w.mcnt; ++i)
       if (mem[i] < 0 || mem[i] >= a.batch) {
-        if (threadIdx.x == 0) flag(a.err, RC_DEVERR_PLAN);
+        if (leader) flag(a.err, RC_DEVERR_PLAN);
         return w;
       }
     const int sl = a.seq_lens[mem[0]];
@@ -229,16 +234,13 @@ __device__ __forceinline__ i16x4 lds_read_tr(const uint16_t* p) {
 }
 
 template <int D>
-__device__ __forceinline__ void attn_bf16_body(const Args& a, const int mode) {
+__device__ __forceinline__ void attn_bf16_body(const Args& a, const int mode, const int L, uint16_t (&sK)[2][BN * D],
+                                               uint16_t (&sV)[2][BN * D]) {
   constexpr int CH = D / 8;          // 16-byte chunks per key row
   constexpr int KPT = BN * CH / NT;  // keys per thread per stage (4 for D=128, 2 for D=64)
   constexpr int NKS = D / 16;        // MFMA k-steps over D
   constexpr int NDB = D / 32;        // 32-row blocks of O^T
-  __shared__ __attribute__((aligned(16))) uint16_t sK[2][BN * D];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[2][BN * D];
-
-  const int L = xcd_remap(blockIdx.x, a.n_work);
-  const Work w = resolve(a, mode, L);
+  const Work w = resolve(a, mode, L, threadIdx.x == 0);
   if (!w.valid) return;  // uniform over the workgroup
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -267,7 +269,7 @@ __device__ __forceinline__ void attn_bf16_body(const Args& a, const int mode) {
   const int64_t rowHD = (int64_t)a.Hkv * D;
   const int32_t* trow = a.table + w.row * a.stride;
   int32_t slot[2][KPT];
-  uint4 kr[KPT], vr[KPT];
+  u32x4 kr[KPT], vr[KPT];
 
   // slots of stage st (pool positions only)
   auto load_slots = [&](int (&sl)[KPT], int kt) {
@@ -278,7 +280,7 @@ __device__ __forceinline__ void attn_bf16_body(const Args& a, const int mode) {
     }
   };
   int bad_slot = 0;  // an out-of-range slot was met (reported once, at the end)
-  auto load_kv = [&](uint4 (&kk)[KPT], uint4 (&vv)[KPT], const int (&sl)[KPT], int kt) {
+  auto load_kv = [&](u32x4 (&kk)[KPT], u32x4 (&vv)[KPT], const int (&sl)[KPT], int kt) {
     if (kt + BN <= w.key_end && kt + BN <= w.ext_begin) {
       // every key of the stage is a cached prefix key: no branches
 #pragma unroll
@@ -287,41 +289,41 @@ __device__ __forceinline__ void attn_bf16_body(const Args& a, const int mode) {
         const bool ok = (uint32_t)s < (uint32_t)a.pool_slots;
         bad_slot |= !ok;
         const int64_t off = (int64_t)(ok ? s : 0) * rowHD + (int64_t)w.hk * D + lc * 8;
-        kk[r] = *(const uint4*)(kpool + off);
-        vv[r] = *(const uint4*)(vpool + off);
+        kk[r] = *(const u32x4*)(kpool + off);
+        vv[r] = *(const u32x4*)(vpool + off);
       }
       return;
     }
 #pragma unroll
     for (int r = 0; r < KPT; ++r) {
       const int j = kt + lk0 + r;
-      kk[r] = make_uint4(0, 0, 0, 0);
-      vv[r] = make_uint4(0, 0, 0, 0);
+      kk[r] = u32x4{0, 0, 0, 0};
+      vv[r] = u32x4{0, 0, 0, 0};
       if (j < w.key_end) {
         if (j >= w.ext_begin) {
           const int64_t off = (w.ext_base + (j - w.ext_begin)) * rowHD + (int64_t)w.hk * D + lc * 8;
-          kk[r] = *(const uint4*)(knew + off);
-          vv[r] = *(const uint4*)(vnew + off);
+          kk[r] = *(const u32x4*)(knew + off);
+          vv[r] = *(const u32x4*)(vnew + off);
         } else {
           const int32_t s = sl[r];
           const bool ok = (uint32_t)s < (uint32_t)a.pool_slots;
           bad_slot |= !ok;
           if (ok) {
             const int64_t off = (int64_t)s * rowHD + (int64_t)w.hk * D + lc * 8;
-            kk[r] = *(const uint4*)(kpool + off);
-            vv[r] = *(const uint4*)(vpool + off);
+            kk[r] = *(const u32x4*)(kpool + off);
+            vv[r] = *(const u32x4*)(vpool + off);
           }
         }
       }
     }
   };
-  auto store = [&](uint16_t* dk, uint16_t* dv, const uint4 (&kk)[KPT], const uint4 (&vv)[KPT]) {
+  auto store = [&](uint16_t* dk, uint16_t* dv, const u32x4 (&kk)[KPT], const u32x4 (&vv)[KPT]) {
 #pragma unroll
     for (int r = 0; r < KPT; ++r) {
       const int key = lk0 + r;
       const int o = key * D + ((lc ^ swz<D>(key)) << 3);
-      *(uint4*)(dk + o) = kk[r];
-      *(uint4*)(dv + o) = vv[r];
+      *(u32x4*)(dk + o) = kk[r];
+      *(u32x4*)(dv + o) = vv[r];
     }
   };
 
@@ -456,14 +458,195 @@ __device__ __forceinline__ void attn_bf16_body(const Args& a, const int mode) {
   }
 }
 
+// Narrow decode items (members x group <= 16 query columns): one wave per
+// (item, kv head), no workgroup barriers.  Per 32-key stage a lane loads
+//   K straight into registers in the A-operand layout of
+//     v_mfma_f32_16x16x32_bf16 (lane l: key l%16 of a 16-key block, head
+//     dims 8*(l/16)..+8 of each 32-wide k-step), so K never touches LDS;
+//   V (4 lanes per key, 64 contiguous bytes per instruction) into registers,
+//     then into a wave-private row-major LDS tile for the transposing reads.
+// The next stage's K and V are in flight while this one is computed; slot
+// indices run one more stage ahead.  S^T = K Q^T and O^T += V^T P^T as in the
+// wide kernel, on 16x16 tiles: a lane owns one query column and 4 keys per
+// 16-key block, so the softmax reductions cross the 4 lane groups (2 steps).
+constexpr int BNN = 32;  // keys per narrow stage
+
 template <int D>
-__global__ __launch_bounds__(NT, 2) void extend_attn_bf16(Args a) {
-  attn_bf16_body<D>(a, EXTEND);
+__device__ __forceinline__ void decode_narrow_body(const Args& a, const int unit, uint16_t* sv) {
+  constexpr int NKS = D / 32;  // k-steps of 32 over D
+  constexpr int NDB = D / 16;  // 16-row blocks of O^T
+  constexpr int VT = D / 32;   // 16-byte V chunks per lane per key (4 lanes per key row)
+  const int lane = threadIdx.x & 63;
+  const int grp = lane >> 4, r16 = lane & 15;
+  const int L = (a.narrow_begin + unit / a.Hkv) * a.Hkv + unit % a.Hkv;
+  const Work w = resolve(a, DECODE, L, lane == 0);
+  if (!w.valid) return;  // uniform over the wave
+  const Col col = column(a, DECODE, w, r16);
+
+  const uint16_t* q = (const uint16_t*)a.q;
+  bf16x8 qf[NKS];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) qf[ks] = *(const bf16x8*)(q + col.qoff * D + ks * 32 + 8 * grp);
+
+  f32x4 acc[NDB];
+#pragma unroll
+  for (int i = 0; i < NDB; ++i) acc[i] = f32x4{};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  const uint16_t* kbase = (const uint16_t*)a.k_pool + (int64_t)w.hk * D;
+  const uint16_t* vbase = (const uint16_t*)a.v_pool + (int64_t)w.hk * D;
+  const int64_t rowHD = (int64_t)a.Hkv * D;
+  const int32_t* trow = a.table + w.row * a.stride;
+  int bad_slot = 0;
+
+  auto load_slots = [&](int (&sl)[2], int kt) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int key = kt + 16 * j + r16;
+      sl[j] = key < w.key_end ? trow[key] : 0;
+    }
+  };
+  auto load_kv = [&](bf16x8 (&kf)[2][NKS], u32x4 (&vr)[2][VT], const int (&sl)[2]) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const bool ok = (uint32_t)sl[j] < (uint32_t)a.pool_slots;
+      bad_slot |= !ok;
+      const int64_t off = (int64_t)(ok ? sl[j] : 0) * rowHD;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) kf[j][ks] = *(const bf16x8*)(kbase + off + ks * 32 + 8 * grp);
+#pragma unroll
+      for (int t = 0; t < VT; ++t) vr[j][t] = *(const u32x4*)(vbase + off + (4 * t + grp) * 8);
+    }
+  };
+  auto store_v = [&](const u32x4 (&vr)[2][VT]) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int key = 16 * j + r16;
+#pragma unroll
+      for (int t = 0; t < VT; ++t) *(u32x4*)(sv + key * D + (((4 * t + grp) ^ swz<D>(key)) << 3)) = vr[j][t];
+    }
+  };
+  auto compute = [&](const bf16x8 (&kf)[2][NKS], int kt) {
+    f32x4 s[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      s[j] = f32x4{};
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) s[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[j][ks], qf[ks], s[j], 0, 0, 0);
+    }
+    const bool need_mask = kt + BNN > w.key_end;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        float x = s[j][v];
+        if (need_mask && kt + 16 * j + 4 * grp + v >= w.key_end) x = -INFINITY;
+        s[j][v] = x;
+        mx = fmaxf(mx, x);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32)) * a.scale_log2;
+    const float m_new = fmaxf(m_run, mx);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    float psum = 0.f;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[j][v], a.scale_log2, -m_use));
+        s[j][v] = p;
+        psum += p;
+      }
+    if (__any(m_new != m_run)) {
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) acc[db] *= alpha;
+    }
+    l_run += psum;
+    m_run = m_new;
+    // P^T operand: k-position 8*grp+i <-> key 16*(i/4) + 4*grp + i%4
+    bf16x8 pf;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      pf[i] = (__bf16)s[0][i];
+      pf[4 + i] = (__bf16)s[1][i];
+    }
+    const int key0 = 4 * grp + (r16 >> 2), key1 = key0 + 16;
+    const int sw0 = swz<D>(key0), sw1 = swz<D>(key1);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const int d = db * 16 + 4 * (r16 & 3);
+      const i16x4 lo = lds_read_tr(sv + key0 * D + (((d >> 3) ^ sw0) << 3) + (d & 7));
+      const i16x4 up = lds_read_tr(sv + key1 * D + (((d >> 3) ^ sw1) << 3) + (d & 7));
+      const i16x8 both = __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7);
+      acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, both), pf, acc[db], 0, 0, 0);
+    }
+  };
+
+  const int kb = w.key_begin;
+  const int n_st = (w.key_end - kb + BNN - 1) / BNN;
+  int slA[2], slB[2];
+  bf16x8 kA[2][NKS], kB[2][NKS];
+  u32x4 vr[2][VT];
+  if (n_st > 0) load_slots(slA, kb);
+  if (n_st > 1) load_slots(slB, kb + BNN);
+  if (n_st > 0) load_kv(kA, vr, slA);
+  if (n_st > 2) load_slots(slA, kb + 2 * BNN);
+  for (int i = 0; i < n_st; i += 2) {
+    int kt = kb + i * BNN;
+    store_v(vr);
+    if (i + 1 < n_st) {
+      load_kv(kB, vr, slB);
+      if (i + 3 < n_st) load_slots(slB, kt + 3 * BNN);
+    }
+    compute(kA, kt);
+    if (i + 1 >= n_st) break;
+    kt += BNN;
+    store_v(vr);
+    if (i + 2 < n_st) {
+      load_kv(kA, vr, slA);
+      if (i + 4 < n_st) load_slots(slA, kt + 3 * BNN);
+    }
+    compute(kB, kt);
+  }
+
+  if (bad_slot) flag(a.err, RC_DEVERR_SLOT);
+  float l_tot = l_run + __shfl_xor(l_run, 16);
+  l_tot += __shfl_xor(l_tot, 32);
+  if (!col.real) return;
+  const int64_t pidx = ((int64_t)col.b * a.Hq + col.head) * a.max_splits + w.split;
+  float* wo = a.ws_o + pidx * D;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+    *(float4*)(wo + db * 16 + 4 * grp) = make_float4(acc[db][0], acc[db][1], acc[db][2], acc[db][3]);
+  if (grp == 0) *(float2*)(a.ws_ml + pidx * 2) = make_float2(m_run, l_tot);
 }
 
 template <int D>
+__global__ __launch_bounds__(NT, 2) void extend_attn_bf16(Args a) {
+  __shared__ __attribute__((aligned(16))) uint16_t sK[2][BN * D];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[2][BN * D];
+  // neighbouring tiles of one (request, kv head) share an XCD's L2
+  attn_bf16_body<D>(a, EXTEND, xcd_remap(blockIdx.x, a.n_work), sK, sV);
+}
+
+// Wide items first (workgroup-cooperative tiles, listed heaviest first and
+// dealt round-robin over the XCDs), then narrow items four waves per block.
+template <int D>
 __global__ __launch_bounds__(NT, 2) void decode_attn_bf16(Args a) {
-  attn_bf16_body<D>(a, DECODE);
+  __shared__ __attribute__((aligned(16))) uint16_t sK[2][BN * D];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[2][BN * D];
+  if ((int)blockIdx.x < a.n_wide_blocks) {
+    attn_bf16_body<D>(a, DECODE, blockIdx.x, sK, sV);
+  } else {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave
+    const int unit = ((int)blockIdx.x - a.n_wide_blocks) * 4 + wave;
+    if (unit >= a.n_narrow_units) return;
+    uint16_t* sv = &sK[wave >> 1][(wave & 1) * BNN * D];
+    decode_narrow_body<D>(a, unit, sv);
+  }
 }
 
 // fp32 path: one wave per column, lanes over head dims, keys one at a time.
@@ -472,7 +655,7 @@ template <int D>
 __device__ __forceinline__ void attn_f32_body(const Args& a, const int mode) {
   constexpr int PER = D / 64;
   const int L = xcd_remap(blockIdx.x, a.n_work);
-  const Work w = resolve(a, mode, L);
+  const Work w = resolve(a, mode, L, threadIdx.x == 0);
   if (!w.valid) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const float* q = (const float*)a.q;
@@ -686,10 +869,19 @@ extern "C" rc_status rc_decode_attention(const rc_shape* shape, void* o, const v
   a.batch = batch;
   a.plan = plan_dev; a.seq_lens = seq_lens;
   a.n_items = info->n_items; a.n_members = info->n_members;
+  a.narrow_begin = info->narrow_begin;
   a.ws_o = (float*)workspace;
   a.ws_ml = (float*)workspace + parts * shape->head_dim;
   a.max_splits = info->max_splits;
-  const int64_t n_work = (int64_t)info->n_items * a.Hkv;
+  if (info->narrow_begin < 0 || info->narrow_begin > info->n_items) return fail(RC_ERR_ARG, "plan summary out of range");
+  int64_t n_work = (int64_t)info->n_items * a.Hkv;
+  if (shape->dtype == RC_BF16) {
+    // wide items: one workgroup each; narrow items: one wave each, four per workgroup
+    a.n_wide_blocks = info->narrow_begin * a.Hkv;
+    const int64_t units = (int64_t)(info->n_items - info->narrow_begin) * a.Hkv;
+    a.n_narrow_units = (int32_t)units;
+    n_work = a.n_wide_blocks + (units + 3) / 4;
+  }
   if (n_work > INT32_MAX) return fail(RC_ERR_RANGE, "grid too large");
   a.n_work = (int32_t)n_work;
   hipStream_t s = (hipStream_t)stream;

@@ -374,6 +374,7 @@ struct PlanBuilder {
   std::vector<int32_t> members;
   std::vector<int32_t> nsplit;
   int32_t shared_items = 0;
+  int32_t narrow_begin = 0;
   int64_t unique_pos = 0;
 
   int32_t row_of(int32_t b) const { return rows ? rows[b] : b; }
@@ -397,23 +398,30 @@ struct PlanBuilder {
     std::stable_sort(order.begin(), order.end(), [&](int32_t a, int32_t b) {
       return ranges[a].members.size() > ranges[b].members.size();
     });
-    for (int32_t r : order) {
-      const Range& R = ranges[r];
-      if (R.end <= R.begin) continue;
-      unique_pos += R.end - R.begin;
-      int32_t sp = first_split[r];
-      for (int64_t p = R.begin; p < R.end; p += chunk, ++sp) {
-        const int64_t pe = std::min<int64_t>(p + chunk, R.end);
-        for (size_t g0 = 0; g0 < R.members.size(); g0 += max_m) {
-          const size_t cnt = std::min<size_t>(max_m, R.members.size() - g0);
-          const int32_t off = (int32_t)members.size();
-          members.insert(members.end(), R.members.begin() + g0, R.members.begin() + g0 + cnt);
-          int32_t it[RC_PLAN_ITEM] = {row_of(R.members[g0]), (int32_t)p, (int32_t)pe, sp, off, (int32_t)cnt, 0, 0};
-          item_rows.insert(item_rows.end(), it, it + RC_PLAN_ITEM);
-          if (R.members.size() > 1) shared_items++;
+    // wide items (members*group > 16) first, heaviest first; narrow ones last
+    for (int pass = 0; pass < 2; ++pass) {
+      if (pass == 1) narrow_begin = (int32_t)(item_rows.size() / RC_PLAN_ITEM);
+      for (int32_t r : order) {
+        const Range& R = ranges[r];
+        if (R.end <= R.begin) continue;
+        int32_t sp = first_split[r];
+        for (int64_t p = R.begin; p < R.end; p += chunk, ++sp) {
+          const int64_t pe = std::min<int64_t>(p + chunk, R.end);
+          for (size_t g0 = 0; g0 < R.members.size(); g0 += max_m) {
+            const size_t cnt = std::min<size_t>(max_m, R.members.size() - g0);
+            const bool narrow = (int64_t)cnt * group <= 16;
+            if (narrow != (pass == 1)) continue;
+            const int32_t off = (int32_t)members.size();
+            members.insert(members.end(), R.members.begin() + g0, R.members.begin() + g0 + cnt);
+            int32_t it[RC_PLAN_ITEM] = {row_of(R.members[g0]), (int32_t)p, (int32_t)pe, sp, off, (int32_t)cnt, 0, 0};
+            item_rows.insert(item_rows.end(), it, it + RC_PLAN_ITEM);
+            if (R.members.size() > 1) shared_items++;
+          }
         }
       }
     }
+    for (int32_t r : order)
+      if (ranges[r].end > ranges[r].begin) unique_pos += ranges[r].end - ranges[r].begin;
   }
 
   rc_status emit(int32_t* plan, int64_t cap, rc_plan_info* info, int64_t logical) {
@@ -429,6 +437,8 @@ struct PlanBuilder {
     info->chunk = chunk;
     info->max_cols = max_m * group;
     info->shared_items = shared_items;
+    info->narrow_begin = narrow_begin;
+    info->reserved = 0;
     info->plan_ints = need;
     info->unique_positions = unique_pos;
     info->logical_positions = logical;
