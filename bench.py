@@ -49,6 +49,7 @@ def parse():
     ap.add_argument("--cpu-decode-steps", type=int, default=16, help="decode steps per request in the oracle sample")
     ap.add_argument("--seed", type=int, default=4)
     ap.add_argument("--no-shuffle", action="store_true", help="hand out pool slots in order (no gather scatter)")
+    ap.add_argument("--decode-rows", type=int, default=0, help="narrow decode by groups of four kv heads (rc_set_tuning)")
     return ap.parse_args()
 
 
@@ -68,6 +69,7 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    pk.set_tuning("decode_rows", args.decode_rows)
     w = W.multi_turn_tree(seed=args.seed, n_decode=args.decode_steps)
     sh = w.shape
     B = len(w.requests)
@@ -112,6 +114,7 @@ def main():
         return out
 
     plan_info = {}
+    narrow_pos = {}
 
     def one_step(step):
         toks = prompts(step)
@@ -120,6 +123,10 @@ def main():
         eng.commit(b)
         st = eng.prepare_decode(b, [len(t) for t in toks], T, chunk=args.chunk)
         plan_info.update(st.plan.summary)
+        if not narrow_pos:
+            # (rep_row, begin, end, ...) of every narrow item, and each row's prompt length
+            narrow_pos["items"] = st.plan.items()[st.plan.info.narrow_begin:].copy()
+            narrow_pos["base"] = {int(r): len(t) for r, t in zip(b.rows, toks)}
         for t in range(T):
             eng.decode_step(st, t, q_dec[t], k_dec[t], v_dec[t], w.sm_scale, o=o_dec)
         eng.release(b)
@@ -150,14 +157,25 @@ def main():
     uniq = cached + B * own
     dec_bytes_steps = uniq * (row_bytes + 4) + 2 * B * Hq * D * 2  # KV + slot index + q + o
     logical = B * (P.mean() + own)
+    # unique positions of narrow items at step t: each item's range clamped to its request's length
+    nitems, seq_base = narrow_pos["items"], narrow_pos["base"]
+    narrow_pos_steps = np.array([sum(max(0, min(int(e), seq_base[int(r)] + t + 1) - int(bg)) for r, bg, e in nitems[:, :3])
+                                 for t in range(T)], np.float64)
     store_bytes = (B * E + B * T) * (2 * row_bytes + 4)  # read new K/V, write pool rows, slot index
-    ext_name, dec_name, mrg_name, st_name = "extend_bf16_d128", "decode_bf16_d128", "decode_merge", "kv_store"
+    ext_name, mrg_name, st_name = "extend_bf16_d128", "decode_merge", "kv_store"
+    wide_name, dec_name = "decode_wide_d128", "decode_narrow_d128"
     ext_ms = prof[ext_name][1] / prof[ext_name][0]
-    dec_n, dec_tot = prof[dec_name]
-    dec_ms = dec_tot / dec_n
+    # decode attention = wide-item launch + narrow-item launch of each step
+    dec_n = prof[dec_name][0]
+    wide_ms = prof[wide_name][1] / dec_n if wide_name in prof else 0.0
+    narrow_ms = prof[dec_name][1] / dec_n
+    dec_ms = wide_ms + narrow_ms
     mrg_ms = prof[mrg_name][1] / prof[mrg_name][0]
     st_tot = prof[st_name][1] / args.steps
     ext_tflops = ext_flops / (ext_ms * 1e-3) / 1e12
+    # narrow items read each request's own positions and the nodes shared by at most 16/group requests
+    narrow_bytes = float(np.mean(narrow_pos_steps)) * (row_bytes + 4) + 2 * B * Hq * D * 2
+    narrow_gbs = narrow_bytes / (narrow_ms * 1e-3) / 1e9
     dec_gbs = float(np.mean(dec_bytes_steps)) / (dec_ms * 1e-3) / 1e9
     tokens_per_step = B * E + B * T
     ms_per_step = elapsed / args.steps * 1e3
@@ -186,9 +204,9 @@ def main():
         },
         "roofline": {
             "bound": "hbm", "kernel": dec_name,
-            "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": None,
-            "avg_launch_ms": round(dec_ms, 5), "algorithmic_bytes_per_launch": float(np.mean(dec_bytes_steps)),
+            "achieved": round(narrow_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(narrow_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+            "avg_launch_ms": round(narrow_ms, 5), "algorithmic_bytes_per_launch": float(narrow_bytes),
         },
         "extend": {
             "kernel": ext_name, "avg_launch_ms": round(ext_ms, 4), "algorithmic_tflop": round(ext_flops / 1e12, 4),
@@ -197,7 +215,8 @@ def main():
             "tokens_per_s": round(B * E / (ext_ms * 1e-3), 1),
         },
         "decode": {
-            "avg_launch_ms": round(dec_ms, 5), "merge_avg_ms": round(mrg_ms, 5), "gbs": round(dec_gbs, 1),
+            "attention_ms": round(dec_ms, 5), "wide_ms": round(wide_ms, 5), "narrow_ms": round(narrow_ms, 5),
+            "merge_avg_ms": round(mrg_ms, 5), "gbs": round(dec_gbs, 1),
             "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
             "unique_bytes_per_step": float(np.mean(dec_bytes_steps)),
             "logical_bytes_per_step": float(np.mean(logical) * row_bytes),

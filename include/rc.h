@@ -283,6 +283,13 @@ rc_status rc_radix_plan_decode(rc_radix* tree, int32_t batch, const int32_t* tok
 
 rc_status rc_radix_stats_get(const rc_radix* tree, rc_radix_stats* out);
 
+/* Tuning switches (process-wide, take effect on the next call):             */
+/*   "decode_rows" 0|1: narrow decode items are computed by groups of four kv */
+/*                 heads per workgroup, each load covering whole slot-row    */
+/*                 segments (1) instead of one wave per kv head (0, default). */
+/* Unknown names return RC_ERR_ARG.                                          */
+rc_status rc_set_tuning(const char* name, int64_t value);
+
 /* ------------------------------------------------------------------------ */
 /* Kernel timing.  While enabled, every kernel the library launches is       */
 /* bracketed by HIP events on its own stream.  rc_prof_collect waits for the */

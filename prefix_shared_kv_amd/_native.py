@@ -70,6 +70,7 @@ _SIGS = {
     "rc_radix_fork": (i32, [P, P, P, i64, i32, P, P, i32, i64]),
     "rc_radix_plan_decode": (i32, [P, i32, P, P, P, P, i32, i32, P, i64, C.POINTER(RcPlanInfo)]),
     "rc_radix_stats_get": (i32, [P, C.POINTER(RcRadixStats)]),
+    "rc_set_tuning": (i32, [C.c_char_p, i64]),
     "rc_prof_enable": (i32, [i32]),
     "rc_prof_collect": (i32, [C.POINTER(RcProfEntry), i32, I32P]),
 }
@@ -77,7 +78,7 @@ _SIGS = {
 
 def _load():
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built; run `python -m prefix_shared_kv_amd.build` "
+        raise ImportError(f"{LIB_PATH} is not built; run `python prefix_shared_kv_amd/build.py` "
                           "(there is no fallback implementation)")
     lib = C.CDLL(LIB_PATH)
     for name, (res, args) in _SIGS.items():

@@ -1,5 +1,6 @@
 """Build librcattn.so in-tree: HIP kernels for gfx950 (hipcc) plus the host
-radix tree and planners (g++).  Run ``python -m prefix_shared_kv_amd.build``."""
+radix tree and planners (g++).  Run ``python prefix_shared_kv_amd/build.py``
+(by path: importing the package would load the library being rebuilt)."""
 from __future__ import annotations
 
 import concurrent.futures as cf

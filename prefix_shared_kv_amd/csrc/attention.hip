@@ -73,8 +73,8 @@ struct Args {
   const int32_t* plan;
   int32_t n_items, n_members;  // from the planner's host summary
   int32_t narrow_begin;        // first item with members*group <= 16
-  int32_t n_wide_blocks;       // workgroups that run wide items
   int32_t n_narrow_units;      // (narrow item, kv head) pairs, one wave each
+  int32_t rows_path;           // narrow items by groups of four kv heads (Hkv % 4 == 0)
   const int32_t* seq_lens;
   float* ws_o;
   float* ws_ml;
@@ -459,23 +459,25 @@ __device__ __forceinline__ void attn_bf16_body(const Args& a, const int mode, co
 }
 
 // Narrow decode items (members x group <= 16 query columns): one wave per
-// (item, kv head), no workgroup barriers.  Per 32-key stage a lane loads
-//   K straight into registers in the A-operand layout of
-//     v_mfma_f32_16x16x32_bf16 (lane l: key l%16 of a 16-key block, head
-//     dims 8*(l/16)..+8 of each 32-wide k-step), so K never touches LDS;
-//   V (4 lanes per key, 64 contiguous bytes per instruction) into registers,
-//     then into a wave-private row-major LDS tile for the transposing reads.
-// The next stage's K and V are in flight while this one is computed; slot
-// indices run one more stage ahead.  S^T = K Q^T and O^T += V^T P^T as in the
-// wide kernel, on 16x16 tiles: a lane owns one query column and 4 keys per
+// (item, kv head), no workgroup barriers.  Per 32-key stage a lane loads 8
+// keys' K and V chunks with 16 lanes per key row, so every load instruction
+// moves 4 keys x 256 contiguous bytes (gathers that scatter an instruction over
+// 16 slots reach only about half the bandwidth); the stage goes into a
+// wave-private row-major LDS tile (chunk-swizzled per key), from which the
+// K operand is read with ds_read_b128 and V^T with transposing reads.  The
+// next stage's K and V are in registers while this one is computed; slot
+// indices run one more stage ahead.  S^T = K Q^T and O^T += V^T P^T on
+// v_mfma_f32_16x16x32_bf16 tiles: a lane owns one query column and 4 keys per
 // 16-key block, so the softmax reductions cross the 4 lane groups (2 steps).
 constexpr int BNN = 32;  // keys per narrow stage
 
 template <int D>
-__device__ __forceinline__ void decode_narrow_body(const Args& a, const int unit, uint16_t* sv) {
-  constexpr int NKS = D / 32;  // k-steps of 32 over D
-  constexpr int NDB = D / 16;  // 16-row blocks of O^T
-  constexpr int VT = D / 32;   // 16-byte V chunks per lane per key (4 lanes per key row)
+__device__ __forceinline__ void decode_narrow_body(const Args& a, const int unit, uint16_t* sk, uint16_t* sv) {
+  constexpr int NKS = D / 32;         // k-steps of 32 over D
+  constexpr int NDB = D / 16;         // 16-row blocks of O^T
+  constexpr int CH = D / 8;           // 16-byte chunks per key row
+  constexpr int KPI = 64 / CH;        // keys per load instruction (4 for D=128, 8 for D=64)
+  constexpr int NI = BNN / KPI;       // load instructions per lane per stage and array
   const int lane = threadIdx.x & 63;
   const int grp = lane >> 4, r16 = lane & 15;
   const int L = (a.narrow_begin + unit / a.Hkv) * a.Hkv + unit % a.Hkv;
@@ -493,46 +495,55 @@ __device__ __forceinline__ void decode_narrow_body(const Args& a, const int unit
   for (int i = 0; i < NDB; ++i) acc[i] = f32x4{};
   float m_run = -INFINITY, l_run = 0.f;
 
-  const uint16_t* kbase = (const uint16_t*)a.k_pool + (int64_t)w.hk * D;
-  const uint16_t* vbase = (const uint16_t*)a.v_pool + (int64_t)w.hk * D;
+  const int lc = lane % CH, lk = lane / CH;  // loader: chunk and key within an instruction
+  const uint16_t* kbase = (const uint16_t*)a.k_pool + (int64_t)w.hk * D + lc * 8;
+  const uint16_t* vbase = (const uint16_t*)a.v_pool + (int64_t)w.hk * D + lc * 8;
   const int64_t rowHD = (int64_t)a.Hkv * D;
   const int32_t* trow = a.table + w.row * a.stride;
   int bad_slot = 0;
 
-  auto load_slots = [&](int (&sl)[2], int kt) {
+  auto load_slots = [&](int (&sl)[NI], int kt) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int key = kt + 16 * j + r16;
-      sl[j] = key < w.key_end ? trow[key] : 0;
+    for (int t = 0; t < NI; ++t) {
+      const int key = kt + t * KPI + lk;
+      sl[t] = key < w.key_end ? trow[key] : INT_MIN;  // INT_MIN: past the range end
     }
   };
-  auto load_kv = [&](bf16x8 (&kf)[2][NKS], u32x4 (&vr)[2][VT], const int (&sl)[2]) {
+  auto load_kv = [&](u32x4 (&kr)[NI], u32x4 (&vr)[NI], const int (&sl)[NI], bool partial) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const bool ok = (uint32_t)sl[j] < (uint32_t)a.pool_slots;
-      bad_slot |= !ok;
-      const int64_t off = (int64_t)(ok ? sl[j] : 0) * rowHD;
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) kf[j][ks] = *(const bf16x8*)(kbase + off + ks * 32 + 8 * grp);
-#pragma unroll
-      for (int t = 0; t < VT; ++t) vr[j][t] = *(const u32x4*)(vbase + off + (4 * t + grp) * 8);
+    for (int t = 0; t < NI; ++t) {
+      const bool ok = (uint32_t)sl[t] < (uint32_t)a.pool_slots;
+      bad_slot |= !ok & (sl[t] != INT_MIN);
+      const int64_t off = (int64_t)(ok ? sl[t] : 0) * rowHD;
+      kr[t] = *(const u32x4*)(kbase + off);
+      vr[t] = *(const u32x4*)(vbase + off);
+      if (partial && !ok) {  // keys past the end must hold finite values: p = 0 multiplies them
+        kr[t] = u32x4{0, 0, 0, 0};
+        vr[t] = u32x4{0, 0, 0, 0};
+      }
     }
   };
-  auto store_v = [&](const u32x4 (&vr)[2][VT]) {
+  auto store = [&](const u32x4 (&kr)[NI], const u32x4 (&vr)[NI]) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int key = 16 * j + r16;
-#pragma unroll
-      for (int t = 0; t < VT; ++t) *(u32x4*)(sv + key * D + (((4 * t + grp) ^ swz<D>(key)) << 3)) = vr[j][t];
+    for (int t = 0; t < NI; ++t) {
+      const int key = t * KPI + lk;
+      const int o = key * D + ((lc ^ swz<D>(key)) << 3);
+      *(u32x4*)(sk + o) = kr[t];
+      *(u32x4*)(sv + o) = vr[t];
     }
   };
-  auto compute = [&](const bf16x8 (&kf)[2][NKS], int kt) {
+  auto compute = [&](int kt) {
     f32x4 s[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       s[j] = f32x4{};
+      const int key = 16 * j + r16;
+      const int sw = swz<D>(key);
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) s[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[j][ks], qf[ks], s[j], 0, 0, 0);
+      for (int ks = 0; ks < NKS; ++ks) {
+        const bf16x8 kf = *(const bf16x8*)(sk + key * D + (((4 * ks + grp) ^ sw) << 3));
+        s[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[ks], s[j], 0, 0, 0);
+      }
     }
     const bool need_mask = kt + BNN > w.key_end;
     float mx = -INFINITY;
@@ -587,29 +598,211 @@ __device__ __forceinline__ void decode_narrow_body(const Args& a, const int unit
 
   const int kb = w.key_begin;
   const int n_st = (w.key_end - kb + BNN - 1) / BNN;
-  int slA[2], slB[2];
-  bf16x8 kA[2][NKS], kB[2][NKS];
-  u32x4 vr[2][VT];
+  int slA[NI], slB[NI];
+  u32x4 kr[NI], vr[NI];
   if (n_st > 0) load_slots(slA, kb);
   if (n_st > 1) load_slots(slB, kb + BNN);
-  if (n_st > 0) load_kv(kA, vr, slA);
+  if (n_st > 0) load_kv(kr, vr, slA, kb + BNN > w.key_end);
   if (n_st > 2) load_slots(slA, kb + 2 * BNN);
+  // The LDS tile is private to the wave and LDS operations of a wave complete
+  // in order, so the next stage may overwrite it right after this stage's reads.
   for (int i = 0; i < n_st; i += 2) {
     int kt = kb + i * BNN;
-    store_v(vr);
+    store(kr, vr);
     if (i + 1 < n_st) {
-      load_kv(kB, vr, slB);
+      load_kv(kr, vr, slB, kt + 2 * BNN > w.key_end);
       if (i + 3 < n_st) load_slots(slB, kt + 3 * BNN);
     }
-    compute(kA, kt);
+    compute(kt);
     if (i + 1 >= n_st) break;
     kt += BNN;
-    store_v(vr);
+    store(kr, vr);
     if (i + 2 < n_st) {
-      load_kv(kA, vr, slA);
+      load_kv(kr, vr, slA, kt + 2 * BNN > w.key_end);
       if (i + 4 < n_st) load_slots(slA, kt + 3 * BNN);
     }
-    compute(kB, kt);
+    compute(kt);
+  }
+
+  if (bad_slot) flag(a.err, RC_DEVERR_SLOT);
+  float l_tot = l_run + __shfl_xor(l_run, 16);
+  l_tot += __shfl_xor(l_tot, 32);
+  if (!col.real) return;
+  const int64_t pidx = ((int64_t)col.b * a.Hq + col.head) * a.max_splits + w.split;
+  float* wo = a.ws_o + pidx * D;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+    *(float4*)(wo + db * 16 + 4 * grp) = make_float4(acc[db][0], acc[db][1], acc[db][2], acc[db][3]);
+  if (grp == 0) *(float2*)(a.ws_ml + pidx * 2) = make_float2(m_run, l_tot);
+}
+
+// Narrow decode items, kv heads in groups of four: one workgroup per (item,
+// head group).  The gather is the bandwidth limiter for decode, and scattered
+// 256-byte reads (one head of one slot) reach far less HBM bandwidth than
+// whole slot rows, so here every load instruction covers one key's four heads
+// (1 KiB contiguous for D = 128): each wave loads 8 keys of a 32-key stage
+// into registers, the stage goes to LDS as [key][head][D] (chunk-swizzled per
+// key), and wave w computes head w from it with the narrow kernel's
+// 16x16x32 tiles (K operand by ds_read_b128, V^T by transposing reads).
+constexpr int HG = 4;     // kv heads per workgroup
+constexpr int BNR = 32;   // keys per stage
+
+template <int D>
+__device__ __forceinline__ void decode_rows_body(const Args& a, const int unit, uint16_t* sk, uint16_t* sv) {
+  constexpr int NKS = D / 32;          // k-steps of 32 over D
+  constexpr int NDB = D / 16;          // 16-row blocks of O^T
+  constexpr int CHH = D / 8;           // 16-byte chunks per (key, head)
+  constexpr int LPK = HG * CHH;        // lanes covering one key's heads (64 for D=128, 32 for D=64)
+  constexpr int KPI = 64 / LPK;        // keys per load instruction
+  constexpr int NI = BNR / 4 / KPI;    // load instructions per lane per stage and array
+  constexpr int RS = HG * D;           // LDS elements per key
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = lane >> 4, r16 = lane & 15;
+  const int groups = a.Hkv / HG;
+  const int L = (a.narrow_begin + unit / groups) * a.Hkv + (unit % groups) * HG;
+  Work w = resolve(a, DECODE, L, tid == 0);
+  if (!w.valid) return;  // uniform over the workgroup
+  const int hk0 = w.hk;
+  w.hk = hk0 + wave;     // this wave's kv head
+  const Col col = column(a, DECODE, w, r16);
+
+  const uint16_t* q = (const uint16_t*)a.q;
+  bf16x8 qf[NKS];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) qf[ks] = *(const bf16x8*)(q + col.qoff * D + ks * 32 + 8 * grp);
+  f32x4 acc[NDB];
+#pragma unroll
+  for (int i = 0; i < NDB; ++i) acc[i] = f32x4{};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  // loader: lane -> (key k0 + lane / LPK, head, chunk) of each instruction
+  const int lk = lane / LPK;                  // key within an instruction
+  const int lh = (lane % LPK) / CHH;          // head within the group
+  const int lc = lane % CHH;                  // chunk within the head's row
+  const int64_t rowHD = (int64_t)a.Hkv * D;
+  const uint16_t* kbase = (const uint16_t*)a.k_pool + (int64_t)hk0 * D + lh * D + lc * 8;
+  const uint16_t* vbase = (const uint16_t*)a.v_pool + (int64_t)hk0 * D + lh * D + lc * 8;
+  const int32_t* trow = a.table + w.row * a.stride;
+  int bad_slot = 0;
+  int sl[2][NI];
+  u32x4 kr[NI], vr[NI];
+
+  auto key_of = [&](int t) { return wave * (BNR / 4) + t * KPI + lk; };  // key within the stage
+  auto load_slots = [&](int (&s)[NI], int kt) {
+#pragma unroll
+    for (int t = 0; t < NI; ++t) {
+      const int j = kt + key_of(t);
+      s[t] = j < w.key_end ? trow[j] : INT_MIN;  // INT_MIN: past the range end
+    }
+  };
+  auto load_kv = [&](const int (&s)[NI], bool partial) {
+#pragma unroll
+    for (int t = 0; t < NI; ++t) {
+      const int32_t sv_ = s[t];
+      const bool ok = (uint32_t)sv_ < (uint32_t)a.pool_slots;
+      bad_slot |= !ok & (sv_ != INT_MIN);
+      const int64_t off = (int64_t)(ok ? sv_ : 0) * rowHD;
+      kr[t] = *(const u32x4*)(kbase + off);
+      vr[t] = *(const u32x4*)(vbase + off);
+      if (partial && !ok) {  // keys past the end must hold finite values: p = 0 multiplies them
+        kr[t] = u32x4{0, 0, 0, 0};
+        vr[t] = u32x4{0, 0, 0, 0};
+      }
+    }
+  };
+  auto store = [&]() {
+#pragma unroll
+    for (int t = 0; t < NI; ++t) {
+      const int key = key_of(t);
+      const int o = key * RS + lh * D + ((lc ^ swz<D>(key)) << 3);
+      *(u32x4*)(sk + o) = kr[t];
+      *(u32x4*)(sv + o) = vr[t];
+    }
+  };
+  auto compute = [&](int kt) {
+    const uint16_t* hk_ = sk + wave * D;
+    const uint16_t* hv_ = sv + wave * D;
+    f32x4 s[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      s[j] = f32x4{};
+      const int key = 16 * j + r16;
+      const int sw = swz<D>(key);
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        const bf16x8 kf = *(const bf16x8*)(hk_ + key * RS + (((4 * ks + grp) ^ sw) << 3));
+        s[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[ks], s[j], 0, 0, 0);
+      }
+    }
+    const bool need_mask = kt + BNR > w.key_end;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        float x = s[j][v];
+        if (need_mask && kt + 16 * j + 4 * grp + v >= w.key_end) x = -INFINITY;
+        s[j][v] = x;
+        mx = fmaxf(mx, x);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32)) * a.scale_log2;
+    const float m_new = fmaxf(m_run, mx);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    float psum = 0.f;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[j][v], a.scale_log2, -m_use));
+        s[j][v] = p;
+        psum += p;
+      }
+    if (__any(m_new != m_run)) {
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) acc[db] *= alpha;
+    }
+    l_run += psum;
+    m_run = m_new;
+    bf16x8 pf;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      pf[i] = (__bf16)s[0][i];
+      pf[4 + i] = (__bf16)s[1][i];
+    }
+    const int key0 = 4 * grp + (r16 >> 2), key1 = key0 + 16;
+    const int sw0 = swz<D>(key0), sw1 = swz<D>(key1);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const int d = db * 16 + 4 * (r16 & 3);
+      const i16x4 lo = lds_read_tr(hv_ + key0 * RS + (((d >> 3) ^ sw0) << 3) + (d & 7));
+      const i16x4 up = lds_read_tr(hv_ + key1 * RS + (((d >> 3) ^ sw1) << 3) + (d & 7));
+      const i16x8 both = __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7);
+      acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, both), pf, acc[db], 0, 0, 0);
+    }
+  };
+
+  const int kb = w.key_begin;
+  const int n_st = (w.key_end - kb + BNR - 1) / BNR;
+  if (n_st > 0) load_slots(sl[0], kb);
+  if (n_st > 1) load_slots(sl[1], kb + BNR);
+  if (n_st > 0) load_kv(sl[0], kb + BNR > w.key_end);
+  auto step = [&](auto bufc, int i) {
+    constexpr int b = decltype(bufc)::value;
+    const int kt = kb + i * BNR;
+    __syncthreads();  // the previous stage's reads are done
+    store();
+    __syncthreads();
+    if (i + 1 < n_st) load_kv(sl[b ^ 1], kt + 2 * BNR > w.key_end);
+    if (i + 2 < n_st) load_slots(sl[b], kt + 2 * BNR);
+    compute(kt);
+  };
+  for (int i = 0; i < n_st; i += 2) {
+    step(std::integral_constant<int, 0>{}, i);
+    if (i + 1 < n_st) step(std::integral_constant<int, 1>{}, i + 1);
   }
 
   if (bad_slot) flag(a.err, RC_DEVERR_SLOT);
@@ -632,21 +825,33 @@ __global__ __launch_bounds__(NT, 2) void extend_attn_bf16(Args a) {
   attn_bf16_body<D>(a, EXTEND, xcd_remap(blockIdx.x, a.n_work), sK, sV);
 }
 
-// Wide items first (workgroup-cooperative tiles, listed heaviest first and
-// dealt round-robin over the XCDs), then narrow items four waves per block.
+// Wide decode items: workgroup-cooperative tiles, listed heaviest first and
+// dealt round-robin over the XCDs.
 template <int D>
 __global__ __launch_bounds__(NT, 2) void decode_attn_bf16(Args a) {
   __shared__ __attribute__((aligned(16))) uint16_t sK[2][BN * D];
   __shared__ __attribute__((aligned(16))) uint16_t sV[2][BN * D];
-  if ((int)blockIdx.x < a.n_wide_blocks) {
-    attn_bf16_body<D>(a, DECODE, blockIdx.x, sK, sV);
-  } else {
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave
-    const int unit = ((int)blockIdx.x - a.n_wide_blocks) * 4 + wave;
-    if (unit >= a.n_narrow_units) return;
-    uint16_t* sv = &sK[wave >> 1][(wave & 1) * BNN * D];
-    decode_narrow_body<D>(a, unit, sv);
-  }
+  attn_bf16_body<D>(a, DECODE, blockIdx.x, sK, sV);
+}
+
+// Narrow decode items: four independent waves per workgroup, each with its own
+// K and V tile.
+template <int D>
+__global__ __launch_bounds__(NT) void decode_narrow_bf16(Args a) {
+  __shared__ __attribute__((aligned(16))) uint16_t sK[4 * BNN * D];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[4 * BNN * D];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave
+  const int unit = (int)blockIdx.x * 4 + wave;
+  if (unit >= a.n_narrow_units) return;
+  decode_narrow_body<D>(a, unit, sK + wave * BNN * D, sV + wave * BNN * D);
+}
+
+// Narrow decode items, one workgroup per group of four kv heads.
+template <int D>
+__global__ __launch_bounds__(NT) void decode_rows_bf16(Args a) {
+  __shared__ __attribute__((aligned(16))) uint16_t sK[HG * BNR * D];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[HG * BNR * D];
+  decode_rows_body<D>(a, (int)blockIdx.x, sK, sV);
 }
 
 // fp32 path: one wave per column, lanes over head dims, keys one at a time.
@@ -874,24 +1079,55 @@ extern "C" rc_status rc_decode_attention(const rc_shape* shape, void* o, const v
   a.ws_ml = (float*)workspace + parts * shape->head_dim;
   a.max_splits = info->max_splits;
   if (info->narrow_begin < 0 || info->narrow_begin > info->n_items) return fail(RC_ERR_ARG, "plan summary out of range");
-  int64_t n_work = (int64_t)info->n_items * a.Hkv;
-  if (shape->dtype == RC_BF16) {
-    // wide items: one workgroup each; narrow items: one wave each, four per workgroup
-    a.n_wide_blocks = info->narrow_begin * a.Hkv;
-    const int64_t units = (int64_t)(info->n_items - info->narrow_begin) * a.Hkv;
-    a.n_narrow_units = (int32_t)units;
-    n_work = a.n_wide_blocks + (units + 3) / 4;
-  }
-  if (n_work > INT32_MAX) return fail(RC_ERR_RANGE, "grid too large");
-  a.n_work = (int32_t)n_work;
   hipStream_t s = (hipStream_t)stream;
   const bool bf16 = shape->dtype == RC_BF16;
-  if (n_work > 0) {
-    if (shape->head_dim == 128)
-      launch_attn<128>(a, DECODE, a.n_work, bf16, s, bf16 ? "decode_bf16_d128" : "decode_f32_d128");
-    else
-      launch_attn<64>(a, DECODE, a.n_work, bf16, s, bf16 ? "decode_bf16_d64" : "decode_f32_d64");
-    st = check_launch("decode attention");
+  if (!bf16) {
+    const int64_t n_work = (int64_t)info->n_items * a.Hkv;
+    if (n_work > INT32_MAX) return fail(RC_ERR_RANGE, "grid too large");
+    a.n_work = (int32_t)n_work;
+    if (n_work > 0) {
+      if (shape->head_dim == 128)
+        launch_attn<128>(a, DECODE, a.n_work, false, s, "decode_f32_d128");
+      else
+        launch_attn<64>(a, DECODE, a.n_work, false, s, "decode_f32_d64");
+      st = check_launch("decode attention");
+      if (st != RC_OK) return st;
+    }
+  } else {
+    // wide items: one workgroup per (item, kv head)
+    const int64_t n_wide = (int64_t)info->narrow_begin * a.Hkv;
+    // narrow items: one wave per (item, kv head), or one workgroup per four kv heads
+    const int64_t units = (int64_t)(info->n_items - info->narrow_begin) * a.Hkv;
+    a.n_narrow_units = (int32_t)units;
+    a.rows_path = rc::tuning().decode_rows && a.Hkv % HG == 0;
+    const int64_t n_narrow = a.rows_path ? units / HG : (units + 3) / 4;
+    if (n_wide > INT32_MAX || n_narrow > INT32_MAX) return fail(RC_ERR_RANGE, "grid too large");
+    if (n_wide > 0) {
+      a.n_work = (int32_t)n_wide;
+      ProfScope p(shape->head_dim == 128 ? "decode_wide_d128" : "decode_wide_d64", s);
+      if (shape->head_dim == 128)
+        hipLaunchKernelGGL(decode_attn_bf16<128>, dim3((unsigned)n_wide), dim3(NT), 0, s, a);
+      else
+        hipLaunchKernelGGL(decode_attn_bf16<64>, dim3((unsigned)n_wide), dim3(NT), 0, s, a);
+    }
+    st = check_launch("decode attention (wide items)");
+    if (st != RC_OK) return st;
+    if (n_narrow > 0) {
+      a.n_work = (int32_t)n_narrow;
+      ProfScope p(shape->head_dim == 128 ? "decode_narrow_d128" : "decode_narrow_d64", s);
+      if (a.rows_path) {
+        if (shape->head_dim == 128)
+          hipLaunchKernelGGL(decode_rows_bf16<128>, dim3((unsigned)n_narrow), dim3(NT), 0, s, a);
+        else
+          hipLaunchKernelGGL(decode_rows_bf16<64>, dim3((unsigned)n_narrow), dim3(NT), 0, s, a);
+      } else {
+        if (shape->head_dim == 128)
+          hipLaunchKernelGGL(decode_narrow_bf16<128>, dim3((unsigned)n_narrow), dim3(NT), 0, s, a);
+        else
+          hipLaunchKernelGGL(decode_narrow_bf16<64>, dim3((unsigned)n_narrow), dim3(NT), 0, s, a);
+      }
+    }
+    st = check_launch("decode attention (narrow items)");
     if (st != RC_OK) return st;
   }
   const int32_t* nsplit = plan_dev + RC_PLAN_HEADER + (int64_t)info->n_items * RC_PLAN_ITEM + info->n_members;

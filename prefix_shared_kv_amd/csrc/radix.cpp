@@ -398,28 +398,36 @@ struct PlanBuilder {
     std::stable_sort(order.begin(), order.end(), [&](int32_t a, int32_t b) {
       return ranges[a].members.size() > ranges[b].members.size();
     });
-    // wide items (members*group > 16) first, heaviest first; narrow ones last
-    for (int pass = 0; pass < 2; ++pass) {
-      if (pass == 1) narrow_begin = (int32_t)(item_rows.size() / RC_PLAN_ITEM);
-      for (int32_t r : order) {
-        const Range& R = ranges[r];
-        if (R.end <= R.begin) continue;
-        int32_t sp = first_split[r];
-        for (int64_t p = R.begin; p < R.end; p += chunk, ++sp) {
-          const int64_t pe = std::min<int64_t>(p + chunk, R.end);
-          for (size_t g0 = 0; g0 < R.members.size(); g0 += max_m) {
-            const size_t cnt = std::min<size_t>(max_m, R.members.size() - g0);
-            const bool narrow = (int64_t)cnt * group <= 16;
-            if (narrow != (pass == 1)) continue;
-            const int32_t off = (int32_t)members.size();
-            members.insert(members.end(), R.members.begin() + g0, R.members.begin() + g0 + cnt);
-            int32_t it[RC_PLAN_ITEM] = {row_of(R.members[g0]), (int32_t)p, (int32_t)pe, sp, off, (int32_t)cnt, 0, 0};
-            item_rows.insert(item_rows.end(), it, it + RC_PLAN_ITEM);
-            if (R.members.size() > 1) shared_items++;
-          }
+    // wide items (members*group > 16) first, then narrow ones; within each
+    // class the longest first (members x positions), so the last workgroups
+    // to start are the short ones
+    struct Item { int64_t cost; int32_t v[RC_PLAN_ITEM]; std::vector<int32_t> mem; };
+    std::vector<Item> wide, narrow;
+    for (int32_t r : order) {
+      const Range& R = ranges[r];
+      if (R.end <= R.begin) continue;
+      int32_t sp = first_split[r];
+      for (int64_t p = R.begin; p < R.end; p += chunk, ++sp) {
+        const int64_t pe = std::min<int64_t>(p + chunk, R.end);
+        for (size_t g0 = 0; g0 < R.members.size(); g0 += max_m) {
+          const size_t cnt = std::min<size_t>(max_m, R.members.size() - g0);
+          Item it{(int64_t)cnt * (pe - p), {row_of(R.members[g0]), (int32_t)p, (int32_t)pe, sp, 0, (int32_t)cnt, 0, 0},
+                  std::vector<int32_t>(R.members.begin() + g0, R.members.begin() + g0 + cnt)};
+          ((int64_t)cnt * group <= 16 ? narrow : wide).push_back(std::move(it));
+          if (R.members.size() > 1) shared_items++;
         }
       }
     }
+    auto by_cost = [](const Item& x, const Item& y) { return x.cost > y.cost; };
+    std::stable_sort(wide.begin(), wide.end(), by_cost);
+    std::stable_sort(narrow.begin(), narrow.end(), by_cost);
+    narrow_begin = (int32_t)wide.size();
+    for (auto* list : {&wide, &narrow})
+      for (Item& it : *list) {
+        it.v[4] = (int32_t)members.size();
+        members.insert(members.end(), it.mem.begin(), it.mem.end());
+        item_rows.insert(item_rows.end(), it.v, it.v + RC_PLAN_ITEM);
+      }
     for (int32_t r : order)
       if (ranges[r].end > ranges[r].begin) unique_pos += ranges[r].end - ranges[r].begin;
   }

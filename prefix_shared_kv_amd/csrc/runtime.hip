@@ -10,6 +10,9 @@ namespace rc {
 static int32_t* g_err_word = nullptr;
 int32_t* error_word() { return g_err_word; }
 
+static Tuning g_tuning;
+Tuning& tuning() { return g_tuning; }
+
 namespace {
 struct Rec {
   const char* name;
@@ -55,6 +58,15 @@ rc_status check_launch(const char* what) {
 extern "C" rc_status rc_set_error_word(int32_t* device_word) {
   rc::g_err_word = device_word;
   return RC_OK;
+}
+
+extern "C" rc_status rc_set_tuning(const char* name, int64_t value) {
+  if (!name) return rc::fail(RC_ERR_ARG, "tuning name is NULL");
+  if (!strcmp(name, "decode_rows")) {
+    rc::g_tuning.decode_rows = value != 0;
+    return RC_OK;
+  }
+  return rc::fail(RC_ERR_ARG, "unknown tuning switch '%s'", name);
 }
 
 extern "C" rc_status rc_prof_enable(int32_t on) {

@@ -211,3 +211,37 @@ def test_decode_is_deterministic(gpu):
         d = eng.decode_step(st, 0, q, k, v, w.sm_scale)
         outs.append((o.view(torch.int16).cpu(), d.view(torch.int16).cpu()))
     assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+
+
+def test_unused_pool_slots_holding_nan_do_not_leak(gpu):
+    # past-the-end keys of a stage read some pool row; its contents must never reach the output
+    w = W.multi_turn_tree(depth=2, fanout=3, seg_lo=7, seg_hi=70, ext=5, n_decode=2)
+    eng = drive.make_engine(w, device=gpu)
+    eng.k_pool.fill_(float("nan"))
+    eng.v_pool.fill_(float("nan"))
+    drive.populate(eng, w, device=gpu)
+    b, o = drive.extend_requests(eng, w, device=gpu)
+    assert torch.isfinite(o.float()).all()
+    st = eng.prepare_decode(b, [len(w.prompt_tokens(r)) for r in w.requests], 2, chunk=48)
+    for t in range(2):
+        q, k, v = drive.decode_inputs(w, range(len(w.requests)), t, device=gpu)
+        d = host(eng.decode_step(st, t, q, k, v, w.sm_scale))
+        for i in range(len(w.requests)):
+            K, V = w.context_kv(i, t + 1)
+            check(d[i], A.decode(w.dec_qkv(i, t)[0], K, V, w.sm_scale), TOL["bf16"], f"decode step {t} request {i}")
+
+
+@pytest.mark.parametrize("rows", [0, 1])
+@pytest.mark.parametrize("Hq,Hkv,D", [(12, 3, 128), (16, 2, 64), (8, 8, 128), (48, 12, 64)])
+def test_decode_head_layouts(gpu, Hq, Hkv, D, rows):
+    # both narrow decode paths (one wave per kv head; groups of four kv heads per
+    # workgroup, used when Hkv % 4 == 0 and the switch is on)
+    w = W.multi_turn_tree(depth=3, fanout=2, seg_lo=20, seg_hi=150, ext=6, n_decode=2)
+    w.shape.num_q_heads, w.shape.num_kv_heads, w.shape.head_dim = Hq, Hkv, D
+    w.sm_scale = 1.0 / np.sqrt(D)
+    api.set_tuning("decode_rows", rows)
+    try:
+        for shared, chunk in [(True, 64), (False, 100)]:
+            _run_workload(gpu, w, shared=shared, chunk=chunk)
+    finally:
+        api.set_tuning("decode_rows", 0)
