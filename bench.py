@@ -50,6 +50,7 @@ def parse():
     ap.add_argument("--seed", type=int, default=4)
     ap.add_argument("--no-shuffle", action="store_true", help="hand out pool slots in order (no gather scatter)")
     ap.add_argument("--decode-rows", type=int, default=0, help="narrow decode by groups of four kv heads (rc_set_tuning)")
+    ap.add_argument("--host-phases", action="store_true", help="report host wall time per phase of the last step")
     return ap.parse_args()
 
 
@@ -114,22 +115,34 @@ def main():
         return out
 
     plan_info = {}
-    narrow_pos = {}
+
+    phases = {}
 
     def one_step(step):
+        tick = time.perf_counter()
+
+        def mark(name):
+            nonlocal tick
+            now = time.perf_counter()
+            phases[name] = round((now - tick) * 1e3, 3)
+            tick = now
+
         toks = prompts(step)
+        mark("prompts")
         b = eng.schedule(toks, reserve=T)
+        mark("schedule")
         eng.extend(b, q_ext, k_ext, v_ext, w.sm_scale, o=o_ext)
+        mark("extend_launch")
         eng.commit(b)
+        mark("commit")
         st = eng.prepare_decode(b, [len(t) for t in toks], T, chunk=args.chunk)
+        mark("prepare_decode")
         plan_info.update(st.plan.summary)
-        if not narrow_pos:
-            # (rep_row, begin, end, ...) of every narrow item, and each row's prompt length
-            narrow_pos["items"] = st.plan.items()[st.plan.info.narrow_begin:].copy()
-            narrow_pos["base"] = {int(r): len(t) for r, t in zip(b.rows, toks)}
         for t in range(T):
             eng.decode_step(st, t, q_dec[t], k_dec[t], v_dec[t], w.sm_scale, o=o_dec)
+        mark("decode_launches")
         eng.release(b)
+        mark("release")
         return b
 
     for s in range(args.warmup):
@@ -157,25 +170,16 @@ def main():
     uniq = cached + B * own
     dec_bytes_steps = uniq * (row_bytes + 4) + 2 * B * Hq * D * 2  # KV + slot index + q + o
     logical = B * (P.mean() + own)
-    # unique positions of narrow items at step t: each item's range clamped to its request's length
-    nitems, seq_base = narrow_pos["items"], narrow_pos["base"]
-    narrow_pos_steps = np.array([sum(max(0, min(int(e), seq_base[int(r)] + t + 1) - int(bg)) for r, bg, e in nitems[:, :3])
-                                 for t in range(T)], np.float64)
+
     store_bytes = (B * E + B * T) * (2 * row_bytes + 4)  # read new K/V, write pool rows, slot index
     ext_name, mrg_name, st_name = "extend_bf16_d128", "decode_merge", "kv_store"
-    wide_name, dec_name = "decode_wide_d128", "decode_narrow_d128"
+    dec_name = "decode_attention_d128"  # one launch per step: wide and narrow items
     ext_ms = prof[ext_name][1] / prof[ext_name][0]
-    # decode attention = wide-item launch + narrow-item launch of each step
-    dec_n = prof[dec_name][0]
-    wide_ms = prof[wide_name][1] / dec_n if wide_name in prof else 0.0
-    narrow_ms = prof[dec_name][1] / dec_n
-    dec_ms = wide_ms + narrow_ms
+    dec_ms = prof[dec_name][1] / prof[dec_name][0]
     mrg_ms = prof[mrg_name][1] / prof[mrg_name][0]
     st_tot = prof[st_name][1] / args.steps
     ext_tflops = ext_flops / (ext_ms * 1e-3) / 1e12
-    # narrow items read each request's own positions and the nodes shared by at most 16/group requests
-    narrow_bytes = float(np.mean(narrow_pos_steps)) * (row_bytes + 4) + 2 * B * Hq * D * 2
-    narrow_gbs = narrow_bytes / (narrow_ms * 1e-3) / 1e9
+
     dec_gbs = float(np.mean(dec_bytes_steps)) / (dec_ms * 1e-3) / 1e9
     tokens_per_step = B * E + B * T
     ms_per_step = elapsed / args.steps * 1e3
@@ -203,10 +207,10 @@ def main():
             "slot_order": "in order" if args.no_shuffle else "shuffled",
         },
         "roofline": {
-            "bound": "hbm", "kernel": dec_name,
-            "achieved": round(narrow_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(narrow_gbs / HBM_PEAK_GBS, 4), "traffic": None,
-            "avg_launch_ms": round(narrow_ms, 5), "algorithmic_bytes_per_launch": float(narrow_bytes),
+            "bound": "hbm", "kernel": "decode_attn_bf16<128> (" + dec_name + ")",
+            "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+            "avg_launch_ms": round(dec_ms, 5), "algorithmic_bytes_per_launch": float(np.mean(dec_bytes_steps)),
         },
         "extend": {
             "kernel": ext_name, "avg_launch_ms": round(ext_ms, 4), "algorithmic_tflop": round(ext_flops / 1e12, 4),
@@ -215,7 +219,7 @@ def main():
             "tokens_per_s": round(B * E / (ext_ms * 1e-3), 1),
         },
         "decode": {
-            "attention_ms": round(dec_ms, 5), "wide_ms": round(wide_ms, 5), "narrow_ms": round(narrow_ms, 5),
+            "attention_ms": round(dec_ms, 5),
             "merge_avg_ms": round(mrg_ms, 5), "gbs": round(dec_gbs, 1),
             "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
             "unique_bytes_per_step": float(np.mean(dec_bytes_steps)),
@@ -228,6 +232,8 @@ def main():
                      "gbs": round(store_bytes / (st_tot * 1e-3) / 1e9, 1)},
         "kernel_ms_per_step": {k: round(v[1] / args.steps, 4) for k, v in prof.items()},
     }
+    if args.host_phases:
+        res["host_phase_ms"] = phases
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_sample, args.cpu_decode_steps, tokens_per_step, T)
     print(json.dumps(res))

@@ -247,6 +247,16 @@ rc_status rc_radix_free(rc_radix* tree, const int32_t* slots, int64_t n);
 rc_status rc_radix_insert(rc_radix* tree, const int32_t* tokens, int32_t* slots_inout, int64_t n,
                           int64_t* n_new);
 
+/* Batched insert ("commit"): for each request b, rc_radix_insert of         */
+/* tokens[tok_off[b] .. tok_off[b+1]) with the slots held in row rows[b] of   */
+/* the host table, rewriting that row in place where the tree already held   */
+/* the tokens.  changed (host, nullable, batch entries) is set to 1 for rows */
+/* that were rewritten.  Requests are processed in order; on a failure the   */
+/* requests before the failing one stay inserted (RC_ERR_* names it).        */
+rc_status rc_radix_insert_rows(rc_radix* tree, int32_t batch, const int32_t* tokens, const int64_t* tok_off,
+                               const int32_t* rows, int32_t* req_to_token, int32_t table_rows, int64_t stride,
+                               int32_t* changed);
+
 /* Rows of the request -> slot table for a batch.  Request b has tokens      */
 /* tokens[tok_off[b] .. tok_off[b+1]) (host, CSR).  Row rows[b] of the host   */
 /* table req_to_token [*, stride] receives [matched prefix slots | new slots */

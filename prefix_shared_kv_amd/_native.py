@@ -67,6 +67,7 @@ _SIGS = {
     "rc_radix_free": (i32, [P, P, i64]),
     "rc_radix_insert": (i32, [P, P, P, i64, I64P]),
     "rc_radix_emit_rows": (i32, [P, i32, P, P, i32, P, P, i32, i64, P, P]),
+    "rc_radix_insert_rows": (i32, [P, i32, P, P, P, P, i32, i64, P]),
     "rc_radix_fork": (i32, [P, P, P, i64, i32, P, P, i32, i64]),
     "rc_radix_plan_decode": (i32, [P, i32, P, P, P, P, i32, i32, P, i64, C.POINTER(RcPlanInfo)]),
     "rc_radix_stats_get": (i32, [P, C.POINTER(RcRadixStats)]),

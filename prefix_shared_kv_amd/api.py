@@ -123,8 +123,9 @@ class DecodePlan:
         self.info = info
         self.dev: Optional[torch.Tensor] = None
 
-    def to(self, device) -> "DecodePlan":
-        self.dev = torch.from_numpy(self.host).to(device)
+    def to(self, device, uploader=None) -> "DecodePlan":
+        """Device copy of the plan; `uploader(array) -> tensor` may supply an asynchronous copy."""
+        self.dev = uploader(self.host) if uploader is not None else torch.from_numpy(self.host).to(device)
         return self
 
     @property
@@ -251,6 +252,20 @@ class RadixTree:
         check(lib.rc_radix_emit_rows(self._h, B, _np_ptr(flat), _np_ptr(off), reserve, _np_ptr(rw), _np_ptr(table),
                                      table.shape[0], table.shape[1], _np_ptr(P), _np_ptr(E)))
         return P, E
+
+    def insert_rows(self, batch: Sequence[Sequence[int]], table: np.ndarray, rows: Sequence[int],
+                    lengths: Optional[Sequence[int]] = None) -> np.ndarray:
+        """Insert each request's first lengths[i] tokens (default: all) with the slots of its table
+        row; rows are rewritten in place to the tree's slots.  Returns a bool mask of changed rows."""
+        if table.dtype != np.int32 or table.ndim != 2 or not table.flags.c_contiguous:
+            raise ValueError("table must be a C-contiguous int32 [rows, stride] array")
+        toks = batch if lengths is None else [np.asarray(t)[:int(n)] for t, n in zip(batch, lengths)]
+        flat, off = _csr(toks)
+        rw = np.ascontiguousarray(rows, np.int32)
+        changed = np.zeros(len(toks), np.int32)
+        check(lib.rc_radix_insert_rows(self._h, len(toks), _np_ptr(flat), _np_ptr(off), _np_ptr(rw), _np_ptr(table),
+                                       table.shape[0], table.shape[1], _np_ptr(changed)))
+        return changed.astype(bool)
 
     def fork(self, tokens, parent_slots, child_rows: Sequence[int], table: np.ndarray) -> None:
         t = np.ascontiguousarray(tokens, np.int32)

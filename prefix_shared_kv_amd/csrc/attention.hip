@@ -73,6 +73,7 @@ struct Args {
   const int32_t* plan;
   int32_t n_items, n_members;  // from the planner's host summary
   int32_t narrow_begin;        // first item with members*group <= 16
+  int32_t n_wide_blocks;       // workgroups that run wide items
   int32_t n_narrow_units;      // (narrow item, kv head) pairs, one wave each
   int32_t rows_path;           // narrow items by groups of four kv heads (Hkv % 4 == 0)
   const int32_t* seq_lens;
@@ -825,25 +826,25 @@ __global__ __launch_bounds__(NT, 2) void extend_attn_bf16(Args a) {
   attn_bf16_body<D>(a, EXTEND, xcd_remap(blockIdx.x, a.n_work), sK, sV);
 }
 
-// Wide decode items: workgroup-cooperative tiles, listed heaviest first and
-// dealt round-robin over the XCDs.
+// Decode, one launch: the plan lists wide items (workgroup-cooperative tiles,
+// heaviest first) before narrow ones, and blocks are dispatched in order, so
+// the long wide workgroups start first and the narrow ones (four independent
+// waves per block, each with its own K and V tile) fill in behind them.  Both
+// paths need 2 waves per SIMD and 64 KiB of LDS, so one kernel costs neither
+// occupancy, and there is no gap between two launches.
 template <int D>
 __global__ __launch_bounds__(NT, 2) void decode_attn_bf16(Args a) {
   __shared__ __attribute__((aligned(16))) uint16_t sK[2][BN * D];
   __shared__ __attribute__((aligned(16))) uint16_t sV[2][BN * D];
-  attn_bf16_body<D>(a, DECODE, blockIdx.x, sK, sV);
-}
-
-// Narrow decode items: four independent waves per workgroup, each with its own
-// K and V tile.
-template <int D>
-__global__ __launch_bounds__(NT) void decode_narrow_bf16(Args a) {
-  __shared__ __attribute__((aligned(16))) uint16_t sK[4 * BNN * D];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[4 * BNN * D];
+  static_assert(2 * BN == 4 * BNN, "narrow tiles reuse the wide stage buffers");
+  if ((int)blockIdx.x < a.n_wide_blocks) {
+    attn_bf16_body<D>(a, DECODE, blockIdx.x, sK, sV);
+    return;
+  }
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave
-  const int unit = (int)blockIdx.x * 4 + wave;
+  const int unit = ((int)blockIdx.x - a.n_wide_blocks) * 4 + wave;
   if (unit >= a.n_narrow_units) return;
-  decode_narrow_body<D>(a, unit, sK + wave * BNN * D, sV + wave * BNN * D);
+  decode_narrow_body<D>(a, unit, &sK[0][0] + wave * BNN * D, &sV[0][0] + wave * BNN * D);
 }
 
 // Narrow decode items, one workgroup per group of four kv heads.
@@ -1102,32 +1103,34 @@ extern "C" rc_status rc_decode_attention(const rc_shape* shape, void* o, const v
     a.rows_path = rc::tuning().decode_rows && a.Hkv % HG == 0;
     const int64_t n_narrow = a.rows_path ? units / HG : (units + 3) / 4;
     if (n_wide > INT32_MAX || n_narrow > INT32_MAX) return fail(RC_ERR_RANGE, "grid too large");
-    if (n_wide > 0) {
-      a.n_work = (int32_t)n_wide;
-      ProfScope p(shape->head_dim == 128 ? "decode_wide_d128" : "decode_wide_d64", s);
-      if (shape->head_dim == 128)
-        hipLaunchKernelGGL(decode_attn_bf16<128>, dim3((unsigned)n_wide), dim3(NT), 0, s, a);
-      else
-        hipLaunchKernelGGL(decode_attn_bf16<64>, dim3((unsigned)n_wide), dim3(NT), 0, s, a);
-    }
-    st = check_launch("decode attention (wide items)");
-    if (st != RC_OK) return st;
-    if (n_narrow > 0) {
-      a.n_work = (int32_t)n_narrow;
-      ProfScope p(shape->head_dim == 128 ? "decode_narrow_d128" : "decode_narrow_d64", s);
-      if (a.rows_path) {
+    ProfScope p(shape->head_dim == 128 ? "decode_attention_d128" : "decode_attention_d64", s);
+    if (a.rows_path) {
+      // grouped-heads variant: wide items, then narrow items, two launches
+      if (n_wide > 0) {
+        Args aw = a;
+        aw.n_wide_blocks = (int32_t)n_wide;
+        aw.n_narrow_units = 0;
+        if (shape->head_dim == 128)
+          hipLaunchKernelGGL(decode_attn_bf16<128>, dim3((unsigned)n_wide), dim3(NT), 0, s, aw);
+        else
+          hipLaunchKernelGGL(decode_attn_bf16<64>, dim3((unsigned)n_wide), dim3(NT), 0, s, aw);
+      }
+      if (n_narrow > 0) {
         if (shape->head_dim == 128)
           hipLaunchKernelGGL(decode_rows_bf16<128>, dim3((unsigned)n_narrow), dim3(NT), 0, s, a);
         else
           hipLaunchKernelGGL(decode_rows_bf16<64>, dim3((unsigned)n_narrow), dim3(NT), 0, s, a);
-      } else {
-        if (shape->head_dim == 128)
-          hipLaunchKernelGGL(decode_narrow_bf16<128>, dim3((unsigned)n_narrow), dim3(NT), 0, s, a);
-        else
-          hipLaunchKernelGGL(decode_narrow_bf16<64>, dim3((unsigned)n_narrow), dim3(NT), 0, s, a);
       }
+    } else if (n_wide + n_narrow > 0) {
+      a.n_wide_blocks = (int32_t)n_wide;
+      const int64_t grid = n_wide + n_narrow;
+      if (grid > INT32_MAX) return fail(RC_ERR_RANGE, "grid too large");
+      if (shape->head_dim == 128)
+        hipLaunchKernelGGL(decode_attn_bf16<128>, dim3((unsigned)grid), dim3(NT), 0, s, a);
+      else
+        hipLaunchKernelGGL(decode_attn_bf16<64>, dim3((unsigned)grid), dim3(NT), 0, s, a);
     }
-    st = check_launch("decode attention (narrow items)");
+    st = check_launch("decode attention");
     if (st != RC_OK) return st;
   }
   const int32_t* nsplit = plan_dev + RC_PLAN_HEADER + (int64_t)info->n_items * RC_PLAN_ITEM + info->n_members;

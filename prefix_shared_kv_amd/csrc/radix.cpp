@@ -278,6 +278,29 @@ rc_status rc_radix_insert(rc_radix* t, const int32_t* tokens, int32_t* slots, in
   return RC_OK;
 }
 
+rc_status rc_radix_insert_rows(rc_radix* t, int32_t batch, const int32_t* tokens, const int64_t* tok_off,
+                               const int32_t* rows, int32_t* table, int32_t table_rows, int64_t stride,
+                               int32_t* changed) {
+  if (!t || batch < 0 || stride <= 0) return fail(RC_ERR_ARG, "bad argument to rc_radix_insert_rows");
+  if (batch > 0 && (!tok_off || !rows || !table)) return fail(RC_ERR_ARG, "NULL array in rc_radix_insert_rows");
+  for (int32_t b = 0; b < batch; ++b) {
+    const int64_t n = tok_off[b + 1] - tok_off[b];
+    if (n < 0 || tok_off[b] < 0) return fail(RC_ERR_ARG, "tok_off not non-decreasing at %d", b);
+    if (rows[b] < 0 || rows[b] >= table_rows) return fail(RC_ERR_RANGE, "row %d of request %d outside [0, %d)", rows[b], b, table_rows);
+    if (n > stride) return fail(RC_ERR_RANGE, "request %d has %lld tokens, stride is %lld", b, (long long)n, (long long)stride);
+  }
+  std::vector<int32_t> before;
+  for (int32_t b = 0; b < batch; ++b) {
+    const int64_t n = tok_off[b + 1] - tok_off[b];
+    int32_t* row = table + (int64_t)rows[b] * stride;
+    if (changed) before.assign(row, row + n);
+    rc_status st = rc_radix_insert(t, tokens + tok_off[b], row, n, nullptr);
+    if (st != RC_OK) return st;
+    if (changed) changed[b] = !std::equal(before.begin(), before.end(), row);
+  }
+  return RC_OK;
+}
+
 rc_status rc_radix_emit_rows(rc_radix* t, int32_t batch, const int32_t* tokens, const int64_t* tok_off,
                              int32_t reserve, const int32_t* rows, int32_t* table, int32_t table_rows,
                              int64_t stride, int32_t* prefix_lens, int32_t* extend_lens) {

@@ -73,17 +73,55 @@ class Engine:
         self.free_rows = list(range(max_rows))
 
     # -- helpers ------------------------------------------------------------
+    # Host->device copies go through a ring of persistent pinned staging
+    # buffers and do not block the host, which keeps preparing (tree calls,
+    # plans) while the GPU works.  A buffer is rewritten only after the copy
+    # that last read it has completed (its event); allocating pinned memory
+    # per copy instead can synchronise the whole device.
+    _RING = 32
+
+    def _pinned(self, a: np.ndarray) -> torch.Tensor:
+        a = np.ascontiguousarray(a)
+        if not hasattr(self, "_ring"):
+            self._ring = [[None, None] for _ in range(self._RING)]
+            self._ring_i = 0
+        slot = self._ring[self._ring_i]
+        self._ring_i = (self._ring_i + 1) % self._RING
+        buf, ev = slot
+        if ev is not None:
+            ev.synchronize()
+        if buf is None or buf.numel() < a.nbytes:
+            buf = torch.empty(max(a.nbytes, 1 << 16), dtype=torch.uint8, pin_memory=True)
+            slot[0] = buf
+        view = buf[:a.nbytes].view(torch.from_numpy(a[:0].reshape(-1)).dtype).view(a.shape)
+        view.copy_(torch.from_numpy(a))
+        slot[1] = None
+        self._last_slot = slot
+        return view
+
+    def _h2d(self, a: np.ndarray, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+        src = self._pinned(a)
+        if out is None:
+            out = torch.empty(src.shape, dtype=src.dtype, device=self.device)
+        out.copy_(src, non_blocking=True)
+        ev = torch.cuda.Event()
+        ev.record(torch.cuda.current_stream(self.device))
+        self._last_slot[1] = ev
+        return out
+
     def _i32(self, a) -> torch.Tensor:
-        return torch.from_numpy(np.ascontiguousarray(a, np.int32)).to(self.device, non_blocking=False)
+        return self._h2d(np.asarray(a, np.int32))
 
     def _upload_rows(self, rows: np.ndarray) -> None:
         if len(rows) == 0:
             return
         r = np.asarray(rows, np.int64)
         if np.all(np.diff(r) == 1):
-            self.table_d[int(r[0]):int(r[-1]) + 1].copy_(torch.from_numpy(self.table_h[int(r[0]):int(r[-1]) + 1]))
+            lo, hi = int(r[0]), int(r[-1]) + 1
+            self._h2d(self.table_h[lo:hi], out=self.table_d[lo:hi])
         else:
-            self.table_d[torch.from_numpy(r).to(self.device)] = torch.from_numpy(self.table_h[r]).to(self.device)
+            idx = self._h2d(r)
+            self.table_d[idx] = self._h2d(self.table_h[r])
 
     # -- cache population (a sequence whose K/V are already known) -----------
     def populate(self, tokens: Sequence[int], k: torch.Tensor, v: torch.Tensor, expect_cached: Optional[int] = None) -> int:
@@ -144,14 +182,8 @@ class Engine:
     def commit(self, b: Batch, lengths: Optional[Sequence[int]] = None) -> None:
         """Insert each request's first `lengths[i]` tokens (default: all) into the tree.
         Where the tree already held them, the row is rewritten to the tree's slots."""
-        dirty = []
-        for i, (t, r) in enumerate(zip(b.tokens, b.rows)):
-            n = len(t) if lengths is None else int(lengths[i])
-            canon, _ = self.tree.insert(t[:n], self.table_h[r, :n])
-            if not np.array_equal(canon, self.table_h[r, :n]):
-                self.table_h[r, :n] = canon
-                dirty.append(r)
-        self._upload_rows(np.array(sorted(dirty), np.int32))
+        changed = self.tree.insert_rows(b.tokens, self.table_h, b.rows, lengths)
+        self._upload_rows(np.sort(b.rows[changed]))
 
     def prepare_decode(self, b: Batch, base_lens: Sequence[int], n_steps: int, chunk: int = 512,
                        shared: bool = True, committed: Optional[Sequence[int]] = None) -> DecodeState:
@@ -167,7 +199,7 @@ class Engine:
             plan = self.tree.plan_decode([t[:c] for t, c in zip(b.tokens, com)], max_seq, g, chunk, rows=b.rows)
         else:
             plan = api.plan_decode_unshared(max_seq, g, chunk, rows=b.rows)
-        plan.to(self.device)
+        plan.to(self.device, uploader=self._h2d)
         steps = np.arange(n_steps, dtype=np.int32)[:, None]
         pos = base[None, :] + steps                                    # [T, B]
         slots = self.table_h[b.rows[None, :].repeat(n_steps, 0), pos]  # [T, B]
@@ -188,10 +220,12 @@ class Engine:
     def release(self, b: Batch, keep: Optional[Sequence[int]] = None) -> None:
         """Return the batch's table rows; slots past `keep[i]` (default: tokens given) go back to the pool
         unless the tree holds them."""
+        tails = []
         for i, (t, r) in enumerate(zip(b.tokens, b.rows)):
             n = len(t) if keep is None else int(keep[i])
-            tail = self.table_h[r, n:len(t) + b.reserve]
-            if tail.size:
-                self.tree.free(tail)
+            tails.append(self.table_h[r, n:len(t) + b.reserve])
+        if tails:
+            self.tree.free(np.concatenate(tails))
+        for r in b.rows:
             self.table_h[r, :] = -1
             self.free_rows.append(int(r))

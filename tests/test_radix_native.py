@@ -82,11 +82,20 @@ def test_tree_matches_bruteforce(sc):
                 n = len(toks) + reserve
                 assert table[b, :n].tolist() == rows_w[b]
             # commit each request's prompt; rows get the tree's slots back
-            for b, toks in enumerate(batch):
-                canon, n_new = tree.insert(toks, table[b, :len(toks)])
-                canon_w, n_new_w = ref.insert(toks, rows_w[b][:len(toks)])
-                assert canon.tolist() == canon_w and n_new == n_new_w
+            if len(ops) % 2:
+                for b, toks in enumerate(batch):
+                    canon, n_new = tree.insert(toks, table[b, :len(toks)])
+                    canon_w, n_new_w = ref.insert(toks, rows_w[b][:len(toks)])
+                    assert canon.tolist() == canon_w and n_new == n_new_w
+            else:  # the batched commit
+                before = table.copy()
+                changed = tree.insert_rows(batch, table, list(range(len(batch))))
+                for b, toks in enumerate(batch):
+                    canon_w, _ = ref.insert(toks, rows_w[b][:len(toks)])
+                    assert table[b, :len(toks)].tolist() == canon_w
+                    assert bool(changed[b]) == (before[b, :len(toks)].tolist() != canon_w)
                 # reserved decode slots are not used here: give them back
+            for b, toks in enumerate(batch):
                 if reserve:
                     tree.free(table[b, len(toks):len(toks) + reserve])
                     ref.free_slots(rows_w[b][len(toks):len(toks) + reserve])
