@@ -168,10 +168,11 @@ def main():
     # unique positions read at decode step t: every cached node once, plus each request's own tokens
     own = E + np.arange(T) + 1  # new tokens + decode tokens so far (the current one included)
     uniq = cached + B * own
-    dec_bytes_steps = uniq * (row_bytes + 4) + 2 * B * Hq * D * 2  # KV + slot index + q + o
+    # KV rows + slot index + q + o, and the current token's K/V: read once, written to its pool slot
+    dec_bytes_steps = uniq * (row_bytes + 4) + 2 * B * Hq * D * 2 + 2 * B * row_bytes
     logical = B * (P.mean() + own)
 
-    store_bytes = (B * E + B * T) * (2 * row_bytes + 4)  # read new K/V, write pool rows, slot index
+    store_bytes = B * E * (2 * row_bytes + 4)  # the extend's new tokens: read K/V, write pool rows, slot index
     ext_name, mrg_name, st_name = "extend_bf16_d128", "decode_merge", "kv_store"
     dec_name = "decode_attention_d128"  # one launch per step: wide and narrow items
     ext_ms = prof[ext_name][1] / prof[ext_name][0]

@@ -181,21 +181,25 @@ int64_t rc_decode_workspace_bytes(const rc_shape* shape, const rc_plan_info* inf
 /* Decode attention  [PC] "How prompt caching works": each new token attends */
 /* to all cached keys and values.  One query token per request b:            */
 /*   o[b, h] = sum_{j < L_b} softmax_j(sm_scale * q[b,h] . k_j) v_j,          */
-/* L_b = seq_lens[b] includes the current token (store its K/V first).       */
-/* Keys come from the pool through the plan's table rows.  Split-K: each     */
-/* item writes fp32 partial (max, sum, unnormalised output) per member and   */
-/* head; a merge kernel combines each request's partials in split order      */
-/* (deterministic, no float atomics).                                         */
+/* L_b = seq_lens[b] counts the current token.  Keys come from the pool      */
+/* through the plan's table rows.  The current token's K/V either are in the */
+/* pool already (k_new = v_new = new_slots = NULL), or are passed in k_new / */
+/* v_new [batch, Hkv, D]: then the call also stores them at pool slot        */
+/* new_slots[b] (what rc_kv_store would do) and uses them as key L_b - 1.    */
+/* Split-K: each item writes fp32 partial (max, sum, unnormalised output)    */
+/* per member and head; a merge kernel combines each request's partials in   */
+/* split order (deterministic, no float atomics).                             */
 /*   o, q          : device [batch, Hq, D]                                    */
+/*   k_pool, v_pool: device [pool_slots, Hkv, D] (written only with k_new)    */
 /*   req_to_token  : device int32 [table_rows, stride]                        */
 /*   seq_lens      : device int32 [batch]                                     */
 /*   plan_dev      : device copy of the plan buffer (info->plan_ints int32);  */
 /*                   info: the summary the planner returned with it          */
 /*   workspace     : device, >= rc_decode_workspace_bytes() bytes             */
 /* ------------------------------------------------------------------------ */
-rc_status rc_decode_attention(const rc_shape* shape, void* o, const void* q, const void* k_pool,
-                              const void* v_pool, const int32_t* req_to_token, int32_t table_rows,
-                              int64_t stride,
+rc_status rc_decode_attention(const rc_shape* shape, void* o, const void* q, void* k_pool, void* v_pool,
+                              const void* k_new, const void* v_new, const int32_t* new_slots,
+                              const int32_t* req_to_token, int32_t table_rows, int64_t stride,
                               const int32_t* seq_lens, int32_t batch, const int32_t* plan_dev,
                               const rc_plan_info* info, float sm_scale, void* workspace,
                               int64_t ws_bytes, void* stream);

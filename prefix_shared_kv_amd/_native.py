@@ -58,8 +58,8 @@ _SIGS = {
     "rc_extend_attention": (i32, [C.POINTER(RcShape), P, P, P, P, P, P, P, i32, i64, P, P, P, P, i32, i64, i32, f32, P]),
     "rc_plan_decode_unshared": (i32, [i32, P, P, i32, i32, P, i64, C.POINTER(RcPlanInfo)]),
     "rc_decode_workspace_bytes": (i64, [C.POINTER(RcShape), C.POINTER(RcPlanInfo)]),
-    "rc_decode_attention": (i32, [C.POINTER(RcShape), P, P, P, P, P, i32, i64, P, i32, P, C.POINTER(RcPlanInfo), f32,
-                                  P, i64, P]),
+    "rc_decode_attention": (i32, [C.POINTER(RcShape), P, P, P, P, P, P, P, P, i32, i64, P, i32, P,
+                                  C.POINTER(RcPlanInfo), f32, P, i64, P]),
     "rc_radix_create": (i32, [i64, P, C.POINTER(P)]),
     "rc_radix_destroy": (None, [P]),
     "rc_radix_match": (i32, [P, P, i64, P, I64P]),

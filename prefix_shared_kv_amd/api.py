@@ -169,8 +169,9 @@ def decode_workspace_bytes(shape: KVShape, plan: DecodePlan) -> int:
 
 
 def decode_attention(shape: KVShape, o, q, k_pool, v_pool, req_to_token, seq_lens, plan: DecodePlan, sm_scale: float,
-                     workspace, stream=None) -> None:
-    """One query token per request over its whole context, through a share plan (rc_decode_attention)."""
+                     workspace, k_new=None, v_new=None, new_slots=None, stream=None) -> None:
+    """One query token per request over its whole context, through a share plan (rc_decode_attention).
+    With k_new/v_new/new_slots the current tokens' K/V are stored into the pool by the same call."""
     Hq, Hkv, D, S = shape.num_q_heads, shape.num_kv_heads, shape.head_dim, shape.pool_slots
     B = q.shape[0]
     _dev(q, "q", shape.dtype, (B, Hq, D))
@@ -179,14 +180,20 @@ def decode_attention(shape: KVShape, o, q, k_pool, v_pool, req_to_token, seq_len
     _dev(v_pool, "v_pool", shape.dtype, (S, Hkv, D))
     _dev(req_to_token, "req_to_token", torch.int32)
     _dev(seq_lens, "seq_lens", torch.int32, (B,))
+    if (k_new is None) != (v_new is None) or (k_new is None) != (new_slots is None):
+        raise ValueError("k_new, v_new and new_slots go together")
+    if k_new is not None:
+        _dev(k_new, "k_new", shape.dtype, (B, Hkv, D))
+        _dev(v_new, "v_new", shape.dtype, (B, Hkv, D))
+        _dev(new_slots, "new_slots", torch.int32, (B,))
     if plan.dev is None:
         raise ValueError("plan has no device copy; call plan.to(device)")
     _dev(workspace, "workspace")
     sh = shape.c()
-    check(lib.rc_decode_attention(C.byref(sh), _vp(o), _vp(q), _vp(k_pool), _vp(v_pool), _vp(req_to_token),
-                                  req_to_token.shape[0], req_to_token.shape[1], _vp(seq_lens), B, _vp(plan.dev),
-                                  C.byref(plan.info), float(sm_scale), _vp(workspace),
-                                  workspace.numel() * workspace.element_size(), _stream(stream)))
+    check(lib.rc_decode_attention(C.byref(sh), _vp(o), _vp(q), _vp(k_pool), _vp(v_pool), _vp(k_new), _vp(v_new),
+                                  _vp(new_slots), _vp(req_to_token), req_to_token.shape[0], req_to_token.shape[1],
+                                  _vp(seq_lens), B, _vp(plan.dev), C.byref(plan.info), float(sm_scale),
+                                  _vp(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
 def _csr(batch: Sequence[Sequence[int]]) -> Tuple[np.ndarray, np.ndarray]:

@@ -71,6 +71,7 @@ struct Args {
   int32_t tok_per_tile;
   // decode
   const int32_t* plan;
+  const int32_t* new_slots;    // decode: pool slot of each request's current token (with k_new/v_new)
   int32_t n_items, n_members;  // from the planner's host summary
   int32_t narrow_begin;        // first item with members*group <= 16
   int32_t n_wide_blocks;       // workgroups that run wide items
@@ -96,6 +97,7 @@ struct Work {
   int32_t t0, E, P;
   // decode
   int32_t split, moff, mcnt;
+  int32_t store_b;     // request whose current token this item stores and reads from k_new (-1: none)
 };
 
 __device__ __forceinline__ void flag(int32_t* err, int32_t bit) {
@@ -105,6 +107,7 @@ __device__ __forceinline__ void flag(int32_t* err, int32_t bit) {
 __device__ Work resolve(const Args& a, int mode, int L, bool leader) {
   Work w{};
   w.valid = false;
+  w.store_b = -1;
   if (mode == EXTEND) {
     const int tile = L % a.tiles;
     const int bh = L / a.tiles;
@@ -171,11 +174,36 @@ __device__ Work resolve(const Args& a, int mode, int L, bool leader) {
     if (w.key_end < w.key_begin) w.key_end = w.key_begin;
     w.ext_begin = INT_MAX;
     w.ext_base = 0;
+    w.store_b = -1;
+    // The item holding a request's last position (its own range) takes the
+    // current token's K/V from k_new/v_new and writes them to the pool.
+    if (a.k_new && w.mcnt == 1 && sl >= 1 && pb <= sl - 1 && pe >= sl) {
+      w.ext_begin = sl - 1;
+      w.ext_base = mem[0];
+      w.store_b = mem[0];
+    }
     w.ncols = w.mcnt * a.g;
     w.min_limit = INT_MAX;
     w.valid = true;
   }
   return w;
+}
+
+// Copy request b's current-token K and V row of kv head hk into its pool slot
+// (threads [0, n) of the caller, 8 elements each; n = D / 8 covers the row).
+template <typename T, int D>
+__device__ __forceinline__ void store_new_token(const Args& a, int b, int hk, int t) {
+  constexpr int VEC = 16 / sizeof(T);
+  if (t >= D / VEC) return;
+  const int32_t s = a.new_slots[b];
+  if ((uint32_t)s >= (uint32_t)a.pool_slots) {
+    if (t == 0) flag(a.err, RC_DEVERR_SLOT);
+    return;
+  }
+  const int64_t src = ((int64_t)b * a.Hkv + hk) * D + t * VEC;
+  const int64_t dst = ((int64_t)s * a.Hkv + hk) * D + t * VEC;
+  *(uint4*)((T*)a.k_pool + dst) = *(const uint4*)((const T*)a.k_new + src);
+  *(uint4*)((T*)a.v_pool + dst) = *(const uint4*)((const T*)a.v_new + src);
 }
 
 // Per-column (query) information.
@@ -249,6 +277,7 @@ __device__ __forceinline__ void attn_bf16_body(const Args& a, const int mode, co
   const int c = wave * 32 + (lane & 31);
   const bool active = wave * 32 < w.ncols;
   const Col col = column(a, mode, w, c);
+  if (w.store_b >= 0) store_new_token<uint16_t, D>(a, w.store_b, w.hk, tid);
 
   const uint16_t* q = (const uint16_t*)a.q;
   bf16x8 qf[NKS];
@@ -503,24 +532,31 @@ __device__ __forceinline__ void decode_narrow_body(const Args& a, const int unit
   const int32_t* trow = a.table + w.row * a.stride;
   int bad_slot = 0;
 
+  constexpr int NEWTOK = INT_MIN + 1;  // the current token: read from k_new/v_new
   auto load_slots = [&](int (&sl)[NI], int kt) {
 #pragma unroll
     for (int t = 0; t < NI; ++t) {
       const int key = kt + t * KPI + lk;
-      sl[t] = key < w.key_end ? trow[key] : INT_MIN;  // INT_MIN: past the range end
+      // INT_MIN: past the range end
+      sl[t] = key < w.key_end ? (key >= w.ext_begin ? NEWTOK : trow[key]) : INT_MIN;
     }
   };
   auto load_kv = [&](u32x4 (&kr)[NI], u32x4 (&vr)[NI], const int (&sl)[NI], bool partial) {
 #pragma unroll
     for (int t = 0; t < NI; ++t) {
       const bool ok = (uint32_t)sl[t] < (uint32_t)a.pool_slots;
-      bad_slot |= !ok & (sl[t] != INT_MIN);
+      bad_slot |= !ok & (sl[t] != INT_MIN) & (sl[t] != NEWTOK);
       const int64_t off = (int64_t)(ok ? sl[t] : 0) * rowHD;
       kr[t] = *(const u32x4*)(kbase + off);
       vr[t] = *(const u32x4*)(vbase + off);
       if (partial && !ok) {  // keys past the end must hold finite values: p = 0 multiplies them
         kr[t] = u32x4{0, 0, 0, 0};
         vr[t] = u32x4{0, 0, 0, 0};
+        if (sl[t] == NEWTOK) {
+          const int64_t noff = ((int64_t)w.ext_base * a.Hkv + w.hk) * D + lc * 8;
+          kr[t] = *(const u32x4*)((const uint16_t*)a.k_new + noff);
+          vr[t] = *(const u32x4*)((const uint16_t*)a.v_new + noff);
+        }
       }
     }
   };
@@ -597,13 +633,15 @@ __device__ __forceinline__ void decode_narrow_body(const Args& a, const int unit
     }
   };
 
+  if (w.store_b >= 0) store_new_token<uint16_t, D>(a, w.store_b, w.hk, lane);
   const int kb = w.key_begin;
   const int n_st = (w.key_end - kb + BNN - 1) / BNN;
+  const int plain_end = min(w.key_end, w.ext_begin);  // stages ending after this take the careful path
   int slA[NI], slB[NI];
   u32x4 kr[NI], vr[NI];
   if (n_st > 0) load_slots(slA, kb);
   if (n_st > 1) load_slots(slB, kb + BNN);
-  if (n_st > 0) load_kv(kr, vr, slA, kb + BNN > w.key_end);
+  if (n_st > 0) load_kv(kr, vr, slA, kb + BNN > plain_end);
   if (n_st > 2) load_slots(slA, kb + 2 * BNN);
   // The LDS tile is private to the wave and LDS operations of a wave complete
   // in order, so the next stage may overwrite it right after this stage's reads.
@@ -611,7 +649,7 @@ __device__ __forceinline__ void decode_narrow_body(const Args& a, const int unit
     int kt = kb + i * BNN;
     store(kr, vr);
     if (i + 1 < n_st) {
-      load_kv(kr, vr, slB, kt + 2 * BNN > w.key_end);
+      load_kv(kr, vr, slB, kt + 2 * BNN > plain_end);
       if (i + 3 < n_st) load_slots(slB, kt + 3 * BNN);
     }
     compute(kt);
@@ -619,7 +657,7 @@ __device__ __forceinline__ void decode_narrow_body(const Args& a, const int unit
     kt += BNN;
     store(kr, vr);
     if (i + 2 < n_st) {
-      load_kv(kr, vr, slA, kt + 2 * BNN > w.key_end);
+      load_kv(kr, vr, slA, kt + 2 * BNN > plain_end);
       if (i + 4 < n_st) load_slots(slA, kt + 3 * BNN);
     }
     compute(kt);
@@ -864,6 +902,7 @@ __device__ __forceinline__ void attn_f32_body(const Args& a, const int mode) {
   const Work w = resolve(a, mode, L, threadIdx.x == 0);
   if (!w.valid) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (w.store_b >= 0) store_new_token<float, D>(a, w.store_b, w.hk, threadIdx.x);
   const float* q = (const float*)a.q;
   const float* kpool = (const float*)a.k_pool;
   const float* vpool = (const float*)a.v_pool;
@@ -1044,8 +1083,9 @@ extern "C" int64_t rc_decode_workspace_bytes(const rc_shape* shape, const rc_pla
   return parts * shape->head_dim * 4 + parts * 2 * 4;
 }
 
-extern "C" rc_status rc_decode_attention(const rc_shape* shape, void* o, const void* q, const void* k_pool,
-                                         const void* v_pool, const int32_t* req_to_token, int32_t table_rows,
+extern "C" rc_status rc_decode_attention(const rc_shape* shape, void* o, const void* q, void* k_pool,
+                                         void* v_pool, const void* k_new, const void* v_new,
+                                         const int32_t* new_slots, const int32_t* req_to_token, int32_t table_rows,
                                          int64_t stride, const int32_t* seq_lens, int32_t batch, const int32_t* plan_dev,
                                          const rc_plan_info* info, float sm_scale, void* workspace,
                                          int64_t ws_bytes, void* stream) {
@@ -1057,6 +1097,8 @@ extern "C" rc_status rc_decode_attention(const rc_shape* shape, void* o, const v
   if (!info) return fail(RC_ERR_ARG, "plan info is NULL");
   if (!o || !q || !k_pool || !v_pool || !req_to_token || !seq_lens || !plan_dev || !workspace)
     return fail(RC_ERR_ARG, "NULL device pointer in rc_decode_attention");
+  if ((k_new != nullptr) != (v_new != nullptr) || (k_new != nullptr) != (new_slots != nullptr))
+    return fail(RC_ERR_ARG, "k_new, v_new and new_slots must be given together");
   const int g = shape->num_q_heads / shape->num_kv_heads;
   if (info->batch != batch) return fail(RC_ERR_ARG, "plan built for batch %d, called with %d", info->batch, batch);
   if (info->group != g) return fail(RC_ERR_SHAPE, "plan built for group %d, shape has %d", info->group, g);
@@ -1068,6 +1110,7 @@ extern "C" rc_status rc_decode_attention(const rc_shape* shape, void* o, const v
   const int64_t parts = (int64_t)batch * shape->num_q_heads * info->max_splits;
   Args a{};
   a.q = q; a.o = o; a.k_pool = k_pool; a.v_pool = v_pool;
+  a.k_new = k_new; a.v_new = v_new; a.new_slots = new_slots;
   a.table = req_to_token; a.table_rows = table_rows; a.stride = stride; a.pool_slots = shape->pool_slots;
   a.Hq = shape->num_q_heads; a.Hkv = shape->num_kv_heads; a.g = g;
   a.scale_log2 = sm_scale * LOG2E;
@@ -1103,6 +1146,13 @@ extern "C" rc_status rc_decode_attention(const rc_shape* shape, void* o, const v
     a.rows_path = rc::tuning().decode_rows && a.Hkv % HG == 0;
     const int64_t n_narrow = a.rows_path ? units / HG : (units + 3) / 4;
     if (n_wide > INT32_MAX || n_narrow > INT32_MAX) return fail(RC_ERR_RANGE, "grid too large");
+    if (a.rows_path && a.k_new) {
+      // the grouped-heads variant reads every key from the pool: store first
+      st = rc_kv_store(shape, k_pool, v_pool, k_new, v_new, new_slots, batch, stream);
+      if (st != RC_OK) return st;
+      a.k_new = a.v_new = nullptr;
+      a.new_slots = nullptr;
+    }
     ProfScope p(shape->head_dim == 128 ? "decode_attention_d128" : "decode_attention_d64", s);
     if (a.rows_path) {
       // grouped-heads variant: wide items, then narrow items, two launches

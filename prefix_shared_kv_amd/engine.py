@@ -208,13 +208,18 @@ class Engine:
         return DecodeState(plan, base, n_steps, self._i32(slots), self._i32(seq), ws)
 
     def decode_step(self, st: DecodeState, t: int, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
-                    sm_scale: float, o: Optional[torch.Tensor] = None) -> torch.Tensor:
-        """Store step t's K/V, then attend over each request's whole context."""
-        api.kv_store(self.shape, self.k_pool, self.v_pool, k, v, st.slots[t])
+                    sm_scale: float, o: Optional[torch.Tensor] = None, fused_store: bool = True) -> torch.Tensor:
+        """Store step t's K/V in the pool and attend over each request's whole context
+        (one call with fused_store, else a scatter then the attention)."""
         if o is None:
             o = torch.empty_like(q)
-        api.decode_attention(self.shape, o, q, self.k_pool, self.v_pool, self.table_d, st.seq_lens[t], st.plan,
-                             sm_scale, st.workspace)
+        if fused_store:
+            api.decode_attention(self.shape, o, q, self.k_pool, self.v_pool, self.table_d, st.seq_lens[t], st.plan,
+                                 sm_scale, st.workspace, k_new=k, v_new=v, new_slots=st.slots[t])
+        else:
+            api.kv_store(self.shape, self.k_pool, self.v_pool, k, v, st.slots[t])
+            api.decode_attention(self.shape, o, q, self.k_pool, self.v_pool, self.table_d, st.seq_lens[t], st.plan,
+                                 sm_scale, st.workspace)
         return o
 
     def release(self, b: Batch, keep: Optional[Sequence[int]] = None) -> None:

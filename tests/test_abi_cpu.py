@@ -91,13 +91,17 @@ def test_decode_argument_checks():
     assert need == 2 * 8 * info.max_splits * (128 + 2) * 4
 
     def call(sh_, batch, ws):
-        return N.lib.rc_decode_attention(C.byref(sh_), FAKE, FAKE, FAKE, FAKE, FAKE, 2, 128, FAKE, batch, FAKE,
-                                         C.byref(info), 0.1, FAKE, ws, None)
+        return N.lib.rc_decode_attention(C.byref(sh_), FAKE, FAKE, FAKE, FAKE, None, None, None, FAKE, 2, 128, FAKE,
+                                         batch, FAKE, C.byref(info), 0.1, FAKE, ws, None)
 
     assert call(sh, 2, need - 1) == N.RC_ERR_RANGE
     assert call(sh, 3, need) == N.RC_ERR_ARG  # plan built for batch 2
     assert call(shape(hq=8, hkv=8), 2, need) == N.RC_ERR_SHAPE  # plan built for group 4
     assert call(sh, 0, need) == N.RC_OK
+    # the current token's K/V come as a triple
+    st = N.lib.rc_decode_attention(C.byref(sh), FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, 2, 128, FAKE, 2, FAKE,
+                                   C.byref(info), 0.1, FAKE, need, None)
+    assert st == N.RC_ERR_ARG
 
 
 def test_unshared_plan_layout():

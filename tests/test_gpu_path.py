@@ -137,7 +137,7 @@ def test_extend_single_token_prefill_is_value(gpu):
 
 
 # ---------------------------------------------------------------- whole workloads
-def _run_workload(gpu, w, shared=True, chunk=512, decode_steps=None):
+def _run_workload(gpu, w, shared=True, chunk=512, decode_steps=None, fused=True):
     tol = TOL[w.shape.dtype]
     eng = drive.make_engine(w, device=gpu)
     errs = []
@@ -170,7 +170,10 @@ def _run_workload(gpu, w, shared=True, chunk=512, decode_steps=None):
         st = eng.prepare_decode(b, base, n_steps, chunk=chunk, shared=shared)
         for t in range(n_steps):
             q, k, v = drive.decode_inputs(w, rids, t, device=gpu)
-            o = host(eng.decode_step(st, t, q, k, v, w.sm_scale))
+            o = host(eng.decode_step(st, t, q, k, v, w.sm_scale, fused_store=fused))
+            # the step's K/V landed in the pool, bit for bit
+            sl = st.slots[t].long()
+            assert torch.equal(eng.k_pool[sl], k) and torch.equal(eng.v_pool[sl], v)
             for j, i in enumerate(rids):
                 K, V = w.context_kv(i, t + 1)
                 want = A.decode(w.dec_qkv(i, t)[0], K, V, w.sm_scale)
@@ -178,14 +181,16 @@ def _run_workload(gpu, w, shared=True, chunk=512, decode_steps=None):
     return eng, b, max(errs)
 
 
-def test_tiny_fp32_workload(gpu):
-    _run_workload(gpu, W.tiny_fp32())
+@pytest.mark.parametrize("fused", [True, False])
+def test_tiny_fp32_workload(gpu, fused):
+    _run_workload(gpu, W.tiny_fp32(), fused=fused)
 
 
-@pytest.mark.parametrize("shared,chunk", [(True, 512), (False, 512), (True, 64), (False, 4096)])
-def test_gpt2_system_prompt_workload(gpu, shared, chunk):
+@pytest.mark.parametrize("shared,chunk,fused", [(True, 512, True), (False, 512, True), (True, 64, False),
+                                                (False, 4096, False)])
+def test_gpt2_system_prompt_workload(gpu, shared, chunk, fused):
     w = W.gpt2_system_prompt()
-    eng, b, err = _run_workload(gpu, w, shared=shared, chunk=chunk)
+    eng, b, err = _run_workload(gpu, w, shared=shared, chunk=chunk, fused=fused)
     # the glossary's bookkeeping: 8 of 417 and 7 of 416 tokens computed
     assert [(int(e), int(p + e)) for p, e in zip(b.prefix_lens, b.extend_lens)] == [(8, 417), (7, 416)]
 
