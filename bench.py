@@ -177,7 +177,7 @@ def main():
     dec_name = "decode_attention_d128"  # one launch per step: wide and narrow items
     ext_ms = prof[ext_name][1] / prof[ext_name][0]
     dec_ms = prof[dec_name][1] / prof[dec_name][0]
-    mrg_ms = prof[mrg_name][1] / prof[mrg_name][0]
+    mrg_ms = prof[mrg_name][1] / prof[mrg_name][0] if mrg_name in prof else 0.0  # merged in the decode kernel
     st_tot = prof[st_name][1] / args.steps
     ext_tflops = ext_flops / (ext_ms * 1e-3) / 1e12
 

@@ -975,6 +975,10 @@ __global__ __launch_bounds__(NT) void decode_attn_f32(Args a) {
 
 // Split merge: for each (request, q head), combine its partials k = 0..n-1 in
 // order: M = max m_k, l = sum l_k 2^(m_k - M), o = sum o_k 2^(m_k - M) / l.
+// One wave per (request, head).  The (max, sum) pairs of 64 splits at a time
+// are loaded at once (one per lane) and reduced across the wave, then the
+// partial outputs are read with all those splits' loads in flight together.
+// Beyond 64 splits the blocks are combined with the usual rescaling.
 template <int D, bool BF16>
 __global__ __launch_bounds__(256) void merge_kernel(void* out, const float* __restrict__ ws_o,
                                                     const float* __restrict__ ws_ml, const int32_t* nsplit,
@@ -987,19 +991,33 @@ __global__ __launch_bounds__(256) void merge_kernel(void* out, const float* __re
   int ns = nsplit[b];
   ns = ns < 0 ? 0 : (ns < max_splits ? ns : max_splits);
   const float* ml = ws_ml + (int64_t)pair * max_splits * 2;
-  float M = -INFINITY;
-  for (int k = 0; k < ns; ++k) M = fmaxf(M, ml[2 * k]);
-  float l = 0.f, acc[PER];
+  const float* po = ws_o + (int64_t)pair * max_splits * D;
+  float acc[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) acc[i] = 0.f;
-  const float* po = ws_o + (int64_t)pair * max_splits * D;
-  for (int k = 0; k < ns; ++k) {
-    const float mk = ml[2 * k];
-    if (mk == -INFINITY) continue;
-    const float wgt = exp2f(mk - M);
-    l += ml[2 * k + 1] * wgt;
+  float l = 0.f, M_run = -INFINITY;
+  for (int k0 = 0; k0 < ns; k0 += 64) {
+    const int k = k0 + lane;
+    const float2 mine = k < ns ? *(const float2*)(ml + 2 * k) : make_float2(-INFINITY, 0.f);
+    float Mb = mine.x;
 #pragma unroll
-    for (int i = 0; i < PER; ++i) acc[i] += po[(int64_t)k * D + lane + 64 * i] * wgt;
+    for (int sh = 32; sh >= 1; sh >>= 1) Mb = fmaxf(Mb, __shfl_xor(Mb, sh));
+    const float M = fmaxf(M_run, Mb);
+    if (k0 > 0 && M_run != M) {  // earlier blocks were weighted against an older maximum
+      const float r = M_run == -INFINITY ? 0.f : exp2f(M_run - M);
+      l *= r;
+#pragma unroll
+      for (int i = 0; i < PER; ++i) acc[i] *= r;
+    }
+    M_run = M;
+    const float wk = mine.x == -INFINITY ? 0.f : exp2f(mine.x - M);
+    const int n = min(64, ns - k0);
+    for (int j = 0; j < n; ++j) {
+      const float wj = __shfl(wk, j);
+      l += __shfl(mine.y, j) * wj;
+#pragma unroll
+      for (int i = 0; i < PER; ++i) acc[i] += po[(int64_t)(k0 + j) * D + lane + 64 * i] * wj;
+    }
   }
   const float inv = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll

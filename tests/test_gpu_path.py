@@ -250,3 +250,9 @@ def test_decode_head_layouts(gpu, Hq, Hkv, D, rows):
             _run_workload(gpu, w, shared=shared, chunk=chunk)
     finally:
         api.set_tuning("decode_rows", 0)
+
+
+def test_decode_merge_of_many_splits(gpu):
+    # more than 64 partials per request: the merge combines blocks of 64 splits
+    w = W.few_shot(n_req=3, prefix=1500, ext=5, n_decode=1)
+    _run_workload(gpu, w, shared=True, chunk=16)
