@@ -31,6 +31,53 @@ import numpy as np
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
+ROOT = os.path.dirname(os.path.abspath(__file__))
+# HBM bytes per launch of the decode kernel from rocprofv3 FETCH_SIZE / WRITE_SIZE
+# counters, with the sha256 of the kernel source they were taken on
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_attention_multi_turn_tree_traffic.txt")
+KERNEL_SOURCE = os.path.join(ROOT, "prefix_shared_kv_amd", "csrc", "attention.hip")
+
+
+def measured_traffic():
+    """Counter-measured bytes per decode launch, or None when absent or taken
+    on a different kernel source."""
+    import hashlib
+    try:
+        kv = {}
+        for line in open(TRAFFIC_FILE):
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+        src = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
+        if kv.get("kernel_source_sha256") != src:
+            return None
+        return float(kv["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def copy_calibration():
+    """kv_store of 65536 rows (K and V, 8 x 128 bf16 each) into slots 0..65535:
+    reads 2 x 128 MiB + the slot list, writes 2 x 128 MiB."""
+    import torch
+
+    import prefix_shared_kv_amd as pk
+    dev = torch.device("cuda:0")
+    n, h, d = 65536, 8, 128
+    kvs = pk.KVShape(32, h, d, torch.bfloat16, n)
+    k_pool = torch.zeros((n, h, d), dtype=torch.bfloat16, device=dev)
+    v_pool = torch.zeros_like(k_pool)
+    k = torch.randn((n, h, d), device=dev).to(torch.bfloat16)
+    v = torch.randn((n, h, d), device=dev).to(torch.bfloat16)
+    slots = torch.arange(n, dtype=torch.int32, device=dev)
+    for _ in range(5):
+        pk.kv_store(kvs, k_pool, v_pool, k, v, slots)
+    torch.cuda.synchronize()
+    if not (torch.equal(k_pool, k) and torch.equal(v_pool, v)):
+        raise RuntimeError("calibration copy mismatch")
+    row = h * d * 2
+    print(json.dumps({"calibration": "kv_store into contiguous slots", "launches": 5,
+                      "read_bytes_per_launch": 2 * n * row + 4 * n, "write_bytes_per_launch": 2 * n * row}))
 
 
 def log(msg):
@@ -45,12 +92,15 @@ def parse():
     ap.add_argument("--chunk", type=int, default=512, help="decode split size (positions per work item)")
     ap.add_argument("--decode-steps", type=int, default=256)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample", type=int, default=8, help="requests in the oracle sample")
-    ap.add_argument("--cpu-decode-steps", type=int, default=16, help="decode steps per request in the oracle sample")
+    ap.add_argument("--cpu-sample", type=int, default=32, help="requests in the oracle sample")
+    ap.add_argument("--cpu-decode-steps", type=int, default=32, help="decode steps per request in the oracle sample")
     ap.add_argument("--seed", type=int, default=4)
     ap.add_argument("--no-shuffle", action="store_true", help="hand out pool slots in order (no gather scatter)")
     ap.add_argument("--decode-rows", type=int, default=0, help="narrow decode by groups of four kv heads (rc_set_tuning)")
     ap.add_argument("--host-phases", action="store_true", help="report host wall time per phase of the last step")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run kv_store into contiguous slots (a plain copy of known size) and print its bytes; "
+                         "the scale for rocprofv3 FETCH_SIZE / WRITE_SIZE readings")
     return ap.parse_args()
 
 
@@ -60,6 +110,9 @@ def main():
         print("bench.py measures one GPU: the path is a single-GPU kernel library and this build runs on "
               "one MI355X; run it with --gpus 1.", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
 
     import torch
 
@@ -210,7 +263,7 @@ def main():
         "roofline": {
             "bound": "hbm", "kernel": "decode_attn_bf16<128> (" + dec_name + ")",
             "achieved": round(dec_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+            "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
             "avg_launch_ms": round(dec_ms, 5), "algorithmic_bytes_per_launch": float(np.mean(dec_bytes_steps)),
         },
         "extend": {
