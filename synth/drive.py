@@ -57,12 +57,17 @@ def path_tokens(w: Workload, nid: int) -> np.ndarray:
     return np.concatenate([w.nodes[i].tokens for i in reversed(path)]).astype(np.int32)
 
 
-def populate(eng: Engine, w: Workload, node_ids: Optional[Sequence[int]] = None, device="cuda") -> None:
-    """Put cached nodes' K/V into the pool and the tree (as if computed earlier)."""
+def populate(eng: Engine, w: Workload, node_ids: Optional[Sequence[int]] = None, device="cuda",
+             device_values: bool = False) -> None:
+    """Put cached nodes' K/V into the pool and the tree (as if computed earlier).
+    device_values: draw them with Workload.node_kv_device instead of on the host."""
     ids = node_order(w) if node_ids is None else list(node_ids)
     for nid in ids:
-        k, v = w.node_kv(nid)
-        eng.populate(path_tokens(w, nid), up(k, w, device), up(v, w, device), expect_cached=w.node_start(nid))
+        if device_values:
+            k, v = w.node_kv_device(nid, device)
+        else:
+            k, v = (up(x, w, device) for x in w.node_kv(nid))
+        eng.populate(path_tokens(w, nid), k, v, expect_cached=w.node_start(nid))
 
 
 def prefill_nodes(eng: Engine, w: Workload, device="cuda") -> Dict[int, torch.Tensor]:

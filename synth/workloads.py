@@ -45,6 +45,7 @@ VOCAB = 50257
 
 # stream tags (arbitrary distinct integers)
 _T_NODE_TOK, _T_NODE_K, _T_NODE_V = 11, 12, 13
+_T_NODE_DEV = 14
 _T_EXT_TOK, _T_EXT_Q, _T_EXT_K, _T_EXT_V = 21, 22, 23, 24
 _T_DEC_Q, _T_DEC_K, _T_DEC_V = 31, 32, 33
 _T_PRE_Q = 41
@@ -56,10 +57,11 @@ def rng(seed: int, tag: int, *ids: int) -> np.random.Generator:
 
 
 def round_bf16(x: np.ndarray) -> np.ndarray:
-    """Round float32 values to the nearest bfloat16 (ties to even); float32 out."""
-    import torch
-
-    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.bfloat16).to(torch.float32).numpy()
+    """Round finite float32 values to the nearest bfloat16 (ties to even); float32 out.
+    On the bit pattern: add 0x7FFF plus the lowest kept bit, then clear the low 16 bits."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    r = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) & np.uint32(0xFFFF0000)
+    return r.view(np.float32)
 
 
 @dataclasses.dataclass
@@ -141,6 +143,24 @@ class Workload:
         n = len(self.nodes[nid].tokens)
         s = (n, self.shape.num_kv_heads, self.shape.head_dim)
         return self._vals(s, _T_NODE_K, nid), self._vals(s, _T_NODE_V, nid)
+
+    def node_kv_device(self, nid: int, device):
+        """Node K/V drawn on a GPU by torch's seeded generator: [n, Hkv, D] tensors
+        in the workload dtype.  For pools too large to draw on the host (the
+        heavy-decode workload holds 9 GB); repeated calls give the same bits, so
+        the oracle side regenerates the nodes it samples and copies them out."""
+        import torch
+        seed = int(np.random.SeedSequence(self.seed, spawn_key=(_T_NODE_DEV, int(nid))).generate_state(1, np.uint64)[0] >> 1)
+        g = torch.Generator(device=device)
+        g.manual_seed(seed)
+        n = len(self.nodes[nid].tokens)
+        s = (n, self.shape.num_kv_heads, self.shape.head_dim)
+        dt = torch.bfloat16 if self.shape.dtype == "bf16" else torch.float32
+        k = torch.randn(s, generator=g, device=device, dtype=torch.float32)
+        v = torch.randn(s, generator=g, device=device, dtype=torch.float32)
+        if self.shape.std != 1.0:
+            k, v = k * self.shape.std, v * self.shape.std
+        return k.to(dt), v.to(dt)
 
     def node_prefill_q(self, nid: int) -> np.ndarray:
         """Queries for prefilling a node's own tokens (extend with the node as new tokens)."""

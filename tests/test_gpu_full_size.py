@@ -1,0 +1,173 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration the
+benchmark times (shared decode plan, 512-position chunks, the step's K/V
+stored by the decode call).  Every phase runs in full on the GPU; the oracle
+recomputes a seeded sample of its outputs one request or one row at a time
+(all heads of each sampled row), within max-abs 2e-2 for bf16 inputs.
+
+Pools too large to draw on the host (the heavy-decode workload's 9 GB, the
+multi-turn tree) take their node K/V from Workload.node_kv_device, a seeded
+torch generator; the oracle copies out the nodes it samples from the same
+generator, never from the pool."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import attention as A
+from synth import drive
+from synth import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-2
+CHUNK = 512
+
+
+def host(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def err_of(got, want):
+    return float(np.max(np.abs(got - want)))
+
+
+class Context:
+    """Logical K/V sequences of a workload's requests, node values cached on the host."""
+
+    def __init__(self, w, device=None):
+        self.w, self.device, self.cache = w, device, {}
+
+    def node(self, nid):
+        if nid not in self.cache:
+            if self.device is None:
+                self.cache[nid] = self.w.node_kv(nid)
+            else:
+                k, v = self.w.node_kv_device(nid, self.device)
+                self.cache[nid] = (k.float().cpu().numpy(), v.float().cpu().numpy())
+        return self.cache[nid]
+
+    def path(self, nid):
+        ids = []
+        while nid >= 0:
+            ids.append(nid)
+            nid = self.w.nodes[nid].parent
+        ids.reverse()
+        return (np.concatenate([self.node(n)[0] for n in ids]), np.concatenate([self.node(n)[1] for n in ids]))
+
+    def request(self, i, n_decoded):
+        r = self.w.requests[i]
+        ks = [self.node(n)[0] for n in r.path]
+        vs = [self.node(n)[1] for n in r.path]
+        if len(r.ext_tokens):
+            _, ek, ev = self.w.ext_qkv(i)
+            ks.append(ek)
+            vs.append(ev)
+        for t in range(n_decoded):
+            _, dk, dv = self.w.dec_qkv(i, t)
+            ks.append(dk[None])
+            vs.append(dv[None])
+        return np.concatenate(ks), np.concatenate(vs)
+
+
+def sample(n, k, seed, always=()):
+    g = np.random.default_rng(seed)
+    picks = set(int(x) for x in always if 0 <= x < n)
+    picks |= set(int(x) for x in g.choice(n, size=min(k, n), replace=False))
+    return sorted(picks)
+
+
+def check_prefill(w, ctx, outs, n_rows=24):
+    worst = 0.0
+    for nid, o in outs.items():
+        q = w.node_prefill_q(nid)
+        K, V = ctx.path(nid)
+        start = w.node_start(nid)
+        n = len(w.nodes[nid].tokens)
+        rows = sample(n, n_rows, nid, always=(0, 1, 31, 32, 63, 64, 127, 128, n - 2, n - 1))
+        got = host(o[rows])
+        for j, i in enumerate(rows):
+            p = start + i
+            want = A.extend(q[i:i + 1], K[:p + 1], V[:p + 1], p, w.sm_scale)[0]
+            e = err_of(got[j], want)
+            assert e <= TOL, f"prefill node {nid} row {i}: max abs error {e:.3e}"
+            worst = max(worst, e)
+    return worst
+
+
+def check_extend(w, ctx, o, rids):
+    starts = np.concatenate([[0], np.cumsum([len(r.ext_tokens) for r in w.requests])])
+    worst = 0.0
+    for i in rids:
+        q, _, _ = w.ext_qkv(i)
+        K, V = ctx.request(i, 0)
+        P = len(w.prefix_tokens(w.requests[i]))
+        want = A.extend(q, K, V, P, w.sm_scale)
+        e = err_of(host(o[starts[i]:starts[i + 1]]), want)
+        assert e <= TOL, f"extend request {i}: max abs error {e:.3e}"
+        worst = max(worst, e)
+    return worst
+
+
+def run_decode(w, eng, b, ctx, rids_checked, steps_checked, device):
+    B = len(w.requests)
+    n_steps = max(r.n_decode for r in w.requests)
+    base = [len(w.prompt_tokens(r)) for r in w.requests]
+    st = eng.prepare_decode(b, base, n_steps, chunk=CHUNK)
+    worst = 0.0
+    for t in range(n_steps):
+        q, k, v = drive.decode_inputs(w, range(B), t, device=device)
+        o = eng.decode_step(st, t, q, k, v, w.sm_scale)
+        if t in steps_checked:
+            sl = st.slots[t].long()
+            assert torch.equal(eng.k_pool[sl], k) and torch.equal(eng.v_pool[sl], v), f"pool rows of step {t}"
+            got = host(o)
+            for i in rids_checked:
+                K, V = ctx.request(i, t + 1)
+                want = A.decode(w.dec_qkv(i, t)[0], K, V, w.sm_scale)
+                e = err_of(got[i], want)
+                assert e <= TOL, f"decode step {t} request {i}: max abs error {e:.3e}"
+                worst = max(worst, e)
+    return worst
+
+
+def test_few_shot_full_size(gpu):
+    # 64 requests x 64 new tokens over a 2048-token prefix prefilled once, 128 decode steps
+    w = W.few_shot()
+    ctx = Context(w)
+    eng = drive.make_engine(w, device=gpu)
+    check_prefill(w, ctx, drive.prefill_nodes(eng, w, device=gpu))
+    b, o = drive.extend_requests(eng, w, device=gpu)
+    check_extend(w, ctx, o, range(len(w.requests)))
+    run_decode(w, eng, b, ctx, sample(64, 8, 1, always=(0, 63)), {0, 1, 63, 127}, gpu)
+
+
+def test_multi_turn_tree_full_size(gpu):
+    # the benchmark's tree: 340 cached segments, 256 leaves x 128 new tokens,
+    # 256 decode steps, shuffled pool slots
+    w = W.multi_turn_tree()
+    ctx = Context(w, device=gpu)
+    eng = drive.make_engine(w, device=gpu)
+    drive.populate(eng, w, device=gpu, device_values=True)
+    b, o = drive.extend_requests(eng, w, device=gpu)
+    check_extend(w, ctx, o, sample(len(w.requests), 16, 2, always=(0, 255)))
+    run_decode(w, eng, b, ctx, sample(len(w.requests), 8, 3, always=(0, 255)), {0, 128, 255}, gpu)
+
+
+def test_classify64_full_size(gpu):
+    # a 4096-token prefix prefilled once, then 64 label branches of 2..16 tokens in one extend
+    w = W.classify64()
+    ctx = Context(w)
+    eng = drive.make_engine(w, device=gpu)
+    check_prefill(w, ctx, drive.prefill_nodes(eng, w, device=gpu), n_rows=32)
+    b, o = drive.extend_requests(eng, w, device=gpu)
+    check_extend(w, ctx, o, range(len(w.requests)))
+
+
+def test_heavy_decode_full_size(gpu):
+    # 1024 requests over 8192-token contexts (4096 shared per group of 16), 8 decode steps;
+    # the pool holds 4.46M slots (9.1 GB of K and V)
+    w = W.heavy_decode()
+    ctx = Context(w, device=gpu)
+    eng = drive.make_engine(w, device=gpu)
+    drive.populate(eng, w, device=gpu, device_values=True)
+    b = drive.schedule_decode_only(eng, w)
+    run_decode(w, eng, b, ctx, sample(len(w.requests), 8, 4, always=(0, 15, 16, 1023)), {0, 3, 7}, gpu)

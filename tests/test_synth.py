@@ -46,3 +46,18 @@ def test_context_kv_is_node_keyed():
     assert k0.shape == (16 + 4 + 2, 8, 128)
     assert np.array_equal(k0[:16], k1[:16])
     assert not np.array_equal(k0[16:], k1[16:])
+
+
+def test_round_bf16_matches_torch_conversion():
+    # random values over many binades, exact ties (low half 0x8000) with even and odd kept bits,
+    # values one ulp either side of a tie, subnormals, zeros
+    import torch
+    g = np.random.default_rng(7)
+    x = (g.standard_normal(200000) * np.exp2(g.integers(-130, 120, 200000))).astype(np.float32)
+    hi = g.integers(0, 1 << 16, 20000, dtype=np.uint32) << 16
+    ties = np.concatenate([hi | 0x8000, hi | 0x7FFF, hi | 0x8001]).astype(np.uint32)
+    ties = ties[np.isfinite(ties.view(np.float32))].view(np.float32)
+    x = np.concatenate([x, ties, np.float32([0.0, -0.0, 1e-45, -3e-39, 1.0, 65504.0])])
+    x = x[np.isfinite(x) & (np.abs(x) < 3.3e38)]
+    want = torch.from_numpy(x).to(torch.bfloat16).to(torch.float32).numpy()
+    assert np.array_equal(W.round_bf16(x).view(np.uint32), want.view(np.uint32))
