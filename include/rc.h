@@ -251,15 +251,20 @@ rc_status rc_radix_free(rc_radix* tree, const int32_t* slots, int64_t n);
 rc_status rc_radix_insert(rc_radix* tree, const int32_t* tokens, int32_t* slots_inout, int64_t n,
                           int64_t* n_new);
 
-/* Batched insert ("commit"): for each request b, rc_radix_insert of         */
-/* tokens[tok_off[b] .. tok_off[b+1]) with the slots held in row rows[b] of   */
-/* the host table, rewriting that row in place where the tree already held   */
-/* the tokens.  changed (host, nullable, batch entries) is set to 1 for rows */
-/* that were rewritten.  Requests are processed in order; on a failure the   */
-/* requests before the failing one stay inserted (RC_ERR_* names it).        */
+/* Token batches (host, CSR): request b owns tokens[tok_off[b] ..          */
+/* tok_off[b+1]).  Where a call takes tok_len (nullable) only the first      */
+/* tok_len[b] of them are used (0 <= tok_len[b] <= its count, else          */
+/* RC_ERR_ARG), so one flattened batch serves schedule, commit and plan.     */
+
+/* Batched insert ("commit"): for each request b, rc_radix_insert of its     */
+/* tokens with the slots held in row rows[b] of the host table, rewriting    */
+/* that row in place where the tree already held the tokens.  changed (host, */
+/* nullable, batch entries) is set to 1 for rows that were rewritten.        */
+/* Requests are processed in order; on a failure the requests before the     */
+/* failing one stay inserted (RC_ERR_* names it).                            */
 rc_status rc_radix_insert_rows(rc_radix* tree, int32_t batch, const int32_t* tokens, const int64_t* tok_off,
-                               const int32_t* rows, int32_t* req_to_token, int32_t table_rows, int64_t stride,
-                               int32_t* changed);
+                               const int64_t* tok_len, const int32_t* rows, int32_t* req_to_token,
+                               int32_t table_rows, int64_t stride, int32_t* changed);
 
 /* Rows of the request -> slot table for a batch.  Request b has tokens      */
 /* tokens[tok_off[b] .. tok_off[b+1]) (host, CSR).  Row rows[b] of the host   */
@@ -282,8 +287,8 @@ rc_status rc_radix_fork(rc_radix* tree, const int32_t* tokens, const int32_t* pa
                         int32_t n_children, const int32_t* child_rows, int32_t* req_to_token,
                         int32_t table_rows, int64_t stride);
 
-/* Shared decode plan from the tree: request b's committed tokens            */
-/* tokens[tok_off[b]..tok_off[b+1]) are walked through the tree; every node  */
+/* Shared decode plan from the tree: request b's committed tokens (its      */
+/* tok_len[b] first, or all) are walked through the tree; every node         */
 /* range is one item whose members are all batch requests passing through    */
 /* it (split into items of at most max(1, 128 / group) members); positions   */
 /* past the walked prefix up to max_seq_lens[b] form the request's own tail. */
@@ -291,7 +296,7 @@ rc_status rc_radix_fork(rc_radix* tree, const int32_t* tokens, const int32_t* pa
 /* hold the tree's slots over the walked prefix (emit_rows + insert give     */
 /* that).  Output as rc_plan_decode_unshared.                                */
 rc_status rc_radix_plan_decode(rc_radix* tree, int32_t batch, const int32_t* tokens,
-                               const int64_t* tok_off, const int32_t* rows,
+                               const int64_t* tok_off, const int64_t* tok_len, const int32_t* rows,
                                const int32_t* max_seq_lens, int32_t group, int32_t chunk,
                                int32_t* plan, int64_t capacity, rc_plan_info* info);
 
@@ -316,6 +321,10 @@ typedef struct rc_prof_entry {
 } rc_prof_entry;
 
 rc_status rc_prof_enable(int32_t on);
+/* Launches timed after this call are reported as "<kernel>@<tag>" (tag cut  */
+/* to 15 characters; NULL or "" for the plain kernel name), so one kernel's  */
+/* launches in different phases of a step are told apart.                    */
+rc_status rc_prof_tag(const char* tag);
 rc_status rc_prof_collect(rc_prof_entry* out, int32_t capacity, int32_t* n_out);
 
 #ifdef __cplusplus

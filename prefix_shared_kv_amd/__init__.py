@@ -5,7 +5,6 @@ kernels in librcattn.so).  Host calls: RadixTree (C++ radix tree, slot
 allocator, table rows, decode share plans).  See include/rc.h for the C ABI.
 """
 from .api import (DecodePlan, KVShape, RadixTree, decode_attention, decode_workspace_bytes,  # noqa: F401
-                  extend_attention, kv_store, plan_decode_unshared, prof_collect, prof_enable, set_error_word,
-                  set_tuning,
-                  version)
+                  extend_attention, kv_store, plan_decode_unshared, prof_collect, prof_enable, prof_tag, set_error_word,
+                  set_tuning, TokenBatch, version)
 from ._native import RcError  # noqa: F401

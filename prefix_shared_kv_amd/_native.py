@@ -67,12 +67,13 @@ _SIGS = {
     "rc_radix_free": (i32, [P, P, i64]),
     "rc_radix_insert": (i32, [P, P, P, i64, I64P]),
     "rc_radix_emit_rows": (i32, [P, i32, P, P, i32, P, P, i32, i64, P, P]),
-    "rc_radix_insert_rows": (i32, [P, i32, P, P, P, P, i32, i64, P]),
+    "rc_radix_insert_rows": (i32, [P, i32, P, P, P, P, P, i32, i64, P]),
     "rc_radix_fork": (i32, [P, P, P, i64, i32, P, P, i32, i64]),
-    "rc_radix_plan_decode": (i32, [P, i32, P, P, P, P, i32, i32, P, i64, C.POINTER(RcPlanInfo)]),
+    "rc_radix_plan_decode": (i32, [P, i32, P, P, P, P, P, i32, i32, P, i64, C.POINTER(RcPlanInfo)]),
     "rc_radix_stats_get": (i32, [P, C.POINTER(RcRadixStats)]),
     "rc_set_tuning": (i32, [C.c_char_p, i64]),
     "rc_prof_enable": (i32, [i32]),
+    "rc_prof_tag": (i32, [C.c_char_p]),
     "rc_prof_collect": (i32, [C.POINTER(RcProfEntry), i32, I32P]),
 }
 

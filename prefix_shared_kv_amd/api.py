@@ -145,14 +145,26 @@ class DecodePlan:
         return self.host[o:o + self.info.batch]
 
 
-def _run_planner(call) -> DecodePlan:
+def _run_planner(call, guess: int = 0) -> DecodePlan:
+    """Build a plan into a buffer of `guess` int32; when that is too small the
+    planner reports the size it needs and runs once more."""
     info = RcPlanInfo()
-    st = call(None, 0, info)
-    if st not in (N.RC_OK, N.RC_ERR_RANGE) or info.plan_ints <= 0:
+    buf = np.empty(max(int(guess), 0), np.int32)
+    st = call(_np_ptr(buf) if buf.size else None, buf.size, info)
+    if st == N.RC_OK:
+        return DecodePlan(buf[:info.plan_ints], info)
+    if st != N.RC_ERR_RANGE or info.plan_ints <= buf.size:
         check(st)
-    buf = np.zeros(info.plan_ints, np.int32)
+    buf = np.empty(info.plan_ints, np.int32)
     check(call(_np_ptr(buf), buf.size, info))
     return DecodePlan(buf, info)
+
+
+def _plan_guess(max_seq: np.ndarray, group: int, chunk: int) -> int:
+    """Plan size for the usual case: every request's positions in chunks, a few
+    shared node ranges per request, members about as many as items."""
+    items = int(np.sum((max_seq.astype(np.int64) + chunk - 1) // chunk)) + 4 * max_seq.size
+    return N.RC_PLAN_HEADER + items * (N.RC_PLAN_ITEM + 2) + max_seq.size
 
 
 def plan_decode_unshared(max_seq_lens: Sequence[int], group: int, chunk: int = 512,
@@ -160,7 +172,7 @@ def plan_decode_unshared(max_seq_lens: Sequence[int], group: int, chunk: int = 5
     ms = np.ascontiguousarray(max_seq_lens, np.int32)
     rw = None if rows is None else np.ascontiguousarray(rows, np.int32)
     return _run_planner(lambda p, cap, info: lib.rc_plan_decode_unshared(
-        ms.size, _np_ptr(rw), _np_ptr(ms), group, chunk, p, cap, C.byref(info)))
+        ms.size, _np_ptr(rw), _np_ptr(ms), group, chunk, p, cap, C.byref(info)), _plan_guess(ms, group, chunk))
 
 
 def decode_workspace_bytes(shape: KVShape, plan: DecodePlan) -> int:
@@ -196,12 +208,40 @@ def decode_attention(shape: KVShape, o, q, k_pool, v_pool, req_to_token, seq_len
                                   _vp(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
-def _csr(batch: Sequence[Sequence[int]]) -> Tuple[np.ndarray, np.ndarray]:
-    lens = np.array([len(t) for t in batch], np.int64)
-    off = np.zeros(len(batch) + 1, np.int64)
-    np.cumsum(lens, out=off[1:])
-    flat = np.concatenate([np.asarray(t, np.int32) for t in batch]) if len(batch) else np.zeros(0, np.int32)
-    return np.ascontiguousarray(flat, np.int32), off
+class TokenBatch:
+    """A batch of token-id lists flattened once (CSR): request b owns
+    flat[off[b]:off[b+1]].  Tree calls take it in place of a list of arrays, so
+    one batch is flattened once for schedule, commit and plan."""
+
+    def __init__(self, batch: Sequence[Sequence[int]]):
+        lens = np.array([len(t) for t in batch], np.int64)
+        self.off = np.zeros(len(batch) + 1, np.int64)
+        np.cumsum(lens, out=self.off[1:])
+        self.flat = np.empty(int(self.off[-1]), np.int32)
+        for b, t in enumerate(batch):
+            self.flat[self.off[b]:self.off[b + 1]] = t
+
+    def __len__(self) -> int:
+        return self.off.size - 1
+
+    def lens(self) -> np.ndarray:
+        return np.diff(self.off)
+
+    def __getitem__(self, b: int) -> np.ndarray:
+        return self.flat[self.off[b]:self.off[b + 1]]
+
+
+def _tb(batch) -> TokenBatch:
+    return batch if isinstance(batch, TokenBatch) else TokenBatch(batch)
+
+
+def _lens(tb: TokenBatch, lengths) -> Optional[np.ndarray]:
+    if lengths is None:
+        return None
+    ln = np.ascontiguousarray(lengths, np.int64)
+    if ln.shape != (len(tb),):
+        raise ValueError("one length per request")
+    return ln
 
 
 class RadixTree:
@@ -217,7 +257,7 @@ class RadixTree:
 
     def __del__(self):
         h = getattr(self, "_h", None)
-        if h is not None and h.value:
+        if h is not None and h.value and lib is not None:  # lib is gone at interpreter shutdown
             lib.rc_radix_destroy(h)
             self._h = None
 
@@ -251,12 +291,12 @@ class RadixTree:
         """Fill rows of a host table [R, stride]; returns (prefix_lens, extend_lens)."""
         if table.dtype != np.int32 or table.ndim != 2 or not table.flags.c_contiguous:
             raise ValueError("table must be a C-contiguous int32 [rows, stride] array")
-        flat, off = _csr(batch)
-        B = len(batch)
+        tb = _tb(batch)
+        B = len(tb)
         rw = np.arange(B, dtype=np.int32) if rows is None else np.ascontiguousarray(rows, np.int32)
         P = np.zeros(B, np.int32)
         E = np.zeros(B, np.int32)
-        check(lib.rc_radix_emit_rows(self._h, B, _np_ptr(flat), _np_ptr(off), reserve, _np_ptr(rw), _np_ptr(table),
+        check(lib.rc_radix_emit_rows(self._h, B, _np_ptr(tb.flat), _np_ptr(tb.off), reserve, _np_ptr(rw), _np_ptr(table),
                                      table.shape[0], table.shape[1], _np_ptr(P), _np_ptr(E)))
         return P, E
 
@@ -266,12 +306,12 @@ class RadixTree:
         row; rows are rewritten in place to the tree's slots.  Returns a bool mask of changed rows."""
         if table.dtype != np.int32 or table.ndim != 2 or not table.flags.c_contiguous:
             raise ValueError("table must be a C-contiguous int32 [rows, stride] array")
-        toks = batch if lengths is None else [np.asarray(t)[:int(n)] for t, n in zip(batch, lengths)]
-        flat, off = _csr(toks)
+        tb = _tb(batch)
+        ln = _lens(tb, lengths)
         rw = np.ascontiguousarray(rows, np.int32)
-        changed = np.zeros(len(toks), np.int32)
-        check(lib.rc_radix_insert_rows(self._h, len(toks), _np_ptr(flat), _np_ptr(off), _np_ptr(rw), _np_ptr(table),
-                                       table.shape[0], table.shape[1], _np_ptr(changed)))
+        changed = np.zeros(len(tb), np.int32)
+        check(lib.rc_radix_insert_rows(self._h, len(tb), _np_ptr(tb.flat), _np_ptr(tb.off), _np_ptr(ln), _np_ptr(rw),
+                                       _np_ptr(table), table.shape[0], table.shape[1], _np_ptr(changed)))
         return changed.astype(bool)
 
     def fork(self, tokens, parent_slots, child_rows: Sequence[int], table: np.ndarray) -> None:
@@ -281,14 +321,17 @@ class RadixTree:
         check(lib.rc_radix_fork(self._h, _np_ptr(t), _np_ptr(s), t.size, cr.size, _np_ptr(cr), _np_ptr(table),
                                 table.shape[0], table.shape[1]))
 
-    def plan_decode(self, batch: Sequence[Sequence[int]], max_seq_lens: Sequence[int], group: int, chunk: int = 512,
-                    rows: Optional[Sequence[int]] = None) -> DecodePlan:
-        flat, off = _csr(batch)
-        B = len(batch)
+    def plan_decode(self, batch, max_seq_lens: Sequence[int], group: int, chunk: int = 512,
+                    rows: Optional[Sequence[int]] = None, lengths: Optional[Sequence[int]] = None) -> DecodePlan:
+        """Shared decode plan; request b's first lengths[b] tokens (default: all) are walked."""
+        tb = _tb(batch)
+        ln = _lens(tb, lengths)
+        B = len(tb)
         rw = np.arange(B, dtype=np.int32) if rows is None else np.ascontiguousarray(rows, np.int32)
         ms = np.ascontiguousarray(max_seq_lens, np.int32)
         return _run_planner(lambda p, cap, info: lib.rc_radix_plan_decode(
-            self._h, B, _np_ptr(flat), _np_ptr(off), _np_ptr(rw), _np_ptr(ms), group, chunk, p, cap, C.byref(info)))
+            self._h, B, _np_ptr(tb.flat), _np_ptr(tb.off), _np_ptr(ln), _np_ptr(rw), _np_ptr(ms), group, chunk, p, cap,
+            C.byref(info)), _plan_guess(ms, group, chunk))
 
     def stats(self) -> dict:
         st = RcRadixStats()
@@ -303,6 +346,11 @@ def set_tuning(name: str, value: int) -> None:
 
 def prof_enable(on: bool = True) -> None:
     check(lib.rc_prof_enable(1 if on else 0))
+
+
+def prof_tag(tag: Optional[str]) -> None:
+    """Report the following launches as '<kernel>@<tag>' (None: plain names)."""
+    check(lib.rc_prof_tag(tag.encode() if tag else None))
 
 
 def prof_collect() -> dict:

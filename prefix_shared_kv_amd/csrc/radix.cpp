@@ -60,8 +60,10 @@ int64_t walk(const rc_radix& t, const int32_t* tok, int64_t n, F&& visit) {
     const Node& c = t.nodes[it->second];
     const int64_t len = (int64_t)c.tok.size();
     const int64_t lim = std::min(len, n - pos);
-    int64_t k = 0;
-    while (k < lim && c.tok[k] == tok[pos + k]) ++k;
+    // whole-edge matches are the common case: compare with memcmp first
+    const int64_t k = std::memcmp(c.tok.data(), tok + pos, (size_t)lim * sizeof(int32_t)) == 0
+                          ? lim
+                          : std::mismatch(c.tok.data(), c.tok.data() + lim, tok + pos).first - c.tok.data();
     visit(it->second, k);
     pos += k;
     if (k < len) break;
@@ -104,6 +106,24 @@ int32_t split(rc_radix& t, int32_t c, int64_t k) {
 }
 
 bool slot_ok(const rc_radix& t, int32_t s) { return s >= 0 && s < t.pool; }
+
+// A batch of token lists in CSR form: request b owns tokens[tok_off[b] ..
+// tok_off[b+1]); with tok_len only its first tok_len[b] tokens are used.
+rc_status check_lens(int32_t batch, const int64_t* tok_off, const int64_t* tok_len) {
+  for (int32_t b = 0; b < batch; ++b) {
+    if (tok_off[b] < 0 || tok_off[b + 1] < tok_off[b]) return fail(RC_ERR_ARG, "tok_off not non-decreasing at %d", b);
+    if (tok_len && (tok_len[b] < 0 || tok_len[b] > tok_off[b + 1] - tok_off[b]))
+      return fail(RC_ERR_ARG, "tok_len[%d] = %lld outside [0, %lld]", b, (long long)tok_len[b], (long long)(tok_off[b + 1] - tok_off[b]));
+  }
+  return RC_OK;
+}
+
+// Do two requests of the batch name the same table row?
+bool rows_repeat(int32_t batch, const int32_t* rows) {
+  std::vector<int32_t> v(rows, rows + batch);
+  std::sort(v.begin(), v.end());
+  return std::adjacent_find(v.begin(), v.end()) != v.end();
+}
 
 }  // namespace
 
@@ -279,19 +299,20 @@ rc_status rc_radix_insert(rc_radix* t, const int32_t* tokens, int32_t* slots, in
 }
 
 rc_status rc_radix_insert_rows(rc_radix* t, int32_t batch, const int32_t* tokens, const int64_t* tok_off,
-                               const int32_t* rows, int32_t* table, int32_t table_rows, int64_t stride,
-                               int32_t* changed) {
+                               const int64_t* tok_len, const int32_t* rows, int32_t* table, int32_t table_rows,
+                               int64_t stride, int32_t* changed) {
   if (!t || batch < 0 || stride <= 0) return fail(RC_ERR_ARG, "bad argument to rc_radix_insert_rows");
   if (batch > 0 && (!tok_off || !rows || !table)) return fail(RC_ERR_ARG, "NULL array in rc_radix_insert_rows");
+  if (rc_status st = check_lens(batch, tok_off, tok_len); st != RC_OK) return st;
+  auto len_of = [&](int32_t b) { return tok_len ? tok_len[b] : tok_off[b + 1] - tok_off[b]; };
   for (int32_t b = 0; b < batch; ++b) {
-    const int64_t n = tok_off[b + 1] - tok_off[b];
-    if (n < 0 || tok_off[b] < 0) return fail(RC_ERR_ARG, "tok_off not non-decreasing at %d", b);
+    const int64_t n = len_of(b);
     if (rows[b] < 0 || rows[b] >= table_rows) return fail(RC_ERR_RANGE, "row %d of request %d outside [0, %d)", rows[b], b, table_rows);
     if (n > stride) return fail(RC_ERR_RANGE, "request %d has %lld tokens, stride is %lld", b, (long long)n, (long long)stride);
   }
   std::vector<int32_t> before;
   for (int32_t b = 0; b < batch; ++b) {
-    const int64_t n = tok_off[b + 1] - tok_off[b];
+    const int64_t n = len_of(b);
     int32_t* row = table + (int64_t)rows[b] * stride;
     if (changed) before.assign(row, row + n);
     rc_status st = rc_radix_insert(t, tokens + tok_off[b], row, n, nullptr);
@@ -306,35 +327,38 @@ rc_status rc_radix_emit_rows(rc_radix* t, int32_t batch, const int32_t* tokens, 
                              int64_t stride, int32_t* prefix_lens, int32_t* extend_lens) {
   if (!t || batch < 0 || reserve < 0 || stride <= 0 || table_rows < 0) return fail(RC_ERR_ARG, "bad argument to rc_radix_emit_rows");
   if (batch > 0 && (!tok_off || !rows || !table || !prefix_lens || !extend_lens)) return fail(RC_ERR_ARG, "NULL array in rc_radix_emit_rows");
+  if (rc_status st = check_lens(batch, tok_off, nullptr); st != RC_OK) return st;
+  // pass 1 (read only): matched length and the edges entered, per request
+  struct Visit { int32_t node; int64_t k; };
   std::vector<int64_t> P(batch);
-  std::vector<std::vector<int32_t>> pre(batch);
-  std::vector<std::vector<int32_t>> touched(batch);
+  std::vector<int64_t> first_visit(batch + 1, 0);
+  std::vector<Visit> visits;
   int64_t need = 0;
   for (int32_t b = 0; b < batch; ++b) {
     const int64_t n = tok_off[b + 1] - tok_off[b];
-    if (n < 0 || tok_off[b] < 0) return fail(RC_ERR_ARG, "tok_off not non-decreasing at %d", b);
     if (n > 0 && !tokens) return fail(RC_ERR_ARG, "tokens is NULL");
     if (rows[b] < 0 || rows[b] >= table_rows) return fail(RC_ERR_RANGE, "row %d of request %d outside [0, %d)", rows[b], b, table_rows);
     if (n + reserve > stride) return fail(RC_ERR_RANGE, "request %d needs %lld table entries, stride is %lld", b, (long long)(n + reserve), (long long)stride);
-    const int64_t cap = n > 0 ? n - 1 : 0;
-    walk(*t, tokens + tok_off[b], n, [&](int32_t id, int64_t k) {
-      touched[b].push_back(id);
-      const Node& c = t->nodes[id];
-      for (int64_t i = 0; i < k && (int64_t)pre[b].size() < cap; ++i) pre[b].push_back(c.slot[i]);
-    });
-    P[b] = (int64_t)pre[b].size();
+    const int64_t m = walk(*t, tokens + tok_off[b], n, [&](int32_t id, int64_t k) { visits.push_back({id, k}); });
+    P[b] = std::min(m, n > 0 ? n - 1 : 0);  // at least one token is always computed
+    first_visit[b + 1] = (int64_t)visits.size();
     need += n - P[b] + reserve;
   }
-  for (int32_t b = 0; b < batch; ++b)
-    for (int32_t b2 = 0; b2 < b; ++b2)
-      if (rows[b] == rows[b2] && batch <= 4096) return fail(RC_ERR_ARG, "requests %d and %d share table row %d", b2, b, rows[b]);
+  if (rows_repeat(batch, rows)) return fail(RC_ERR_ARG, "two requests of the batch share a table row");
   if (need > (int64_t)t->free_q.size())
     return fail(RC_ERR_NOMEM, "batch needs %lld slots, %zu free", (long long)need, t->free_q.size());
+  // pass 2: write rows, allocate
   const int64_t now = ++t->clock;
   for (int32_t b = 0; b < batch; ++b) {
     const int64_t n = tok_off[b + 1] - tok_off[b];
     int32_t* row = table + (int64_t)rows[b] * stride;
-    std::copy(pre[b].begin(), pre[b].end(), row);
+    int64_t w = 0;
+    for (int64_t v = first_visit[b]; v < first_visit[b + 1] && w < P[b]; ++v) {
+      const Node& c = t->nodes[visits[v].node];
+      const int64_t k = std::min(visits[v].k, P[b] - w);
+      std::copy(c.slot.data(), c.slot.data() + k, row + w);
+      w += k;
+    }
     for (int64_t i = P[b]; i < n + reserve; ++i) {
       int32_t s = t->free_q.front();
       t->free_q.pop_front();
@@ -343,7 +367,7 @@ rc_status rc_radix_emit_rows(rc_radix* t, int32_t batch, const int32_t* tokens, 
     }
     prefix_lens[b] = (int32_t)P[b];
     extend_lens[b] = (int32_t)(n - P[b]);
-    for (int32_t id : touched[b]) t->nodes[id].last_use = now;
+    for (int64_t v = first_visit[b]; v < first_visit[b + 1]; ++v) t->nodes[visits[v].node].last_use = now;
     t->st.matches++;
     t->st.matched_tokens += P[b];
   }
@@ -512,20 +536,21 @@ extern "C" rc_status rc_plan_decode_unshared(int32_t batch, const int32_t* rows,
 }
 
 extern "C" rc_status rc_radix_plan_decode(rc_radix* t, int32_t batch, const int32_t* tokens, const int64_t* tok_off,
-                                          const int32_t* rows, const int32_t* max_seq, int32_t group, int32_t chunk,
-                                          int32_t* plan, int64_t cap, rc_plan_info* info) {
+                                          const int64_t* tok_len, const int32_t* rows, const int32_t* max_seq,
+                                          int32_t group, int32_t chunk, int32_t* plan, int64_t cap,
+                                          rc_plan_info* info) {
   if (!t) return fail(RC_ERR_ARG, "tree is NULL");
   rc_status st = plan_args(batch, max_seq, group, chunk, info);
   if (st != RC_OK) return st;
   if (batch > 0 && !tok_off) return fail(RC_ERR_ARG, "tok_off is NULL");
+  if ((st = check_lens(batch, tok_off, tok_len)) != RC_OK) return st;
   // walk every request; per node, the members and how far into the node each goes
   struct Visit { int32_t node; int64_t end; };
   std::vector<std::vector<Visit>> walks(batch);
   std::unordered_map<int32_t, std::vector<std::pair<int64_t, int32_t>>> by_node;  // node -> (end, b)
   std::vector<int64_t> walked(batch);
   for (int32_t b = 0; b < batch; ++b) {
-    const int64_t n = tok_off[b + 1] - tok_off[b];
-    if (n < 0) return fail(RC_ERR_ARG, "tok_off not non-decreasing at %d", b);
+    const int64_t n = tok_len ? tok_len[b] : tok_off[b + 1] - tok_off[b];
     if (n > 0 && !tokens) return fail(RC_ERR_ARG, "tokens is NULL");
     walked[b] = walk(*t, tokens + tok_off[b], n, [&](int32_t id, int64_t k) {
       const int64_t e = t->nodes[id].start + k;

@@ -15,10 +15,11 @@ Tuning& tuning() { return g_tuning; }
 
 namespace {
 struct Rec {
-  const char* name;
+  std::string name;
   hipEvent_t a, b;
 };
 bool g_on = false;
+std::string g_tag;
 std::vector<Rec> g_recs;
 std::vector<hipEvent_t> g_pool;
 
@@ -39,7 +40,7 @@ ProfScope::ProfScope(const char* name, hipStream_t stream) : stream_(stream) {
   hipEvent_t a = get_event(), b = get_event();
   if (!a || !b) return;
   hipEventRecord(a, stream);
-  g_recs.push_back({name, a, b});
+  g_recs.push_back({g_tag.empty() ? std::string(name) : std::string(name) + "@" + g_tag, a, b});
   idx_ = (int)g_recs.size() - 1;
 }
 
@@ -74,6 +75,12 @@ extern "C" rc_status rc_prof_enable(int32_t on) {
   return RC_OK;
 }
 
+extern "C" rc_status rc_prof_tag(const char* tag) {
+  rc::g_tag = tag ? tag : "";
+  if (rc::g_tag.size() > 15) rc::g_tag.resize(15);
+  return RC_OK;
+}
+
 extern "C" rc_status rc_prof_collect(rc_prof_entry* out, int32_t capacity, int32_t* n_out) {
   using namespace rc;
   if (!n_out || capacity < 0 || (capacity > 0 && !out)) return fail(RC_ERR_ARG, "bad argument to rc_prof_collect");
@@ -82,15 +89,15 @@ extern "C" rc_status rc_prof_collect(rc_prof_entry* out, int32_t capacity, int32
   for (auto& r : g_recs) {
     float ms = 0.f;
     if (hipEventSynchronize(r.b) != hipSuccess || hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess) {
-      st = fail(RC_ERR_HIP, "event timing failed for %s", r.name);
+      st = fail(RC_ERR_HIP, "event timing failed for %s", r.name.c_str());
       ms = 0.f;
     }
     size_t i = 0;
     for (; i < agg.size(); ++i)
-      if (!strncmp(agg[i].name, r.name, sizeof(agg[i].name))) break;
+      if (!strncmp(agg[i].name, r.name.c_str(), sizeof(agg[i].name) - 1)) break;
     if (i == agg.size()) {
       rc_prof_entry e{};
-      strncpy(e.name, r.name, sizeof(e.name) - 1);
+      strncpy(e.name, r.name.c_str(), sizeof(e.name) - 1);
       agg.push_back(e);
     }
     agg[i].launches++;

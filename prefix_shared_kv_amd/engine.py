@@ -26,12 +26,12 @@ import numpy as np
 import torch
 
 from . import api
-from .api import DecodePlan, KVShape, RadixTree
+from .api import DecodePlan, KVShape, RadixTree, TokenBatch
 
 
 @dataclasses.dataclass
 class Batch:
-    tokens: List[np.ndarray]
+    tb: TokenBatch             # the requests' token ids, flattened once
     rows: np.ndarray           # table row of each request
     prefix_lens: np.ndarray    # P_b
     extend_lens: np.ndarray    # E_b
@@ -40,7 +40,11 @@ class Batch:
 
     @property
     def size(self) -> int:
-        return len(self.tokens)
+        return len(self.tb)
+
+    @property
+    def tokens(self) -> List[np.ndarray]:
+        return [self.tb[i] for i in range(len(self.tb))]
 
     @property
     def total_extend(self) -> int:
@@ -68,7 +72,11 @@ class Engine:
         self.v_pool = v_pool if v_pool is not None else torch.zeros((S, H, D), dtype=shape.dtype, device=self.device)
         self.tree = RadixTree(S, free_order)
         self.stride = stride
-        self.table_h = np.full((max_rows, stride), -1, np.int32)
+        # the host table lives in pinned memory so that runs of rows upload
+        # straight from it; host writes to it wait for the last such upload
+        self._table_pin = torch.full((max_rows, stride), -1, dtype=torch.int32, pin_memory=True)
+        self.table_h = self._table_pin.numpy()
+        self._table_ev = None
         self.table_d = torch.full((max_rows, stride), -1, dtype=torch.int32, device=self.device)
         self.free_rows = list(range(max_rows))
 
@@ -118,10 +126,18 @@ class Engine:
         r = np.asarray(rows, np.int64)
         if np.all(np.diff(r) == 1):
             lo, hi = int(r[0]), int(r[-1]) + 1
-            self._h2d(self.table_h[lo:hi], out=self.table_d[lo:hi])
+            self.table_d[lo:hi].copy_(self._table_pin[lo:hi], non_blocking=True)
+            self._table_ev = torch.cuda.Event()
+            self._table_ev.record(torch.cuda.current_stream(self.device))
         else:
             idx = self._h2d(r)
             self.table_d[idx] = self._h2d(self.table_h[r])
+
+    def _table_writable(self) -> None:
+        """Wait until no upload still reads the host table."""
+        if self._table_ev is not None:
+            self._table_ev.synchronize()
+            self._table_ev = None
 
     # -- cache population (a sequence whose K/V are already known) -----------
     def populate(self, tokens: Sequence[int], k: torch.Tensor, v: torch.Tensor, expect_cached: Optional[int] = None) -> int:
@@ -142,16 +158,18 @@ class Engine:
         return m
 
     # -- a batch of requests --------------------------------------------------
-    def schedule(self, batch_tokens: Sequence[Sequence[int]], reserve: int = 0) -> Batch:
-        B = len(batch_tokens)
+    def schedule(self, batch_tokens, reserve: int = 0) -> Batch:
+        """batch_tokens: a list of token-id arrays or a TokenBatch."""
+        tb = batch_tokens if isinstance(batch_tokens, TokenBatch) else TokenBatch(batch_tokens)
+        B = len(tb)
         if B > len(self.free_rows):
             raise RuntimeError("no free table rows")
         rows = np.array(self.free_rows[:B], np.int32)
-        toks = [np.ascontiguousarray(t, np.int32) for t in batch_tokens]
-        P, E = self.tree.emit_rows(toks, self.table_h, rows=rows, reserve=reserve)
+        self._table_writable()
+        P, E = self.tree.emit_rows(tb, self.table_h, rows=rows, reserve=reserve)
         del self.free_rows[:B]
         self._upload_rows(rows)
-        b = Batch(toks, rows, P, E, reserve)
+        b = Batch(tb, rows, P, E, reserve)
         start = np.zeros(B, np.int32)
         if B:
             start[1:] = np.cumsum(E)[:-1]
@@ -182,7 +200,8 @@ class Engine:
     def commit(self, b: Batch, lengths: Optional[Sequence[int]] = None) -> None:
         """Insert each request's first `lengths[i]` tokens (default: all) into the tree.
         Where the tree already held them, the row is rewritten to the tree's slots."""
-        changed = self.tree.insert_rows(b.tokens, self.table_h, b.rows, lengths)
+        self._table_writable()
+        changed = self.tree.insert_rows(b.tb, self.table_h, b.rows, lengths)
         self._upload_rows(np.sort(b.rows[changed]))
 
     def prepare_decode(self, b: Batch, base_lens: Sequence[int], n_steps: int, chunk: int = 512,
@@ -190,13 +209,13 @@ class Engine:
         """Plan decode steps t = 0..n_steps-1; step t's token sits at position base_lens[i] + t.
         `committed[i]` tokens of request i are in the tree (default: base_lens)."""
         base = np.asarray(base_lens, np.int32)
-        if np.any(base + n_steps > np.array([len(t) for t in b.tokens]) + b.reserve):
+        if np.any(base + n_steps > b.tb.lens() + b.reserve):
             raise ValueError("decode steps run past the reserved slots")
         max_seq = base + n_steps
         g = self.shape.group
         com = base if committed is None else np.asarray(committed, np.int32)
         if shared:
-            plan = self.tree.plan_decode([t[:c] for t, c in zip(b.tokens, com)], max_seq, g, chunk, rows=b.rows)
+            plan = self.tree.plan_decode(b.tb, max_seq, g, chunk, rows=b.rows, lengths=com)
         else:
             plan = api.plan_decode_unshared(max_seq, g, chunk, rows=b.rows)
         plan.to(self.device, uploader=self._h2d)
@@ -225,12 +244,11 @@ class Engine:
     def release(self, b: Batch, keep: Optional[Sequence[int]] = None) -> None:
         """Return the batch's table rows; slots past `keep[i]` (default: tokens given) go back to the pool
         unless the tree holds them."""
-        tails = []
-        for i, (t, r) in enumerate(zip(b.tokens, b.rows)):
-            n = len(t) if keep is None else int(keep[i])
-            tails.append(self.table_h[r, n:len(t) + b.reserve])
+        lens = b.tb.lens()
+        keep = lens if keep is None else np.asarray(keep, np.int64)
+        tails = [self.table_h[r, k:n + b.reserve] for r, k, n in zip(b.rows, keep, lens)]
         if tails:
             self.tree.free(np.concatenate(tails))
-        for r in b.rows:
-            self.table_h[r, :] = -1
-            self.free_rows.append(int(r))
+        # the rows' entries are left as they are: the next schedule rewrites
+        # every entry a request can read
+        self.free_rows.extend(int(r) for r in b.rows)

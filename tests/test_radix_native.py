@@ -10,6 +10,7 @@ from hypothesis import strategies as st
 from oracle.radix_ref import OutOfSlots, RadixRef
 from prefix_shared_kv_amd import RadixTree, RcError
 from prefix_shared_kv_amd import _native as N
+from prefix_shared_kv_amd import api
 
 
 def _seq(draw, base, vocab):
@@ -157,3 +158,25 @@ def test_gpt2_bookkeeping_through_the_native_tree():
     t.insert(prefix, table[0, :409])
     P, E = t.emit_rows([prefix + list(range(9000, 9008)), prefix + list(range(9100, 9107))], table, rows=[1, 2])
     assert [(int(p), int(e), int(p + e)) for p, e in zip(P, E)] == [(409, 8, 417), (409, 7, 416)]
+
+
+def test_token_batch_lengths_equal_sliced_lists():
+    # a prefix of each request given by tok_len walks exactly like the sliced token lists
+    g = np.random.default_rng(3)
+    t = RadixTree(4000)
+    base = g.integers(0, 50, 300).astype(np.int32)
+    seqs = [np.concatenate([base[:g.integers(50, 300)], g.integers(0, 50, g.integers(1, 40))]).astype(np.int32)
+            for _ in range(12)]
+    for s in seqs[:6]:
+        m, pre = t.match(np.concatenate([s, [-1]]))
+        t.insert(s, np.concatenate([pre, t.alloc(len(s) - m)]))
+    tb = api.TokenBatch(seqs)
+    lengths = [int(g.integers(0, len(s) + 1)) for s in seqs]
+    max_seq = [len(s) + 3 for s in seqs]
+    a = t.plan_decode([s[:n] for s, n in zip(seqs, lengths)], max_seq, 4, 64)
+    b = t.plan_decode(tb, max_seq, 4, 64, lengths=lengths)
+    assert np.array_equal(a.host, b.host)
+    with pytest.raises(RcError):
+        t.plan_decode(tb, max_seq, 4, 64, lengths=[len(seqs[0]) + 1] + lengths[1:])
+    with pytest.raises(RcError):
+        t.insert_rows(tb, np.zeros((12, 400), np.int32), list(range(12)), lengths=[-1] + lengths[1:])
