@@ -25,7 +25,7 @@ HIP_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", INCLUDE, "-I", CSRC,
 ]
-CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-I", INCLUDE, "-I", CSRC]
+CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-pthread", "-Wall", "-Wextra", "-I", INCLUDE, "-I", CSRC]
 
 
 def _run(cmd):
@@ -59,7 +59,7 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
             if o.strip():
                 print(o)
     tmp = LIB + ".tmp"
-    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *[o for _, o in jobs_list]])
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-pthread", "-o", tmp, *[o for _, o in jobs_list]])
     shutil.move(tmp, LIB)
     return LIB
 

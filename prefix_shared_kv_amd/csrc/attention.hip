@@ -119,7 +119,7 @@ __device__ Work resolve(const Args& a, int mode, int L, bool leader) {
       return w;
     }
     if (E > a.max_extend && tile == 0 && w.hk == 0 && leader) flag(a.err, RC_DEVERR_LENGTH);
-    if ((int64_t)P > a.stride) {
+    if ((int64_t)P > a.stride || (P > 0 && a.pool_slots < 1)) {
       if (tile == 0 && leader) flag(a.err, RC_DEVERR_TABLE);
       return w;
     }
@@ -156,7 +156,8 @@ __device__ Work resolve(const Args& a, int mode, int L, bool leader) {
     w.split = it[3];
     w.moff = it[4];
     w.mcnt = it[5];
-    if (rep < 0 || rep >= a.table_rows || pb < 0 || pe < pb || (int64_t)pe > a.stride || w.split < 0 || w.split >= a.max_splits ||
+    if (rep < 0 || rep >= a.table_rows || pb < 0 || pe < pb || (int64_t)pe > a.stride || a.pool_slots < 1 ||
+        w.split < 0 || w.split >= a.max_splits ||
         w.moff < 0 || w.mcnt < 1 || w.mcnt * a.g > NCOL || w.moff + w.mcnt > n_members) {
       if (leader) flag(a.err, RC_DEVERR_PLAN);
       return w;
@@ -262,6 +263,13 @@ __device__ __forceinline__ i16x4 lds_read_tr(const uint16_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p));
 }
 
+// Lazy rescaling: a column's reference maximum moves only when a score
+// exceeds it by more than this many powers of two, so p = 2^(s - m) stays
+// below 2^8 and the O accumulator is rescaled a few times per tile instead of
+// whenever the running maximum creeps up.  Partials and the final o = acc / l
+// are exact up to rounding for any reference maximum.
+constexpr float RESCALE_SLACK = 8.f;
+
 template <int D>
 __device__ __forceinline__ void attn_bf16_body(const Args& a, const int mode, const int L, uint16_t (&sK)[2][BN * D],
                                                uint16_t (&sV)[2][BN * D]) {
@@ -272,7 +280,8 @@ __device__ __forceinline__ void attn_bf16_body(const Args& a, const int mode, co
   const Work w = resolve(a, mode, L, threadIdx.x == 0);
   if (!w.valid) return;  // uniform over the workgroup
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: LDS block addresses stay scalar
   const int hi = lane >> 5;  // which half of the wave
   const int c = wave * 32 + (lane & 31);
   const bool active = wave * 32 < w.ncols;
@@ -289,134 +298,134 @@ __device__ __forceinline__ void attn_bf16_body(const Args& a, const int mode, co
   for (int i = 0; i < NDB; ++i) acc[i] = f32x16{};
   float m_run = -INFINITY, l_run = 0.f;
 
-  // loader: thread -> (chunk lc of the row, keys lk0 .. lk0+KPT-1 of the stage)
-  const int lc = tid % CH;
-  const int lk0 = (tid / CH) * KPT;
-  const uint16_t* kpool = (const uint16_t*)a.k_pool;
-  const uint16_t* vpool = (const uint16_t*)a.v_pool;
-  const uint16_t* knew = (const uint16_t*)a.k_new;
-  const uint16_t* vnew = (const uint16_t*)a.v_new;
-  const int64_t rowHD = (int64_t)a.Hkv * D;
-  const int32_t* trow = a.table + w.row * a.stride;
+  // Loader.  Global -> LDS loads (global_load_lds_dwordx4) move 16 bytes per
+  // lane into 1 KiB of LDS at lane-consecutive addresses, so each load
+  // instruction fills one block of KPB keys x CH chunks of the row-major,
+  // chunk-swizzled tile; a lane fetches the logical chunk that belongs at its
+  // position.  Load r of wave w fills block 4r + w of K and of V: a lane's
+  // keys are then 4*KPB apart, the same in the swizzle, so one column offset
+  // serves all of them.
+  constexpr int KPB = 64 / CH;  // keys per 1 KiB block
+  const uint32_t row_bytes = (uint32_t)(a.Hkv * D * 2);
+  const uint32_t nslots = (uint32_t)a.pool_slots;  // >= 1 (checked when the work is resolved)
+  const int plain_end = min(w.key_end, w.ext_begin);  // stages ending here read pool slots only
+  const int lkey0 = wave * KPB + lane / CH;           // this lane's key in block w; + r*4*KPB in block 4r+w
+  const int coff = (w.hk * D + (((lane % CH) ^ swz<D>(lkey0)) << 3)) * 2;
+  // this lane's chunk in slot 0 / new token 0; + index x row_bytes
+  const char* kcol = (const char*)a.k_pool + coff;
+  const char* vcol = (const char*)a.v_pool + coff;
+  const char* kncol = (const char*)a.k_new + coff;
+  const char* vncol = (const char*)a.v_new + coff;
+  const int32_t* trow = a.table + w.row * a.stride + lkey0;
+  auto lkey = [&](int r) { return lkey0 + r * 4 * KPB; };
   int32_t slot[2][KPT];
-  u32x4 kr[KPT], vr[KPT];
 
-  // slots of stage st (pool positions only)
+  // slots of this lane's keys in the stage starting at kt (pool keys only)
   auto load_slots = [&](int (&sl)[KPT], int kt) {
+    if (kt + BN <= plain_end) {
 #pragma unroll
-    for (int r = 0; r < KPT; ++r) {
-      const int j = kt + lk0 + r;
-      sl[r] = (j < w.key_end && j < w.ext_begin) ? trow[j] : -1;
-    }
-  };
-  int bad_slot = 0;  // an out-of-range slot was met (reported once, at the end)
-  auto load_kv = [&](u32x4 (&kk)[KPT], u32x4 (&vv)[KPT], const int (&sl)[KPT], int kt) {
-    if (kt + BN <= w.key_end && kt + BN <= w.ext_begin) {
-      // every key of the stage is a cached prefix key: no branches
-#pragma unroll
-      for (int r = 0; r < KPT; ++r) {
-        const int32_t s = sl[r];
-        const bool ok = (uint32_t)s < (uint32_t)a.pool_slots;
-        bad_slot |= !ok;
-        const int64_t off = (int64_t)(ok ? s : 0) * rowHD + (int64_t)w.hk * D + lc * 8;
-        kk[r] = *(const u32x4*)(kpool + off);
-        vv[r] = *(const u32x4*)(vpool + off);
-      }
+      for (int r = 0; r < KPT; ++r) sl[r] = trow[kt + r * 4 * KPB];
       return;
     }
 #pragma unroll
     for (int r = 0; r < KPT; ++r) {
-      const int j = kt + lk0 + r;
-      kk[r] = u32x4{0, 0, 0, 0};
-      vv[r] = u32x4{0, 0, 0, 0};
-      if (j < w.key_end) {
-        if (j >= w.ext_begin) {
-          const int64_t off = (w.ext_base + (j - w.ext_begin)) * rowHD + (int64_t)w.hk * D + lc * 8;
-          kk[r] = *(const u32x4*)(knew + off);
-          vv[r] = *(const u32x4*)(vnew + off);
-        } else {
-          const int32_t s = sl[r];
-          const bool ok = (uint32_t)s < (uint32_t)a.pool_slots;
-          bad_slot |= !ok;
-          if (ok) {
-            const int64_t off = (int64_t)s * rowHD + (int64_t)w.hk * D + lc * 8;
-            kk[r] = *(const u32x4*)(kpool + off);
-            vv[r] = *(const u32x4*)(vpool + off);
-          }
-        }
-      }
+      const int j = min(kt + lkey(r), w.key_end - 1);  // keys past the end repeat the last one
+      sl[r] = j < w.ext_begin ? trow[j - lkey0] : -1;
     }
   };
-  auto store = [&](uint16_t* dk, uint16_t* dv, const u32x4 (&kk)[KPT], const u32x4 (&vv)[KPT]) {
+  int bad_slot = 0;  // an out-of-range slot was met (reported once, at the end)
+  auto dma = [&](const char* src, uint16_t* dst) {
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                     (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+  };
+  // Out-of-range slots are clamped (and reported), so every load stays in
+  // the pool.  Keys past the range end are loaded as copies of the last key,
+  // so the tile holds finite values where p = 0 multiplies them.
+  auto issue = [&](uint16_t* dk, uint16_t* dv, const int (&sl)[KPT], int kt) {
+    if (kt + BN <= plain_end) {  // every key of the stage is a cached prefix key
+      uint32_t mx = 0;
+#pragma unroll
+      for (int r = 0; r < KPT; ++r) mx = max(mx, (uint32_t)sl[r]);
+      bad_slot |= mx >= nslots;
+#pragma unroll
+      for (int r = 0; r < KPT; ++r) {
+        const uint64_t off = (uint64_t)min((uint32_t)sl[r], nslots - 1) * row_bytes;
+        const int blk = (4 * r + wave) * KPB * D;
+        dma(kcol + off, dk + blk);
+        dma(vcol + off, dv + blk);
+      }
+      return;
+    }
+    // (integer selects, not a choice between pointers, keep this in registers)
 #pragma unroll
     for (int r = 0; r < KPT; ++r) {
-      const int key = lk0 + r;
-      const int o = key * D + ((lc ^ swz<D>(key)) << 3);
-      *(u32x4*)(dk + o) = kk[r];
-      *(u32x4*)(dv + o) = vv[r];
+      const int blk = (4 * r + wave) * KPB * D;
+      const int j = min(kt + lkey(r), w.key_end - 1);
+      const bool is_new = j >= w.ext_begin;
+      bad_slot |= !is_new && (uint32_t)sl[r] >= nslots;
+      const uint64_t idx = is_new ? (uint64_t)(w.ext_base + (j - w.ext_begin)) : (uint64_t)min((uint32_t)sl[r], nslots - 1);
+      const uint64_t kb_ = is_new ? (uint64_t)kncol : (uint64_t)kcol;
+      const uint64_t vb_ = is_new ? (uint64_t)vncol : (uint64_t)vcol;
+      dma((const char*)(kb_ + idx * row_bytes), dk + blk);
+      dma((const char*)(vb_ + idx * row_bytes), dv + blk);
     }
   };
 
-  auto compute = [&](const uint16_t* tk, const uint16_t* tv, int kt) {
-    // S^T = K Q^T over two 32-key blocks
-    f32x16 s[2];
+  // S^T for the 32 keys of half h of the stage in LDS
+  auto qk = [&](const uint16_t* tk, int h) {
+    f32x16 s = f32x16{};
+    const int key = h * 32 + (lane & 31);
+    const uint16_t* row = tk + key * D;
+    const int sw = swz<D>(key);
 #pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      s[m] = f32x16{};
-      const int key = m * 32 + (lane & 31);
-      const uint16_t* row = tk + key * D;
-      const int sw = swz<D>(key);
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        const bf16x8 kf = *(const bf16x8*)(row + (((2 * ks + hi) ^ sw) << 3));
-        s[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s[m], 0, 0, 0);
-      }
+    for (int ks = 0; ks < NKS; ++ks) {
+      const bf16x8 kf = *(const bf16x8*)(row + (((2 * ks + hi) ^ sw) << 3));
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s, 0, 0, 0);
     }
-    const bool need_mask = (kt + BN > w.key_end) || ((int64_t)kt + BN - 1 > (int64_t)w.min_limit);
+    return s;
+  };
+  // online softmax of half h (masked on boundary stages only), then
+  // O^T += V^T P^T over its two 16-key steps; V^T fragments by transposing reads
+  auto softmax_pv = [&](f32x16& s, const uint16_t* tv, int kt, int h, auto maskc) {
+    constexpr bool MASK = decltype(maskc)::value;
     float mx = -INFINITY;
 #pragma unroll
-    for (int m = 0; m < 2; ++m)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        float x = s[m][v];
-        if (need_mask) {
-          const int key = kt + m * 32 + (v >> 2) * 8 + hi * 4 + (v & 3);
-          if (key >= w.key_end || key > col.limit) x = -INFINITY;
-        }
-        s[m][v] = x;
-        mx = fmaxf(mx, x);
+    for (int v = 0; v < 16; ++v) {
+      float x = s[v];
+      if constexpr (MASK) {
+        const int key = kt + h * 32 + (v >> 2) * 8 + hi * 4 + (v & 3);
+        x = (key >= w.key_end || key > col.limit) ? -INFINITY : x;
       }
+      s[v] = x;
+      mx = fmaxf(mx, x);
+    }
     mx = fmaxf(mx, __shfl_xor(mx, 32)) * a.scale_log2;
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    float psum = 0.f;
-#pragma unroll
-    for (int m = 0; m < 2; ++m)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(s[m][v], a.scale_log2, -m_use));
-        s[m][v] = p;
-        psum += p;
-      }
-    // rescale only when some running max moved (alpha == 1 exactly otherwise)
-    if (__any(m_new != m_run)) {
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+    const bool upd = mx > m_run + RESCALE_SLACK;
+    if (__any(upd)) {
+      const float m_new = upd ? mx : m_run;
+      const float alpha = upd ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
       l_run *= alpha;
 #pragma unroll
       for (int db = 0; db < NDB; ++db) acc[db] *= alpha;
+      m_run = m_new;
+    }
+    const float m_use = m_run == -INFINITY ? 0.f : m_run;
+    float psum = 0.f;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const float p = __builtin_amdgcn_exp2f(fmaf(s[v], a.scale_log2, -m_use));
+      s[v] = p;
+      psum += p;
     }
     l_run += psum;
-    m_run = m_new;
-
-    // O^T += V^T P^T, four 16-key steps; V^T fragments by transposing reads
     const int g = lane >> 4, r = lane & 15;
     const int dsub = 16 * (g & 1) + 4 * (r & 3);
 #pragma unroll
-    for (int k2 = 0; k2 < 4; ++k2) {
-      const int m = k2 >> 1, h = k2 & 1;
+    for (int hh = 0; hh < 2; ++hh) {
+      const int k2 = 2 * h + hh;
       bf16x8 pf;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) pf[i] = (__bf16)s[m][8 * h + i];
+      for (int i = 0; i < 8; ++i) pf[i] = (__bf16)s[8 * hh + i];
       const int key0 = 16 * k2 + 4 * (g >> 1) + (r >> 2);
       const int key1 = key0 + 8;
       const int sw0 = swz<D>(key0), sw1 = swz<D>(key1);
@@ -430,28 +439,56 @@ __device__ __forceinline__ void attn_bf16_body(const Args& a, const int mode, co
       }
     }
   };
+  // both halves' S^T first, so the second half's MFMAs can overlap the
+  // first half's softmax
+  auto compute = [&](const uint16_t* tk, const uint16_t* tv, int kt, auto maskc) {
+    f32x16 s0 = qk(tk, 0);
+    f32x16 s1 = qk(tk, 1);
+    softmax_pv(s0, tv, kt, 0, maskc);
+    softmax_pv(s1, tv, kt, 1, maskc);
+  };
 
-  // Pipeline: LDS double buffer (one barrier per stage), the next stage's K/V
-  // in registers while this one is computed, slot indices one stage ahead of
-  // the loads that use them.
+  // Pipeline: LDS double buffer.  At each stage's barrier the stage's tile has
+  // landed (every wave waited for its own loads) and the other buffer's reads
+  // are done; the next stage's loads then fly while this one is computed, and
+  // slot indices run one stage further ahead.
   const int kb = w.key_begin;
   const int n_st = (w.key_end - kb + BN - 1) / BN;
   if (n_st > 0) load_slots(slot[0], kb);
   if (n_st > 1) load_slots(slot[1], kb + BN);
-  if (n_st > 0) load_kv(kr, vr, slot[0], kb);
+  if (n_st > 0) issue(sK[0], sV[0], slot[0], kb);
 
-  auto step = [&](auto bufc, int i) {
+  auto step = [&](auto bufc, int i, auto maskc) {
     constexpr int b = decltype(bufc)::value;
     const int kt = kb + i * BN;
-    store(sK[b], sV[b], kr, vr);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (i + 1 < n_st) load_kv(kr, vr, slot[b ^ 1], kt + BN);
+    if (i + 1 < n_st) issue(sK[b ^ 1], sV[b ^ 1], slot[b ^ 1], kt + BN);
     if (i + 2 < n_st) load_slots(slot[b], kt + 2 * BN);
-    if (active) compute(sK[b], sV[b], kt);
+    if (active) compute(sK[b], sV[b], kt, maskc);
   };
-  for (int i = 0; i < n_st; i += 2) {
-    step(std::integral_constant<int, 0>{}, i);
-    if (i + 1 < n_st) step(std::integral_constant<int, 1>{}, i + 1);
+  // stages before n_plain need no mask: every key is below the range end and
+  // at or below every column's causal limit; the rest (a tail) are masked
+  int n_plain = (w.key_end - kb) / BN;
+  if (w.min_limit != INT_MAX) n_plain = min(n_plain, max(0, (w.min_limit + 1 - kb) / BN));
+  const auto B0 = std::integral_constant<int, 0>{};
+  const auto B1 = std::integral_constant<int, 1>{};
+  int i = 0;
+  for (; i + 1 < n_plain; i += 2) {
+    step(B0, i, std::false_type{});
+    step(B1, i + 1, std::false_type{});
+  }
+  if (i < n_plain) {
+    step(B0, i, std::false_type{});
+    ++i;
+    if (i < n_st) {
+      step(B1, i, std::true_type{});
+      ++i;
+    }
+  }
+  for (; i < n_st; i += 2) {
+    step(B0, i, std::true_type{});
+    if (i + 1 < n_st) step(B1, i + 1, std::true_type{});
   }
 
   if (bad_slot) flag(a.err, RC_DEVERR_SLOT);

@@ -14,6 +14,8 @@
 #include <cstring>
 #include <deque>
 #include <new>
+#include <system_error>
+#include <thread>
 #include <unordered_map>
 #include <vector>
 
@@ -123,6 +125,34 @@ bool rows_repeat(int32_t batch, const int32_t* rows) {
   std::vector<int32_t> v(rows, rows + batch);
   std::sort(v.begin(), v.end());
   return std::adjacent_find(v.begin(), v.end()) != v.end();
+}
+
+// f(b) for b in [0, n), on several host threads when the batch holds enough
+// tokens to pay for them (f must only read shared state, or write to b's own
+// outputs).  Requests are dealt in interleaved order so that long and short
+// ones mix across threads.
+template <class F>
+void for_requests(int32_t n, int64_t tokens, F&& f) {
+  constexpr int64_t kTokensPerThread = 1 << 19;
+  const unsigned hw = std::max(1u, std::thread::hardware_concurrency());
+  const int32_t nt = (int32_t)std::min<int64_t>({(int64_t)hw, 8, (int64_t)n, tokens / kTokensPerThread});
+  if (nt <= 1) {
+    for (int32_t b = 0; b < n; ++b) f(b);
+    return;
+  }
+  std::vector<std::thread> pool;
+  try {
+    for (int32_t i = 1; i < nt; ++i)
+      pool.emplace_back([&, i] {
+        for (int32_t b = i; b < n; b += nt) f(b);
+      });
+  } catch (const std::system_error&) {  // no threads to spare: the caller's thread does the rest
+  }
+  const int32_t started = (int32_t)pool.size() + 1;
+  for (int32_t i = started; i < nt; ++i)
+    for (int32_t b = i; b < n; b += nt) f(b);
+  for (int32_t b = 0; b < n; b += nt) f(b);
+  for (auto& th : pool) th.join();
 }
 
 }  // namespace
@@ -331,34 +361,29 @@ rc_status rc_radix_emit_rows(rc_radix* t, int32_t batch, const int32_t* tokens, 
   // pass 1 (read only): matched length and the edges entered, per request
   struct Visit { int32_t node; int64_t k; };
   std::vector<int64_t> P(batch);
-  std::vector<int64_t> first_visit(batch + 1, 0);
-  std::vector<Visit> visits;
+  std::vector<std::vector<Visit>> visits(batch);
   int64_t need = 0;
   for (int32_t b = 0; b < batch; ++b) {
     const int64_t n = tok_off[b + 1] - tok_off[b];
     if (n > 0 && !tokens) return fail(RC_ERR_ARG, "tokens is NULL");
     if (rows[b] < 0 || rows[b] >= table_rows) return fail(RC_ERR_RANGE, "row %d of request %d outside [0, %d)", rows[b], b, table_rows);
     if (n + reserve > stride) return fail(RC_ERR_RANGE, "request %d needs %lld table entries, stride is %lld", b, (long long)(n + reserve), (long long)stride);
-    const int64_t m = walk(*t, tokens + tok_off[b], n, [&](int32_t id, int64_t k) { visits.push_back({id, k}); });
-    P[b] = std::min(m, n > 0 ? n - 1 : 0);  // at least one token is always computed
-    first_visit[b + 1] = (int64_t)visits.size();
-    need += n - P[b] + reserve;
   }
+  const int64_t total = batch > 0 ? tok_off[batch] - tok_off[0] : 0;
+  for_requests(batch, total, [&](int32_t b) {
+    const int64_t n = tok_off[b + 1] - tok_off[b];
+    const int64_t m = walk(*t, tokens + tok_off[b], n, [&](int32_t id, int64_t k) { visits[b].push_back({id, k}); });
+    P[b] = std::min(m, n > 0 ? n - 1 : 0);  // at least one token is always computed
+  });
+  for (int32_t b = 0; b < batch; ++b) need += tok_off[b + 1] - tok_off[b] - P[b] + reserve;
   if (rows_repeat(batch, rows)) return fail(RC_ERR_ARG, "two requests of the batch share a table row");
   if (need > (int64_t)t->free_q.size())
     return fail(RC_ERR_NOMEM, "batch needs %lld slots, %zu free", (long long)need, t->free_q.size());
-  // pass 2: write rows, allocate
+  // pass 2: allocate in request order, then copy the matched prefixes' slots
   const int64_t now = ++t->clock;
   for (int32_t b = 0; b < batch; ++b) {
     const int64_t n = tok_off[b + 1] - tok_off[b];
     int32_t* row = table + (int64_t)rows[b] * stride;
-    int64_t w = 0;
-    for (int64_t v = first_visit[b]; v < first_visit[b + 1] && w < P[b]; ++v) {
-      const Node& c = t->nodes[visits[v].node];
-      const int64_t k = std::min(visits[v].k, P[b] - w);
-      std::copy(c.slot.data(), c.slot.data() + k, row + w);
-      w += k;
-    }
     for (int64_t i = P[b]; i < n + reserve; ++i) {
       int32_t s = t->free_q.front();
       t->free_q.pop_front();
@@ -367,10 +392,21 @@ rc_status rc_radix_emit_rows(rc_radix* t, int32_t batch, const int32_t* tokens, 
     }
     prefix_lens[b] = (int32_t)P[b];
     extend_lens[b] = (int32_t)(n - P[b]);
-    for (int64_t v = first_visit[b]; v < first_visit[b + 1]; ++v) t->nodes[visits[v].node].last_use = now;
+    for (const Visit& v : visits[b]) t->nodes[v.node].last_use = now;
     t->st.matches++;
     t->st.matched_tokens += P[b];
   }
+  for_requests(batch, total, [&](int32_t b) {
+    int32_t* row = table + (int64_t)rows[b] * stride;
+    int64_t w = 0;
+    for (const Visit& v : visits[b]) {
+      if (w >= P[b]) break;
+      const Node& c = t->nodes[v.node];
+      const int64_t k = std::min(v.k, P[b] - w);
+      std::memcpy(row + w, c.slot.data(), (size_t)k * sizeof(int32_t));
+      w += k;
+    }
+  });
   return RC_OK;
 }
 
@@ -448,7 +484,7 @@ struct PlanBuilder {
     // wide items (members*group > 16) first, then narrow ones; within each
     // class the longest first (members x positions), so the last workgroups
     // to start are the short ones
-    struct Item { int64_t cost; int32_t v[RC_PLAN_ITEM]; std::vector<int32_t> mem; };
+    struct Item { int64_t cost; int32_t v[RC_PLAN_ITEM]; int32_t range, first; };
     std::vector<Item> wide, narrow;
     for (int32_t r : order) {
       const Range& R = ranges[r];
@@ -458,9 +494,9 @@ struct PlanBuilder {
         const int64_t pe = std::min<int64_t>(p + chunk, R.end);
         for (size_t g0 = 0; g0 < R.members.size(); g0 += max_m) {
           const size_t cnt = std::min<size_t>(max_m, R.members.size() - g0);
-          Item it{(int64_t)cnt * (pe - p), {row_of(R.members[g0]), (int32_t)p, (int32_t)pe, sp, 0, (int32_t)cnt, 0, 0},
-                  std::vector<int32_t>(R.members.begin() + g0, R.members.begin() + g0 + cnt)};
-          ((int64_t)cnt * group <= 16 ? narrow : wide).push_back(std::move(it));
+          const Item it{(int64_t)cnt * (pe - p), {row_of(R.members[g0]), (int32_t)p, (int32_t)pe, sp, 0, (int32_t)cnt, 0, 0},
+                        r, (int32_t)g0};
+          ((int64_t)cnt * group <= 16 ? narrow : wide).push_back(it);
           if (R.members.size() > 1) shared_items++;
         }
       }
@@ -469,10 +505,12 @@ struct PlanBuilder {
     std::stable_sort(wide.begin(), wide.end(), by_cost);
     std::stable_sort(narrow.begin(), narrow.end(), by_cost);
     narrow_begin = (int32_t)wide.size();
+    item_rows.reserve((wide.size() + narrow.size()) * RC_PLAN_ITEM);
     for (auto* list : {&wide, &narrow})
       for (Item& it : *list) {
         it.v[4] = (int32_t)members.size();
-        members.insert(members.end(), it.mem.begin(), it.mem.end());
+        const auto& mem = ranges[it.range].members;
+        members.insert(members.end(), mem.begin() + it.first, mem.begin() + it.first + it.v[5]);
         item_rows.insert(item_rows.end(), it.v, it.v + RC_PLAN_ITEM);
       }
     for (int32_t r : order)
@@ -549,15 +587,21 @@ extern "C" rc_status rc_radix_plan_decode(rc_radix* t, int32_t batch, const int3
   std::vector<std::vector<Visit>> walks(batch);
   std::unordered_map<int32_t, std::vector<std::pair<int64_t, int32_t>>> by_node;  // node -> (end, b)
   std::vector<int64_t> walked(batch);
+  int64_t total = 0;
   for (int32_t b = 0; b < batch; ++b) {
     const int64_t n = tok_len ? tok_len[b] : tok_off[b + 1] - tok_off[b];
     if (n > 0 && !tokens) return fail(RC_ERR_ARG, "tokens is NULL");
+    total += n;
+  }
+  for_requests(batch, total, [&](int32_t b) {
+    const int64_t n = tok_len ? tok_len[b] : tok_off[b + 1] - tok_off[b];
     walked[b] = walk(*t, tokens + tok_off[b], n, [&](int32_t id, int64_t k) {
-      const int64_t e = t->nodes[id].start + k;
-      walks[b].push_back({id, e});
-      by_node[id].push_back({e, b});
+      walks[b].push_back({id, t->nodes[id].start + k});
     });
+  });
+  for (int32_t b = 0; b < batch; ++b) {
     if (max_seq[b] < walked[b]) return fail(RC_ERR_RANGE, "max_seq_lens[%d] = %d shorter than its cached prefix %lld", b, max_seq[b], (long long)walked[b]);
+    for (const Visit& v : walks[b]) by_node[v.node].push_back({v.end, b});
   }
   PlanBuilder pb{batch, group, chunk, std::max(1, 128 / group), rows, {}, {}, {}, {}, {}};
   pb.path.resize(batch);

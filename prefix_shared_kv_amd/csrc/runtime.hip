@@ -39,13 +39,14 @@ ProfScope::ProfScope(const char* name, hipStream_t stream) : stream_(stream) {
   if (!g_on) return;
   hipEvent_t a = get_event(), b = get_event();
   if (!a || !b) return;
-  hipEventRecord(a, stream);
+  if (hipEventRecord(a, stream) != hipSuccess) return;  // not timed
   g_recs.push_back({g_tag.empty() ? std::string(name) : std::string(name) + "@" + g_tag, a, b});
   idx_ = (int)g_recs.size() - 1;
 }
 
 ProfScope::~ProfScope() {
-  if (idx_ >= 0) hipEventRecord(g_recs[idx_].b, stream_);
+  // a failed end record is reported by rc_prof_collect when it times the pair
+  if (idx_ >= 0) (void)hipEventRecord(g_recs[idx_].b, stream_);
 }
 
 rc_status check_launch(const char* what) {

@@ -19,6 +19,7 @@ RadixAttention and `fork`):
 """
 from __future__ import annotations
 
+import collections
 import dataclasses
 from typing import List, Optional, Sequence
 
@@ -72,11 +73,16 @@ class Engine:
         self.v_pool = v_pool if v_pool is not None else torch.zeros((S, H, D), dtype=shape.dtype, device=self.device)
         self.tree = RadixTree(S, free_order)
         self.stride = stride
-        # the host table lives in pinned memory so that runs of rows upload
-        # straight from it; host writes to it wait for the last such upload
+        # The host table lives in pinned memory so that runs of rows upload
+        # straight from it.  Such an upload reads the rows when the stream
+        # reaches it, so a row is rewritten on the host only after the last
+        # upload that covered it has completed: each row remembers the number
+        # of that upload, and the uploads' events complete in stream order.
         self._table_pin = torch.full((max_rows, stride), -1, dtype=torch.int32, pin_memory=True)
         self.table_h = self._table_pin.numpy()
-        self._table_ev = None
+        self._row_upload = np.zeros(max_rows, np.int64)  # number of the last upload reading each row
+        self._uploads = collections.deque()              # (number, event) of uploads not known complete
+        self._n_uploads = 0
         self.table_d = torch.full((max_rows, stride), -1, dtype=torch.int32, device=self.device)
         self.free_rows = list(range(max_rows))
 
@@ -86,20 +92,24 @@ class Engine:
     # plans) while the GPU works.  A buffer is rewritten only after the copy
     # that last read it has completed (its event); allocating pinned memory
     # per copy instead can synchronise the whole device.
-    _RING = 32
+    # Every buffer is allocated up front at _RING_BYTES, so steady-state
+    # copies allocate no pinned memory; a larger array gets a buffer of its own.
+    _RING = 64
+    _RING_BYTES = 1 << 20
 
     def _pinned(self, a: np.ndarray) -> torch.Tensor:
         a = np.ascontiguousarray(a)
         if not hasattr(self, "_ring"):
-            self._ring = [[None, None] for _ in range(self._RING)]
+            self._ring = [[torch.empty(self._RING_BYTES, dtype=torch.uint8, pin_memory=True), None]
+                          for _ in range(self._RING)]
             self._ring_i = 0
         slot = self._ring[self._ring_i]
         self._ring_i = (self._ring_i + 1) % self._RING
         buf, ev = slot
         if ev is not None:
             ev.synchronize()
-        if buf is None or buf.numel() < a.nbytes:
-            buf = torch.empty(max(a.nbytes, 1 << 16), dtype=torch.uint8, pin_memory=True)
+        if buf.numel() < a.nbytes:
+            buf = torch.empty(a.nbytes, dtype=torch.uint8, pin_memory=True)
             slot[0] = buf
         view = buf[:a.nbytes].view(torch.from_numpy(a[:0].reshape(-1)).dtype).view(a.shape)
         view.copy_(torch.from_numpy(a))
@@ -123,21 +133,30 @@ class Engine:
     def _upload_rows(self, rows: np.ndarray) -> None:
         if len(rows) == 0:
             return
-        r = np.asarray(rows, np.int64)
-        if np.all(np.diff(r) == 1):
-            lo, hi = int(r[0]), int(r[-1]) + 1
-            self.table_d[lo:hi].copy_(self._table_pin[lo:hi], non_blocking=True)
-            self._table_ev = torch.cuda.Event()
-            self._table_ev.record(torch.cuda.current_stream(self.device))
-        else:
-            idx = self._h2d(r)
-            self.table_d[idx] = self._h2d(self.table_h[r])
+        # one copy per run of consecutive rows, straight from the pinned table
+        r = np.unique(np.asarray(rows, np.int64))
+        cuts = np.flatnonzero(np.diff(r) != 1) + 1
+        for lo, hi in zip(np.concatenate([[0], cuts]), np.concatenate([cuts, [len(r)]])):
+            a, b = int(r[lo]), int(r[hi - 1]) + 1
+            self.table_d[a:b].copy_(self._table_pin[a:b], non_blocking=True)
+        ev = torch.cuda.Event()
+        ev.record(torch.cuda.current_stream(self.device))
+        self._n_uploads += 1
+        self._uploads.append((self._n_uploads, ev))
+        self._row_upload[r] = self._n_uploads
 
-    def _table_writable(self) -> None:
-        """Wait until no upload still reads the host table."""
-        if self._table_ev is not None:
-            self._table_ev.synchronize()
-            self._table_ev = None
+    def _rows_writable(self, rows: np.ndarray) -> None:
+        """Wait until no pending upload still reads these rows of the host table."""
+        if len(rows) == 0 or not self._uploads:
+            return
+        need = int(self._row_upload[np.asarray(rows, np.int64)].max())
+        while self._uploads and self._uploads[0][0] <= need:
+            n, ev = self._uploads.popleft()
+            if n == need or not self._uploads or self._uploads[0][0] > need:
+                ev.synchronize()  # later events of the stream imply the earlier ones
+                break
+        while self._uploads and self._uploads[0][1].query():
+            self._uploads.popleft()
 
     # -- cache population (a sequence whose K/V are already known) -----------
     def populate(self, tokens: Sequence[int], k: torch.Tensor, v: torch.Tensor, expect_cached: Optional[int] = None) -> int:
@@ -165,7 +184,7 @@ class Engine:
         if B > len(self.free_rows):
             raise RuntimeError("no free table rows")
         rows = np.array(self.free_rows[:B], np.int32)
-        self._table_writable()
+        self._rows_writable(rows)
         P, E = self.tree.emit_rows(tb, self.table_h, rows=rows, reserve=reserve)
         del self.free_rows[:B]
         self._upload_rows(rows)
@@ -200,9 +219,17 @@ class Engine:
     def commit(self, b: Batch, lengths: Optional[Sequence[int]] = None) -> None:
         """Insert each request's first `lengths[i]` tokens (default: all) into the tree.
         Where the tree already held them, the row is rewritten to the tree's slots."""
-        self._table_writable()
-        changed = self.tree.insert_rows(b.tb, self.table_h, b.rows, lengths)
-        self._upload_rows(np.sort(b.rows[changed]))
+        # The insert works on a copy of the batch's rows (the table's rows may
+        # still be uploading); only rows the tree rewrote are written back.
+        n = b.tb.lens() if lengths is None else np.asarray(lengths, np.int64)
+        width = max(int(n.max()) if b.size else 0, 1)
+        work = np.ascontiguousarray(self.table_h[b.rows, :width])
+        changed = self.tree.insert_rows(b.tb, work, np.arange(b.size, dtype=np.int32), lengths)
+        if changed.any():
+            rows = b.rows[changed]
+            self._rows_writable(rows)
+            self.table_h[rows, :width] = work[changed]
+            self._upload_rows(np.sort(rows))
 
     def prepare_decode(self, b: Batch, base_lens: Sequence[int], n_steps: int, chunk: int = 512,
                        shared: bool = True, committed: Optional[Sequence[int]] = None) -> DecodeState:
