@@ -237,15 +237,17 @@ __device__ __forceinline__ Col column(const Args& a, int mode, const Work& w, in
 }
 
 // LDS tiles hold K and V row-major, [key][head dim], with the 16-byte chunks
-// of each row XOR-swizzled by a function of the key.  For D = 128 the swizzle
-// is a bijection of the key's low 4 bits chosen so that both access patterns
-// are free of bank conflicts: 16 consecutive keys reading one chunk (the K
-// operand, ds_read_b128) and 8 consecutive keys x 4 chunks (the transposing
-// V reads, ds_read_b64_tr_b16).
+// of each row XOR-swizzled by a function of the key.  For D = 128 (256-byte
+// rows, so the row itself never moves a bank) the swizzle is a linear
+// bijection of the key's low 4 bits, found by exhaustive search over a model
+// of 64 four-byte banks, that leaves every read pattern here free of bank
+// conflicts: 16 keys reading one chunk (K operands, ds_read_b128, 16 lanes
+// per pass), and the transposing V reads (32 lanes per pass) of both tile
+// shapes: 4 keys x 4 chunks (32x32x16) and 8 keys x 2 chunks (16x16x32).
 template <int D>
 __device__ __forceinline__ int swz(int key) {
   if constexpr (D == 128)
-    return ((key & 7) << 1) | ((key >> 3) & 1);
+    return ((key & 3) << 2) | ((key >> 1) & 2) | ((key >> 3) & 1);
   else
     return key & 7;
 }
@@ -371,35 +373,53 @@ __device__ __forceinline__ void attn_bf16_body(const Args& a, const int mode, co
     }
   };
 
-  // S^T for the 32 keys of half h of the stage in LDS
-  auto qk = [&](const uint16_t* tk, int h) {
-    f32x16 s = f32x16{};
-    const int key = h * 32 + (lane & 31);
-    const uint16_t* row = tk + key * D;
-    const int sw = swz<D>(key);
+  // S^T for the two 32-key halves of the stage in LDS: the halves' MFMA
+  // chains interleave, and each k-step's K fragments are read one step ahead
+  auto qk = [&](const uint16_t* tk, f32x16& s0, f32x16& s1) {
+    s0 = f32x16{};
+    s1 = f32x16{};
+    const int key = lane & 31;
+    const uint16_t* row0 = tk + key * D;
+    const uint16_t* row1 = tk + (32 + key) * D;
+    const int sw = swz<D>(key);  // the same for key + 32
+    bf16x8 k0[NKS], k1[NKS];
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
-      const bf16x8 kf = *(const bf16x8*)(row + (((2 * ks + hi) ^ sw) << 3));
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s, 0, 0, 0);
+      const int ch = ((2 * ks + hi) ^ sw) << 3;
+      k0[ks] = *(const bf16x8*)(row0 + ch);
+      k1[ks] = *(const bf16x8*)(row1 + ch);
     }
-    return s;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0[ks], qf[ks], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1[ks], qf[ks], s1, 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+    for (int i = 0; i < NKS - 3; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
   };
-  // online softmax of half h (masked on boundary stages only), then
-  // O^T += V^T P^T over its two 16-key steps; V^T fragments by transposing reads
-  auto softmax_pv = [&](f32x16& s, const uint16_t* tv, int kt, int h, auto maskc) {
+  // Online softmax over the stage's 64 keys (masked on boundary stages only):
+  // one maximum per column per stage, the cross-half exchange by a lane swap
+  auto softmax = [&](f32x16& s0, f32x16& s1, int kt, auto maskc) {
     constexpr bool MASK = decltype(maskc)::value;
+    if constexpr (MASK) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int key = kt + (v >> 2) * 8 + hi * 4 + (v & 3);
+        s0[v] = (key >= w.key_end || key > col.limit) ? -INFINITY : s0[v];
+        s1[v] = (key + 32 >= w.key_end || key + 32 > col.limit) ? -INFINITY : s1[v];
+      }
+    }
     float mx = -INFINITY;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      float x = s[v];
-      if constexpr (MASK) {
-        const int key = kt + h * 32 + (v >> 2) * 8 + hi * 4 + (v & 3);
-        x = (key >= w.key_end || key > col.limit) ? -INFINITY : x;
-      }
-      s[v] = x;
-      mx = fmaxf(mx, x);
-    }
-    mx = fmaxf(mx, __shfl_xor(mx, 32)) * a.scale_log2;
+    for (int v = 0; v < 16; ++v) mx = fmaxf(mx, fmaxf(s0[v], s1[v]));
+    const auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, mx), __builtin_bit_cast(uint32_t, mx),
+                                                     false, false);
+    mx = fmaxf(__builtin_bit_cast(float, (uint32_t)sw[0]), __builtin_bit_cast(float, (uint32_t)sw[1])) * a.scale_log2;
     const bool upd = mx > m_run + RESCALE_SLACK;
     if (__any(upd)) {
       const float m_new = upd ? mx : m_run;
@@ -410,14 +430,21 @@ __device__ __forceinline__ void attn_bf16_body(const Args& a, const int mode, co
       m_run = m_new;
     }
     const float m_use = m_run == -INFINITY ? 0.f : m_run;
-    float psum = 0.f;
+    float ps0 = 0.f, ps1 = 0.f;
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-      const float p = __builtin_amdgcn_exp2f(fmaf(s[v], a.scale_log2, -m_use));
-      s[v] = p;
-      psum += p;
+      s0[v] = __builtin_amdgcn_exp2f(fmaf(s0[v], a.scale_log2, -m_use));
+      ps0 += s0[v];
     }
-    l_run += psum;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      s1[v] = __builtin_amdgcn_exp2f(fmaf(s1[v], a.scale_log2, -m_use));
+      ps1 += s1[v];
+    }
+    l_run += ps0 + ps1;
+  };
+  // O^T += V^T P^T for half h (two 16-key steps); V^T by transposing reads
+  auto pv = [&](const f32x16& p, const uint16_t* tv, int h) {
     const int g = lane >> 4, r = lane & 15;
     const int dsub = 16 * (g & 1) + 4 * (r & 3);
 #pragma unroll
@@ -425,7 +452,7 @@ __device__ __forceinline__ void attn_bf16_body(const Args& a, const int mode, co
       const int k2 = 2 * h + hh;
       bf16x8 pf;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) pf[i] = (__bf16)s[8 * hh + i];
+      for (int i = 0; i < 8; ++i) pf[i] = (__bf16)p[8 * hh + i];
       const int key0 = 16 * k2 + 4 * (g >> 1) + (r >> 2);
       const int key1 = key0 + 8;
       const int sw0 = swz<D>(key0), sw1 = swz<D>(key1);
@@ -439,13 +466,12 @@ __device__ __forceinline__ void attn_bf16_body(const Args& a, const int mode, co
       }
     }
   };
-  // both halves' S^T first, so the second half's MFMAs can overlap the
-  // first half's softmax
   auto compute = [&](const uint16_t* tk, const uint16_t* tv, int kt, auto maskc) {
-    f32x16 s0 = qk(tk, 0);
-    f32x16 s1 = qk(tk, 1);
-    softmax_pv(s0, tv, kt, 0, maskc);
-    softmax_pv(s1, tv, kt, 1, maskc);
+    f32x16 s0, s1;
+    qk(tk, s0, s1);
+    softmax(s0, s1, kt, maskc);
+    pv(s0, tv, 0);
+    pv(s1, tv, 1);
   };
 
   // Pipeline: LDS double buffer.  At each stage's barrier the stage's tile has
