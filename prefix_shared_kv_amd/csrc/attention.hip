@@ -373,8 +373,10 @@ __device__ __forceinline__ void attn_bf16_body(const Args& a, const int mode, co
     }
   };
 
-  // S^T for the two 32-key halves of the stage in LDS: the halves' MFMA
-  // chains interleave, and each k-step's K fragments are read one step ahead
+  // S^T for the two 32-key halves of the stage in LDS.  The halves' MFMA
+  // chains interleave; the issue order is pinned (sched_group_barrier) so
+  // the K fragment reads run three k-steps ahead of the MFMAs that use them
+  // (the compiler otherwise reads each fragment just before its MFMA).
   auto qk = [&](const uint16_t* tk, f32x16& s0, f32x16& s1) {
     s0 = f32x16{};
     s1 = f32x16{};
