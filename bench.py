@@ -104,7 +104,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", choices=["classify_heavy", "multi_turn_tree"], default="classify_heavy")
-    ap.add_argument("--chunk", type=int, default=512, help="decode split size (positions per work item)")
+    ap.add_argument("--chunk", type=int, default=4096, help="decode split size (nominal positions per work item)")
     ap.add_argument("--decode-steps", type=int, default=None,
                     help="decode steps per step (default 8 for classify_heavy, 256 for multi_turn_tree)")
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -155,7 +155,8 @@ typedef struct rc_plan_info {
   int32_t max_splits;
   int32_t batch;
   int32_t group;       /* Hq / Hkv the plan was built for                       */
-  int32_t chunk;       /* max positions per item                               */
+  int32_t chunk;       /* nominal positions per item (pieces are balanced and */
+                       /* at most chunk + chunk/8 long)                        */
   int32_t max_cols;    /* max members*group per item                           */
   int32_t shared_items;/* items with more than one member                       */
   int32_t narrow_begin;/* items from here on have members*group <= 16 (the plan */
@@ -166,7 +167,7 @@ typedef struct rc_plan_info {
   int64_t logical_positions;/* sum over requests of their context length       */
 } rc_plan_info;
 
-/* A plan without sharing: one chain of chunks per request over positions   */
+/* A plan without sharing: one chain of pieces per request over positions   */
 /* [0, max_seq_lens[b]) of table row rows[b] (NULL rows: b).                 */
 /* plan (host) receives plan_ints int32; if capacity is too small the call   */
 /* returns RC_ERR_RANGE with info->plan_ints set to the size needed.         */
@@ -292,7 +293,8 @@ rc_status rc_radix_fork(rc_radix* tree, const int32_t* tokens, const int32_t* pa
 /* range is one item whose members are all batch requests passing through    */
 /* it (split into items of at most max(1, 128 / group) members); positions   */
 /* past the walked prefix up to max_seq_lens[b] form the request's own tail. */
-/* Ranges are cut into chunks of at most `chunk` positions.  Table rows must */
+/* A range is cut into the fewest near-equal pieces of at most chunk +      */
+/* chunk/8 positions.  Table rows must                                        */
 /* hold the tree's slots over the walked prefix (emit_rows + insert give     */
 /* that).  Output as rc_plan_decode_unshared.                                */
 rc_status rc_radix_plan_decode(rc_radix* tree, int32_t batch, const int32_t* tokens,

@@ -462,6 +462,16 @@ struct PlanBuilder {
 
   int32_t row_of(int32_t b) const { return rows ? rows[b] : b; }
 
+  // A range of n positions is cut into the fewest near-equal pieces of at
+  // most chunk + chunk/8 positions, so a context a few tokens longer than
+  // the chunk leaves no tiny last item: every item pays a fixed start-up cost.
+  int64_t piece_len(int64_t n) const {
+    if (n <= 0) return 1;
+    const int64_t cap = (int64_t)chunk + chunk / 8;
+    const int64_t k = (n + cap - 1) / cap;
+    return (n + k - 1) / k;
+  }
+
   void build() {
     nsplit.assign(batch, 0);
     // split index of each range: chunks of the ranges before it on any member's path
@@ -471,7 +481,8 @@ struct PlanBuilder {
       for (int32_t r : path[b]) {
         if (first_split[r] < 0) first_split[r] = acc;
         const int64_t len = ranges[r].end - ranges[r].begin;
-        acc += (int32_t)((len + chunk - 1) / chunk);
+        const int64_t pl = piece_len(len);
+        acc += (int32_t)(len > 0 ? (len + pl - 1) / pl : 0);
       }
       nsplit[b] = acc;
     }
@@ -490,8 +501,9 @@ struct PlanBuilder {
       const Range& R = ranges[r];
       if (R.end <= R.begin) continue;
       int32_t sp = first_split[r];
-      for (int64_t p = R.begin; p < R.end; p += chunk, ++sp) {
-        const int64_t pe = std::min<int64_t>(p + chunk, R.end);
+      const int64_t pl = piece_len(R.end - R.begin);
+      for (int64_t p = R.begin; p < R.end; p += pl, ++sp) {
+        const int64_t pe = std::min<int64_t>(p + pl, R.end);
         for (size_t g0 = 0; g0 < R.members.size(); g0 += max_m) {
           const size_t cnt = std::min<size_t>(max_m, R.members.size() - g0);
           const Item it{(int64_t)cnt * (pe - p), {row_of(R.members[g0]), (int32_t)p, (int32_t)pe, sp, 0, (int32_t)cnt, 0, 0},

@@ -231,7 +231,7 @@ class Engine:
             self.table_h[rows, :width] = work[changed]
             self._upload_rows(np.sort(rows))
 
-    def prepare_decode(self, b: Batch, base_lens: Sequence[int], n_steps: int, chunk: int = 512,
+    def prepare_decode(self, b: Batch, base_lens: Sequence[int], n_steps: int, chunk: int = 4096,
                        shared: bool = True, committed: Optional[Sequence[int]] = None) -> DecodeState:
         """Plan decode steps t = 0..n_steps-1; step t's token sits at position base_lens[i] + t.
         `committed[i]` tokens of request i are in the tree (default: base_lens)."""

@@ -105,21 +105,24 @@ def test_decode_argument_checks():
 
 
 def test_unshared_plan_layout():
-    buf, info = _plan([100, 70, 1], 4, chunk=64)
+    # chunk 64: ranges up to 72 (chunk + chunk/8) stay whole, longer ones are
+    # cut into the fewest near-equal pieces of at most 72
+    buf, info = _plan([100, 70, 1, 200], 4, chunk=64)
     assert buf[0] == N.RC_PLAN_MAGIC
-    assert info.n_items == 2 + 2 + 1
-    assert info.max_splits == 2
+    assert info.n_items == 2 + 1 + 1 + 3
+    assert info.max_splits == 3
     items = buf[8:8 + 8 * info.n_items].reshape(-1, 8)
     cover = {}
     for rep, pb, pe, sp, mo, mc, _, _ in items:
         assert mc == 1
         b = buf[8 + 8 * info.n_items + mo]
         cover.setdefault(int(b), []).append((int(pb), int(pe), int(sp)))
-    assert sorted(cover[0]) == [(0, 64, 0), (64, 100, 1)]
-    assert sorted(cover[1]) == [(0, 64, 0), (64, 70, 1)]
+    assert sorted(cover[0]) == [(0, 50, 0), (50, 100, 1)]
+    assert sorted(cover[1]) == [(0, 70, 0)]
     assert sorted(cover[2]) == [(0, 1, 0)]
+    assert sorted(cover[3]) == [(0, 67, 0), (67, 134, 1), (134, 200, 2)]
     nsplit = buf[8 + 8 * info.n_items + info.n_members:]
-    assert nsplit.tolist() == [2, 2, 1]
+    assert nsplit.tolist() == [2, 1, 1, 3]
 
 
 def test_error_text_is_thread_local_and_set():

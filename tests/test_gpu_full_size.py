@@ -1,5 +1,5 @@
 """GPU parity at the workloads' full sizes, in the launch configuration the
-benchmark times (shared decode plan, 512-position chunks, the step's K/V
+benchmark times (shared decode plan, 4096-position pieces, the step's K/V
 stored by the decode call).  Every phase runs in full on the GPU; the oracle
 recomputes a seeded sample of its outputs one request or one row at a time
 (all heads of each sampled row), within max-abs 2e-2 for bf16 inputs.
@@ -19,7 +19,7 @@ from synth import workloads as W
 pytestmark = pytest.mark.gpu
 
 TOL = 2e-2
-CHUNK = 512
+CHUNK = 4096
 
 
 def host(t):
