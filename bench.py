@@ -43,7 +43,9 @@ import numpy as np
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
 ROOT = os.path.dirname(os.path.abspath(__file__))
-KERNEL_SOURCE = os.path.join(ROOT, "prefix_shared_kv_amd", "csrc", "attention.hip")
+# the decode kernel's sources: a traffic figure stands only while these are unchanged
+KERNEL_SOURCES = [os.path.join(ROOT, "prefix_shared_kv_amd", "csrc", f)
+                  for f in ("decode.hip", "attn_tile.h", "hip_common.h")]
 METRIC = "extend-attn TFLOP/s (% MFMA peak) + decode-attn HBM GB/s, tokens/s, 1 GPU"
 
 
@@ -51,6 +53,13 @@ def traffic_file(workload: str) -> str:
     """HBM bytes per launch of the decode kernel from rocprofv3 FETCH_SIZE /
     WRITE_SIZE counters, with the sha256 of the kernel source they were taken on."""
     return os.path.join(ROOT, "profiles", f"decode_attention_{workload}_traffic.txt")
+
+
+def kernel_sources_sha256() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
 
 
 def measured_traffic(workload: str):
@@ -62,8 +71,7 @@ def measured_traffic(workload: str):
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
                 kv[k.strip()] = v.strip()
-        src = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
-        if kv.get("kernel_source_sha256") != src:
+        if kv.get("kernel_sources_sha256") != kernel_sources_sha256():
             return None
         return float(kv["traffic_bytes_per_launch"])
     except (OSError, KeyError, ValueError):

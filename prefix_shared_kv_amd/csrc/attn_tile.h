@@ -1,0 +1,634 @@
+#pragma once
+// Shared attention tile for extend and decode (included by extend.hip and
+// decode.hip): attention over a prefix-shared KV pool, gfx950.
+//
+// What is computed follows the "Prompt Caching" glossary, section "How prompt
+// caching works" and its GPT-2 example: a request's new tokens attend causally,
+// by absolute position, over the cached K/V of its prefix and over their own
+// K/V; a decode token attends over the whole context.  The result equals a full
+// recompute up to floating-point rounding (the page's closing "related terms").
+//
+// One MFMA kernel serves both.  A workgroup (4 waves) owns up to 128 query
+// "columns" that read the same kv head over the same key positions:
+//   extend : columns = (new token, q head of the kv head's group) of one request
+//   decode : columns = (member request, q head) of one plan item, i.e. every
+//            request whose context holds this range of slots — a prefix shared
+//            by many branches is loaded from HBM once for all of them.
+// Keys are processed in stages of 64.  Each stage is gathered from the pool
+// through the request->slot table (or read from k_new/v_new for the extend's
+// own tokens), staged in LDS — K row-major, V transposed — and consumed by
+//   S^T = K Q^T    (v_mfma_f32_32x32x16_bf16, rows = keys, columns = queries)
+//   O^T += V^T P^T (same instruction, rows = head dims)
+// Computing S transposed puts one query column per lane: the softmax max and
+// the rescale of O are in-lane, plus one exchange between lanes l and l^32
+// per stage.  The 16 keys a lane holds for one PV step come straight from the
+// S^T accumulator; V^T is stored in LDS with the matching key permutation so
+// each MFMA operand is one 16-byte LDS read.  Online softmax runs in base 2
+// with log2(e) folded into the scale.
+#include <cfloat>
+#include <cmath>
+#include <type_traits>
+
+#include "hip_common.h"
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int BN = 64;     // keys per stage
+constexpr int NCOL = 128;  // query columns per workgroup (4 waves x 32)
+constexpr int NT = 256;
+constexpr float LOG2E = 1.4426950408889634f;
+
+enum Mode { EXTEND = 0, DECODE = 1 };
+
+struct Args {
+  const void* q;
+  void* o;
+  const void* k_new;
+  const void* v_new;
+  const void* k_pool;
+  const void* v_pool;
+  const int32_t* table;
+  int32_t table_rows;
+  int64_t stride;
+  int64_t pool_slots;
+  int32_t Hq, Hkv, g;
+  float scale_log2;  // sm_scale * log2(e)
+  int32_t* err;
+  int32_t n_work;    // workgroups in the grid
+  // extend
+  const int32_t* rows;
+  const int32_t* prefix_lens;
+  const int32_t* extend_lens;
+  const int32_t* extend_start;
+  int32_t batch;
+  int32_t max_extend;
+  int64_t total_extend;
+  int32_t tiles;     // tiles per (request, kv head)
+  int32_t tok_per_tile;
+  // decode
+  const int32_t* plan;
+  const int32_t* new_slots;    // decode: pool slot of each request's current token (with k_new/v_new)
+  int32_t n_items, n_members;  // from the planner's host summary
+  int32_t narrow_begin;        // first item with members*group <= 16
+  int32_t n_wide_blocks;       // workgroups that run wide items
+  int32_t n_narrow_units;      // (narrow item, kv head) pairs, one wave each
+  int32_t rows_path;           // narrow items by groups of four kv heads (Hkv % 4 == 0)
+  const int32_t* seq_lens;
+  float* ws_o;
+  float* ws_ml;
+  int32_t max_splits;
+};
+
+// What one workgroup computes, resolved from the grid position.
+struct Work {
+  bool valid;
+  int32_t hk;
+  int64_t row;         // table row for positions < ext_begin
+  int32_t key_begin, key_end;
+  int32_t ext_begin;   // positions >= ext_begin come from k_new/v_new
+  int64_t ext_base;    // token index in k_new of position ext_begin
+  int32_t ncols;
+  int32_t min_limit;   // smallest causal limit over the columns
+  // extend
+  int32_t t0, E, P;
+  // decode
+  int32_t split, moff, mcnt;
+  int32_t store_b;     // request whose current token this item stores and reads from k_new (-1: none)
+};
+
+__device__ __forceinline__ void flag(int32_t* err, int32_t bit) {
+  if (err) atomicOr(err, bit);
+}
+
+__device__ Work resolve(const Args& a, int mode, int L, bool leader) {
+  Work w{};
+  w.valid = false;
+  w.store_b = -1;
+  if (mode == EXTEND) {
+    const int tile = L % a.tiles;
+    const int bh = L / a.tiles;
+    const int b = bh / a.Hkv;
+    w.hk = bh - b * a.Hkv;
+    const int P = a.prefix_lens[b], E = a.extend_lens[b];
+    if (P < 0 || E < 0) {
+      if (tile == 0 && leader) flag(a.err, RC_DEVERR_LENGTH);
+      return w;
+    }
+    if (E > a.max_extend && tile == 0 && w.hk == 0 && leader) flag(a.err, RC_DEVERR_LENGTH);
+    if ((int64_t)P > a.stride || (P > 0 && a.pool_slots < 1)) {
+      if (tile == 0 && leader) flag(a.err, RC_DEVERR_TABLE);
+      return w;
+    }
+    const int t0 = tile * a.tok_per_tile;
+    const int Ec = E < a.max_extend ? E : a.max_extend;
+    if (t0 >= Ec) return w;
+    const int nt = min(a.tok_per_tile, Ec - t0);
+    const int64_t s0 = a.extend_start[b];
+    if (s0 < 0 || s0 + Ec > a.total_extend) {
+      if (tile == 0 && leader) flag(a.err, RC_DEVERR_LENGTH);
+      return w;
+    }
+    w.row = a.rows ? a.rows[b] : b;
+    if (w.row < 0 || w.row >= a.table_rows) {
+      if (leader) flag(a.err, RC_DEVERR_TABLE);
+      return w;
+    }
+    w.key_begin = 0;
+    w.key_end = P + t0 + nt;
+    w.ext_begin = P;
+    w.ext_base = s0;
+    w.ncols = nt * a.g;
+    w.min_limit = P + t0;
+    w.t0 = t0;
+    w.E = Ec;
+    w.P = P;
+    w.valid = true;
+  } else {
+    const int item = L / a.Hkv;
+    w.hk = L - item * a.Hkv;
+    const int32_t* it = a.plan + RC_PLAN_HEADER + (int64_t)item * RC_PLAN_ITEM;
+    const int32_t n_members = a.n_members;
+    const int32_t rep = it[0], pb = it[1], pe = it[2];
+    w.split = it[3];
+    w.moff = it[4];
+    w.mcnt = it[5];
+    if (rep < 0 || rep >= a.table_rows || pb < 0 || pe < pb || (int64_t)pe > a.stride || a.pool_slots < 1 ||
+        w.split < 0 || w.split >= a.max_splits ||
+        w.moff < 0 || w.mcnt < 1 || w.mcnt * a.g > NCOL || w.moff + w.mcnt > n_members) {
+      if (leader) flag(a.err, RC_DEVERR_PLAN);
+      return w;
+    }
+    const int32_t* mem = a.plan + RC_PLAN_HEADER + (int64_t)a.n_items * RC_PLAN_ITEM + w.moff;
+    for (int i = 0; i < w.mcnt; ++i)
+      if (mem[i] < 0 || mem[i] >= a.batch) {
+        if (leader) flag(a.err, RC_DEVERR_PLAN);
+        return w;
+      }
+    const int sl = a.seq_lens[mem[0]];
+    w.row = rep;
+    w.key_begin = pb;
+    w.key_end = pe < sl ? pe : sl;
+    if (w.key_end < w.key_begin) w.key_end = w.key_begin;
+    w.ext_begin = INT_MAX;
+    w.ext_base = 0;
+    w.store_b = -1;
+    // The item holding a request's last position (its own range) takes the
+    // current token's K/V from k_new/v_new and writes them to the pool.
+    if (a.k_new && w.mcnt == 1 && sl >= 1 && pb <= sl - 1 && pe >= sl) {
+      w.ext_begin = sl - 1;
+      w.ext_base = mem[0];
+      w.store_b = mem[0];
+    }
+    w.ncols = w.mcnt * a.g;
+    w.min_limit = INT_MAX;
+    w.valid = true;
+  }
+  return w;
+}
+
+// Copy request b's current-token K and V row of kv head hk into its pool slot
+// (threads [0, n) of the caller, 8 elements each; n = D / 8 covers the row).
+template <typename T, int D>
+__device__ __forceinline__ void store_new_token(const Args& a, int b, int hk, int t) {
+  constexpr int VEC = 16 / sizeof(T);
+  if (t >= D / VEC) return;
+  const int32_t s = a.new_slots[b];
+  if ((uint32_t)s >= (uint32_t)a.pool_slots) {
+    if (t == 0) flag(a.err, RC_DEVERR_SLOT);
+    return;
+  }
+  const int64_t src = ((int64_t)b * a.Hkv + hk) * D + t * VEC;
+  const int64_t dst = ((int64_t)s * a.Hkv + hk) * D + t * VEC;
+  *(uint4*)((T*)a.k_pool + dst) = *(const uint4*)((const T*)a.k_new + src);
+  *(uint4*)((T*)a.v_pool + dst) = *(const uint4*)((const T*)a.v_new + src);
+}
+
+// Per-column (query) information.
+struct Col {
+  int64_t qoff;   // element offset of the query row (token, head)
+  int32_t limit;  // last visible key position
+  int32_t head;
+  int32_t b;      // decode: batch index
+  bool real;
+};
+
+__device__ __forceinline__ Col column(const Args& a, int mode, const Work& w, int c) {
+  Col k;
+  k.real = c < w.ncols;
+  const int cc = k.real ? c : w.ncols - 1;
+  const int u = cc / a.g, j = cc - (cc / a.g) * a.g;
+  k.head = w.hk * a.g + j;
+  if (mode == EXTEND) {
+    const int t = w.t0 + u;
+    k.qoff = (w.ext_base + t) * (int64_t)a.Hq + k.head;
+    k.limit = w.P + t;
+    k.b = -1;
+  } else {
+    const int32_t* mem = a.plan + RC_PLAN_HEADER + (int64_t)a.n_items * RC_PLAN_ITEM + w.moff;
+    k.b = mem[u];
+    k.qoff = (int64_t)k.b * a.Hq + k.head;
+    k.limit = INT_MAX;
+  }
+  return k;
+}
+
+// LDS tiles hold K and V row-major, [key][head dim], with the 16-byte chunks
+// of each row XOR-swizzled by a function of the key.  For D = 128 (256-byte
+// rows, so the row itself never moves a bank) the swizzle is a linear
+// bijection of the key's low 4 bits, found by exhaustive search over a model
+// of 64 four-byte banks, that leaves every read pattern here free of bank
+// conflicts: 16 keys reading one chunk (K operands, ds_read_b128, 16 lanes
+// per pass), and the transposing V reads (32 lanes per pass) of both tile
+// shapes: 4 keys x 4 chunks (32x32x16) and 8 keys x 2 chunks (16x16x32).
+template <int D>
+__device__ __forceinline__ int swz(int key) {
+  if constexpr (D == 128)
+    return ((key & 3) << 2) | ((key >> 1) & 2) | ((key >> 3) & 1);
+  else
+    return key & 7;
+}
+
+__device__ __forceinline__ uint32_t pack2(uint32_t lo16, uint32_t hi16) { return (lo16 & 0xffffu) | (hi16 << 16); }
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+
+// Transposing LDS read (gfx950): within each 16-lane group, lane j receives
+// element j%4 of the 8-byte blocks addressed by lanes j/4, 4+j/4, 8+j/4 and
+// 12+j/4.  Lanes addressing 4 keys x 4 column blocks therefore receive a
+// 16 (head dims) x 4 (keys) tile: one lane per head dim, 4 keys each.
+__device__ __forceinline__ i16x4 lds_read_tr(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p));
+}
+
+// Lazy rescaling: a column's reference maximum moves only when a score
+// exceeds it by more than this many powers of two, so p = 2^(s - m) stays
+// below 2^8 and the O accumulator is rescaled a few times per tile instead of
+// whenever the running maximum creeps up.  Partials and the final o = acc / l
+// are exact up to rounding for any reference maximum.
+constexpr float RESCALE_SLACK = 8.f;
+
+template <int D>
+__device__ __forceinline__ void attn_bf16_body(const Args& a, const int mode, const int L, uint16_t (&sK)[2][BN * D],
+                                               uint16_t (&sV)[2][BN * D]) {
+  constexpr int CH = D / 8;          // 16-byte chunks per key row
+  constexpr int KPT = BN * CH / NT;  // keys per thread per stage (4 for D=128, 2 for D=64)
+  constexpr int NKS = D / 16;        // MFMA k-steps over D
+  constexpr int NDB = D / 32;        // 32-row blocks of O^T
+  const Work w = resolve(a, mode, L, threadIdx.x == 0);
+  if (!w.valid) return;  // uniform over the workgroup
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: LDS block addresses stay scalar
+  const int hi = lane >> 5;  // which half of the wave
+  const int c = wave * 32 + (lane & 31);
+  const bool active = wave * 32 < w.ncols;
+  const Col col = column(a, mode, w, c);
+  if (w.store_b >= 0) store_new_token<uint16_t, D>(a, w.store_b, w.hk, tid);
+
+  const uint16_t* q = (const uint16_t*)a.q;
+  bf16x8 qf[NKS];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) qf[ks] = *(const bf16x8*)(q + col.qoff * D + ks * 16 + 8 * hi);
+
+  f32x16 acc[NDB];
+#pragma unroll
+  for (int i = 0; i < NDB; ++i) acc[i] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  // Loader.  Global -> LDS loads (global_load_lds_dwordx4) move 16 bytes per
+  // lane into 1 KiB of LDS at lane-consecutive addresses, so each load
+  // instruction fills one block of KPB keys x CH chunks of the row-major,
+  // chunk-swizzled tile; a lane fetches the logical chunk that belongs at its
+  // position.  Load r of wave w fills block 4r + w of K and of V: a lane's
+  // keys are then 4*KPB apart, the same in the swizzle, so one column offset
+  // serves all of them.
+  constexpr int KPB = 64 / CH;  // keys per 1 KiB block
+  const uint32_t row_bytes = (uint32_t)(a.Hkv * D * 2);
+  const uint32_t nslots = (uint32_t)a.pool_slots;  // >= 1 (checked when the work is resolved)
+  const int plain_end = min(w.key_end, w.ext_begin);  // stages ending here read pool slots only
+  const int lkey0 = wave * KPB + lane / CH;           // this lane's key in block w; + r*4*KPB in block 4r+w
+  const int coff = (w.hk * D + (((lane % CH) ^ swz<D>(lkey0)) << 3)) * 2;
+  // this lane's chunk in slot 0 / new token 0; + index x row_bytes
+  const char* kcol = (const char*)a.k_pool + coff;
+  const char* vcol = (const char*)a.v_pool + coff;
+  const char* kncol = (const char*)a.k_new + coff;
+  const char* vncol = (const char*)a.v_new + coff;
+  const int32_t* trow = a.table + w.row * a.stride + lkey0;
+  auto lkey = [&](int r) { return lkey0 + r * 4 * KPB; };
+  int32_t slot[2][KPT];
+
+  // slots of this lane's keys in the stage starting at kt (pool keys only)
+  auto load_slots = [&](int (&sl)[KPT], int kt) {
+    if (kt + BN <= plain_end) {
+#pragma unroll
+      for (int r = 0; r < KPT; ++r) sl[r] = trow[kt + r * 4 * KPB];
+      return;
+    }
+#pragma unroll
+    for (int r = 0; r < KPT; ++r) {
+      const int j = min(kt + lkey(r), w.key_end - 1);  // keys past the end repeat the last one
+      sl[r] = j < w.ext_begin ? trow[j - lkey0] : -1;
+    }
+  };
+  int bad_slot = 0;  // an out-of-range slot was met (reported once, at the end)
+  auto dma = [&](const char* src, uint16_t* dst) {
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                     (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+  };
+  // Out-of-range slots are clamped (and reported), so every load stays in
+  // the pool.  Keys past the range end are loaded as copies of the last key,
+  // so the tile holds finite values where p = 0 multiplies them.
+  auto issue = [&](uint16_t* dk, uint16_t* dv, const int (&sl)[KPT], int kt) {
+    if (kt + BN <= plain_end) {  // every key of the stage is a cached prefix key
+      uint32_t mx = 0;
+#pragma unroll
+      for (int r = 0; r < KPT; ++r) mx = max(mx, (uint32_t)sl[r]);
+      bad_slot |= mx >= nslots;
+#pragma unroll
+      for (int r = 0; r < KPT; ++r) {
+        const uint64_t off = (uint64_t)min((uint32_t)sl[r], nslots - 1) * row_bytes;
+        const int blk = (4 * r + wave) * KPB * D;
+        dma(kcol + off, dk + blk);
+        dma(vcol + off, dv + blk);
+      }
+      return;
+    }
+    // (integer selects, not a choice between pointers, keep this in registers)
+#pragma unroll
+    for (int r = 0; r < KPT; ++r) {
+      const int blk = (4 * r + wave) * KPB * D;
+      const int j = min(kt + lkey(r), w.key_end - 1);
+      const bool is_new = j >= w.ext_begin;
+      bad_slot |= !is_new && (uint32_t)sl[r] >= nslots;
+      const uint64_t idx = is_new ? (uint64_t)(w.ext_base + (j - w.ext_begin)) : (uint64_t)min((uint32_t)sl[r], nslots - 1);
+      const uint64_t kb_ = is_new ? (uint64_t)kncol : (uint64_t)kcol;
+      const uint64_t vb_ = is_new ? (uint64_t)vncol : (uint64_t)vcol;
+      dma((const char*)(kb_ + idx * row_bytes), dk + blk);
+      dma((const char*)(vb_ + idx * row_bytes), dv + blk);
+    }
+  };
+
+  // S^T for the two 32-key halves of the stage in LDS.  The halves' MFMA
+  // chains interleave; the issue order is pinned (sched_group_barrier) so
+  // the K fragment reads run three k-steps ahead of the MFMAs that use them
+  // (the compiler otherwise reads each fragment just before its MFMA).
+  auto qk = [&](const uint16_t* tk, f32x16& s0, f32x16& s1) {
+    s0 = f32x16{};
+    s1 = f32x16{};
+    const int key = lane & 31;
+    const uint16_t* row0 = tk + key * D;
+    const uint16_t* row1 = tk + (32 + key) * D;
+    const int sw = swz<D>(key);  // the same for key + 32
+    bf16x8 k0[NKS], k1[NKS];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      const int ch = ((2 * ks + hi) ^ sw) << 3;
+      k0[ks] = *(const bf16x8*)(row0 + ch);
+      k1[ks] = *(const bf16x8*)(row1 + ch);
+    }
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0[ks], qf[ks], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1[ks], qf[ks], s1, 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+    for (int i = 0; i < NKS - 3; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
+  };
+  // Online softmax over the stage's 64 keys (masked on boundary stages only):
+  // one maximum per column per stage, the cross-half exchange by a lane swap
+  auto softmax = [&](f32x16& s0, f32x16& s1, int kt, auto maskc) {
+    constexpr bool MASK = decltype(maskc)::value;
+    if constexpr (MASK) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int key = kt + (v >> 2) * 8 + hi * 4 + (v & 3);
+        s0[v] = (key >= w.key_end || key > col.limit) ? -INFINITY : s0[v];
+        s1[v] = (key + 32 >= w.key_end || key + 32 > col.limit) ? -INFINITY : s1[v];
+      }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) mx = fmaxf(mx, fmaxf(s0[v], s1[v]));
+    const auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, mx), __builtin_bit_cast(uint32_t, mx),
+                                                     false, false);
+    mx = fmaxf(__builtin_bit_cast(float, (uint32_t)sw[0]), __builtin_bit_cast(float, (uint32_t)sw[1])) * a.scale_log2;
+    const bool upd = mx > m_run + RESCALE_SLACK;
+    if (__any(upd)) {
+      const float m_new = upd ? mx : m_run;
+      const float alpha = upd ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) acc[db] *= alpha;
+      m_run = m_new;
+    }
+    const float m_use = m_run == -INFINITY ? 0.f : m_run;
+    float ps0 = 0.f, ps1 = 0.f;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      s0[v] = __builtin_amdgcn_exp2f(fmaf(s0[v], a.scale_log2, -m_use));
+      ps0 += s0[v];
+    }
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      s1[v] = __builtin_amdgcn_exp2f(fmaf(s1[v], a.scale_log2, -m_use));
+      ps1 += s1[v];
+    }
+    l_run += ps0 + ps1;
+  };
+  // O^T += V^T P^T for half h (two 16-key steps); V^T by transposing reads
+  auto pv = [&](const f32x16& p, const uint16_t* tv, int h) {
+    const int g = lane >> 4, r = lane & 15;
+    const int dsub = 16 * (g & 1) + 4 * (r & 3);
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int k2 = 2 * h + hh;
+      bf16x8 pf;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) pf[i] = (__bf16)p[8 * hh + i];
+      const int key0 = 16 * k2 + 4 * (g >> 1) + (r >> 2);
+      const int key1 = key0 + 8;
+      const int sw0 = swz<D>(key0), sw1 = swz<D>(key1);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const int d = db * 32 + dsub;
+        const i16x4 lo = lds_read_tr(tv + key0 * D + (((d >> 3) ^ sw0) << 3) + (d & 7));
+        const i16x4 up = lds_read_tr(tv + key1 * D + (((d >> 3) ^ sw1) << 3) + (d & 7));
+        const i16x8 both = __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7);
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, both), pf, acc[db], 0, 0, 0);
+      }
+    }
+  };
+  auto compute = [&](const uint16_t* tk, const uint16_t* tv, int kt, auto maskc) {
+    f32x16 s0, s1;
+    qk(tk, s0, s1);
+    softmax(s0, s1, kt, maskc);
+    pv(s0, tv, 0);
+    pv(s1, tv, 1);
+  };
+
+  // Pipeline: LDS double buffer.  At each stage's barrier the stage's tile has
+  // landed (every wave waited for its own loads) and the other buffer's reads
+  // are done; the next stage's loads then fly while this one is computed, and
+  // slot indices run one stage further ahead.
+  const int kb = w.key_begin;
+  const int n_st = (w.key_end - kb + BN - 1) / BN;
+  if (n_st > 0) load_slots(slot[0], kb);
+  if (n_st > 1) load_slots(slot[1], kb + BN);
+  if (n_st > 0) issue(sK[0], sV[0], slot[0], kb);
+
+  auto step = [&](auto bufc, int i, auto maskc) {
+    constexpr int b = decltype(bufc)::value;
+    const int kt = kb + i * BN;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (i + 1 < n_st) issue(sK[b ^ 1], sV[b ^ 1], slot[b ^ 1], kt + BN);
+    if (i + 2 < n_st) load_slots(slot[b], kt + 2 * BN);
+    if (active) compute(sK[b], sV[b], kt, maskc);
+  };
+  // stages before n_plain need no mask: every key is below the range end and
+  // at or below every column's causal limit; the rest (a tail) are masked
+  int n_plain = (w.key_end - kb) / BN;
+  if (w.min_limit != INT_MAX) n_plain = min(n_plain, max(0, (w.min_limit + 1 - kb) / BN));
+  const auto B0 = std::integral_constant<int, 0>{};
+  const auto B1 = std::integral_constant<int, 1>{};
+  int i = 0;
+  for (; i + 1 < n_plain; i += 2) {
+    step(B0, i, std::false_type{});
+    step(B1, i + 1, std::false_type{});
+  }
+  if (i < n_plain) {
+    step(B0, i, std::false_type{});
+    ++i;
+    if (i < n_st) {
+      step(B1, i, std::true_type{});
+      ++i;
+    }
+  }
+  for (; i < n_st; i += 2) {
+    step(B0, i, std::true_type{});
+    if (i + 1 < n_st) step(B1, i + 1, std::true_type{});
+  }
+
+  if (bad_slot) flag(a.err, RC_DEVERR_SLOT);
+  if (!active || !col.real) return;
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  if (mode == EXTEND) {
+    const float inv = 1.f / l_tot;
+    {
+      uint16_t* o = (uint16_t*)a.o + col.qoff * D;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int d = db * 32 + g4 * 8 + hi * 4;
+          __bf16 b0 = (__bf16)(acc[db][4 * g4 + 0] * inv), b1 = (__bf16)(acc[db][4 * g4 + 1] * inv);
+          __bf16 b2 = (__bf16)(acc[db][4 * g4 + 2] * inv), b3 = (__bf16)(acc[db][4 * g4 + 3] * inv);
+          uint2 pk;
+          pk.x = pack2(__builtin_bit_cast(uint16_t, b0), __builtin_bit_cast(uint16_t, b1));
+          pk.y = pack2(__builtin_bit_cast(uint16_t, b2), __builtin_bit_cast(uint16_t, b3));
+          *(uint2*)(o + d) = pk;
+        }
+    }
+  } else {
+    const int64_t pidx = ((int64_t)col.b * a.Hq + col.head) * a.max_splits + w.split;
+    float* wo = a.ws_o + pidx * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d = db * 32 + g4 * 8 + hi * 4;
+        *(float4*)(wo + d) = make_float4(acc[db][4 * g4], acc[db][4 * g4 + 1], acc[db][4 * g4 + 2], acc[db][4 * g4 + 3]);
+      }
+    if (hi == 0) *(float2*)(a.ws_ml + pidx * 2) = make_float2(m_run, l_tot);
+  }
+}
+
+// fp32 path: one wave per column, lanes over head dims, keys one at a time.
+// Same work decomposition and outputs as the MFMA kernel; used for fp32 data.
+template <int D>
+__device__ __forceinline__ void attn_f32_body(const Args& a, const int mode) {
+  constexpr int PER = D / 64;
+  const int L = xcd_remap(blockIdx.x, a.n_work);
+  const Work w = resolve(a, mode, L, threadIdx.x == 0);
+  if (!w.valid) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (w.store_b >= 0) store_new_token<float, D>(a, w.store_b, w.hk, threadIdx.x);
+  const float* q = (const float*)a.q;
+  const float* kpool = (const float*)a.k_pool;
+  const float* vpool = (const float*)a.v_pool;
+  const float* knew = (const float*)a.k_new;
+  const float* vnew = (const float*)a.v_new;
+  const int64_t rowHD = (int64_t)a.Hkv * D;
+  for (int c = wave; c < w.ncols; c += NT / 64) {
+    const Col col = column(a, mode, w, c);
+    float qv[PER], ov[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      qv[i] = q[col.qoff * D + lane + 64 * i];
+      ov[i] = 0.f;
+    }
+    float m_run = -INFINITY, l_run = 0.f;
+    const int end = min(w.key_end, col.limit == INT_MAX ? w.key_end : col.limit + 1);
+    for (int j = w.key_begin; j < end; ++j) {
+      const float *kp, *vp;
+      if (j >= w.ext_begin) {
+        const int64_t off = (w.ext_base + (j - w.ext_begin)) * rowHD + (int64_t)w.hk * D;
+        kp = knew + off;
+        vp = vnew + off;
+      } else {
+        const int32_t s = a.table[w.row * a.stride + j];
+        if (s < 0 || (int64_t)s >= a.pool_slots) {
+          if (lane == 0) flag(a.err, RC_DEVERR_SLOT);
+          continue;
+        }
+        const int64_t off = (int64_t)s * rowHD + (int64_t)w.hk * D;
+        kp = kpool + off;
+        vp = vpool + off;
+      }
+      float dot = 0.f;
+#pragma unroll
+      for (int i = 0; i < PER; ++i) dot += qv[i] * kp[lane + 64 * i];
+#pragma unroll
+      for (int sh = 32; sh >= 1; sh >>= 1) dot += __shfl_xor(dot, sh);
+      const float x = dot * a.scale_log2;
+      const float m_new = fmaxf(m_run, x);
+      const float alpha = exp2f(m_run - m_new);
+      const float p = exp2f(x - m_new);
+      l_run = l_run * alpha + p;
+#pragma unroll
+      for (int i = 0; i < PER; ++i) ov[i] = ov[i] * alpha + p * vp[lane + 64 * i];
+      m_run = m_new;
+    }
+    if (!col.real) continue;
+    if (mode == EXTEND) {
+      float* o = (float*)a.o + col.qoff * D;
+#pragma unroll
+      for (int i = 0; i < PER; ++i) o[lane + 64 * i] = ov[i] / l_run;
+    } else {
+      const int64_t pidx = ((int64_t)col.b * a.Hq + col.head) * a.max_splits + w.split;
+#pragma unroll
+      for (int i = 0; i < PER; ++i) a.ws_o[pidx * D + lane + 64 * i] = ov[i];
+      if (lane == 0) *(float2*)(a.ws_ml + pidx * 2) = make_float2(m_run, l_run);
+    }
+  }
+}
+
+rc_status check_common(const rc_shape* shape, float sm_scale) {
+  rc_status st = rc::check_shape(shape);
+  if (st != RC_OK) return st;
+  if (!std::isfinite(sm_scale)) return rc::fail(RC_ERR_ARG, "sm_scale is not finite");
+  return RC_OK;
+}
+
+}  // namespace

@@ -1,0 +1,599 @@
+// Split-K decode attention over a shared plan: one query token per request
+// attends over its whole context; shared tree ranges are read once for all
+// the requests that pass through them.
+#include "attn_tile.h"
+
+namespace {
+
+// Narrow decode items (members x group <= 16 query columns): one wave per
+// (item, kv head), no workgroup barriers.  Per 32-key stage a lane loads 8
+// keys' K and V chunks with 16 lanes per key row, so every load instruction
+// moves 4 keys x 256 contiguous bytes (gathers that scatter an instruction over
+// 16 slots reach only about half the bandwidth); the stage goes into a
+// wave-private row-major LDS tile (chunk-swizzled per key), from which the
+// K operand is read with ds_read_b128 and V^T with transposing reads.  The
+// next stage's K and V are in registers while this one is computed; slot
+// indices run one more stage ahead.  S^T = K Q^T and O^T += V^T P^T on
+// v_mfma_f32_16x16x32_bf16 tiles: a lane owns one query column and 4 keys per
+// 16-key block, so the softmax reductions cross the 4 lane groups (2 steps).
+constexpr int BNN = 32;  // keys per narrow stage
+
+template <int D>
+__device__ __forceinline__ void decode_narrow_body(const Args& a, const int unit, uint16_t* sk, uint16_t* sv) {
+  constexpr int NKS = D / 32;         // k-steps of 32 over D
+  constexpr int NDB = D / 16;         // 16-row blocks of O^T
+  constexpr int CH = D / 8;           // 16-byte chunks per key row
+  constexpr int KPI = 64 / CH;        // keys per load instruction (4 for D=128, 8 for D=64)
+  constexpr int NI = BNN / KPI;       // load instructions per lane per stage and array
+  const int lane = threadIdx.x & 63;
+  const int grp = lane >> 4, r16 = lane & 15;
+  const int L = (a.narrow_begin + unit / a.Hkv) * a.Hkv + unit % a.Hkv;
+  const Work w = resolve(a, DECODE, L, lane == 0);
+  if (!w.valid) return;  // uniform over the wave
+  const Col col = column(a, DECODE, w, r16);
+
+  const uint16_t* q = (const uint16_t*)a.q;
+  bf16x8 qf[NKS];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) qf[ks] = *(const bf16x8*)(q + col.qoff * D + ks * 32 + 8 * grp);
+
+  f32x4 acc[NDB];
+#pragma unroll
+  for (int i = 0; i < NDB; ++i) acc[i] = f32x4{};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  const int lc = lane % CH, lk = lane / CH;  // loader: chunk and key within an instruction
+  const uint16_t* kbase = (const uint16_t*)a.k_pool + (int64_t)w.hk * D + lc * 8;
+  const uint16_t* vbase = (const uint16_t*)a.v_pool + (int64_t)w.hk * D + lc * 8;
+  const int64_t rowHD = (int64_t)a.Hkv * D;
+  const int32_t* trow = a.table + w.row * a.stride;
+  int bad_slot = 0;
+
+  constexpr int NEWTOK = INT_MIN + 1;  // the current token: read from k_new/v_new
+  auto load_slots = [&](int (&sl)[NI], int kt) {
+#pragma unroll
+    for (int t = 0; t < NI; ++t) {
+      const int key = kt + t * KPI + lk;
+      // INT_MIN: past the range end
+      sl[t] = key < w.key_end ? (key >= w.ext_begin ? NEWTOK : trow[key]) : INT_MIN;
+    }
+  };
+  auto load_kv = [&](u32x4 (&kr)[NI], u32x4 (&vr)[NI], const int (&sl)[NI], bool partial) {
+#pragma unroll
+    for (int t = 0; t < NI; ++t) {
+      const bool ok = (uint32_t)sl[t] < (uint32_t)a.pool_slots;
+      bad_slot |= !ok & (sl[t] != INT_MIN) & (sl[t] != NEWTOK);
+      const int64_t off = (int64_t)(ok ? sl[t] : 0) * rowHD;
+      kr[t] = *(const u32x4*)(kbase + off);
+      vr[t] = *(const u32x4*)(vbase + off);
+      if (partial && !ok) {  // keys past the end must hold finite values: p = 0 multiplies them
+        kr[t] = u32x4{0, 0, 0, 0};
+        vr[t] = u32x4{0, 0, 0, 0};
+        if (sl[t] == NEWTOK) {
+          const int64_t noff = ((int64_t)w.ext_base * a.Hkv + w.hk) * D + lc * 8;
+          kr[t] = *(const u32x4*)((const uint16_t*)a.k_new + noff);
+          vr[t] = *(const u32x4*)((const uint16_t*)a.v_new + noff);
+        }
+      }
+    }
+  };
+  auto store = [&](const u32x4 (&kr)[NI], const u32x4 (&vr)[NI]) {
+#pragma unroll
+    for (int t = 0; t < NI; ++t) {
+      const int key = t * KPI + lk;
+      const int o = key * D + ((lc ^ swz<D>(key)) << 3);
+      *(u32x4*)(sk + o) = kr[t];
+      *(u32x4*)(sv + o) = vr[t];
+    }
+  };
+  auto compute = [&](int kt) {
+    f32x4 s[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      s[j] = f32x4{};
+      const int key = 16 * j + r16;
+      const int sw = swz<D>(key);
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        const bf16x8 kf = *(const bf16x8*)(sk + key * D + (((4 * ks + grp) ^ sw) << 3));
+        s[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[ks], s[j], 0, 0, 0);
+      }
+    }
+    const bool need_mask = kt + BNN > w.key_end;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        float x = s[j][v];
+        if (need_mask && kt + 16 * j + 4 * grp + v >= w.key_end) x = -INFINITY;
+        s[j][v] = x;
+        mx = fmaxf(mx, x);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32)) * a.scale_log2;
+    const float m_new = fmaxf(m_run, mx);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    float psum = 0.f;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[j][v], a.scale_log2, -m_use));
+        s[j][v] = p;
+        psum += p;
+      }
+    if (__any(m_new != m_run)) {
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) acc[db] *= alpha;
+    }
+    l_run += psum;
+    m_run = m_new;
+    // P^T operand: k-position 8*grp+i <-> key 16*(i/4) + 4*grp + i%4
+    bf16x8 pf;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      pf[i] = (__bf16)s[0][i];
+      pf[4 + i] = (__bf16)s[1][i];
+    }
+    const int key0 = 4 * grp + (r16 >> 2), key1 = key0 + 16;
+    const int sw0 = swz<D>(key0), sw1 = swz<D>(key1);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const int d = db * 16 + 4 * (r16 & 3);
+      const i16x4 lo = lds_read_tr(sv + key0 * D + (((d >> 3) ^ sw0) << 3) + (d & 7));
+      const i16x4 up = lds_read_tr(sv + key1 * D + (((d >> 3) ^ sw1) << 3) + (d & 7));
+      const i16x8 both = __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7);
+      acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, both), pf, acc[db], 0, 0, 0);
+    }
+  };
+
+  if (w.store_b >= 0) store_new_token<uint16_t, D>(a, w.store_b, w.hk, lane);
+  const int kb = w.key_begin;
+  const int n_st = (w.key_end - kb + BNN - 1) / BNN;
+  const int plain_end = min(w.key_end, w.ext_begin);  // stages ending after this take the careful path
+  int slA[NI], slB[NI];
+  u32x4 kr[NI], vr[NI];
+  if (n_st > 0) load_slots(slA, kb);
+  if (n_st > 1) load_slots(slB, kb + BNN);
+  if (n_st > 0) load_kv(kr, vr, slA, kb + BNN > plain_end);
+  if (n_st > 2) load_slots(slA, kb + 2 * BNN);
+  // The LDS tile is private to the wave and LDS operations of a wave complete
+  // in order, so the next stage may overwrite it right after this stage's reads.
+  for (int i = 0; i < n_st; i += 2) {
+    int kt = kb + i * BNN;
+    store(kr, vr);
+    if (i + 1 < n_st) {
+      load_kv(kr, vr, slB, kt + 2 * BNN > plain_end);
+      if (i + 3 < n_st) load_slots(slB, kt + 3 * BNN);
+    }
+    compute(kt);
+    if (i + 1 >= n_st) break;
+    kt += BNN;
+    store(kr, vr);
+    if (i + 2 < n_st) {
+      load_kv(kr, vr, slA, kt + 2 * BNN > plain_end);
+      if (i + 4 < n_st) load_slots(slA, kt + 3 * BNN);
+    }
+    compute(kt);
+  }
+
+  if (bad_slot) flag(a.err, RC_DEVERR_SLOT);
+  float l_tot = l_run + __shfl_xor(l_run, 16);
+  l_tot += __shfl_xor(l_tot, 32);
+  if (!col.real) return;
+  const int64_t pidx = ((int64_t)col.b * a.Hq + col.head) * a.max_splits + w.split;
+  float* wo = a.ws_o + pidx * D;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+    *(float4*)(wo + db * 16 + 4 * grp) = make_float4(acc[db][0], acc[db][1], acc[db][2], acc[db][3]);
+  if (grp == 0) *(float2*)(a.ws_ml + pidx * 2) = make_float2(m_run, l_tot);
+}
+
+// Narrow decode items, kv heads in groups of four: one workgroup per (item,
+// head group).  The gather is the bandwidth limiter for decode, and scattered
+// 256-byte reads (one head of one slot) reach far less HBM bandwidth than
+// whole slot rows, so here every load instruction covers one key's four heads
+// (1 KiB contiguous for D = 128): each wave loads 8 keys of a 32-key stage
+// into registers, the stage goes to LDS as [key][head][D] (chunk-swizzled per
+// key), and wave w computes head w from it with the narrow kernel's
+// 16x16x32 tiles (K operand by ds_read_b128, V^T by transposing reads).
+constexpr int HG = 4;     // kv heads per workgroup
+constexpr int BNR = 32;   // keys per stage
+
+template <int D>
+__device__ __forceinline__ void decode_rows_body(const Args& a, const int unit, uint16_t* sk, uint16_t* sv) {
+  constexpr int NKS = D / 32;          // k-steps of 32 over D
+  constexpr int NDB = D / 16;          // 16-row blocks of O^T
+  constexpr int CHH = D / 8;           // 16-byte chunks per (key, head)
+  constexpr int LPK = HG * CHH;        // lanes covering one key's heads (64 for D=128, 32 for D=64)
+  constexpr int KPI = 64 / LPK;        // keys per load instruction
+  constexpr int NI = BNR / 4 / KPI;    // load instructions per lane per stage and array
+  constexpr int RS = HG * D;           // LDS elements per key
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = lane >> 4, r16 = lane & 15;
+  const int groups = a.Hkv / HG;
+  const int L = (a.narrow_begin + unit / groups) * a.Hkv + (unit % groups) * HG;
+  Work w = resolve(a, DECODE, L, tid == 0);
+  if (!w.valid) return;  // uniform over the workgroup
+  const int hk0 = w.hk;
+  w.hk = hk0 + wave;     // this wave's kv head
+  const Col col = column(a, DECODE, w, r16);
+
+  const uint16_t* q = (const uint16_t*)a.q;
+  bf16x8 qf[NKS];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) qf[ks] = *(const bf16x8*)(q + col.qoff * D + ks * 32 + 8 * grp);
+  f32x4 acc[NDB];
+#pragma unroll
+  for (int i = 0; i < NDB; ++i) acc[i] = f32x4{};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  // loader: lane -> (key k0 + lane / LPK, head, chunk) of each instruction
+  const int lk = lane / LPK;                  // key within an instruction
+  const int lh = (lane % LPK) / CHH;          // head within the group
+  const int lc = lane % CHH;                  // chunk within the head's row
+  const int64_t rowHD = (int64_t)a.Hkv * D;
+  const uint16_t* kbase = (const uint16_t*)a.k_pool + (int64_t)hk0 * D + lh * D + lc * 8;
+  const uint16_t* vbase = (const uint16_t*)a.v_pool + (int64_t)hk0 * D + lh * D + lc * 8;
+  const int32_t* trow = a.table + w.row * a.stride;
+  int bad_slot = 0;
+  int sl[2][NI];
+  u32x4 kr[NI], vr[NI];
+
+  auto key_of = [&](int t) { return wave * (BNR / 4) + t * KPI + lk; };  // key within the stage
+  auto load_slots = [&](int (&s)[NI], int kt) {
+#pragma unroll
+    for (int t = 0; t < NI; ++t) {
+      const int j = kt + key_of(t);
+      s[t] = j < w.key_end ? trow[j] : INT_MIN;  // INT_MIN: past the range end
+    }
+  };
+  auto load_kv = [&](const int (&s)[NI], bool partial) {
+#pragma unroll
+    for (int t = 0; t < NI; ++t) {
+      const int32_t sv_ = s[t];
+      const bool ok = (uint32_t)sv_ < (uint32_t)a.pool_slots;
+      bad_slot |= !ok & (sv_ != INT_MIN);
+      const int64_t off = (int64_t)(ok ? sv_ : 0) * rowHD;
+      kr[t] = *(const u32x4*)(kbase + off);
+      vr[t] = *(const u32x4*)(vbase + off);
+      if (partial && !ok) {  // keys past the end must hold finite values: p = 0 multiplies them
+        kr[t] = u32x4{0, 0, 0, 0};
+        vr[t] = u32x4{0, 0, 0, 0};
+      }
+    }
+  };
+  auto store = [&]() {
+#pragma unroll
+    for (int t = 0; t < NI; ++t) {
+      const int key = key_of(t);
+      const int o = key * RS + lh * D + ((lc ^ swz<D>(key)) << 3);
+      *(u32x4*)(sk + o) = kr[t];
+      *(u32x4*)(sv + o) = vr[t];
+    }
+  };
+  auto compute = [&](int kt) {
+    const uint16_t* hk_ = sk + wave * D;
+    const uint16_t* hv_ = sv + wave * D;
+    f32x4 s[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      s[j] = f32x4{};
+      const int key = 16 * j + r16;
+      const int sw = swz<D>(key);
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        const bf16x8 kf = *(const bf16x8*)(hk_ + key * RS + (((4 * ks + grp) ^ sw) << 3));
+        s[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[ks], s[j], 0, 0, 0);
+      }
+    }
+    const bool need_mask = kt + BNR > w.key_end;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        float x = s[j][v];
+        if (need_mask && kt + 16 * j + 4 * grp + v >= w.key_end) x = -INFINITY;
+        s[j][v] = x;
+        mx = fmaxf(mx, x);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32)) * a.scale_log2;
+    const float m_new = fmaxf(m_run, mx);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    float psum = 0.f;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[j][v], a.scale_log2, -m_use));
+        s[j][v] = p;
+        psum += p;
+      }
+    if (__any(m_new != m_run)) {
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) acc[db] *= alpha;
+    }
+    l_run += psum;
+    m_run = m_new;
+    bf16x8 pf;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      pf[i] = (__bf16)s[0][i];
+      pf[4 + i] = (__bf16)s[1][i];
+    }
+    const int key0 = 4 * grp + (r16 >> 2), key1 = key0 + 16;
+    const int sw0 = swz<D>(key0), sw1 = swz<D>(key1);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const int d = db * 16 + 4 * (r16 & 3);
+      const i16x4 lo = lds_read_tr(hv_ + key0 * RS + (((d >> 3) ^ sw0) << 3) + (d & 7));
+      const i16x4 up = lds_read_tr(hv_ + key1 * RS + (((d >> 3) ^ sw1) << 3) + (d & 7));
+      const i16x8 both = __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7);
+      acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, both), pf, acc[db], 0, 0, 0);
+    }
+  };
+
+  const int kb = w.key_begin;
+  const int n_st = (w.key_end - kb + BNR - 1) / BNR;
+  if (n_st > 0) load_slots(sl[0], kb);
+  if (n_st > 1) load_slots(sl[1], kb + BNR);
+  if (n_st > 0) load_kv(sl[0], kb + BNR > w.key_end);
+  auto step = [&](auto bufc, int i) {
+    constexpr int b = decltype(bufc)::value;
+    const int kt = kb + i * BNR;
+    __syncthreads();  // the previous stage's reads are done
+    store();
+    __syncthreads();
+    if (i + 1 < n_st) load_kv(sl[b ^ 1], kt + 2 * BNR > w.key_end);
+    if (i + 2 < n_st) load_slots(sl[b], kt + 2 * BNR);
+    compute(kt);
+  };
+  for (int i = 0; i < n_st; i += 2) {
+    step(std::integral_constant<int, 0>{}, i);
+    if (i + 1 < n_st) step(std::integral_constant<int, 1>{}, i + 1);
+  }
+
+  if (bad_slot) flag(a.err, RC_DEVERR_SLOT);
+  float l_tot = l_run + __shfl_xor(l_run, 16);
+  l_tot += __shfl_xor(l_tot, 32);
+  if (!col.real) return;
+  const int64_t pidx = ((int64_t)col.b * a.Hq + col.head) * a.max_splits + w.split;
+  float* wo = a.ws_o + pidx * D;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+    *(float4*)(wo + db * 16 + 4 * grp) = make_float4(acc[db][0], acc[db][1], acc[db][2], acc[db][3]);
+  if (grp == 0) *(float2*)(a.ws_ml + pidx * 2) = make_float2(m_run, l_tot);
+}
+
+// Decode, one launch: the plan lists wide items (workgroup-cooperative tiles,
+// heaviest first) before narrow ones, and blocks are dispatched in order, so
+// the long wide workgroups start first and the narrow ones (four independent
+// waves per block, each with its own K and V tile) fill in behind them.  Both
+// paths need 2 waves per SIMD and 64 KiB of LDS, so one kernel costs neither
+// occupancy, and there is no gap between two launches.
+template <int D>
+__global__ __launch_bounds__(NT, 2) void decode_attn_bf16(Args a) {
+  __shared__ __attribute__((aligned(16))) uint16_t sK[2][BN * D];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[2][BN * D];
+  static_assert(2 * BN == 4 * BNN, "narrow tiles reuse the wide stage buffers");
+  if ((int)blockIdx.x < a.n_wide_blocks) {
+    attn_bf16_body<D>(a, DECODE, blockIdx.x, sK, sV);
+    return;
+  }
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave
+  const int unit = ((int)blockIdx.x - a.n_wide_blocks) * 4 + wave;
+  if (unit >= a.n_narrow_units) return;
+  decode_narrow_body<D>(a, unit, &sK[0][0] + wave * BNN * D, &sV[0][0] + wave * BNN * D);
+}
+
+// Narrow decode items, one workgroup per group of four kv heads.
+template <int D>
+__global__ __launch_bounds__(NT) void decode_rows_bf16(Args a) {
+  __shared__ __attribute__((aligned(16))) uint16_t sK[HG * BNR * D];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[HG * BNR * D];
+  decode_rows_body<D>(a, (int)blockIdx.x, sK, sV);
+}
+
+template <int D>
+__global__ __launch_bounds__(NT) void decode_attn_f32(Args a) {
+  attn_f32_body<D>(a, DECODE);
+}
+
+// Split merge: for each (request, q head), combine its partials k = 0..n-1 in
+// order: M = max m_k, l = sum l_k 2^(m_k - M), o = sum o_k 2^(m_k - M) / l.
+// One wave per (request, head).  The (max, sum) pairs of 64 splits at a time
+// are loaded at once (one per lane) and reduced across the wave, then the
+// partial outputs are read with all those splits' loads in flight together.
+// Beyond 64 splits the blocks are combined with the usual rescaling.
+template <int D, bool BF16>
+__global__ __launch_bounds__(256) void merge_kernel(void* out, const float* __restrict__ ws_o,
+                                                    const float* __restrict__ ws_ml, const int32_t* nsplit,
+                                                    int32_t batch, int32_t Hq, int32_t max_splits) {
+  constexpr int PER = D / 64;
+  const int pair = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (pair >= batch * Hq) return;
+  const int lane = threadIdx.x & 63;
+  const int b = pair / Hq;
+  int ns = nsplit[b];
+  ns = ns < 0 ? 0 : (ns < max_splits ? ns : max_splits);
+  const float* ml = ws_ml + (int64_t)pair * max_splits * 2;
+  const float* po = ws_o + (int64_t)pair * max_splits * D;
+  float acc[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) acc[i] = 0.f;
+  float l = 0.f, M_run = -INFINITY;
+  for (int k0 = 0; k0 < ns; k0 += 64) {
+    const int k = k0 + lane;
+    const float2 mine = k < ns ? *(const float2*)(ml + 2 * k) : make_float2(-INFINITY, 0.f);
+    float Mb = mine.x;
+#pragma unroll
+    for (int sh = 32; sh >= 1; sh >>= 1) Mb = fmaxf(Mb, __shfl_xor(Mb, sh));
+    const float M = fmaxf(M_run, Mb);
+    if (k0 > 0 && M_run != M) {  // earlier blocks were weighted against an older maximum
+      const float r = M_run == -INFINITY ? 0.f : exp2f(M_run - M);
+      l *= r;
+#pragma unroll
+      for (int i = 0; i < PER; ++i) acc[i] *= r;
+    }
+    M_run = M;
+    const float wk = mine.x == -INFINITY ? 0.f : exp2f(mine.x - M);
+    const int n = min(64, ns - k0);
+    for (int j = 0; j < n; ++j) {
+      const float wj = __shfl(wk, j);
+      l += __shfl(mine.y, j) * wj;
+#pragma unroll
+      for (int i = 0; i < PER; ++i) acc[i] += po[(int64_t)(k0 + j) * D + lane + 64 * i] * wj;
+    }
+  }
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const float r = acc[i] * inv;
+    if (BF16)
+      ((__bf16*)out)[(int64_t)pair * D + lane + 64 * i] = (__bf16)r;
+    else
+      ((float*)out)[(int64_t)pair * D + lane + 64 * i] = r;
+  }
+}
+
+template <int D>
+void launch_decode_f32(const Args& a, int n_work, hipStream_t s, const char* name) {
+  rc::ProfScope p(name, s);
+  hipLaunchKernelGGL(decode_attn_f32<D>, dim3(n_work), dim3(NT), 0, s, a);
+}
+
+}  // namespace
+
+extern "C" int64_t rc_decode_workspace_bytes(const rc_shape* shape, const rc_plan_info* info) {
+  if (!shape || !info || shape->head_dim <= 0) return -1;
+  const int64_t parts = (int64_t)info->batch * shape->num_q_heads * (info->max_splits > 0 ? info->max_splits : 1);
+  return parts * shape->head_dim * 4 + parts * 2 * 4;
+}
+
+extern "C" rc_status rc_decode_attention(const rc_shape* shape, void* o, const void* q, void* k_pool,
+                                         void* v_pool, const void* k_new, const void* v_new,
+                                         const int32_t* new_slots, const int32_t* req_to_token, int32_t table_rows,
+                                         int64_t stride, const int32_t* seq_lens, int32_t batch, const int32_t* plan_dev,
+                                         const rc_plan_info* info, float sm_scale, void* workspace,
+                                         int64_t ws_bytes, void* stream) {
+  using namespace rc;
+  rc_status st = check_common(shape, sm_scale);
+  if (st != RC_OK) return st;
+  if (batch < 0 || stride <= 0 || table_rows < 0) return fail(RC_ERR_ARG, "batch < 0, stride <= 0 or table_rows < 0");
+  if (batch == 0) return RC_OK;
+  if (!info) return fail(RC_ERR_ARG, "plan info is NULL");
+  if (!o || !q || !k_pool || !v_pool || !req_to_token || !seq_lens || !plan_dev || !workspace)
+    return fail(RC_ERR_ARG, "NULL device pointer in rc_decode_attention");
+  if ((k_new != nullptr) != (v_new != nullptr) || (k_new != nullptr) != (new_slots != nullptr))
+    return fail(RC_ERR_ARG, "k_new, v_new and new_slots must be given together");
+  const int g = shape->num_q_heads / shape->num_kv_heads;
+  if (info->batch != batch) return fail(RC_ERR_ARG, "plan built for batch %d, called with %d", info->batch, batch);
+  if (info->group != g) return fail(RC_ERR_SHAPE, "plan built for group %d, shape has %d", info->group, g);
+  if (info->max_cols > NCOL || info->n_items < 0 || info->n_members < 0 || info->max_splits < 1 ||
+      info->plan_ints != RC_PLAN_HEADER + (int64_t)info->n_items * RC_PLAN_ITEM + info->n_members + batch)
+    return fail(RC_ERR_ARG, "plan summary out of range");
+  const int64_t need = rc_decode_workspace_bytes(shape, info);
+  if (ws_bytes < need) return fail(RC_ERR_RANGE, "workspace of %lld bytes, %lld needed", (long long)ws_bytes, (long long)need);
+  const int64_t parts = (int64_t)batch * shape->num_q_heads * info->max_splits;
+  Args a{};
+  a.q = q; a.o = o; a.k_pool = k_pool; a.v_pool = v_pool;
+  a.k_new = k_new; a.v_new = v_new; a.new_slots = new_slots;
+  a.table = req_to_token; a.table_rows = table_rows; a.stride = stride; a.pool_slots = shape->pool_slots;
+  a.Hq = shape->num_q_heads; a.Hkv = shape->num_kv_heads; a.g = g;
+  a.scale_log2 = sm_scale * LOG2E;
+  a.err = error_word();
+  a.batch = batch;
+  a.plan = plan_dev; a.seq_lens = seq_lens;
+  a.n_items = info->n_items; a.n_members = info->n_members;
+  a.narrow_begin = info->narrow_begin;
+  a.ws_o = (float*)workspace;
+  a.ws_ml = (float*)workspace + parts * shape->head_dim;
+  a.max_splits = info->max_splits;
+  if (info->narrow_begin < 0 || info->narrow_begin > info->n_items) return fail(RC_ERR_ARG, "plan summary out of range");
+  hipStream_t s = (hipStream_t)stream;
+  const bool bf16 = shape->dtype == RC_BF16;
+  if (!bf16) {
+    const int64_t n_work = (int64_t)info->n_items * a.Hkv;
+    if (n_work > INT32_MAX) return fail(RC_ERR_RANGE, "grid too large");
+    a.n_work = (int32_t)n_work;
+    if (n_work > 0) {
+      if (shape->head_dim == 128)
+        launch_decode_f32<128>(a, a.n_work, s, "decode_f32_d128");
+      else
+        launch_decode_f32<64>(a, a.n_work, s, "decode_f32_d64");
+      st = check_launch("decode attention");
+      if (st != RC_OK) return st;
+    }
+  } else {
+    // wide items: one workgroup per (item, kv head)
+    const int64_t n_wide = (int64_t)info->narrow_begin * a.Hkv;
+    // narrow items: one wave per (item, kv head), or one workgroup per four kv heads
+    const int64_t units = (int64_t)(info->n_items - info->narrow_begin) * a.Hkv;
+    a.n_narrow_units = (int32_t)units;
+    a.rows_path = rc::tuning().decode_rows && a.Hkv % HG == 0;
+    const int64_t n_narrow = a.rows_path ? units / HG : (units + 3) / 4;
+    if (n_wide > INT32_MAX || n_narrow > INT32_MAX) return fail(RC_ERR_RANGE, "grid too large");
+    if (a.rows_path && a.k_new) {
+      // the grouped-heads variant reads every key from the pool: store first
+      st = rc_kv_store(shape, k_pool, v_pool, k_new, v_new, new_slots, batch, stream);
+      if (st != RC_OK) return st;
+      a.k_new = a.v_new = nullptr;
+      a.new_slots = nullptr;
+    }
+    ProfScope p(shape->head_dim == 128 ? "decode_attention_d128" : "decode_attention_d64", s);
+    if (a.rows_path) {
+      // grouped-heads variant: wide items, then narrow items, two launches
+      if (n_wide > 0) {
+        Args aw = a;
+        aw.n_wide_blocks = (int32_t)n_wide;
+        aw.n_narrow_units = 0;
+        if (shape->head_dim == 128)
+          hipLaunchKernelGGL(decode_attn_bf16<128>, dim3((unsigned)n_wide), dim3(NT), 0, s, aw);
+        else
+          hipLaunchKernelGGL(decode_attn_bf16<64>, dim3((unsigned)n_wide), dim3(NT), 0, s, aw);
+      }
+      if (n_narrow > 0) {
+        if (shape->head_dim == 128)
+          hipLaunchKernelGGL(decode_rows_bf16<128>, dim3((unsigned)n_narrow), dim3(NT), 0, s, a);
+        else
+          hipLaunchKernelGGL(decode_rows_bf16<64>, dim3((unsigned)n_narrow), dim3(NT), 0, s, a);
+      }
+    } else if (n_wide + n_narrow > 0) {
+      a.n_wide_blocks = (int32_t)n_wide;
+      const int64_t grid = n_wide + n_narrow;
+      if (grid > INT32_MAX) return fail(RC_ERR_RANGE, "grid too large");
+      if (shape->head_dim == 128)
+        hipLaunchKernelGGL(decode_attn_bf16<128>, dim3((unsigned)grid), dim3(NT), 0, s, a);
+      else
+        hipLaunchKernelGGL(decode_attn_bf16<64>, dim3((unsigned)grid), dim3(NT), 0, s, a);
+    }
+    st = check_launch("decode attention");
+    if (st != RC_OK) return st;
+  }
+  const int32_t* nsplit = plan_dev + RC_PLAN_HEADER + (int64_t)info->n_items * RC_PLAN_ITEM + info->n_members;
+  const int pairs = batch * shape->num_q_heads;
+  const dim3 grid((pairs + 3) / 4);
+  {
+    ProfScope p("decode_merge", s);
+    if (shape->head_dim == 128) {
+      if (bf16)
+        hipLaunchKernelGGL((merge_kernel<128, true>), grid, dim3(256), 0, s, o, a.ws_o, a.ws_ml, nsplit, batch, a.Hq, a.max_splits);
+      else
+        hipLaunchKernelGGL((merge_kernel<128, false>), grid, dim3(256), 0, s, o, a.ws_o, a.ws_ml, nsplit, batch, a.Hq, a.max_splits);
+    } else {
+      if (bf16)
+        hipLaunchKernelGGL((merge_kernel<64, true>), grid, dim3(256), 0, s, o, a.ws_o, a.ws_ml, nsplit, batch, a.Hq, a.max_splits);
+      else
+        hipLaunchKernelGGL((merge_kernel<64, false>), grid, dim3(256), 0, s, o, a.ws_o, a.ws_ml, nsplit, batch, a.Hq, a.max_splits);
+    }
+  }
+  return check_launch("decode merge");
+}
