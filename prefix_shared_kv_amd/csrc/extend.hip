@@ -4,12 +4,30 @@
 
 namespace {
 
+// Order of extend tiles.  Workgroup p goes to XCD p % 8 (blocks are dealt to
+// the XCDs in turn).  Tiles are grouped into chunks of up to CK consecutive
+// tiles of one (request, kv head), which run back to back on one XCD and
+// share its L2; chunks are dealt to the XCDs in turn, later tile positions
+// first: under a causal mask a later tile sees more keys, so every XCD gets
+// the same mix of long and short tiles and the long ones start first.
+// Returns the tile's work index (bh * tiles + tile), or -1 for padding.
+__device__ __forceinline__ int extend_order(int p, int n_bh, int tiles, int ck) {
+  const int n_tc = (tiles + ck - 1) / ck;
+  const int x = p & 7, i = p >> 3;
+  const int c = (i / ck) * 8 + x;
+  if (c >= n_bh * n_tc) return -1;
+  const int tc = n_tc - 1 - c / n_bh, bh = c - (c / n_bh) * n_bh;
+  const int t = tc * ck + i % ck;
+  return t < tiles ? bh * tiles + t : -1;
+}
+
 template <int D>
-__global__ __launch_bounds__(NT, 2) void extend_attn_bf16(Args a) {
+__global__ __launch_bounds__(NT, 2) void extend_attn_bf16(Args a, int n_bh, int ck) {
   __shared__ __attribute__((aligned(16))) uint16_t sK[2][BN * D];
   __shared__ __attribute__((aligned(16))) uint16_t sV[2][BN * D];
-  // neighbouring tiles of one (request, kv head) share an XCD's L2
-  attn_bf16_body<D>(a, EXTEND, xcd_remap(blockIdx.x, a.n_work), sK, sV);
+  const int L = extend_order(blockIdx.x, n_bh, a.tiles, ck);
+  if (L < 0) return;
+  attn_bf16_body<D>(a, EXTEND, L, sK, sV);
 }
 
 template <int D>
@@ -18,12 +36,16 @@ __global__ __launch_bounds__(NT) void extend_attn_f32(Args a) {
 }
 
 template <int D>
-void launch_extend(const Args& a, int n_work, bool bf16, hipStream_t s, const char* name) {
+void launch_extend(const Args& a, int n_bh, bool bf16, hipStream_t s, const char* name) {
   rc::ProfScope p(name, s);
-  if (bf16)
-    hipLaunchKernelGGL(extend_attn_bf16<D>, dim3(n_work), dim3(NT), 0, s, a);
-  else
-    hipLaunchKernelGGL(extend_attn_f32<D>, dim3(n_work), dim3(NT), 0, s, a);
+  if (bf16) {
+    const int ck = a.tiles < 4 ? a.tiles : 4;
+    const int64_t chunks = (int64_t)n_bh * ((a.tiles + ck - 1) / ck);
+    const int64_t grid = (chunks + 7) / 8 * 8 * ck;
+    hipLaunchKernelGGL(extend_attn_bf16<D>, dim3((unsigned)grid), dim3(NT), 0, s, a, n_bh, ck);
+  } else {
+    hipLaunchKernelGGL(extend_attn_f32<D>, dim3(a.n_work), dim3(NT), 0, s, a);
+  }
 }
 
 }  // namespace
@@ -57,13 +79,13 @@ extern "C" rc_status rc_extend_attention(const rc_shape* shape, void* o, const v
   a.tok_per_tile = NCOL / g;
   a.tiles = (max_extend + a.tok_per_tile - 1) / a.tok_per_tile;
   const int64_t n_work = (int64_t)batch * a.Hkv * a.tiles;
-  if (n_work > INT32_MAX) return fail(RC_ERR_RANGE, "grid of %lld workgroups too large", (long long)n_work);
+  if (n_work > INT32_MAX / 8) return fail(RC_ERR_RANGE, "grid of %lld workgroups too large", (long long)n_work);
   a.n_work = (int32_t)n_work;
   hipStream_t s = (hipStream_t)stream;
   const bool bf16 = shape->dtype == RC_BF16;
   if (shape->head_dim == 128)
-    launch_extend<128>(a, a.n_work, bf16, s, bf16 ? "extend_bf16_d128" : "extend_f32_d128");
+    launch_extend<128>(a, batch * a.Hkv, bf16, s, bf16 ? "extend_bf16_d128" : "extend_f32_d128");
   else
-    launch_extend<64>(a, a.n_work, bf16, s, bf16 ? "extend_bf16_d64" : "extend_f32_d64");
+    launch_extend<64>(a, batch * a.Hkv, bf16, s, bf16 ? "extend_bf16_d64" : "extend_f32_d64");
   return check_launch("extend attention");
 }
