@@ -14,7 +14,9 @@ The pool holds the 4.46M cached positions (9.1 GB of K and V).
 A step, all of it inside the timed region:
   schedule the document (radix match, slots, table rows: host C++) -> upload
   its K/V scatter and prefill extend (HIP, MFMA); commit
-  schedule the 64 branches; their scatter and extend; commit
+  schedule the 64 branches; their scatter; their extend over a shared-prefix
+  plan (host C++ planner, then the split-K kernel and merge: the document is
+  read once per 16 label tokens, not once per branch); commit
   schedule the 1024 decode requests (their 8192 tokens are cached)
   decode share plan from the tree (host C++) -> upload
   8 decode steps: decode, which also stores the step's K/V, then merge (HIP)
@@ -120,6 +122,10 @@ def parse():
     ap.add_argument("--cpu-decode-steps", type=int, default=8, help="decode steps per sampled request")
     ap.add_argument("--seed", type=int, default=4, help="seed of the GPU-drawn q/k/v")
     ap.add_argument("--no-shuffle", action="store_true", help="multi_turn_tree: hand out pool slots in order")
+    ap.add_argument("--branch-chunk", type=int, default=1024,
+                    help="classify_heavy: split size of the shared-prefix plan of the label branches")
+    ap.add_argument("--branch-tiles", action="store_true",
+                    help="classify_heavy: label branches on the extend tiles instead of the shared-prefix plan")
     ap.add_argument("--decode-rows", type=int, default=0, help="narrow decode by groups of four kv heads (rc_set_tuning)")
     ap.add_argument("--host-phases", action="store_true", help="report host wall time per phase of the last step")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -276,7 +282,7 @@ def bench_classify_heavy(args):
         ph.mark("document")
         pk.prof_tag("branch")
         bb = eng.schedule(br_tb[s])
-        eng.extend(bb, q_br, k_br, v_br, scale, o=o_br)
+        eng.extend(bb, q_br, k_br, v_br, scale, o=o_br, cascade=not args.branch_tiles, chunk=args.branch_chunk)
         eng.commit(bb)
         eng.release(bb)
         ph.mark("branches")
@@ -304,7 +310,11 @@ def bench_classify_heavy(args):
     dec_name, mrg_name = "decode_attention_d128", "decode_merge"
     dec_ms, mrg_ms = avg_ms(prof, dec_name), avg_ms(prof, mrg_name)
     pre_ms = avg_ms(prof, "extend_bf16_d128@prefill")
-    br_ms = avg_ms(prof, "extend_bf16_d128@branch")
+    if args.branch_tiles:
+        br_name, br_ms = "extend_bf16_d128@branch", avg_ms(prof, "extend_bf16_d128@branch")
+    else:  # the shared-prefix plan: split-K launch + merge
+        br_name = "extend_shared_d128@branch + extend_shared_merge@branch"
+        br_ms = avg_ms(prof, "extend_shared_d128@branch") + avg_ms(prof, "extend_shared_merge@branch")
     tokens_per_step = L + n_lab + B * T
     res = {
         "metric": METRIC,
@@ -325,7 +335,7 @@ def bench_classify_heavy(args):
         "roofline": roofline("classify_heavy", dec_name, dec_bytes, dec_ms),
         "extend": {
             "prefill": extend_report("extend_bf16_d128@prefill", pre_flops, pre_ms, L),
-            "branches": extend_report("extend_bf16_d128@branch", br_flops, br_ms, n_lab),
+            "branches": extend_report(br_name, br_flops, br_ms, n_lab),
         },
         "decode": {
             "attention_ms": round(dec_ms, 5), "merge_avg_ms": round(mrg_ms, 5),

@@ -302,6 +302,48 @@ rc_status rc_radix_plan_decode(rc_radix* tree, int32_t batch, const int32_t* tok
                                const int32_t* max_seq_lens, int32_t group, int32_t chunk,
                                int32_t* plan, int64_t capacity, rc_plan_info* info);
 
+/* Shared-prefix ("cascade") extend plan.  The members of this plan are the  */
+/* batch's new tokens, in batch order (member m = loc_b + i for token i of   */
+/* request b, the same index as in q/o of rc_extend_attention).  Request b   */
+/* has tokens tokens[tok_off[b] .. tok_off[b+1]) (host, CSR), of which the   */
+/* first prefix_lens[b] are cached in the tree and the next extend_lens[b]   */
+/* are new (their K/V already stored in their slots).  Token i of request b  */
+/* attends over positions [0, prefix_lens[b] + i] of table row rows[b]        */
+/* (NULL rows: b): the attention is the extend's (the SGLang summary's       */
+/* RadixAttention over a shared prompt, "Prompt Caching" glossary, new       */
+/* tokens over the cached prefix) computed as split-K decode over the plan:  */
+/* every tree range on the prefixes is read once for all the new tokens      */
+/* that pass through it (e.g. 64 label branches of one document read the     */
+/* document once per group of 128 / group tokens, not once per branch), and  */
+/* each token reads its own request's new tokens up to itself alone.        */
+/* Run it with rc_extend_attention_shared.  Output and sizing as            */
+/* rc_plan_decode_unshared; RC_ERR_RANGE also when a request's prefix +      */
+/* extend exceed its tokens.                                                 */
+rc_status rc_radix_plan_extend(rc_radix* tree, int32_t batch, const int32_t* tokens, const int64_t* tok_off,
+                               const int32_t* prefix_lens, const int32_t* extend_lens, const int32_t* rows,
+                               int32_t group, int32_t chunk, int32_t* plan, int64_t capacity,
+                               rc_plan_info* info);
+
+/* Extend attention over a shared-prefix plan (rc_radix_plan_extend): the    */
+/* same outputs as rc_extend_attention, o[m] for new token m (token i of     */
+/* request b) = softmax attention of q[m] over positions [0, seq_lens[m])    */
+/* of its request's table row, computed by the split-K kernels and the       */
+/* merge of rc_decode_attention (the kernels are the decode kernels; their   */
+/* launches are named extend_shared_* in profiles).                          */
+/*   o, q      device [n_tokens, Hq, D] (shape dtype); q is read only.       */
+/*   k_pool, v_pool  device [pool_slots, Hkv, D]: every key, the new tokens' */
+/*             own included, is read from the pool, so store the new K/V    */
+/*             first (rc_kv_store).                                          */
+/*   seq_lens  device int32 [n_tokens]: prefix_lens[b] + i + 1.              */
+/*   plan_dev / info / workspace: as rc_decode_attention (workspace size     */
+/*             from rc_decode_workspace_bytes of this plan).                 */
+/* Errors as rc_decode_attention; info->batch must equal n_tokens.           */
+rc_status rc_extend_attention_shared(const rc_shape* shape, void* o, const void* q, const void* k_pool,
+                                     const void* v_pool, const int32_t* req_to_token, int32_t table_rows,
+                                     int64_t stride, const int32_t* seq_lens, int32_t n_tokens,
+                                     const int32_t* plan_dev, const rc_plan_info* info, float sm_scale,
+                                     void* workspace, int64_t ws_bytes, void* stream);
+
 rc_status rc_radix_stats_get(const rc_radix* tree, rc_radix_stats* out);
 
 /* Tuning switches (process-wide, take effect on the next call):             */

@@ -60,6 +60,8 @@ _SIGS = {
     "rc_decode_workspace_bytes": (i64, [C.POINTER(RcShape), C.POINTER(RcPlanInfo)]),
     "rc_decode_attention": (i32, [C.POINTER(RcShape), P, P, P, P, P, P, P, P, i32, i64, P, i32, P,
                                   C.POINTER(RcPlanInfo), f32, P, i64, P]),
+    "rc_extend_attention_shared": (i32, [C.POINTER(RcShape), P, P, P, P, P, i32, i64, P, i32, P,
+                                         C.POINTER(RcPlanInfo), f32, P, i64, P]),
     "rc_radix_create": (i32, [i64, P, C.POINTER(P)]),
     "rc_radix_destroy": (None, [P]),
     "rc_radix_match": (i32, [P, P, i64, P, I64P]),
@@ -70,6 +72,7 @@ _SIGS = {
     "rc_radix_insert_rows": (i32, [P, i32, P, P, P, P, P, i32, i64, P]),
     "rc_radix_fork": (i32, [P, P, P, i64, i32, P, P, i32, i64]),
     "rc_radix_plan_decode": (i32, [P, i32, P, P, P, P, P, i32, i32, P, i64, C.POINTER(RcPlanInfo)]),
+    "rc_radix_plan_extend": (i32, [P, i32, P, P, P, P, P, i32, i32, P, i64, C.POINTER(RcPlanInfo)]),
     "rc_radix_stats_get": (i32, [P, C.POINTER(RcRadixStats)]),
     "rc_set_tuning": (i32, [C.c_char_p, i64]),
     "rc_prof_enable": (i32, [i32]),

@@ -208,6 +208,28 @@ def decode_attention(shape: KVShape, o, q, k_pool, v_pool, req_to_token, seq_len
                                   _vp(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
+def extend_attention_shared(shape: KVShape, o, q, k_pool, v_pool, req_to_token, seq_lens, plan: DecodePlan,
+                            sm_scale: float, workspace, stream=None) -> None:
+    """Extend attention over a shared-prefix plan (rc_extend_attention_shared): row m of q/o is new
+    token m of the batch; the new tokens' K/V must already be in the pool."""
+    Hq, Hkv, D, S = shape.num_q_heads, shape.num_kv_heads, shape.head_dim, shape.pool_slots
+    T = q.shape[0]
+    _dev(q, "q", shape.dtype, (T, Hq, D))
+    _dev(o, "o", shape.dtype, (T, Hq, D))
+    _dev(k_pool, "k_pool", shape.dtype, (S, Hkv, D))
+    _dev(v_pool, "v_pool", shape.dtype, (S, Hkv, D))
+    _dev(req_to_token, "req_to_token", torch.int32)
+    _dev(seq_lens, "seq_lens", torch.int32, (T,))
+    if plan.dev is None:
+        raise ValueError("plan has no device copy; call plan.to(device)")
+    _dev(workspace, "workspace")
+    sh = shape.c()
+    check(lib.rc_extend_attention_shared(C.byref(sh), _vp(o), _vp(q), _vp(k_pool), _vp(v_pool), _vp(req_to_token),
+                                         req_to_token.shape[0], req_to_token.shape[1], _vp(seq_lens), T,
+                                         _vp(plan.dev), C.byref(plan.info), float(sm_scale), _vp(workspace),
+                                         workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
 class TokenBatch:
     """A batch of token-id lists flattened once (CSR): request b owns
     flat[off[b]:off[b+1]].  Tree calls take it in place of a list of arrays, so
@@ -332,6 +354,21 @@ class RadixTree:
         return _run_planner(lambda p, cap, info: lib.rc_radix_plan_decode(
             self._h, B, _np_ptr(tb.flat), _np_ptr(tb.off), _np_ptr(ln), _np_ptr(rw), _np_ptr(ms), group, chunk, p, cap,
             C.byref(info)), _plan_guess(ms, group, chunk))
+
+    def plan_extend(self, batch, prefix_lens: Sequence[int], extend_lens: Sequence[int], group: int,
+                    chunk: int = 4096, rows: Optional[Sequence[int]] = None) -> DecodePlan:
+        """Cascade extend plan: members are the batch's new tokens (rc_radix_plan_extend)."""
+        tb = _tb(batch)
+        B = len(tb)
+        P = np.ascontiguousarray(prefix_lens, np.int32)
+        E = np.ascontiguousarray(extend_lens, np.int32)
+        if P.shape != (B,) or E.shape != (B,):
+            raise ValueError("one prefix and one extend length per request")
+        rw = np.arange(B, dtype=np.int32) if rows is None else np.ascontiguousarray(rows, np.int32)
+        seq = np.concatenate([p + np.arange(1, e + 1) for p, e in zip(P, E)]) if B else np.zeros(0, np.int64)
+        return _run_planner(lambda p, cap, info: lib.rc_radix_plan_extend(
+            self._h, B, _np_ptr(tb.flat), _np_ptr(tb.off), _np_ptr(P), _np_ptr(E), _np_ptr(rw), group, chunk, p, cap,
+            C.byref(info)), _plan_guess(np.asarray(seq, np.int32), group, chunk))
 
     def stats(self) -> dict:
         st = RcRadixStats()

@@ -378,8 +378,10 @@ __device__ __forceinline__ void decode_rows_body(const Args& a, const int unit, 
 // the long wide workgroups start first and the narrow ones (four independent
 // waves per block, each with its own K and V tile) fill in behind them.  Both
 // paths need 2 waves per SIMD and 64 KiB of LDS, so one kernel costs neither
-// occupancy, and there is no gap between two launches.
-template <int D>
+// occupancy, and there is no gap between two launches.  ROLE only names the
+// instantiation: 0 for decode steps, 1 for extends run over a shared-prefix
+// plan (the members are new tokens), so profiles tell the two apart.
+template <int D, int ROLE>
 __global__ __launch_bounds__(NT, 2) void decode_attn_bf16(Args a) {
   __shared__ __attribute__((aligned(16))) uint16_t sK[2][BN * D];
   __shared__ __attribute__((aligned(16))) uint16_t sV[2][BN * D];
@@ -478,20 +480,28 @@ extern "C" int64_t rc_decode_workspace_bytes(const rc_shape* shape, const rc_pla
   return parts * shape->head_dim * 4 + parts * 2 * 4;
 }
 
-extern "C" rc_status rc_decode_attention(const rc_shape* shape, void* o, const void* q, void* k_pool,
-                                         void* v_pool, const void* k_new, const void* v_new,
-                                         const int32_t* new_slots, const int32_t* req_to_token, int32_t table_rows,
-                                         int64_t stride, const int32_t* seq_lens, int32_t batch, const int32_t* plan_dev,
-                                         const rc_plan_info* info, float sm_scale, void* workspace,
-                                         int64_t ws_bytes, void* stream) {
+namespace {
+
+// Split-K attention over a plan, then the merge: the body of both
+// rc_decode_attention (role 0) and rc_extend_attention_shared (role 1).
+template <int ROLE>
+rc_status split_k_attention(const rc_shape* shape, void* o, const void* q, void* k_pool, void* v_pool,
+                            const void* k_new, const void* v_new, const int32_t* new_slots,
+                            const int32_t* req_to_token, int32_t table_rows, int64_t stride, const int32_t* seq_lens,
+                            int32_t batch, const int32_t* plan_dev, const rc_plan_info* info, float sm_scale,
+                            void* workspace, int64_t ws_bytes, void* stream) {
   using namespace rc;
+  const bool d128 = shape && shape->head_dim == 128;
+  const char* attn_name = ROLE == 0 ? (d128 ? "decode_attention_d128" : "decode_attention_d64")
+                                    : (d128 ? "extend_shared_d128" : "extend_shared_d64");
+  const char* merge_name = ROLE == 0 ? "decode_merge" : "extend_shared_merge";
   rc_status st = check_common(shape, sm_scale);
   if (st != RC_OK) return st;
   if (batch < 0 || stride <= 0 || table_rows < 0) return fail(RC_ERR_ARG, "batch < 0, stride <= 0 or table_rows < 0");
   if (batch == 0) return RC_OK;
   if (!info) return fail(RC_ERR_ARG, "plan info is NULL");
   if (!o || !q || !k_pool || !v_pool || !req_to_token || !seq_lens || !plan_dev || !workspace)
-    return fail(RC_ERR_ARG, "NULL device pointer in rc_decode_attention");
+    return fail(RC_ERR_ARG, "NULL device pointer in the split-K attention call");
   if ((k_new != nullptr) != (v_new != nullptr) || (k_new != nullptr) != (new_slots != nullptr))
     return fail(RC_ERR_ARG, "k_new, v_new and new_slots must be given together");
   const int g = shape->num_q_heads / shape->num_kv_heads;
@@ -548,7 +558,7 @@ extern "C" rc_status rc_decode_attention(const rc_shape* shape, void* o, const v
       a.k_new = a.v_new = nullptr;
       a.new_slots = nullptr;
     }
-    ProfScope p(shape->head_dim == 128 ? "decode_attention_d128" : "decode_attention_d64", s);
+    ProfScope p(attn_name, s);
     if (a.rows_path) {
       // grouped-heads variant: wide items, then narrow items, two launches
       if (n_wide > 0) {
@@ -556,9 +566,9 @@ extern "C" rc_status rc_decode_attention(const rc_shape* shape, void* o, const v
         aw.n_wide_blocks = (int32_t)n_wide;
         aw.n_narrow_units = 0;
         if (shape->head_dim == 128)
-          hipLaunchKernelGGL(decode_attn_bf16<128>, dim3((unsigned)n_wide), dim3(NT), 0, s, aw);
+          hipLaunchKernelGGL((decode_attn_bf16<128, ROLE>), dim3((unsigned)n_wide), dim3(NT), 0, s, aw);
         else
-          hipLaunchKernelGGL(decode_attn_bf16<64>, dim3((unsigned)n_wide), dim3(NT), 0, s, aw);
+          hipLaunchKernelGGL((decode_attn_bf16<64, ROLE>), dim3((unsigned)n_wide), dim3(NT), 0, s, aw);
       }
       if (n_narrow > 0) {
         if (shape->head_dim == 128)
@@ -571,9 +581,9 @@ extern "C" rc_status rc_decode_attention(const rc_shape* shape, void* o, const v
       const int64_t grid = n_wide + n_narrow;
       if (grid > INT32_MAX) return fail(RC_ERR_RANGE, "grid too large");
       if (shape->head_dim == 128)
-        hipLaunchKernelGGL(decode_attn_bf16<128>, dim3((unsigned)grid), dim3(NT), 0, s, a);
+        hipLaunchKernelGGL((decode_attn_bf16<128, ROLE>), dim3((unsigned)grid), dim3(NT), 0, s, a);
       else
-        hipLaunchKernelGGL(decode_attn_bf16<64>, dim3((unsigned)grid), dim3(NT), 0, s, a);
+        hipLaunchKernelGGL((decode_attn_bf16<64, ROLE>), dim3((unsigned)grid), dim3(NT), 0, s, a);
     }
     st = check_launch("decode attention");
     if (st != RC_OK) return st;
@@ -582,7 +592,7 @@ extern "C" rc_status rc_decode_attention(const rc_shape* shape, void* o, const v
   const int pairs = batch * shape->num_q_heads;
   const dim3 grid((pairs + 3) / 4);
   {
-    ProfScope p("decode_merge", s);
+    ProfScope p(merge_name, s);
     if (shape->head_dim == 128) {
       if (bf16)
         hipLaunchKernelGGL((merge_kernel<128, true>), grid, dim3(256), 0, s, o, a.ws_o, a.ws_ml, nsplit, batch, a.Hq, a.max_splits);
@@ -596,4 +606,26 @@ extern "C" rc_status rc_decode_attention(const rc_shape* shape, void* o, const v
     }
   }
   return check_launch("decode merge");
+}
+
+}  // namespace
+
+extern "C" rc_status rc_decode_attention(const rc_shape* shape, void* o, const void* q, void* k_pool,
+                                         void* v_pool, const void* k_new, const void* v_new,
+                                         const int32_t* new_slots, const int32_t* req_to_token, int32_t table_rows,
+                                         int64_t stride, const int32_t* seq_lens, int32_t batch, const int32_t* plan_dev,
+                                         const rc_plan_info* info, float sm_scale, void* workspace,
+                                         int64_t ws_bytes, void* stream) {
+  return split_k_attention<0>(shape, o, q, k_pool, v_pool, k_new, v_new, new_slots, req_to_token, table_rows, stride,
+                              seq_lens, batch, plan_dev, info, sm_scale, workspace, ws_bytes, stream);
+}
+
+extern "C" rc_status rc_extend_attention_shared(const rc_shape* shape, void* o, const void* q, const void* k_pool,
+                                                const void* v_pool, const int32_t* req_to_token, int32_t table_rows,
+                                                int64_t stride, const int32_t* seq_lens, int32_t n_tokens,
+                                                const int32_t* plan_dev, const rc_plan_info* info, float sm_scale,
+                                                void* workspace, int64_t ws_bytes, void* stream) {
+  return split_k_attention<1>(shape, o, q, const_cast<void*>(k_pool), const_cast<void*>(v_pool), nullptr, nullptr,
+                              nullptr, req_to_token, table_rows, stride, seq_lens, n_tokens, plan_dev, info, sm_scale,
+                              workspace, ws_bytes, stream);
 }

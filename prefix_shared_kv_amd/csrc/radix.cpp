@@ -585,38 +585,30 @@ extern "C" rc_status rc_plan_decode_unshared(int32_t batch, const int32_t* rows,
   return pb.emit(plan, cap, info, logical);
 }
 
-extern "C" rc_status rc_radix_plan_decode(rc_radix* t, int32_t batch, const int32_t* tokens, const int64_t* tok_off,
-                                          const int64_t* tok_len, const int32_t* rows, const int32_t* max_seq,
-                                          int32_t group, int32_t chunk, int32_t* plan, int64_t cap,
-                                          rc_plan_info* info) {
-  if (!t) return fail(RC_ERR_ARG, "tree is NULL");
-  rc_status st = plan_args(batch, max_seq, group, chunk, info);
-  if (st != RC_OK) return st;
-  if (batch > 0 && !tok_off) return fail(RC_ERR_ARG, "tok_off is NULL");
-  if ((st = check_lens(batch, tok_off, tok_len)) != RC_OK) return st;
-  // walk every request; per node, the members and how far into the node each goes
-  struct Visit { int32_t node; int64_t end; };
-  std::vector<std::vector<Visit>> walks(batch);
-  std::unordered_map<int32_t, std::vector<std::pair<int64_t, int32_t>>> by_node;  // node -> (end, b)
-  std::vector<int64_t> walked(batch);
-  int64_t total = 0;
-  for (int32_t b = 0; b < batch; ++b) {
-    const int64_t n = tok_len ? tok_len[b] : tok_off[b + 1] - tok_off[b];
-    if (n > 0 && !tokens) return fail(RC_ERR_ARG, "tokens is NULL");
-    total += n;
+namespace {
+
+struct Visit {
+  int32_t node;
+  int64_t end;  // absolute position just past the part of the node walked
+};
+
+// Shared plan for n_mem members.  Member m walks the tree like request
+// req_of[m] did (walks / walked per request), reads its context through table
+// row rows_of[m] and has max_seq[m] positions.  Every node range is one item
+// whose members are all members passing through it; positions past the last
+// shared range up to max_seq[m] are the member's own range.
+rc_status plan_from_walks(const rc_radix* t, int32_t n_mem, const std::vector<int32_t>& req_of,
+                          const std::vector<std::vector<Visit>>& walks, const std::vector<int64_t>& walked,
+                          const std::vector<int32_t>& rows_of, const int32_t* max_seq, int32_t group, int32_t chunk,
+                          int32_t* plan, int64_t cap, rc_plan_info* info) {
+  std::unordered_map<int32_t, std::vector<std::pair<int64_t, int32_t>>> by_node;  // node -> (end, member)
+  for (int32_t m = 0; m < n_mem; ++m) {
+    const int32_t r = req_of[m];
+    if (max_seq[m] < walked[r]) return fail(RC_ERR_RANGE, "max_seq_lens[%d] = %d shorter than its cached prefix %lld", m, max_seq[m], (long long)walked[r]);
+    for (const Visit& v : walks[r]) by_node[v.node].push_back({v.end, m});
   }
-  for_requests(batch, total, [&](int32_t b) {
-    const int64_t n = tok_len ? tok_len[b] : tok_off[b + 1] - tok_off[b];
-    walked[b] = walk(*t, tokens + tok_off[b], n, [&](int32_t id, int64_t k) {
-      walks[b].push_back({id, t->nodes[id].start + k});
-    });
-  });
-  for (int32_t b = 0; b < batch; ++b) {
-    if (max_seq[b] < walked[b]) return fail(RC_ERR_RANGE, "max_seq_lens[%d] = %d shorter than its cached prefix %lld", b, max_seq[b], (long long)walked[b]);
-    for (const Visit& v : walks[b]) by_node[v.node].push_back({v.end, b});
-  }
-  PlanBuilder pb{batch, group, chunk, std::max(1, 128 / group), rows, {}, {}, {}, {}, {}};
-  pb.path.resize(batch);
+  PlanBuilder pb{n_mem, group, chunk, std::max(1, 128 / group), rows_of.data(), {}, {}, {}, {}, {}};
+  pb.path.resize(n_mem);
   // node -> list of (sub-range id, sub-range end); members of a sub-range reach at least its end
   std::unordered_map<int32_t, std::vector<std::pair<int32_t, int64_t>>> subs;
   for (auto& kv : by_node) {
@@ -640,17 +632,17 @@ extern "C" rc_status rc_radix_plan_decode(rc_radix* t, int32_t batch, const int3
   }
   const size_t n_node_ranges = pb.ranges.size();
   int64_t logical = 0;
-  for (int32_t b = 0; b < batch; ++b) {
-    logical += max_seq[b];
-    // shared part of the path, then everything this request alone reads as one range
+  for (int32_t m = 0; m < n_mem; ++m) {
+    logical += max_seq[m];
+    // shared part of the path, then everything this member alone reads as one range
     int64_t own_begin = 0;
     bool own = false;
-    for (const Visit& v : walks[b]) {
+    for (const Visit& v : walks[req_of[m]]) {
       for (auto& sr : subs[v.node]) {
         if (sr.second > v.end) break;
         const Range& R = pb.ranges[sr.first];
         if (R.members.size() > 1) {
-          pb.path[b].push_back(sr.first);
+          pb.path[m].push_back(sr.first);
           own_begin = R.end;
         } else {
           own = true;
@@ -659,14 +651,92 @@ extern "C" rc_status rc_radix_plan_decode(rc_radix* t, int32_t batch, const int3
       }
       if (own) break;
     }
-    if (max_seq[b] > own_begin) {
-      pb.ranges.push_back(Range{own_begin, max_seq[b], {b}});
-      pb.path[b].push_back((int32_t)pb.ranges.size() - 1);
+    if (max_seq[m] > own_begin) {
+      pb.ranges.push_back(Range{own_begin, max_seq[m], {m}});
+      pb.path[m].push_back((int32_t)pb.ranges.size() - 1);
     }
   }
-  // drop the single-member node ranges: each request's own range covers them
+  // drop the single-member node ranges: each member's own range covers them
   for (size_t r = 0; r < n_node_ranges; ++r)
     if (pb.ranges[r].members.size() == 1) pb.ranges[r].end = pb.ranges[r].begin;
   pb.build();
   return pb.emit(plan, cap, info, logical);
+}
+
+// Walk request b's first len(b) tokens through the tree (several threads
+// for large batches).
+template <class LenF>
+void walk_requests(const rc_radix* t, int32_t batch, const int32_t* tokens, const int64_t* tok_off, LenF&& len,
+                   std::vector<std::vector<Visit>>& walks, std::vector<int64_t>& walked) {
+  walks.assign(batch, {});
+  walked.assign(batch, 0);
+  int64_t total = 0;
+  for (int32_t b = 0; b < batch; ++b) total += len(b);
+  for_requests(batch, total, [&](int32_t b) {
+    walked[b] = walk(*t, tokens + tok_off[b], len(b), [&](int32_t id, int64_t k) {
+      walks[b].push_back({id, t->nodes[id].start + k});
+    });
+  });
+}
+
+}  // namespace
+
+extern "C" rc_status rc_radix_plan_decode(rc_radix* t, int32_t batch, const int32_t* tokens, const int64_t* tok_off,
+                                          const int64_t* tok_len, const int32_t* rows, const int32_t* max_seq,
+                                          int32_t group, int32_t chunk, int32_t* plan, int64_t cap,
+                                          rc_plan_info* info) {
+  if (!t) return fail(RC_ERR_ARG, "tree is NULL");
+  rc_status st = plan_args(batch, max_seq, group, chunk, info);
+  if (st != RC_OK) return st;
+  if (batch > 0 && !tok_off) return fail(RC_ERR_ARG, "tok_off is NULL");
+  if ((st = check_lens(batch, tok_off, tok_len)) != RC_OK) return st;
+  auto len = [&](int32_t b) { return tok_len ? tok_len[b] : tok_off[b + 1] - tok_off[b]; };
+  for (int32_t b = 0; b < batch; ++b)
+    if (len(b) > 0 && !tokens) return fail(RC_ERR_ARG, "tokens is NULL");
+  std::vector<std::vector<Visit>> walks;
+  std::vector<int64_t> walked;
+  walk_requests(t, batch, tokens, tok_off, len, walks, walked);
+  std::vector<int32_t> req_of(batch), rows_of(batch);
+  for (int32_t b = 0; b < batch; ++b) {
+    req_of[b] = b;
+    rows_of[b] = rows ? rows[b] : b;
+  }
+  return plan_from_walks(t, batch, req_of, walks, walked, rows_of, max_seq, group, chunk, plan, cap, info);
+}
+
+extern "C" rc_status rc_radix_plan_extend(rc_radix* t, int32_t batch, const int32_t* tokens, const int64_t* tok_off,
+                                          const int32_t* prefix_lens, const int32_t* extend_lens, const int32_t* rows,
+                                          int32_t group, int32_t chunk, int32_t* plan, int64_t cap,
+                                          rc_plan_info* info) {
+  if (!t || !info) return fail(RC_ERR_ARG, "tree or info is NULL");
+  if (batch < 0) return fail(RC_ERR_ARG, "batch < 0");
+  if (batch > 0 && (!tok_off || !prefix_lens || !extend_lens)) return fail(RC_ERR_ARG, "NULL array in rc_radix_plan_extend");
+  rc_status st = check_lens(batch, tok_off, nullptr);
+  if (st != RC_OK) return st;
+  int64_t n_tok = 0;
+  for (int32_t b = 0; b < batch; ++b) {
+    const int64_t n = tok_off[b + 1] - tok_off[b];
+    if (prefix_lens[b] < 0 || extend_lens[b] < 0 || (int64_t)prefix_lens[b] + extend_lens[b] > n)
+      return fail(RC_ERR_RANGE, "request %d: prefix %d + extend %d exceed its %lld tokens", b, prefix_lens[b], extend_lens[b], (long long)n);
+    if (prefix_lens[b] > 0 && !tokens) return fail(RC_ERR_ARG, "tokens is NULL");
+    n_tok += extend_lens[b];
+  }
+  if (n_tok > INT32_MAX) return fail(RC_ERR_RANGE, "%lld new tokens", (long long)n_tok);
+  // members: the new tokens in batch order; token i of request b sees
+  // positions [0, prefix_lens[b] + i]
+  std::vector<int32_t> req_of((size_t)n_tok), rows_of((size_t)n_tok), max_seq((size_t)n_tok);
+  int64_t m = 0;
+  for (int32_t b = 0; b < batch; ++b)
+    for (int32_t i = 0; i < extend_lens[b]; ++i, ++m) {
+      req_of[m] = b;
+      rows_of[m] = rows ? rows[b] : b;
+      max_seq[m] = prefix_lens[b] + i + 1;
+    }
+  st = plan_args((int32_t)n_tok, max_seq.data(), group, chunk, info);
+  if (st != RC_OK) return st;
+  std::vector<std::vector<Visit>> walks;
+  std::vector<int64_t> walked;
+  walk_requests(t, batch, tokens, tok_off, [&](int32_t b) { return (int64_t)prefix_lens[b]; }, walks, walked);
+  return plan_from_walks(t, (int32_t)n_tok, req_of, walks, walked, rows_of, max_seq.data(), group, chunk, plan, cap,
+                         info);
 }

@@ -200,17 +200,30 @@ class Engine:
                               ).astype(np.int32)
 
     def extend(self, b: Batch, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, sm_scale: float,
-               o: Optional[torch.Tensor] = None, store: bool = True) -> torch.Tensor:
-        """Store the new tokens' K/V in their slots, then attend (new tokens over prefix + themselves)."""
+               o: Optional[torch.Tensor] = None, store: bool = True, cascade: bool = False,
+               chunk: int = 4096) -> torch.Tensor:
+        """Store the new tokens' K/V in their slots, then attend (new tokens over prefix + themselves).
+        cascade: compute it from a shared-prefix plan (rc_radix_plan_extend) with the split-K
+        kernel, so a prefix shared by many requests is read once for all their new tokens."""
         T = b.total_extend
         if q.shape[0] != T:
             raise ValueError(f"q has {q.shape[0]} rows, the batch has {T} new tokens")
-        if store:
-            if "slots" not in b.dev:
-                b.dev["slots"] = self._i32(self.new_token_slots(b))
+        if (store or cascade) and "slots" not in b.dev:
+            b.dev["slots"] = self._i32(self.new_token_slots(b))
+        if store or cascade:  # the cascade path reads every key, the new ones too, from the pool
             api.kv_store(self.shape, self.k_pool, self.v_pool, k_new, v_new, b.dev["slots"])
         if o is None:
             o = torch.empty_like(q)
+        if T == 0:
+            return o
+        if cascade:
+            plan = self.tree.plan_extend(b.tb, b.prefix_lens, b.extend_lens, self.shape.group, chunk, rows=b.rows)
+            plan.to(self.device, uploader=self._h2d)
+            seq = np.concatenate([p + np.arange(1, e + 1) for p, e in zip(b.prefix_lens, b.extend_lens)])
+            ws = torch.empty(api.decode_workspace_bytes(self.shape, plan), dtype=torch.uint8, device=self.device)
+            api.extend_attention_shared(self.shape, o, q, self.k_pool, self.v_pool, self.table_d, self._i32(seq),
+                                        plan, sm_scale, ws)
+            return o
         api.extend_attention(self.shape, o, q, k_new, v_new, self.k_pool, self.v_pool, self.table_d, b.dev["P"],
                              b.dev["E"], b.dev["start"], int(b.extend_lens.max()) if b.size else 0, sm_scale,
                              rows=b.dev["rows"])

@@ -87,9 +87,10 @@ def prefill_nodes(eng: Engine, w: Workload, device="cuda") -> Dict[int, torch.Te
     return out
 
 
-def extend_requests(eng: Engine, w: Workload, rids: Optional[Sequence[int]] = None, device="cuda", commit=True):
-    """Schedule requests (prompt = path + own tokens, decode slots reserved) and run the extend.
-    Returns (batch, o) with o [sum E, Hq, D] in request order."""
+def extend_requests(eng: Engine, w: Workload, rids: Optional[Sequence[int]] = None, device="cuda", commit=True,
+                    cascade=False):
+    """Schedule requests (prompt = path + own tokens, decode slots reserved) and run the extend
+    (cascade: from the shared-prefix plan).  Returns (batch, o) with o [sum E, Hq, D] in request order."""
     rids = list(range(len(w.requests))) if rids is None else list(rids)
     reqs = [w.requests[i] for i in rids]
     reserve = max(r.n_decode for r in reqs) if reqs else 0
@@ -99,7 +100,7 @@ def extend_requests(eng: Engine, w: Workload, rids: Optional[Sequence[int]] = No
         raise RuntimeError(f"matched prefixes {b.prefix_lens.tolist()[:8]}.. differ from the workload's {expect[:8]}..")
     qs, ks, vs = zip(*(w.ext_qkv(i) for i in rids))
     q, k, v = (up(np.concatenate(x), w, device) for x in (qs, ks, vs))
-    o = eng.extend(b, q, k, v, w.sm_scale)
+    o = eng.extend(b, q, k, v, w.sm_scale, cascade=cascade)
     if commit:
         eng.commit(b)
     return b, o

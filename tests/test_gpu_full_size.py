@@ -162,6 +162,17 @@ def test_classify64_full_size(gpu):
     check_extend(w, ctx, o, range(len(w.requests)))
 
 
+def test_classify64_cascade_full_size(gpu):
+    # the same 64 branches through the shared-prefix plan: the 4096-token
+    # document is read once per group of 16 label tokens
+    w = W.classify64()
+    ctx = Context(w)
+    eng = drive.make_engine(w, device=gpu)
+    drive.prefill_nodes(eng, w, device=gpu)
+    b, o = drive.extend_requests(eng, w, device=gpu, cascade=True)
+    check_extend(w, ctx, o, range(len(w.requests)))
+
+
 def test_heavy_decode_full_size(gpu):
     # 1024 requests over 8192-token contexts (4096 shared per group of 16), 8 decode steps;
     # the pool holds 4.46M slots (9.1 GB of K and V)

@@ -137,7 +137,7 @@ def test_extend_single_token_prefill_is_value(gpu):
 
 
 # ---------------------------------------------------------------- whole workloads
-def _run_workload(gpu, w, shared=True, chunk=512, decode_steps=None, fused=True):
+def _run_workload(gpu, w, shared=True, chunk=512, decode_steps=None, fused=True, cascade=False):
     tol = TOL[w.shape.dtype]
     eng = drive.make_engine(w, device=gpu)
     errs = []
@@ -151,7 +151,7 @@ def _run_workload(gpu, w, shared=True, chunk=512, decode_steps=None, fused=True)
     rids = list(range(len(w.requests)))
     has_ext = any(len(r.ext_tokens) for r in w.requests)
     if has_ext:
-        b, o = drive.extend_requests(eng, w, rids, device=gpu)
+        b, o = drive.extend_requests(eng, w, rids, device=gpu, cascade=cascade)
         got = host(o)
         s = 0
         for i in rids:
@@ -202,6 +202,17 @@ def test_small_radix_tree_workload_shared_vs_unshared(gpu, dtype):
         w.shape.dtype = "f32"
     for shared, chunk in [(True, 32), (True, 4096), (False, 64)]:
         _run_workload(gpu, w, shared=shared, chunk=chunk)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_cascade_extend_matches_the_oracle(gpu, dtype):
+    # new tokens through the shared-prefix plan (split-K kernel + merge):
+    # a nested tree, branches over one document, and the GPT-2 system prompt
+    for w in (W.multi_turn_tree(depth=3, fanout=3, seg_lo=5, seg_hi=90, ext=9, n_decode=2),
+              W.classify64(prefix=300, n_branch=12), W.gpt2_system_prompt()):
+        if dtype == "f32":
+            w.shape.dtype = "f32"
+        _run_workload(gpu, w, cascade=True, decode_steps=0)
 
 
 def test_decode_is_deterministic(gpu):

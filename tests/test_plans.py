@@ -1,0 +1,138 @@
+"""Decode and cascade-extend plans from the native tree (host only).
+
+Every plan is checked against what its definition requires, with a table
+built by the tree itself:
+  * each member's items cover its positions [0, max_seq) exactly once, with
+    distinct split indices below its split count;
+  * an item's positions hold the same slots in every member's table row as
+    in the representative row the kernel reads them through;
+  * members per item stay within max(1, 128 / group).
+"""
+import numpy as np
+import pytest
+from hypothesis import given, settings
+from hypothesis import strategies as st
+
+from prefix_shared_kv_amd import RadixTree
+from prefix_shared_kv_amd import _native as N
+
+
+def parse(plan):
+    buf, info = plan.host, plan.info
+    H, I = N.RC_PLAN_HEADER, N.RC_PLAN_ITEM
+    items = buf[H:H + I * info.n_items].reshape(-1, I)
+    mem = buf[H + I * info.n_items:H + I * info.n_items + info.n_members]
+    nsplit = buf[H + I * info.n_items + info.n_members:]
+    return items, mem, nsplit
+
+
+def check_plan(plan, max_seq, rows, table, group):
+    items, mem, nsplit = parse(plan)
+    max_m = max(1, 128 // group)
+    cover = {m: [] for m in range(len(max_seq))}
+    for rep, pb, pe, sp, mo, mc, _, _ in items:
+        assert 1 <= mc <= max_m and pb < pe
+        for m in mem[mo:mo + mc]:
+            m = int(m)
+            cover[m].append((int(pb), int(pe), int(sp)))
+            # the kernel reads the range through rep's row for every member
+            assert np.array_equal(table[rep, pb:pe], table[rows[m], pb:pe]), (m, pb, pe)
+    for m, ranges in cover.items():
+        ranges.sort()
+        pos = 0
+        for pb, pe, _ in ranges:
+            assert pb == pos, (m, ranges)
+            pos = pe
+        assert pos == max_seq[m], (m, ranges, max_seq[m])
+        splits = sorted(sp for _, _, sp in ranges)
+        assert len(set(splits)) == len(splits) and splits[-1] < nsplit[m] <= plan.info.max_splits
+    return items, mem
+
+
+def build(seqs, pool=20000, insert=None):
+    """A tree holding `insert` (default: all of seqs) with table rows for seqs."""
+    t = RadixTree(pool)
+    for s in (seqs if insert is None else insert):
+        m, pre = t.match(np.concatenate([s, [-1]]).astype(np.int32))
+        t.insert(s, np.concatenate([pre, t.alloc(len(s) - m)]).astype(np.int32))
+    return t
+
+
+def test_extend_plan_reads_a_shared_document_once_per_token_group():
+    g = np.random.default_rng(1)
+    doc = g.integers(0, 1000, 300).astype(np.int32)
+    labels = [g.integers(1000, 2000, n).astype(np.int32) for n in (2, 5, 16, 1, 9)]
+    for i, lab in enumerate(labels):  # distinct first tokens: no sharing among the labels
+        lab[0] = 5000 + i
+    t = build([doc])
+    batch = [np.concatenate([doc, lab]) for lab in labels]
+    table = np.full((len(batch), 400), -1, np.int32)
+    P, E = t.emit_rows(batch, table)
+    assert P.tolist() == [300] * 5 and E.tolist() == [2, 5, 16, 1, 9]
+    group = 8
+    plan = t.plan_extend(batch, P, E, group)
+    rows = np.repeat(np.arange(5), E)
+    max_seq = np.concatenate([p + np.arange(1, e + 1) for p, e in zip(P, E)])
+    items, mem = check_plan(plan, max_seq, rows, table, group)
+    doc_items = [it for it in items if it[1] == 0 and it[2] == 300]
+    # 33 new tokens in groups of 128 / 8 = 16: the document is read by 3 items, not 5 or 33
+    assert sorted(int(it[5]) for it in doc_items) == [1, 16, 16]
+    own = [it for it in items if it[1] >= 300]
+    assert len(own) == 33 and all(it[5] == 1 for it in own)
+    assert plan.info.batch == 33 and plan.info.max_splits == 2
+
+
+def test_extend_plan_without_a_cached_prefix():
+    t = RadixTree(1000)
+    batch = [np.arange(10, 30, dtype=np.int32), np.arange(50, 57, dtype=np.int32)]
+    table = np.full((2, 32), -1, np.int32)
+    P, E = t.emit_rows(batch, table)
+    assert P.tolist() == [0, 0]
+    plan = t.plan_extend(batch, P, E, 4)
+    check_plan(plan, np.concatenate([np.arange(1, 21), np.arange(1, 8)]), np.repeat([0, 1], E), table, 4)
+    assert plan.info.shared_items == 0
+
+
+def test_extend_plan_rejects_lengths_past_the_tokens():
+    t = RadixTree(100)
+    with pytest.raises(N.RcError):
+        t.plan_extend([np.arange(5, dtype=np.int32)], [3], [3], 4)
+
+
+@st.composite
+def tree_batches(draw):
+    vocab = draw(st.integers(2, 5))
+    n_seq = draw(st.integers(1, 6))
+    base = draw(st.lists(st.integers(0, vocab - 1), min_size=1, max_size=60))
+    seqs = []
+    for _ in range(n_seq):
+        cut = draw(st.integers(0, len(base)))
+        tail = draw(st.lists(st.integers(0, vocab - 1), min_size=1, max_size=30))
+        seqs.append(np.array(base[:cut] + tail, np.int32))
+    n_cached = draw(st.integers(0, n_seq))
+    n_new = [draw(st.integers(1, 12)) for _ in range(n_seq)]
+    group = draw(st.sampled_from([1, 4, 8, 32]))
+    chunk = draw(st.sampled_from([3, 16, 64, 4096]))
+    return seqs, n_cached, n_new, group, chunk
+
+
+@settings(max_examples=120, deadline=None)
+@given(tree_batches())
+def test_plans_cover_every_context_with_shared_slots(case):
+    seqs, n_cached, n_new, group, chunk = case
+    t = build(seqs, insert=seqs[:n_cached])
+    g = np.random.default_rng(len(seqs) + n_cached)
+    batch = [np.concatenate([s, 100 + g.integers(0, 3, k)]).astype(np.int32) for s, k in zip(seqs, n_new)]
+    reserve = 4
+    table = np.full((len(batch), max(len(b) for b in batch) + reserve), -1, np.int32)
+    P, E = t.emit_rows(batch, table, reserve=reserve)
+    # cascade extend over the new tokens
+    plan = t.plan_extend(batch, P, E, group, chunk)
+    rows = np.repeat(np.arange(len(batch)), E)
+    max_seq = np.concatenate([p + np.arange(1, e + 1) for p, e in zip(P, E)])
+    check_plan(plan, max_seq, rows, table, group)
+    # decode plan after commit: contexts up to the reserved slots
+    t.insert_rows(batch, table, np.arange(len(batch), dtype=np.int32))
+    lens = np.array([len(b) for b in batch])
+    plan = t.plan_decode(batch, lens + reserve, group, chunk)
+    check_plan(plan, lens + reserve, np.arange(len(batch)), table, group)
