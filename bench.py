@@ -238,7 +238,10 @@ def bench_classify_heavy(args):
     kvs = pk.KVShape(Hq, Hkv, D, torch.bfloat16, pool)
     base = np.array([len(wh.prompt_tokens(r)) for r in wh.requests], np.int32)
     stride = int(base.max()) + T + 8
-    eng = Engine(kvs, stride, B + 8, dev)
+    # Table rows for two steps' batches: rows are handed out oldest-free first,
+    # so a step's batches never reuse rows whose uploads are still queued
+    # behind the previous step's decode launches, and the host runs ahead.
+    eng = Engine(kvs, stride, 2 * (B + len(wc.requests) + 8), dev)
 
     # ---- cached contexts of the decode requests (untimed set-up) ----
     drive.populate(eng, wh, device=dev, device_values=True)
@@ -429,7 +432,7 @@ def bench_multi_turn_tree(args):
     kvs = pk.KVShape(Hq, Hkv, D, torch.bfloat16, pool)
     stride = max(len(w.prompt_tokens(r)) for r in w.requests) + T + 8
     order = None if args.no_shuffle else np.random.default_rng(args.seed).permutation(pool).astype(np.int32)
-    eng = Engine(kvs, stride, B + 8, dev, free_order=order)
+    eng = Engine(kvs, stride, 2 * (B + 8), dev, free_order=order)  # two steps' rows, as above
     drive.populate(eng, w, device=dev, device_values=True)
     log("cached tree populated")
     gen = torch.Generator(device=dev)

@@ -73,6 +73,11 @@ class Engine:
         self.v_pool = v_pool if v_pool is not None else torch.zeros((S, H, D), dtype=shape.dtype, device=self.device)
         self.tree = RadixTree(S, free_order)
         self.stride = stride
+        # Rows are handed out oldest-free first.  With about two batches' worth
+        # of rows, a batch never waits for rows whose upload is still queued
+        # behind the GPU work of the batch before it.  (Row uploads stay on the
+        # compute stream: run beside the decode kernels on a copy stream they
+        # cost those kernels more than the copy takes.)
         # The host table lives in pinned memory so that runs of rows upload
         # straight from it.  Such an upload reads the rows when the stream
         # reaches it, so a row is rewritten on the host only after the last
