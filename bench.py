@@ -234,7 +234,12 @@ def bench_classify_heavy(args):
     labels = [r.ext_tokens for r in wc.requests]
     n_lab = sum(len(x) for x in labels)
     cached = sum(len(n.tokens) for n in wh.nodes)
-    pool = cached + n_total * (len(doc) + n_lab) + B * T + 1024
+    # Steady-state pool: the decode contexts, one document with its branches and
+    # the decode steps' slots.  From the second step on, the decode schedule
+    # finds the pool short and evicts the least recently used unpinned nodes:
+    # the previous step's branches and document (the decode contexts are
+    # pinned by the batch that reads them).
+    pool = cached + (len(doc) + n_lab) + B * T + 1024
     kvs = pk.KVShape(Hq, Hkv, D, torch.bfloat16, pool)
     base = np.array([len(wh.prompt_tokens(r)) for r in wh.requests], np.int32)
     stride = int(base.max()) + T + 8
@@ -301,7 +306,9 @@ def bench_classify_heavy(args):
         eng.release(bh, keep=base)
         ph.mark("release")
 
+    ev0 = eng.tree.stats()["evicted_tokens"]
     elapsed, prof = run_steps(args, one_step)
+    evicted = eng.tree.stats()["evicted_tokens"] - ev0
 
     # ---- algorithmic work ----
     pre_flops = extend_flops(D, Hq, [0], [L])
@@ -333,8 +340,9 @@ def bench_classify_heavy(args):
                         "1024 decode requests over 8192-token contexts (4096 shared per group of 16), 8 decode steps",
             "document_tokens": L, "branches": len(labels), "label_tokens": n_lab,
             "decode_batch": B, "decode_steps": T, "cached_positions": cached, "decode_chunk": args.chunk,
-            "tokens_per_step": tokens_per_step,
+            "tokens_per_step": tokens_per_step, "pool_slots": pool,
         },
+        "cache": {"evicted_tokens_per_step": round(evicted / n_total, 1)},
         "roofline": roofline("classify_heavy", dec_name, dec_bytes, dec_ms),
         "extend": {
             "prefill": extend_report("extend_bf16_d128@prefill", pre_flops, pre_ms, L),

@@ -223,7 +223,9 @@ typedef struct rc_radix_stats {
   int64_t matched_tokens;  /* sum of matched lengths                           */
   int64_t inserted_tokens; /* tokens newly stored by insert                    */
   int64_t duplicate_slots; /* slots freed because their prefix was already stored */
-  int64_t evicted_tokens;
+  int64_t evicted_tokens;  /* tokens removed by LRU eviction                   */
+  int64_t evicted_nodes;
+  int64_t locked_tokens;   /* tokens in nodes pinned by at least one lock       */
 } rc_radix_stats;
 
 /* free_order (host, nullable): the initial order in which slots are handed   */
@@ -233,7 +235,8 @@ void rc_radix_destroy(rc_radix* tree);
 
 /* Longest cached prefix of tokens[0..n), capped at n-1 (a request always     */
 /* runs at least one token).  out_slots (host, capacity n, nullable) gets    */
-/* the slots of the matched tokens.  Marks the matched nodes as used now.    */
+/* the slots of the matched tokens.  Marks every node that tokens[0..n)     */
+/* enter (at least one token matched) as used now.                           */
 rc_status rc_radix_match(rc_radix* tree, const int32_t* tokens, int64_t n, int32_t* out_slots,
                          int64_t* matched);
 
@@ -249,6 +252,8 @@ rc_status rc_radix_free(rc_radix* tree, const int32_t* slots, int64_t n);
 /* caller's different slots for those positions are freed (ascending         */
 /* position order) and slots_inout is overwritten with the stored ones, so   */
 /* the caller can rewrite its table row.  n_new (nullable): tokens stored.   */
+/* Marks as used now the nodes the tokens pass through and the new leaf; of  */
+/* a split edge only the upper part (the part the tokens matched).           */
 rc_status rc_radix_insert(rc_radix* tree, const int32_t* tokens, int32_t* slots_inout, int64_t n,
                           int64_t* n_new);
 
@@ -275,10 +280,49 @@ rc_status rc_radix_insert_rows(rc_radix* tree, int32_t batch, const int32_t* tok
 /* whole batch is all or nothing, in request order.  Entries after the row's */
 /* end are not touched.  table_rows bounds rows[b]; each row must fit in     */
 /* stride (n_b + reserve <= stride) or the call fails with RC_ERR_RANGE.     */
+/* Every node the requests' tokens enter is marked as used now (one time     */
+/* for the whole batch).                                                     */
+/*   handles (host, nullable, batch entries): also lock each request's       */
+/*             matched prefix (as rc_radix_lock of its first P_b tokens) and */
+/*             return the handles; release them with rc_radix_unlock.        */
+/*   evict     0: too few free slots fail with RC_ERR_NOMEM and change       */
+/*             nothing.  1: first free the missing slots by rc_radix_evict   */
+/*             (the batch's matched prefixes are pinned meanwhile, so the    */
+/*             rows still get them); if that is not enough the call fails    */
+/*             with RC_ERR_NOMEM, the rows and locks untouched, but what was */
+/*             evicted and the use marks stay.                                */
 rc_status rc_radix_emit_rows(rc_radix* tree, int32_t batch, const int32_t* tokens,
                              const int64_t* tok_off, int32_t reserve, const int32_t* rows,
                              int32_t* req_to_token, int32_t table_rows, int64_t stride,
-                             int32_t* prefix_lens, int32_t* extend_lens);
+                             int32_t* prefix_lens, int32_t* extend_lens, int32_t evict,
+                             int64_t* handles);
+
+/* Locks and LRU eviction ([SG] RadixAttention bullet: an LRU cache of KV in */
+/* the radix tree; nine-step example, steps 5, 8 and 9: least recently used  */
+/* nodes are evicted when memory runs short, never the ones a running        */
+/* request reads).                                                           */
+/* rc_radix_lock: for each request b, pin the nodes holding the cached       */
+/* prefix of its first tok_len[b] tokens (all with tok_len NULL): the        */
+/* deepest node entered and all its ancestors, that whole node included      */
+/* even when the prefix ends inside its edge.  handles[b] (host) receives a  */
+/* handle (0 when nothing is cached: nothing pinned), locked[b] (nullable)   */
+/* the cached length.  A pinned node is never evicted; when its edge is      */
+/* split later both parts stay pinned.  Locks do not mark nodes as used.     */
+rc_status rc_radix_lock(rc_radix* tree, int32_t batch, const int32_t* tokens, const int64_t* tok_off,
+                        const int64_t* tok_len, int64_t* handles, int64_t* locked);
+
+/* Release n locks (handles from rc_radix_lock or rc_radix_emit_rows; 0 is a */
+/* no-op).  Each lock is released once; a handle whose node no longer exists */
+/* or whose counts are not held fails with RC_ERR_ARG and nothing changes.   */
+rc_status rc_radix_unlock(rc_radix* tree, const int64_t* handles, int32_t n);
+
+/* Free at least n_slots slots by evicting whole nodes: repeatedly the leaf  */
+/* that no lock pins with the oldest last use (ties: the lower first slot of */
+/* its edge); its slots go to the back of the free list in position order,   */
+/* and a parent left without children becomes a candidate.  Stops early when */
+/* nothing is evictable; freed (nullable) gets the number of slots freed.    */
+/* n_slots <= 0 evicts nothing.                                              */
+rc_status rc_radix_evict(rc_radix* tree, int64_t n_slots, int64_t* freed);
 
 /* fork ([SG] primitive list: parallel copies of a prompt state): store the  */
 /* parent's first n tokens with their slots (parent_slots, from its row) and */

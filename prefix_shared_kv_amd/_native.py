@@ -32,7 +32,8 @@ class RcPlanInfo(C.Structure):
 
 class RcRadixStats(C.Structure):
     _fields_ = [(n, C.c_int64) for n in ("nodes", "cached_tokens", "free_slots", "pool_slots", "splits", "matches",
-                                         "matched_tokens", "inserted_tokens", "duplicate_slots", "evicted_tokens")]
+                                         "matched_tokens", "inserted_tokens", "duplicate_slots", "evicted_tokens",
+                                         "evicted_nodes", "locked_tokens")]
 
 
 class RcProfEntry(C.Structure):
@@ -68,7 +69,10 @@ _SIGS = {
     "rc_radix_alloc": (i32, [P, i64, P]),
     "rc_radix_free": (i32, [P, P, i64]),
     "rc_radix_insert": (i32, [P, P, P, i64, I64P]),
-    "rc_radix_emit_rows": (i32, [P, i32, P, P, i32, P, P, i32, i64, P, P]),
+    "rc_radix_emit_rows": (i32, [P, i32, P, P, i32, P, P, i32, i64, P, P, i32, P]),
+    "rc_radix_lock": (i32, [P, i32, P, P, P, P, P]),
+    "rc_radix_unlock": (i32, [P, P, i32]),
+    "rc_radix_evict": (i32, [P, i64, I64P]),
     "rc_radix_insert_rows": (i32, [P, i32, P, P, P, P, P, i32, i64, P]),
     "rc_radix_fork": (i32, [P, P, P, i64, i32, P, P, i32, i64]),
     "rc_radix_plan_decode": (i32, [P, i32, P, P, P, P, P, i32, i32, P, i64, C.POINTER(RcPlanInfo)]),

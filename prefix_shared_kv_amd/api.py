@@ -309,8 +309,11 @@ class RadixTree:
         return s, n_new.value
 
     def emit_rows(self, batch: Sequence[Sequence[int]], table: np.ndarray, rows: Optional[Sequence[int]] = None,
-                  reserve: int = 0) -> Tuple[np.ndarray, np.ndarray]:
-        """Fill rows of a host table [R, stride]; returns (prefix_lens, extend_lens)."""
+                  reserve: int = 0, evict: bool = False,
+                  handles: Optional[np.ndarray] = None) -> Tuple[np.ndarray, np.ndarray]:
+        """Fill rows of a host table [R, stride]; returns (prefix_lens, extend_lens).
+        evict: evict least recently used unpinned nodes when the free slots fall short.
+        handles: an int64 array of one entry per request that receives locks on the matched prefixes."""
         if table.dtype != np.int32 or table.ndim != 2 or not table.flags.c_contiguous:
             raise ValueError("table must be a C-contiguous int32 [rows, stride] array")
         tb = _tb(batch)
@@ -318,9 +321,33 @@ class RadixTree:
         rw = np.arange(B, dtype=np.int32) if rows is None else np.ascontiguousarray(rows, np.int32)
         P = np.zeros(B, np.int32)
         E = np.zeros(B, np.int32)
+        if handles is not None and (handles.dtype != np.int64 or handles.shape != (B,) or not handles.flags.c_contiguous):
+            raise ValueError("handles must be a contiguous int64 array with one entry per request")
         check(lib.rc_radix_emit_rows(self._h, B, _np_ptr(tb.flat), _np_ptr(tb.off), reserve, _np_ptr(rw), _np_ptr(table),
-                                     table.shape[0], table.shape[1], _np_ptr(P), _np_ptr(E)))
+                                     table.shape[0], table.shape[1], _np_ptr(P), _np_ptr(E), int(bool(evict)),
+                                     _np_ptr(handles)))
         return P, E
+
+    def lock(self, batch, lengths: Optional[Sequence[int]] = None) -> Tuple[np.ndarray, np.ndarray]:
+        """Pin the cached prefix of each request's first lengths[b] tokens (default: all) against
+        eviction.  Returns (handles int64, locked lengths)."""
+        tb = _tb(batch)
+        ln = _lens(tb, lengths)
+        B = len(tb)
+        h = np.zeros(B, np.int64)
+        m = np.zeros(B, np.int64)
+        check(lib.rc_radix_lock(self._h, B, _np_ptr(tb.flat), _np_ptr(tb.off), _np_ptr(ln), _np_ptr(h), _np_ptr(m)))
+        return h, m
+
+    def unlock(self, handles) -> None:
+        h = np.ascontiguousarray(handles, np.int64)
+        check(lib.rc_radix_unlock(self._h, _np_ptr(h), h.size))
+
+    def evict(self, n_slots: int) -> int:
+        """Evict least recently used unpinned leaves until n_slots slots are freed; returns the number freed."""
+        got = C.c_int64()
+        check(lib.rc_radix_evict(self._h, int(n_slots), C.byref(got)))
+        return got.value
 
     def insert_rows(self, batch: Sequence[Sequence[int]], table: np.ndarray, rows: Sequence[int],
                     lengths: Optional[Sequence[int]] = None) -> np.ndarray:

@@ -14,7 +14,9 @@
 #include <cstring>
 #include <deque>
 #include <new>
+#include <queue>
 #include <system_error>
+#include <tuple>
 #include <thread>
 #include <unordered_map>
 #include <vector>
@@ -31,7 +33,8 @@ struct Node {
   std::vector<int32_t> tok, slot;
   std::unordered_map<int32_t, int32_t> kids;  // first token of child edge -> child
   int64_t last_use = 0;
-  int32_t lock = 0;
+  int32_t lock = 0;     // locks whose pinned path runs through this node
+  uint32_t gen = 0;     // bumped when the node is evicted: stale lock handles are refused
   bool alive = true;
 };
 
@@ -78,7 +81,9 @@ int32_t new_node(rc_radix& t) {
   if (!t.dead_ids.empty()) {
     int32_t id = t.dead_ids.back();
     t.dead_ids.pop_back();
+    const uint32_t g = t.nodes[id].gen;
     t.nodes[id] = Node();
+    t.nodes[id].gen = g;
     return id;
   }
   t.nodes.emplace_back();
@@ -153,6 +158,68 @@ void for_requests(int32_t n, int64_t tokens, F&& f) {
     for (int32_t b = i; b < n; b += nt) f(b);
   for (int32_t b = 0; b < n; b += nt) f(b);
   for (auto& th : pool) th.join();
+}
+
+// Locks.  A lock pins the path from the root to one node (the deepest node
+// holding a locked token): that node and its ancestors count the lock and are
+// not evicted while it is held.  When a pinned edge is split later, both parts
+// keep the count (split copies it to the new upper part), so the pinned token
+// positions never change.  A handle is the node id in the low 32 bits and the
+// node's generation above them; 0 pins nothing.
+int64_t handle_of(const rc_radix& t, int32_t id) {
+  return id == 0 ? 0 : (int64_t)(((uint64_t)t.nodes[id].gen << 32) | (uint32_t)id);
+}
+
+void pin(rc_radix& t, int32_t id, int32_t delta) {
+  for (; id > 0; id = t.nodes[id].parent) t.nodes[id].lock += delta;
+}
+
+bool evictable(const rc_radix& t, int32_t id) {
+  const Node& nd = t.nodes[id];
+  return id > 0 && nd.alive && nd.kids.empty() && nd.lock == 0;
+}
+
+// LRU eviction (SGLang summary, RadixAttention bullet and steps 5, 8 and 9 of
+// the nine-step example: the least recently used nodes go when memory runs
+// short): repeatedly remove the unpinned leaf with the oldest last use (ties:
+// the lower first slot), returning its slots, in position order, to the back
+// of the free list; a parent left without children becomes a candidate.
+// Stops once `want` slots are freed or nothing is evictable.  Returns the
+// number freed (whole edges, so possibly more than `want`).
+int64_t evict_lru(rc_radix& t, int64_t want) {
+  using Key = std::tuple<int64_t, int32_t, int32_t>;  // last use, first slot, node
+  std::priority_queue<Key, std::vector<Key>, std::greater<Key>> heap;
+  auto key = [&](int32_t id) { return Key(t.nodes[id].last_use, t.nodes[id].slot[0], id); };
+  int64_t got = 0;
+  if (want <= 0) return 0;
+  for (int32_t id = 1; id < (int32_t)t.nodes.size(); ++id)
+    if (evictable(t, id)) heap.push(key(id));
+  while (got < want && !heap.empty()) {
+    const int32_t id = std::get<2>(heap.top());
+    heap.pop();
+    Node& nd = t.nodes[id];
+    const int32_t par = nd.parent;
+    const int64_t len = (int64_t)nd.tok.size();
+    t.nodes[par].kids.erase(nd.tok[0]);
+    for (int32_t s : nd.slot) {
+      t.in_tree[s] = 0;
+      t.is_free[s] = 1;
+      t.free_q.push_back(s);
+    }
+    got += len;
+    t.st.evicted_tokens += len;
+    t.st.evicted_nodes++;
+    t.st.cached_tokens -= len;
+    t.st.nodes--;
+    nd.alive = false;
+    nd.gen++;
+    std::vector<int32_t>().swap(nd.tok);
+    std::vector<int32_t>().swap(nd.slot);
+    nd.kids.clear();
+    t.dead_ids.push_back(id);
+    if (evictable(t, par)) heap.push(key(par));
+  }
+  return got;
 }
 
 }  // namespace
@@ -308,17 +375,19 @@ rc_status rc_radix_insert(rc_radix* t, const int32_t* tokens, int32_t* slots, in
           slots[pos + i] = have;
         }
       }
-      t->nodes[c].last_use = now;
       pos += k;
       if (k < len) {
         if (pos < n) {
+          // the walk used the upper part only; the lower part keeps its time
           int32_t u = split(*t, c, k);
           t->nodes[u].last_use = now;
           cur = u;
           continue;  // next lookup adds the new leaf under u
         }
+        t->nodes[c].last_use = now;
         break;  // the sequence ends inside this edge: nothing new to store
       }
+      t->nodes[c].last_use = now;
       cur = c;
     }
     if (n_new) *n_new = n - m;
@@ -354,7 +423,8 @@ rc_status rc_radix_insert_rows(rc_radix* t, int32_t batch, const int32_t* tokens
 
 rc_status rc_radix_emit_rows(rc_radix* t, int32_t batch, const int32_t* tokens, const int64_t* tok_off,
                              int32_t reserve, const int32_t* rows, int32_t* table, int32_t table_rows,
-                             int64_t stride, int32_t* prefix_lens, int32_t* extend_lens) {
+                             int64_t stride, int32_t* prefix_lens, int32_t* extend_lens, int32_t evict,
+                             int64_t* handles) {
   if (!t || batch < 0 || reserve < 0 || stride <= 0 || table_rows < 0) return fail(RC_ERR_ARG, "bad argument to rc_radix_emit_rows");
   if (batch > 0 && (!tok_off || !rows || !table || !prefix_lens || !extend_lens)) return fail(RC_ERR_ARG, "NULL array in rc_radix_emit_rows");
   if (rc_status st = check_lens(batch, tok_off, nullptr); st != RC_OK) return st;
@@ -377,10 +447,39 @@ rc_status rc_radix_emit_rows(rc_radix* t, int32_t batch, const int32_t* tokens, 
   });
   for (int32_t b = 0; b < batch; ++b) need += tok_off[b + 1] - tok_off[b] - P[b] + reserve;
   if (rows_repeat(batch, rows)) return fail(RC_ERR_ARG, "two requests of the batch share a table row");
-  if (need > (int64_t)t->free_q.size())
+  const int64_t free0 = (int64_t)t->free_q.size();
+  if (need > free0 && !evict)
     return fail(RC_ERR_NOMEM, "batch needs %lld slots, %zu free", (long long)need, t->free_q.size());
-  // pass 2: allocate in request order, then copy the matched prefixes' slots
+  // pin the matched prefixes: for the caller (handles), and while evicting,
+  // so that eviction never takes what the batch has matched
+  const bool pinning = handles || need > free0;
+  std::vector<int32_t> end(batch, 0);
+  if (pinning)
+    for (int32_t b = 0; b < batch; ++b) {
+      int64_t w = 0;
+      for (const Visit& v : visits[b]) {
+        if (w >= P[b]) break;
+        end[b] = v.node;
+        w += v.k;
+      }
+      pin(*t, end[b], +1);
+    }
   const int64_t now = ++t->clock;
+  for (int32_t b = 0; b < batch; ++b)
+    for (const Visit& v : visits[b]) t->nodes[v.node].last_use = now;
+  if (need > free0) {
+    try {
+      evict_lru(*t, need - free0);
+    } catch (const std::bad_alloc&) {
+      for (int32_t b = 0; b < batch; ++b) pin(*t, end[b], -1);
+      return fail(RC_ERR_INTERNAL, "host allocation failed during eviction");
+    }
+    if (need > (int64_t)t->free_q.size()) {
+      for (int32_t b = 0; b < batch; ++b) pin(*t, end[b], -1);
+      return fail(RC_ERR_NOMEM, "batch needs %lld slots, %zu free after eviction", (long long)need, t->free_q.size());
+    }
+  }
+  // pass 2: allocate in request order, then copy the matched prefixes' slots
   for (int32_t b = 0; b < batch; ++b) {
     const int64_t n = tok_off[b + 1] - tok_off[b];
     int32_t* row = table + (int64_t)rows[b] * stride;
@@ -392,7 +491,6 @@ rc_status rc_radix_emit_rows(rc_radix* t, int32_t batch, const int32_t* tokens, 
     }
     prefix_lens[b] = (int32_t)P[b];
     extend_lens[b] = (int32_t)(n - P[b]);
-    for (const Visit& v : visits[b]) t->nodes[v.node].last_use = now;
     t->st.matches++;
     t->st.matched_tokens += P[b];
   }
@@ -407,6 +505,12 @@ rc_status rc_radix_emit_rows(rc_radix* t, int32_t batch, const int32_t* tokens, 
       w += k;
     }
   });
+  for (int32_t b = 0; b < batch; ++b) {
+    if (handles)
+      handles[b] = handle_of(*t, end[b]);
+    else if (pinning)
+      pin(*t, end[b], -1);
+  }
   return RC_OK;
 }
 
@@ -424,10 +528,70 @@ rc_status rc_radix_fork(rc_radix* t, const int32_t* tokens, const int32_t* paren
   return RC_OK;
 }
 
+rc_status rc_radix_lock(rc_radix* t, int32_t batch, const int32_t* tokens, const int64_t* tok_off,
+                        const int64_t* tok_len, int64_t* handles, int64_t* locked) {
+  if (!t || batch < 0) return fail(RC_ERR_ARG, "bad argument to rc_radix_lock");
+  if (batch > 0 && (!tok_off || !handles)) return fail(RC_ERR_ARG, "NULL array in rc_radix_lock");
+  if (rc_status st = check_lens(batch, tok_off, tok_len); st != RC_OK) return st;
+  auto len_of = [&](int32_t b) { return tok_len ? tok_len[b] : tok_off[b + 1] - tok_off[b]; };
+  int64_t total = 0;
+  for (int32_t b = 0; b < batch; ++b) {
+    if (len_of(b) > 0 && !tokens) return fail(RC_ERR_ARG, "tokens is NULL");
+    total += len_of(b);
+  }
+  std::vector<int32_t> end(batch, 0);
+  std::vector<int64_t> m(batch, 0);
+  for_requests(batch, total, [&](int32_t b) {
+    int32_t last = 0;
+    m[b] = walk(*t, tokens + tok_off[b], len_of(b), [&](int32_t id, int64_t) { last = id; });
+    end[b] = last;
+  });
+  for (int32_t b = 0; b < batch; ++b) {
+    pin(*t, end[b], +1);
+    handles[b] = handle_of(*t, end[b]);
+    if (locked) locked[b] = m[b];
+  }
+  return RC_OK;
+}
+
+rc_status rc_radix_unlock(rc_radix* t, const int64_t* handles, int32_t n) {
+  if (!t || n < 0 || (n > 0 && !handles)) return fail(RC_ERR_ARG, "bad argument to rc_radix_unlock");
+  // validate every handle and that the counts it releases are held, then release
+  std::unordered_map<int32_t, int32_t> dec;
+  for (int32_t i = 0; i < n; ++i) {
+    const int64_t h = handles[i];
+    if (h == 0) continue;
+    const int64_t id = (int64_t)(uint32_t)((uint64_t)h & 0xffffffffu);
+    const uint32_t gen = (uint32_t)((uint64_t)h >> 32);
+    if (id <= 0 || id >= (int64_t)t->nodes.size() || !t->nodes[id].alive || t->nodes[id].gen != gen)
+      return fail(RC_ERR_ARG, "handle %d (0x%llx) is not a held lock", i, (unsigned long long)h);
+    for (int32_t x = (int32_t)id; x > 0; x = t->nodes[x].parent) dec[x]++;
+  }
+  for (const auto& [x, c] : dec)
+    if (t->nodes[x].lock < c) return fail(RC_ERR_ARG, "more unlocks than locks on a node");
+  for (const auto& [x, c] : dec) t->nodes[x].lock -= c;
+  return RC_OK;
+}
+
+rc_status rc_radix_evict(rc_radix* t, int64_t n_slots, int64_t* freed) {
+  if (!t) return fail(RC_ERR_ARG, "bad argument to rc_radix_evict");
+  int64_t got = 0;
+  try {
+    got = evict_lru(*t, n_slots);
+  } catch (const std::bad_alloc&) {
+    return fail(RC_ERR_INTERNAL, "host allocation failed during eviction");
+  }
+  if (freed) *freed = got;
+  return RC_OK;
+}
+
 rc_status rc_radix_stats_get(const rc_radix* t, rc_radix_stats* out) {
   if (!t || !out) return fail(RC_ERR_ARG, "NULL argument");
   *out = t->st;
   out->free_slots = (int64_t)t->free_q.size();
+  out->locked_tokens = 0;
+  for (size_t id = 1; id < t->nodes.size(); ++id)
+    if (t->nodes[id].alive && t->nodes[id].lock > 0) out->locked_tokens += (int64_t)t->nodes[id].tok.size();
   return RC_OK;
 }
 

@@ -8,10 +8,13 @@ lists, lengths, plans) are the only other device traffic.
 
 Flow of one batch ("Prompt Caching" glossary, GPT-2 example; SGLang summary,
 RadixAttention and `fork`):
-  schedule   longest cached prefix per request, slots for the new tokens and
-             for the decode steps, table rows            (host, C++)
+  schedule   longest cached prefix per request (pinned while the request
+             runs), slots for the new tokens and for the decode steps,
+             evicting least recently used unpinned nodes when the pool is
+             short, table rows                           (host, C++)
   extend     store new K/V in the pool, attend            (kv_store, extend)
-  commit     insert prompts into the tree; rows get the tree's slots
+  commit     insert prompts into the tree; rows get the tree's slots; the
+             request's pin moves to what it stored
   prepare_decode  share plan from the tree (who reads which node), per-step
              slot and length tables uploaded once
   decode_step  store the token's K/V, split-K attention over shared nodes,
@@ -37,6 +40,7 @@ class Batch:
     prefix_lens: np.ndarray    # P_b
     extend_lens: np.ndarray    # E_b
     reserve: int
+    locks: Optional[np.ndarray] = None  # lock handles pinning each request's cached tokens
     dev: dict = dataclasses.field(default_factory=dict)
 
     @property
@@ -168,32 +172,42 @@ class Engine:
         """Store K/V for the uncached tail of `tokens` and insert the sequence.
         k, v hold rows for positions [cached, n).  Returns the cached length found."""
         t = np.ascontiguousarray(tokens, np.int32)
-        probe = np.concatenate([t, np.array([-1], np.int32)])  # no stored edge starts with -1: full match allowed
-        m, pre = self.tree.match(probe)
-        if expect_cached is not None and m != expect_cached:
-            raise RuntimeError(f"expected {expect_cached} cached tokens, found {m}")
-        n_new = len(t) - m
-        if k.shape[0] != n_new or v.shape[0] != n_new:
-            raise ValueError(f"need K/V for {n_new} uncached tokens, got {k.shape[0]}")
-        new = self.tree.alloc(n_new)
-        if n_new:
-            api.kv_store(self.shape, self.k_pool, self.v_pool, k, v, self._i32(new))
-        self.tree.insert(t, np.concatenate([pre, new]).astype(np.int32))
+        h, _ = self.tree.lock([t])  # the cached part stays while room is made for the rest
+        try:
+            probe = np.concatenate([t, np.array([-1], np.int32)])  # no stored edge starts with -1: full match allowed
+            m, pre = self.tree.match(probe)
+            if expect_cached is not None and m != expect_cached:
+                raise RuntimeError(f"expected {expect_cached} cached tokens, found {m}")
+            n_new = len(t) - m
+            if k.shape[0] != n_new or v.shape[0] != n_new:
+                raise ValueError(f"need K/V for {n_new} uncached tokens, got {k.shape[0]}")
+            short = n_new - self.tree.stats()["free_slots"]
+            if short > 0:
+                self.tree.evict(short)
+            new = self.tree.alloc(n_new)
+            if n_new:
+                api.kv_store(self.shape, self.k_pool, self.v_pool, k, v, self._i32(new))
+            self.tree.insert(t, np.concatenate([pre, new]).astype(np.int32))
+        finally:
+            self.tree.unlock(h)
         return m
 
     # -- a batch of requests --------------------------------------------------
-    def schedule(self, batch_tokens, reserve: int = 0) -> Batch:
-        """batch_tokens: a list of token-id arrays or a TokenBatch."""
+    def schedule(self, batch_tokens, reserve: int = 0, evict: bool = True) -> Batch:
+        """batch_tokens: a list of token-id arrays or a TokenBatch.  Each request's cached prefix
+        is pinned until release; with evict, least recently used unpinned nodes make room when
+        the free slots fall short."""
         tb = batch_tokens if isinstance(batch_tokens, TokenBatch) else TokenBatch(batch_tokens)
         B = len(tb)
         if B > len(self.free_rows):
             raise RuntimeError("no free table rows")
         rows = np.array(self.free_rows[:B], np.int32)
         self._rows_writable(rows)
-        P, E = self.tree.emit_rows(tb, self.table_h, rows=rows, reserve=reserve)
+        locks = np.zeros(B, np.int64)
+        P, E = self.tree.emit_rows(tb, self.table_h, rows=rows, reserve=reserve, evict=evict, handles=locks)
         del self.free_rows[:B]
         self._upload_rows(rows)
-        b = Batch(tb, rows, P, E, reserve)
+        b = Batch(tb, rows, P, E, reserve, locks)
         start = np.zeros(B, np.int32)
         if B:
             start[1:] = np.cumsum(E)[:-1]
@@ -243,6 +257,10 @@ class Engine:
         width = max(int(n.max()) if b.size else 0, 1)
         work = np.ascontiguousarray(self.table_h[b.rows, :width])
         changed = self.tree.insert_rows(b.tb, work, np.arange(b.size, dtype=np.int32), lengths)
+        if b.locks is not None:  # pin what is stored now, then drop the old pins
+            locks, _ = self.tree.lock(b.tb, lengths)
+            self.tree.unlock(b.locks)
+            b.locks = locks
         if changed.any():
             rows = b.rows[changed]
             self._rows_writable(rows)
@@ -289,6 +307,9 @@ class Engine:
     def release(self, b: Batch, keep: Optional[Sequence[int]] = None) -> None:
         """Return the batch's table rows; slots past `keep[i]` (default: tokens given) go back to the pool
         unless the tree holds them."""
+        if b.locks is not None:
+            self.tree.unlock(b.locks)
+            b.locks = None
         lens = b.tb.lens()
         keep = lens if keep is None else np.asarray(keep, np.int64)
         tails = [self.table_h[r, k:n + b.reserve] for r, k, n in zip(b.rows, keep, lens)]

@@ -50,6 +50,7 @@ _T_EXT_TOK, _T_EXT_Q, _T_EXT_K, _T_EXT_V = 21, 22, 23, 24
 _T_DEC_Q, _T_DEC_K, _T_DEC_V = 31, 32, 33
 _T_PRE_Q = 41
 _T_SLOTS, _T_LEN, _T_FIRST = 51, 52, 53
+_T_PFX_K, _T_PFX_V, _T_PFX_Q = 61, 62, 63
 
 
 def rng(seed: int, tag: int, *ids: int) -> np.random.Generator:
@@ -62,6 +63,39 @@ def round_bf16(x: np.ndarray) -> np.ndarray:
     u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
     r = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) & np.uint32(0xFFFF0000)
     return r.view(np.float32)
+
+
+def prefix_hashes(tokens: np.ndarray) -> np.ndarray:
+    """h[p] identifies tokens[:p+1] (a polynomial hash modulo the prime 2^61 - 1)."""
+    M, h, out = (1 << 61) - 1, 0, np.zeros(len(tokens), np.int64)
+    for p, t in enumerate(np.asarray(tokens, np.int64).tolist()):
+        h = (h * 1000003 + t + 1) % M
+        out[p] = h
+    return out
+
+
+def prefix_keyed_kv(seed: int, tokens: np.ndarray, shape: "Shape", start: int = 0) -> Tuple[np.ndarray, np.ndarray]:
+    """K and V [len(tokens) - start, Hkv, D] for positions start.. of a sequence.  Position p's
+    values come from a stream keyed by tokens[:p+1] alone, so every sequence with the same first
+    p+1 tokens gets bit-identical K/V at p, whatever was cached, evicted or recomputed."""
+    h = prefix_hashes(tokens)
+    n = len(tokens) - start
+    k = np.zeros((n, shape.num_kv_heads, shape.head_dim), np.float32)
+    v = np.zeros_like(k)
+    for i in range(n):
+        key = (int(h[start + i]) & 0xFFFFFFFF, int(h[start + i]) >> 32)
+        k[i] = rng(seed, _T_PFX_K, *key).standard_normal(k.shape[1:], dtype=np.float32) * shape.std
+        v[i] = rng(seed, _T_PFX_V, *key).standard_normal(k.shape[1:], dtype=np.float32) * shape.std
+    if shape.dtype == "bf16":
+        k, v = round_bf16(k), round_bf16(v)
+    return k, v
+
+
+def keyed_q(seed: int, shape: "Shape", n: int, *ids: int) -> np.ndarray:
+    """Queries [n, Hq, D] from a stream keyed by ids."""
+    q = rng(seed, _T_PFX_Q, *ids).standard_normal((n, shape.num_q_heads, shape.head_dim), dtype=np.float32)
+    q *= shape.std
+    return round_bf16(q) if shape.dtype == "bf16" else q
 
 
 @dataclasses.dataclass
