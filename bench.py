@@ -276,6 +276,14 @@ def bench_classify_heavy(args):
     q_br, k_br, v_br = randn(n_lab, Hq, D), randn(n_lab, Hkv, D), randn(n_lab, Hkv, D)
     q_dec, k_dec, v_dec = randn(T, B, Hq, D), randn(T, B, Hkv, D), randn(T, B, Hkv, D)
     o_doc, o_br = torch.empty_like(q_doc), torch.empty_like(q_br)
+    # next-token logits after each branch (one row per question, full vocabulary),
+    # the 64 label tokens and the options of each question
+    n_br = len(labels)
+    logits = torch.from_numpy(W.next_token_logits(args.seed, n_br)).to(dev).to(torch.bfloat16)
+    label_ids = torch.from_numpy(W.label_token_ids(args.seed)).to(dev)
+    n_opts = torch.from_numpy(W.option_counts(args.seed, n_br)).to(dev)
+    lab_out = (torch.empty(n_br, label_ids.numel(), device=dev), torch.empty(n_br, dtype=torch.int32, device=dev),
+               torch.empty(n_br, device=dev), torch.empty(n_br, device=dev))
     o_dec = torch.empty(B, Hq, D, device=dev, dtype=torch.bfloat16)
     scale = wh.sm_scale
     plan_info, ph = {}, Phases()
@@ -291,6 +299,7 @@ def bench_classify_heavy(args):
         pk.prof_tag("branch")
         bb = eng.schedule(br_tb[s])
         eng.extend(bb, q_br, k_br, v_br, scale, o=o_br, cascade=not args.branch_tiles, chunk=args.branch_chunk)
+        pk.label_distribution(logits, label_ids, n_opts, out=lab_out)
         eng.commit(bb)
         eng.release(bb)
         ph.mark("branches")
@@ -348,6 +357,8 @@ def bench_classify_heavy(args):
             "prefill": extend_report("extend_bf16_d128@prefill", pre_flops, pre_ms, L),
             "branches": extend_report(br_name, br_flops, br_ms, n_lab),
         },
+        "labels": {"kernel": "label_distribution@branch", "avg_launch_ms": round(avg_ms(prof, "label_distribution@branch"), 5),
+                   "questions": n_br, "labels": int(label_ids.numel())},
         "decode": {
             "attention_ms": round(dec_ms, 5), "merge_avg_ms": round(mrg_ms, 5),
             "unique_bytes_per_step": dec_bytes, "logical_bytes_per_step": logical * row,
@@ -361,11 +372,11 @@ def bench_classify_heavy(args):
         res["host_phase_ms"] = ph.ms
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline_classify_heavy(wc, wh, args.cpu_sample, args.cpu_decode_steps,
-                                                          tokens_per_step, T)
+                                                          tokens_per_step, T, args.seed)
     return res
 
 
-def cpu_baseline_classify_heavy(wc, wh, n_req, n_dec, tokens_per_step, T):
+def cpu_baseline_classify_heavy(wc, wh, n_req, n_dec, tokens_per_step, T, seed):
     """The float64 oracle, as it stands, on a bounded sample of one step: the
     document's prefill and the 64 branch extends in full, and the decode of
     `n_req` requests at `n_dec` of the T steps; the per-token decode time is
@@ -373,8 +384,13 @@ def cpu_baseline_classify_heavy(wc, wh, n_req, n_dec, tokens_per_step, T):
     from threadpoolctl import threadpool_limits
 
     from oracle import attention as A
+    from oracle import labels as LB
+    from synth import workloads as W
 
     cores = len(os.sched_getaffinity(0))
+    n_q = len(wc.requests)
+    logits = W.next_token_logits(seed, n_q)
+    label_ids, n_opts = W.label_token_ids(seed), W.option_counts(seed, n_q)
     pre = wc.prefill_nodes[0]
     q_doc = wc.node_prefill_q(pre)
     K_doc, V_doc = wc.node_kv(pre)
@@ -393,6 +409,7 @@ def cpu_baseline_classify_heavy(wc, wh, n_req, n_dec, tokens_per_step, T):
         t0 = time.perf_counter()
         for q, K, V in branches:
             A.extend(q, K, V, len(K_doc), wc.sm_scale)
+        LB.classify(logits, label_ids, n_opts)
         t_br = time.perf_counter() - t0
         t_dec = 0.0
         for i in rids:
@@ -408,7 +425,7 @@ def cpu_baseline_classify_heavy(wc, wh, n_req, n_dec, tokens_per_step, T):
     est = t_pre + t_br + B * T * t_dec
     return {"value": round(tokens_per_step / est, 2), "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"float64 numpy oracle on {cores} threads: the 4096-token prefill and the {len(branches)} branch "
-                      f"extends in full, and {n_tok} decode tokens ({len(rids)} requests x {len(steps)} of the {T} "
+                      f"extends and their label distributions in full, and {n_tok} decode tokens ({len(rids)} requests x {len(steps)} of the {T} "
                       f"steps); the decode time per token scaled to {B}x{T}: one step = {est:.1f} s",
             "sample_seconds": round(t_pre + t_br + n_tok * t_dec, 2)}
 

@@ -77,6 +77,8 @@ typedef struct rc_shape {
 #define RC_DEVERR_TABLE 2   /* a table position outside [0, stride)              */
 #define RC_DEVERR_LENGTH 4  /* extend_len > max_extend or a negative length      */
 #define RC_DEVERR_PLAN 8    /* a malformed plan entry                            */
+#define RC_DEVERR_LABEL 16  /* a label id outside [0, vocab) or an option count  */
+                            /* outside [1, n_labels]                             */
 
 const char* rc_last_error(void);
 const char* rc_version(void);
@@ -389,6 +391,37 @@ rc_status rc_extend_attention_shared(const rc_shape* shape, void* o, const void*
                                      void* workspace, int64_t ws_bytes, void* stream);
 
 rc_status rc_radix_stats_get(const rc_radix* tree, rc_radix_stats* out);
+
+/* ------------------------------------------------------------------------ */
+/* Label-restricted next-token distribution for single-token classification */
+/* (openjev-sglang tutorial: "how inference works", step 5, the question     */
+/* types and "interpret confidence carefully").  For row r of logits (the   */
+/* next-token logits after a branch, e.g. the classification branches of    */
+/* one document) with k_r = counts[r] options (all n_labels when counts is  */
+/* NULL), over the first k_r label tokens label_ids[0..k_r):                 */
+/*   probs[r, i]   = exp(x_i - max x) / sum_j exp(x_j - max x), x_i =        */
+/*                   logits[r, label_ids[i]] (stable softmax), 0 for i >= k_r */
+/*   choice[r]     = the option with the largest logit (lowest index on ties) */
+/*   expected[r]   = sum_i i * probs[r, i] (the Score question's expected     */
+/*                   zero-based level)                                       */
+/*   confidence[r] = 1 - H(probs[r]) / log(k_r), natural log, 0 log 0 = 0;  */
+/*                   1 when k_r = 1                                          */
+/* A Bool question is the two-option case with the labels (yes, no): its    */
+/* answer is probs[r, 0].                                                    */
+/*   logits     device [n_rows, row_stride] of dtype (RC_F32 or RC_BF16),     */
+/*              finite; only the first vocab entries of a row are read.     */
+/*   label_ids  device int32 [n_labels], 1 <= n_labels <= 64, each in        */
+/*              [0, vocab) (else RC_DEVERR_LABEL and the label gets          */
+/*              probability 0).                                              */
+/*   counts     device int32 [n_rows] or NULL; out-of-range counts are       */
+/*              clamped into [1, n_labels] and raise RC_DEVERR_LABEL.        */
+/*   probs      device float [n_rows, n_labels]; choice (int32), expected,   */
+/*              confidence (float): device [n_rows], each nullable.          */
+/* fp32 arithmetic; deterministic (fixed reduction order).                   */
+rc_status rc_label_distribution(const void* logits, int32_t dtype, int64_t row_stride, int64_t vocab,
+                                int32_t n_rows, const int32_t* label_ids, int32_t n_labels,
+                                const int32_t* counts, float* probs, int32_t* choice, float* expected,
+                                float* confidence, void* stream);
 
 /* Tuning switches (process-wide, take effect on the next call):             */
 /*   "decode_rows" 0|1: narrow decode items are computed by groups of four kv */

@@ -56,6 +56,7 @@ _SIGS = {
     "rc_version": (C.c_char_p, []),
     "rc_set_error_word": (i32, [P]),
     "rc_kv_store": (i32, [C.POINTER(RcShape), P, P, P, P, P, i64, P]),
+    "rc_label_distribution": (i32, [P, i32, i64, i64, i32, P, i32, P, P, P, P, P, P]),
     "rc_extend_attention": (i32, [C.POINTER(RcShape), P, P, P, P, P, P, P, i32, i64, P, P, P, P, i32, i64, i32, f32, P]),
     "rc_plan_decode_unshared": (i32, [i32, P, P, i32, i32, P, i64, C.POINTER(RcPlanInfo)]),
     "rc_decode_workspace_bytes": (i64, [C.POINTER(RcShape), C.POINTER(RcPlanInfo)]),

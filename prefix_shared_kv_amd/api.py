@@ -115,6 +115,40 @@ def extend_attention(shape: KVShape, o, q, k_new, v_new, k_pool, v_pool, req_to_
                                   float(sm_scale), _stream(stream)))
 
 
+def label_distribution(logits, label_ids, counts=None, vocab: Optional[int] = None, out=None, stream=None):
+    """Stable softmax over each row's allowed label logits, the most probable option, the expected
+    index and the confidence 1 - H/log k (rc_label_distribution).  logits: [rows, stride] fp32 or
+    bf16 (rows may be a strided view with unit inner stride); label_ids: int32 [n_labels]; counts:
+    int32 [rows] options per row or None.  Returns (probs [rows, n_labels], choice, expected,
+    confidence), written into `out` when given."""
+    if not isinstance(logits, torch.Tensor) or logits.device.type != "cuda" or logits.dim() != 2:
+        raise ValueError("logits must be a 2-D GPU tensor")
+    if logits.stride(1) != 1:
+        raise ValueError("logits rows must be contiguous")
+    dt = _DT.get(logits.dtype)
+    if dt is None:
+        raise TypeError(f"logits dtype {logits.dtype} not supported")
+    R = logits.shape[0]
+    L = label_ids.numel()
+    _dev(label_ids, "label_ids", torch.int32, (L,))
+    if counts is not None:
+        _dev(counts, "counts", torch.int32, (R,))
+    if out is None:
+        dev = logits.device
+        out = (torch.empty(R, L, dtype=torch.float32, device=dev), torch.empty(R, dtype=torch.int32, device=dev),
+               torch.empty(R, dtype=torch.float32, device=dev), torch.empty(R, dtype=torch.float32, device=dev))
+    probs, choice, expected, confidence = out
+    _dev(probs, "probs", torch.float32, (R, L))
+    _dev(choice, "choice", torch.int32, (R,))
+    _dev(expected, "expected", torch.float32, (R,))
+    _dev(confidence, "confidence", torch.float32, (R,))
+    stride = logits.stride(0) if R > 1 else logits.shape[1]
+    check(lib.rc_label_distribution(_vp(logits), dt, stride, int(vocab or logits.shape[1]), R, _vp(label_ids), L,
+                                    _vp(counts), _vp(probs), _vp(choice), _vp(expected), _vp(confidence),
+                                    _stream(stream)))
+    return probs, choice, expected, confidence
+
+
 class DecodePlan:
     """A decode work plan: the host int32 buffer, its summary, and a device copy."""
 

@@ -51,6 +51,7 @@ _T_DEC_Q, _T_DEC_K, _T_DEC_V = 31, 32, 33
 _T_PRE_Q = 41
 _T_SLOTS, _T_LEN, _T_FIRST = 51, 52, 53
 _T_PFX_K, _T_PFX_V, _T_PFX_Q = 61, 62, 63
+_T_LOGITS, _T_LABELS, _T_OPTIONS = 71, 72, 73
 
 
 def rng(seed: int, tag: int, *ids: int) -> np.random.Generator:
@@ -96,6 +97,21 @@ def keyed_q(seed: int, shape: "Shape", n: int, *ids: int) -> np.ndarray:
     q = rng(seed, _T_PFX_Q, *ids).standard_normal((n, shape.num_q_heads, shape.head_dim), dtype=np.float32)
     q *= shape.std
     return round_bf16(q) if shape.dtype == "bf16" else q
+
+
+def label_token_ids(seed: int, n: int = 64, vocab: int = VOCAB) -> np.ndarray:
+    """n distinct token ids standing for the answer labels A..Z, AA, AB, ... (int32)."""
+    return rng(seed, _T_LABELS).choice(vocab, size=n, replace=False).astype(np.int32)
+
+
+def next_token_logits(seed: int, rows: int, vocab: int = VOCAB, std: float = 3.0, row: int = 0) -> np.ndarray:
+    """Next-token logits [rows, vocab] float32, N(0, std): the rows of one batch of branches."""
+    return rng(seed, _T_LOGITS, row).standard_normal((rows, vocab), dtype=np.float32) * np.float32(std)
+
+
+def option_counts(seed: int, rows: int, lo: int = 2, hi: int = 64) -> np.ndarray:
+    """Options per question, uniform in [lo, hi] (int32)."""
+    return rng(seed, _T_OPTIONS).integers(lo, hi + 1, size=rows).astype(np.int32)
 
 
 @dataclasses.dataclass
