@@ -46,8 +46,10 @@ HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
 ROOT = os.path.dirname(os.path.abspath(__file__))
 # the decode kernel's sources: a traffic figure stands only while these are unchanged
+# what the decode kernel's code depends on: its sources and the build flags
 KERNEL_SOURCES = [os.path.join(ROOT, "prefix_shared_kv_amd", "csrc", f)
-                  for f in ("decode.hip", "attn_tile.h", "hip_common.h")]
+                  for f in ("decode.hip", "attn_tile.h", "hip_common.h")] + [
+                  os.path.join(ROOT, "prefix_shared_kv_amd", "build.py")]
 METRIC = "extend-attn TFLOP/s (% MFMA peak) + decode-attn HBM GB/s, tokens/s, 1 GPU"
 
 
