@@ -8,8 +8,9 @@
 // K/V; a decode token attends over the whole context.  The result equals a full
 // recompute up to floating-point rounding (the page's closing "related terms").
 //
-// One MFMA kernel serves both.  A workgroup (4 waves) owns up to 128 query
-// "columns" that read the same kv head over the same key positions:
+// One MFMA kernel serves both.  A workgroup of NW waves (4 for decode, 8 for
+// extend) owns up to 32 NW query "columns" that read the same kv head over
+// the same key positions:
 //   extend : columns = (new token, q head of the kv head's group) of one request
 //   decode : columns = (member request, q head) of one plan item, i.e. every
 //            request whose context holds this range of slots — a prefix shared
@@ -273,11 +274,11 @@ __device__ __forceinline__ i16x4 lds_read_tr(const uint16_t* p) {
 // are exact up to rounding for any reference maximum.
 constexpr float RESCALE_SLACK = 8.f;
 
-template <int D>
+template <int D, int NW = 4>
 __device__ __forceinline__ void attn_bf16_body(const Args& a, const int mode, const int L, uint16_t (&sK)[2][BN * D],
                                                uint16_t (&sV)[2][BN * D]) {
-  constexpr int CH = D / 8;          // 16-byte chunks per key row
-  constexpr int KPT = BN * CH / NT;  // keys per thread per stage (4 for D=128, 2 for D=64)
+  constexpr int CH = D / 8;                 // 16-byte chunks per key row
+  constexpr int KPT = BN * CH / (64 * NW);  // keys per thread per stage
   constexpr int NKS = D / 16;        // MFMA k-steps over D
   constexpr int NDB = D / 32;        // 32-row blocks of O^T
   const Work w = resolve(a, mode, L, threadIdx.x == 0);
@@ -305,8 +306,8 @@ __device__ __forceinline__ void attn_bf16_body(const Args& a, const int mode, co
   // lane into 1 KiB of LDS at lane-consecutive addresses, so each load
   // instruction fills one block of KPB keys x CH chunks of the row-major,
   // chunk-swizzled tile; a lane fetches the logical chunk that belongs at its
-  // position.  Load r of wave w fills block 4r + w of K and of V: a lane's
-  // keys are then 4*KPB apart, the same in the swizzle, so one column offset
+  // position.  Load r of wave w fills block NW r + w of K and of V: a lane's
+  // keys are then NW*KPB apart, the same in the swizzle, so one column offset
   // serves all of them.
   constexpr int KPB = 64 / CH;  // keys per 1 KiB block
   const uint32_t row_bytes = (uint32_t)(a.Hkv * D * 2);
@@ -320,14 +321,14 @@ __device__ __forceinline__ void attn_bf16_body(const Args& a, const int mode, co
   const char* kncol = (const char*)a.k_new + coff;
   const char* vncol = (const char*)a.v_new + coff;
   const int32_t* trow = a.table + w.row * a.stride + lkey0;
-  auto lkey = [&](int r) { return lkey0 + r * 4 * KPB; };
+  auto lkey = [&](int r) { return lkey0 + r * NW * KPB; };
   int32_t slot[2][KPT];
 
   // slots of this lane's keys in the stage starting at kt (pool keys only)
   auto load_slots = [&](int (&sl)[KPT], int kt) {
     if (kt + BN <= plain_end) {
 #pragma unroll
-      for (int r = 0; r < KPT; ++r) sl[r] = trow[kt + r * 4 * KPB];
+      for (int r = 0; r < KPT; ++r) sl[r] = trow[kt + r * NW * KPB];
       return;
     }
 #pragma unroll
@@ -337,9 +338,17 @@ __device__ __forceinline__ void attn_bf16_body(const Args& a, const int mode, co
     }
   };
   int bad_slot = 0;  // an out-of-range slot was met (reported once, at the end)
+  // The loads are written as assembly.  Issued through the compiler builtin,
+  // the compiler cannot tell their LDS writes (the next stage's buffer) from
+  // the tile being read, and waits for all of them before the stage's first
+  // LDS read, which puts the full load latency into every stage.  Hidden from
+  // the compiler, they are ordered by the stage loop alone: each stage waits
+  // for its own loads (vmcnt(0)) before the barrier that precedes any read of
+  // the buffer they fill.  M0 holds the LDS destination; one wait state
+  // separates its write from the load that reads it.
   auto dma = [&](const char* src, uint16_t* dst) {
-    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                     (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+    const uint32_t lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint16_t*)dst;
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(lds) : "memory", "m0");
   };
   // Out-of-range slots are clamped (and reported), so every load stays in
   // the pool.  Keys past the range end are loaded as copies of the last key,
@@ -353,7 +362,7 @@ __device__ __forceinline__ void attn_bf16_body(const Args& a, const int mode, co
 #pragma unroll
       for (int r = 0; r < KPT; ++r) {
         const uint64_t off = (uint64_t)min((uint32_t)sl[r], nslots - 1) * row_bytes;
-        const int blk = (4 * r + wave) * KPB * D;
+        const int blk = (NW * r + wave) * KPB * D;
         dma(kcol + off, dk + blk);
         dma(vcol + off, dv + blk);
       }
@@ -362,7 +371,7 @@ __device__ __forceinline__ void attn_bf16_body(const Args& a, const int mode, co
     // (integer selects, not a choice between pointers, keep this in registers)
 #pragma unroll
     for (int r = 0; r < KPT; ++r) {
-      const int blk = (4 * r + wave) * KPB * D;
+      const int blk = (NW * r + wave) * KPB * D;
       const int j = min(kt + lkey(r), w.key_end - 1);
       const bool is_new = j >= w.ext_begin;
       bad_slot |= !is_new && (uint32_t)sl[r] >= nslots;
@@ -490,7 +499,10 @@ __device__ __forceinline__ void attn_bf16_body(const Args& a, const int mode, co
   auto step = [&](auto bufc, int i, auto maskc) {
     constexpr int b = decltype(bufc)::value;
     const int kt = kb + i * BN;
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // vmcnt(0) through the builtin, so the compiler knows every earlier load
+    // (the slot indices among them) has landed and adds no waits of its own
+    // that would also count the assembly loads in flight
+    __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
     if (i + 1 < n_st) issue(sK[b ^ 1], sV[b ^ 1], slot[b ^ 1], kt + BN);
     if (i + 2 < n_st) load_slots(slot[b], kt + 2 * BN);

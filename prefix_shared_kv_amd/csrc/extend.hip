@@ -21,13 +21,18 @@ __device__ __forceinline__ int extend_order(int p, int n_bh, int tiles, int ck) 
   return t < tiles ? bh * tiles + t : -1;
 }
 
+// Extend tiles take 8 waves (256 query columns, two waves per SIMD, one
+// workgroup per CU): each K/V stage loaded into LDS feeds twice the columns of
+// a 4-wave tile, which halves the loads per FLOP.
+constexpr int EXT_WAVES = 8;
+
 template <int D>
-__global__ __launch_bounds__(NT, 2) void extend_attn_bf16(Args a, int n_bh, int ck) {
+__global__ __launch_bounds__(64 * EXT_WAVES, 1) void extend_attn_bf16(Args a, int n_bh, int ck) {
   __shared__ __attribute__((aligned(16))) uint16_t sK[2][BN * D];
   __shared__ __attribute__((aligned(16))) uint16_t sV[2][BN * D];
   const int L = extend_order(blockIdx.x, n_bh, a.tiles, ck);
   if (L < 0) return;
-  attn_bf16_body<D>(a, EXTEND, L, sK, sV);
+  attn_bf16_body<D, EXT_WAVES>(a, EXTEND, L, sK, sV);
 }
 
 template <int D>
@@ -42,7 +47,7 @@ void launch_extend(const Args& a, int n_bh, bool bf16, hipStream_t s, const char
     const int ck = a.tiles < 4 ? a.tiles : 4;
     const int64_t chunks = (int64_t)n_bh * ((a.tiles + ck - 1) / ck);
     const int64_t grid = (chunks + 7) / 8 * 8 * ck;
-    hipLaunchKernelGGL(extend_attn_bf16<D>, dim3((unsigned)grid), dim3(NT), 0, s, a, n_bh, ck);
+    hipLaunchKernelGGL(extend_attn_bf16<D>, dim3((unsigned)grid), dim3(64 * EXT_WAVES), 0, s, a, n_bh, ck);
   } else {
     hipLaunchKernelGGL(extend_attn_f32<D>, dim3(a.n_work), dim3(NT), 0, s, a);
   }
@@ -76,7 +81,7 @@ extern "C" rc_status rc_extend_attention(const rc_shape* shape, void* o, const v
   a.total_extend = total_extend;
   a.rows = rows; a.prefix_lens = prefix_lens; a.extend_lens = extend_lens; a.extend_start = extend_start;
   a.batch = batch; a.max_extend = max_extend;
-  a.tok_per_tile = NCOL / g;
+  a.tok_per_tile = (shape->dtype == RC_BF16 ? 32 * EXT_WAVES : NCOL) / g;
   a.tiles = (max_extend + a.tok_per_tile - 1) / a.tok_per_tile;
   const int64_t n_work = (int64_t)batch * a.Hkv * a.tiles;
   if (n_work > INT32_MAX / 8) return fail(RC_ERR_RANGE, "grid of %lld workgroups too large", (long long)n_work);
