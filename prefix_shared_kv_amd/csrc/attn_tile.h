@@ -325,16 +325,15 @@ __device__ __forceinline__ void attn_bf16_body(const Args& a, const int mode, co
   int32_t slot[2][KPT];
 
   // slots of this lane's keys in the stage starting at kt (pool keys only)
+  // Branch-free and never read here: every lane loads a table entry the row
+  // holds (a key past the prefix loads a dummy one, ignored when the loads
+  // are issued), so no wait for these loads lands before their use a stage
+  // later.
   auto load_slots = [&](int (&sl)[KPT], int kt) {
-    if (kt + BN <= plain_end) {
-#pragma unroll
-      for (int r = 0; r < KPT; ++r) sl[r] = trow[kt + r * NW * KPB];
-      return;
-    }
 #pragma unroll
     for (int r = 0; r < KPT; ++r) {
       const int j = min(kt + lkey(r), w.key_end - 1);  // keys past the end repeat the last one
-      sl[r] = j < w.ext_begin ? trow[j - lkey0] : -1;
+      sl[r] = trow[max(min(j, w.ext_begin - 1), 0) - lkey0];
     }
   };
   int bad_slot = 0;  // an out-of-range slot was met (reported once, at the end)
