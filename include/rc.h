@@ -70,6 +70,17 @@ typedef struct rc_shape {
   int32_t num_kv_heads;
   int32_t head_dim;
   int64_t pool_slots;   /* rows of k_pool / v_pool                              */
+  int32_t page_size;    /* 0 or 1: req_to_token holds one slot per position.   */
+                        /* A power of two up to 1024: the pool is made of pages */
+                        /* of page_size consecutive slots (pool_slots a        */
+                        /* multiple of it) and req_to_token holds one page id  */
+                        /* per page_size positions (its stride counts pages): */
+                        /* position p reads slot page(p / page_size) *         */
+                        /* page_size + p % page_size ("Prompt Caching"        */
+                        /* glossary, serving engines: paged KV blocks).        */
+                        /* Slot arguments (new_slots, rc_kv_store) stay per   */
+                        /* token.                                              */
+  int32_t reserved;     /* 0                                                    */
 } rc_shape;
 
 /* Bits OR-ed into the device error word. */

@@ -21,7 +21,8 @@ STATUS_NAMES = {0: "RC_OK", 1: "RC_ERR_ARG", 2: "RC_ERR_SHAPE", 3: "RC_ERR_DTYPE
 
 class RcShape(C.Structure):
     _fields_ = [("dtype", C.c_int32), ("num_q_heads", C.c_int32), ("num_kv_heads", C.c_int32),
-                ("head_dim", C.c_int32), ("pool_slots", C.c_int64)]
+                ("head_dim", C.c_int32), ("pool_slots", C.c_int64), ("page_size", C.c_int32),
+                ("reserved", C.c_int32)]
 
 
 class RcPlanInfo(C.Structure):

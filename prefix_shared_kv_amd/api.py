@@ -40,6 +40,7 @@ class KVShape:
     head_dim: int
     dtype: torch.dtype
     pool_slots: int
+    page_size: int = 1  # > 1: req_to_token holds page ids, one per page_size positions
 
     @property
     def group(self) -> int:
@@ -48,7 +49,8 @@ class KVShape:
     def c(self) -> RcShape:
         if self.dtype not in _DT:
             raise TypeError(f"dtype {self.dtype} not supported")
-        return RcShape(_DT[self.dtype], self.num_q_heads, self.num_kv_heads, self.head_dim, self.pool_slots)
+        return RcShape(_DT[self.dtype], self.num_q_heads, self.num_kv_heads, self.head_dim, self.pool_slots,
+                       self.page_size, 0)
 
 
 def _dev(t: torch.Tensor, name: str, dtype=None, shape=None):

@@ -55,8 +55,9 @@ struct Args {
   const void* v_pool;
   const int32_t* table;
   int32_t table_rows;
-  int64_t stride;
+  int64_t stride;      // table entries per row
   int64_t pool_slots;
+  int32_t page_shift;  // log2(page size): table entries are page ids when > 0
   int32_t Hq, Hkv, g;
   float scale_log2;  // sm_scale * log2(e)
   int32_t* err;
@@ -106,6 +107,13 @@ __device__ __forceinline__ void flag(int32_t* err, int32_t bit) {
   if (err) atomicOr(err, bit);
 }
 
+// Position p's slot from its table entry: one entry per position, or with
+// paging (shift > 0) one page id per 2^shift positions, a page's slots being
+// consecutive.  A page id outside the pool gives -1, an invalid slot.
+__device__ __forceinline__ int32_t page_slot(int32_t entry, int p, int shift, uint32_t n_pages) {
+  return (uint32_t)entry < n_pages ? (entry << shift) | (p & ((1 << shift) - 1)) : -1;
+}
+
 __device__ Work resolve(const Args& a, int mode, int L, bool leader) {
   Work w{};
   w.valid = false;
@@ -121,7 +129,7 @@ __device__ Work resolve(const Args& a, int mode, int L, bool leader) {
       return w;
     }
     if (E > a.max_extend && tile == 0 && w.hk == 0 && leader) flag(a.err, RC_DEVERR_LENGTH);
-    if ((int64_t)P > a.stride || (P > 0 && a.pool_slots < 1)) {
+    if ((int64_t)P > (a.stride << a.page_shift) || (P > 0 && a.pool_slots < 1)) {
       if (tile == 0 && leader) flag(a.err, RC_DEVERR_TABLE);
       return w;
     }
@@ -158,7 +166,8 @@ __device__ Work resolve(const Args& a, int mode, int L, bool leader) {
     w.split = it[3];
     w.moff = it[4];
     w.mcnt = it[5];
-    if (rep < 0 || rep >= a.table_rows || pb < 0 || pe < pb || (int64_t)pe > a.stride || a.pool_slots < 1 ||
+    if (rep < 0 || rep >= a.table_rows || pb < 0 || pe < pb || (int64_t)pe > (a.stride << a.page_shift) ||
+        a.pool_slots < 1 ||
         w.split < 0 || w.split >= a.max_splits ||
         w.moff < 0 || w.mcnt < 1 || w.mcnt * a.g > NCOL || w.moff + w.mcnt > n_members) {
       if (leader) flag(a.err, RC_DEVERR_PLAN);
@@ -320,7 +329,9 @@ __device__ __forceinline__ void attn_bf16_body(const Args& a, const int mode, co
   const char* vcol = (const char*)a.v_pool + coff;
   const char* kncol = (const char*)a.k_new + coff;
   const char* vncol = (const char*)a.v_new + coff;
-  const int32_t* trow = a.table + w.row * a.stride + lkey0;
+  const int32_t* trow = a.table + w.row * a.stride;
+  const int sh = a.page_shift;
+  const uint32_t npages = (uint32_t)(a.pool_slots >> sh);
   auto lkey = [&](int r) { return lkey0 + r * NW * KPB; };
   int32_t slot[2][KPT];
 
@@ -333,7 +344,7 @@ __device__ __forceinline__ void attn_bf16_body(const Args& a, const int mode, co
 #pragma unroll
     for (int r = 0; r < KPT; ++r) {
       const int j = min(kt + lkey(r), w.key_end - 1);  // keys past the end repeat the last one
-      sl[r] = trow[max(min(j, w.ext_begin - 1), 0) - lkey0];
+      sl[r] = trow[max(min(j, w.ext_begin - 1), 0) >> sh];  // raw entry: converted when issued
     }
   };
   int bad_slot = 0;  // an out-of-range slot was met (reported once, at the end)
@@ -354,13 +365,16 @@ __device__ __forceinline__ void attn_bf16_body(const Args& a, const int mode, co
   // so the tile holds finite values where p = 0 multiplies them.
   auto issue = [&](uint16_t* dk, uint16_t* dv, const int (&sl)[KPT], int kt) {
     if (kt + BN <= plain_end) {  // every key of the stage is a cached prefix key
-      uint32_t mx = 0;
+      uint32_t s[KPT], mx = 0;
 #pragma unroll
-      for (int r = 0; r < KPT; ++r) mx = max(mx, (uint32_t)sl[r]);
+      for (int r = 0; r < KPT; ++r) {
+        s[r] = (uint32_t)page_slot(sl[r], kt + lkey(r), sh, npages);
+        mx = max(mx, s[r]);
+      }
       bad_slot |= mx >= nslots;
 #pragma unroll
       for (int r = 0; r < KPT; ++r) {
-        const uint64_t off = (uint64_t)min((uint32_t)sl[r], nslots - 1) * row_bytes;
+        const uint64_t off = (uint64_t)min(s[r], nslots - 1) * row_bytes;
         const int blk = (NW * r + wave) * KPB * D;
         dma(kcol + off, dk + blk);
         dma(vcol + off, dv + blk);
@@ -373,8 +387,9 @@ __device__ __forceinline__ void attn_bf16_body(const Args& a, const int mode, co
       const int blk = (NW * r + wave) * KPB * D;
       const int j = min(kt + lkey(r), w.key_end - 1);
       const bool is_new = j >= w.ext_begin;
-      bad_slot |= !is_new && (uint32_t)sl[r] >= nslots;
-      const uint64_t idx = is_new ? (uint64_t)(w.ext_base + (j - w.ext_begin)) : (uint64_t)min((uint32_t)sl[r], nslots - 1);
+      const uint32_t sr = (uint32_t)page_slot(sl[r], j, sh, npages);
+      bad_slot |= !is_new && sr >= nslots;
+      const uint64_t idx = is_new ? (uint64_t)(w.ext_base + (j - w.ext_begin)) : (uint64_t)min(sr, nslots - 1);
       const uint64_t kb_ = is_new ? (uint64_t)kncol : (uint64_t)kcol;
       const uint64_t vb_ = is_new ? (uint64_t)vncol : (uint64_t)vcol;
       dma((const char*)(kb_ + idx * row_bytes), dk + blk);
@@ -598,7 +613,8 @@ __device__ __forceinline__ void attn_f32_body(const Args& a, const int mode) {
         kp = knew + off;
         vp = vnew + off;
       } else {
-        const int32_t s = a.table[w.row * a.stride + j];
+        const int32_t s = page_slot(a.table[w.row * a.stride + (j >> a.page_shift)], j, a.page_shift,
+                                    (uint32_t)(a.pool_slots >> a.page_shift));
         if (s < 0 || (int64_t)s >= a.pool_slots) {
           if (lane == 0) flag(a.err, RC_DEVERR_SLOT);
           continue;

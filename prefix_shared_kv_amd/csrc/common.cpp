@@ -31,6 +31,10 @@ rc_status check_shape(const rc_shape* s) {
     return fail(RC_ERR_SHAPE, "group size %d above 128", s->num_q_heads / s->num_kv_heads);
   if (s->head_dim != 64 && s->head_dim != 128) return fail(RC_ERR_SHAPE, "head_dim %d not in {64,128}", s->head_dim);
   if (s->pool_slots < 0 || s->pool_slots > INT32_MAX) return fail(RC_ERR_SHAPE, "pool_slots %lld out of range", (long long)s->pool_slots);
+  if (s->page_size < 0 || s->page_size > 1024 || (s->page_size & (s->page_size - 1)))
+    return fail(RC_ERR_SHAPE, "page_size %d is not 0, 1 or a power of two up to 1024", s->page_size);
+  if (s->page_size > 1 && s->pool_slots % s->page_size)
+    return fail(RC_ERR_SHAPE, "pool_slots %lld is not a multiple of page_size %d", (long long)s->pool_slots, s->page_size);
   return RC_OK;
 }
 

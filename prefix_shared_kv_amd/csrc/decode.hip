@@ -47,29 +47,34 @@ __device__ __forceinline__ void decode_narrow_body(const Args& a, const int unit
   const uint16_t* vbase = (const uint16_t*)a.v_pool + (int64_t)w.hk * D + lc * 8;
   const int64_t rowHD = (int64_t)a.Hkv * D;
   const int32_t* trow = a.table + w.row * a.stride;
+  const int sh = a.page_shift;
+  const uint32_t npages = (uint32_t)(a.pool_slots >> sh);
   int bad_slot = 0;
 
   constexpr int NEWTOK = INT_MIN + 1;  // the current token: read from k_new/v_new
+  // raw table entries, converted to slots when the stage's K/V are loaded
   auto load_slots = [&](int (&sl)[NI], int kt) {
 #pragma unroll
     for (int t = 0; t < NI; ++t) {
       const int key = kt + t * KPI + lk;
       // INT_MIN: past the range end
-      sl[t] = key < w.key_end ? (key >= w.ext_begin ? NEWTOK : trow[key]) : INT_MIN;
+      sl[t] = key < w.key_end ? (key >= w.ext_begin ? NEWTOK : trow[key >> sh]) : INT_MIN;
     }
   };
-  auto load_kv = [&](u32x4 (&kr)[NI], u32x4 (&vr)[NI], const int (&sl)[NI], bool partial) {
+  auto load_kv = [&](u32x4 (&kr)[NI], u32x4 (&vr)[NI], const int (&sl)[NI], int kt, bool partial) {
 #pragma unroll
     for (int t = 0; t < NI; ++t) {
-      const bool ok = (uint32_t)sl[t] < (uint32_t)a.pool_slots;
-      bad_slot |= !ok & (sl[t] != INT_MIN) & (sl[t] != NEWTOK);
-      const int64_t off = (int64_t)(ok ? sl[t] : 0) * rowHD;
+      const bool special = sl[t] == INT_MIN || sl[t] == NEWTOK;
+      const int32_t st = special ? sl[t] : page_slot(sl[t], kt + t * KPI + lk, sh, npages);
+      const bool ok = (uint32_t)st < (uint32_t)a.pool_slots;
+      bad_slot |= !ok & !special;
+      const int64_t off = (int64_t)(ok ? st : 0) * rowHD;
       kr[t] = *(const u32x4*)(kbase + off);
       vr[t] = *(const u32x4*)(vbase + off);
       if (partial && !ok) {  // keys past the end must hold finite values: p = 0 multiplies them
         kr[t] = u32x4{0, 0, 0, 0};
         vr[t] = u32x4{0, 0, 0, 0};
-        if (sl[t] == NEWTOK) {
+        if (st == NEWTOK) {
           const int64_t noff = ((int64_t)w.ext_base * a.Hkv + w.hk) * D + lc * 8;
           kr[t] = *(const u32x4*)((const uint16_t*)a.k_new + noff);
           vr[t] = *(const u32x4*)((const uint16_t*)a.v_new + noff);
@@ -158,7 +163,7 @@ __device__ __forceinline__ void decode_narrow_body(const Args& a, const int unit
   u32x4 kr[NI], vr[NI];
   if (n_st > 0) load_slots(slA, kb);
   if (n_st > 1) load_slots(slB, kb + BNN);
-  if (n_st > 0) load_kv(kr, vr, slA, kb + BNN > plain_end);
+  if (n_st > 0) load_kv(kr, vr, slA, kb, kb + BNN > plain_end);
   if (n_st > 2) load_slots(slA, kb + 2 * BNN);
   // The LDS tile is private to the wave and LDS operations of a wave complete
   // in order, so the next stage may overwrite it right after this stage's reads.
@@ -166,7 +171,7 @@ __device__ __forceinline__ void decode_narrow_body(const Args& a, const int unit
     int kt = kb + i * BNN;
     store(kr, vr);
     if (i + 1 < n_st) {
-      load_kv(kr, vr, slB, kt + 2 * BNN > plain_end);
+      load_kv(kr, vr, slB, kt + BNN, kt + 2 * BNN > plain_end);
       if (i + 3 < n_st) load_slots(slB, kt + 3 * BNN);
     }
     compute(kt);
@@ -174,7 +179,7 @@ __device__ __forceinline__ void decode_narrow_body(const Args& a, const int unit
     kt += BNN;
     store(kr, vr);
     if (i + 2 < n_st) {
-      load_kv(kr, vr, slA, kt + 2 * BNN > plain_end);
+      load_kv(kr, vr, slA, kt + BNN, kt + 2 * BNN > plain_end);
       if (i + 4 < n_st) load_slots(slA, kt + 3 * BNN);
     }
     compute(kt);
@@ -240,6 +245,8 @@ __device__ __forceinline__ void decode_rows_body(const Args& a, const int unit, 
   const uint16_t* kbase = (const uint16_t*)a.k_pool + (int64_t)hk0 * D + lh * D + lc * 8;
   const uint16_t* vbase = (const uint16_t*)a.v_pool + (int64_t)hk0 * D + lh * D + lc * 8;
   const int32_t* trow = a.table + w.row * a.stride;
+  const int sh = a.page_shift;
+  const uint32_t npages = (uint32_t)(a.pool_slots >> sh);
   int bad_slot = 0;
   int sl[2][NI];
   u32x4 kr[NI], vr[NI];
@@ -249,13 +256,13 @@ __device__ __forceinline__ void decode_rows_body(const Args& a, const int unit, 
 #pragma unroll
     for (int t = 0; t < NI; ++t) {
       const int j = kt + key_of(t);
-      s[t] = j < w.key_end ? trow[j] : INT_MIN;  // INT_MIN: past the range end
+      s[t] = j < w.key_end ? trow[j >> sh] : INT_MIN;  // INT_MIN: past the range end; raw entries
     }
   };
-  auto load_kv = [&](const int (&s)[NI], bool partial) {
+  auto load_kv = [&](const int (&s)[NI], int kt, bool partial) {
 #pragma unroll
     for (int t = 0; t < NI; ++t) {
-      const int32_t sv_ = s[t];
+      const int32_t sv_ = s[t] == INT_MIN ? INT_MIN : page_slot(s[t], kt + key_of(t), sh, npages);
       const bool ok = (uint32_t)sv_ < (uint32_t)a.pool_slots;
       bad_slot |= !ok & (sv_ != INT_MIN);
       const int64_t off = (int64_t)(ok ? sv_ : 0) * rowHD;
@@ -345,14 +352,14 @@ __device__ __forceinline__ void decode_rows_body(const Args& a, const int unit, 
   const int n_st = (w.key_end - kb + BNR - 1) / BNR;
   if (n_st > 0) load_slots(sl[0], kb);
   if (n_st > 1) load_slots(sl[1], kb + BNR);
-  if (n_st > 0) load_kv(sl[0], kb + BNR > w.key_end);
+  if (n_st > 0) load_kv(sl[0], kb, kb + BNR > w.key_end);
   auto step = [&](auto bufc, int i) {
     constexpr int b = decltype(bufc)::value;
     const int kt = kb + i * BNR;
     __syncthreads();  // the previous stage's reads are done
     store();
     __syncthreads();
-    if (i + 1 < n_st) load_kv(sl[b ^ 1], kt + 2 * BNR > w.key_end);
+    if (i + 1 < n_st) load_kv(sl[b ^ 1], kt + BNR, kt + 2 * BNR > w.key_end);
     if (i + 2 < n_st) load_slots(sl[b], kt + 2 * BNR);
     compute(kt);
   };
@@ -517,6 +524,7 @@ rc_status split_k_attention(const rc_shape* shape, void* o, const void* q, void*
   a.q = q; a.o = o; a.k_pool = k_pool; a.v_pool = v_pool;
   a.k_new = k_new; a.v_new = v_new; a.new_slots = new_slots;
   a.table = req_to_token; a.table_rows = table_rows; a.stride = stride; a.pool_slots = shape->pool_slots;
+  a.page_shift = shape->page_size > 1 ? __builtin_ctz((unsigned)shape->page_size) : 0;
   a.Hq = shape->num_q_heads; a.Hkv = shape->num_kv_heads; a.g = g;
   a.scale_log2 = sm_scale * LOG2E;
   a.err = error_word();

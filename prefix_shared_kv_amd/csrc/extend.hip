@@ -75,6 +75,7 @@ extern "C" rc_status rc_extend_attention(const rc_shape* shape, void* o, const v
   Args a{};
   a.q = q; a.o = o; a.k_new = k_new; a.v_new = v_new; a.k_pool = k_pool; a.v_pool = v_pool;
   a.table = req_to_token; a.table_rows = table_rows; a.stride = stride; a.pool_slots = shape->pool_slots;
+  a.page_shift = shape->page_size > 1 ? __builtin_ctz((unsigned)shape->page_size) : 0;
   a.Hq = shape->num_q_heads; a.Hkv = shape->num_kv_heads; a.g = g;
   a.scale_log2 = sm_scale * LOG2E;
   a.err = error_word();

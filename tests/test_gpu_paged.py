@@ -1,0 +1,185 @@
+"""GPU parity for a paged KV pool (page_size > 1): req_to_token holds page ids,
+one per page_size positions, pages drawn in shuffled order.  Every output must
+equal, bit for bit, the same call with the table expanded to one slot per
+position (page * page_size + offset: the same slots, so the same arithmetic),
+and the oracle within max-abs 2e-2 (bf16) / 1e-4 (fp32).  Page ids outside the
+pool are flagged and never dereferenced."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import attention as A
+from prefix_shared_kv_amd import KVShape, api
+from synth import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+DT = {"f32": torch.float32, "bf16": torch.bfloat16}
+HEADS = {"bf16": (32, 8, 128), "f32": (8, 2, 64)}
+
+
+def host(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def dev(a, gpu):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(gpu)
+
+
+def tables(g, lens, ps, n_pages, rows):
+    """Page table [R, max pages] and the equivalent per-position slot table [R, max pages * ps]."""
+    need = [(n + ps - 1) // ps for n in lens]
+    order = g.permutation(n_pages).astype(np.int32)
+    mp = max(need) + 1
+    pt = np.full((len(rows) + 2, mp), -1, np.int32)
+    st = np.full((len(rows) + 2, mp * ps), -1, np.int32)
+    used = 0
+    for b, k in enumerate(need):
+        pg = order[used:used + k]
+        used += k
+        pt[rows[b], :k] = pg
+        st[rows[b], :k * ps] = (pg[:, None] * ps + np.arange(ps)[None, :]).reshape(-1)
+    return pt, st
+
+
+def fill_pool(g, S, Hkv, D, dtype):
+    x = g.standard_normal((S, Hkv, D)).astype(np.float32)
+    return W.round_bf16(x) if dtype == "bf16" else x
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("ps", [4, 16, 64])
+def test_paged_extend_equals_expanded_table(gpu, dtype, ps):
+    g = np.random.default_rng(ps)
+    Hq, Hkv, D = HEADS[dtype]
+    P_list = [0, 1, 63, 64, 130, 300, 5]
+    E_list = [70, 1, 65, 0, 33, 129, 8]
+    B = len(P_list)
+    rows = (np.arange(B) + 1).astype(np.int32)
+    n_pages = sum((p + ps - 1) // ps for p in P_list) + 8
+    S = n_pages * ps
+    pool = fill_pool(g, S, Hkv, D, dtype), fill_pool(g, S, Hkv, D, dtype)
+    pt, st = tables(g, P_list, ps, n_pages, rows)
+    T = sum(E_list)
+    rnd = lambda *s: (W.round_bf16 if dtype == "bf16" else (lambda x: x))(g.standard_normal(s).astype(np.float32))
+    q, kn, vn = rnd(T, Hq, D), rnd(T, Hkv, D), rnd(T, Hkv, D)
+    start = np.concatenate([[0], np.cumsum(E_list)[:-1]]).astype(np.int32)
+    to = lambda a: torch.from_numpy(a).to(gpu).to(DT[dtype])
+    kp, vp = to(pool[0]), to(pool[1])
+    outs = []
+    for shape, tab in ((KVShape(Hq, Hkv, D, DT[dtype], S, ps), pt), (KVShape(Hq, Hkv, D, DT[dtype], S), st)):
+        o = torch.full((T, Hq, D), 7.0, device=gpu, dtype=DT[dtype])
+        err = torch.zeros(1, dtype=torch.int32, device=gpu)
+        api.set_error_word(err)
+        try:
+            api.extend_attention(shape, o, to(q), to(kn), to(vn), kp, vp, dev(tab, gpu), dev(np.array(P_list, np.int32), gpu),
+                                 dev(np.array(E_list, np.int32), gpu), dev(start, gpu), max(E_list), 1.0 / np.sqrt(D),
+                                 rows=dev(rows, gpu))
+            torch.cuda.synchronize()
+        finally:
+            api.set_error_word(None)
+        assert int(err.item()) == 0
+        outs.append(o)
+    assert torch.equal(outs[0], outs[1]), "paged table and expanded table give different bits"
+    got = host(outs[0])
+    for b in range(B):
+        E, P = E_list[b], P_list[b]
+        if E == 0:
+            continue
+        s0 = start[b]
+        slots = st[rows[b], :P]
+        K = np.concatenate([pool[0][slots], kn[s0:s0 + E]])
+        V = np.concatenate([pool[1][slots], vn[s0:s0 + E]])
+        want = A.extend(q[s0:s0 + E], K, V, P, 1.0 / np.sqrt(D))
+        e = float(np.max(np.abs(got[s0:s0 + E] - want)))
+        assert e <= TOL[dtype], f"request {b}: max abs error {e:.3e}"
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("ps", [4, 16, 64])
+def test_paged_decode_with_store_equals_expanded_table(gpu, dtype, ps):
+    g = np.random.default_rng(100 + ps)
+    Hq, Hkv, D = HEADS[dtype]
+    L = [1, 5, 64, 65, 130, 700, 2049, 33]  # context lengths, the current token included
+    B = len(L)
+    rows = (np.arange(B) + 1).astype(np.int32)
+    n_pages = sum((n + ps - 1) // ps for n in L) + 4
+    S = n_pages * ps
+    base = fill_pool(g, S, Hkv, D, dtype), fill_pool(g, S, Hkv, D, dtype)
+    pt, st = tables(g, L, ps, n_pages, rows)
+    rnd = lambda *s: (W.round_bf16 if dtype == "bf16" else (lambda x: x))(g.standard_normal(s).astype(np.float32))
+    q, kn, vn = rnd(B, Hq, D), rnd(B, Hkv, D), rnd(B, Hkv, D)
+    new_slots = np.array([st[rows[b], L[b] - 1] for b in range(B)], np.int32)
+    to = lambda a: torch.from_numpy(a).to(gpu).to(DT[dtype])
+    plan = api.plan_decode_unshared(L, Hq // Hkv, 256, rows=rows)
+    plan.to(gpu)
+    results = []
+    for shape, tab in ((KVShape(Hq, Hkv, D, DT[dtype], S, ps), pt), (KVShape(Hq, Hkv, D, DT[dtype], S), st)):
+        kp, vp = to(base[0]), to(base[1])
+        o = torch.empty(B, Hq, D, device=gpu, dtype=DT[dtype])
+        ws = torch.empty(api.decode_workspace_bytes(shape, plan), dtype=torch.uint8, device=gpu)
+        err = torch.zeros(1, dtype=torch.int32, device=gpu)
+        api.set_error_word(err)
+        try:
+            api.decode_attention(shape, o, to(q), kp, vp, dev(tab, gpu), dev(np.array(L, np.int32), gpu), plan,
+                                 1.0 / np.sqrt(D), ws, k_new=to(kn), v_new=to(vn), new_slots=dev(new_slots, gpu))
+            torch.cuda.synchronize()
+        finally:
+            api.set_error_word(None)
+        assert int(err.item()) == 0
+        results.append((o, kp, vp))
+    assert torch.equal(results[0][0], results[1][0]), "paged and expanded decode outputs differ"
+    assert torch.equal(results[0][1], results[1][1]) and torch.equal(results[0][2], results[1][2])
+    got = host(results[0][0])
+    pk, pv = base[0].copy(), base[1].copy()
+    pk[new_slots], pv[new_slots] = kn, vn
+    for b in range(B):
+        slots = st[rows[b], :L[b]]
+        want = A.decode(q[b], pk[slots], pv[slots], 1.0 / np.sqrt(D))
+        e = float(np.max(np.abs(got[b] - want)))
+        assert e <= TOL[dtype], f"request {b} (L={L[b]}): max abs error {e:.3e}"
+
+
+def test_page_ids_outside_the_pool_are_flagged(gpu):
+    ps, Hq, Hkv, D = 16, 8, 2, 128
+    n_pages = 8
+    S = n_pages * ps
+    shape = KVShape(Hq, Hkv, D, torch.bfloat16, S, ps)
+    kp = torch.randn(S, Hkv, D, device=gpu).to(torch.bfloat16)
+    vp = torch.randn(S, Hkv, D, device=gpu).to(torch.bfloat16)
+    tab = np.array([[0, 1, n_pages + 3, 2, -5]], np.int32)  # the third and fifth pages are invalid
+    L = [5 * ps]
+    plan = api.plan_decode_unshared(L, Hq // Hkv, 256)
+    plan.to(gpu)
+    o = torch.empty(1, Hq, D, device=gpu, dtype=torch.bfloat16)
+    ws = torch.empty(api.decode_workspace_bytes(shape, plan), dtype=torch.uint8, device=gpu)
+    err = torch.zeros(1, dtype=torch.int32, device=gpu)
+    api.set_error_word(err)
+    try:
+        api.decode_attention(shape, o, torch.randn(1, Hq, D, device=gpu).to(torch.bfloat16), kp, vp, dev(tab, gpu),
+                             dev(np.array(L, np.int32), gpu), plan, 0.1, ws)
+        q = torch.randn(8, Hq, D, device=gpu).to(torch.bfloat16)
+        kn = torch.randn(8, Hkv, D, device=gpu).to(torch.bfloat16)
+        ext_o = torch.empty_like(q)
+        api.extend_attention(shape, ext_o, q, kn, kn, kp, vp, dev(tab, gpu), dev(np.array([4 * ps], np.int32), gpu),
+                             dev(np.array([8], np.int32), gpu), dev(np.array([0], np.int32), gpu), 8, 0.1)
+        torch.cuda.synchronize()
+    finally:
+        api.set_error_word(None)
+    assert int(err.item()) & 1  # RC_DEVERR_SLOT
+
+
+def test_rejects_bad_page_sizes(gpu):
+    for ps, S in ((3, 96), (16, 100), (2048, 4096)):
+        shape = KVShape(8, 2, 128, torch.bfloat16, S, ps)
+        with pytest.raises(Exception):
+            api.extend_attention(shape, torch.empty(1, 8, 128, device=gpu, dtype=torch.bfloat16),
+                                 torch.empty(1, 8, 128, device=gpu, dtype=torch.bfloat16),
+                                 torch.empty(1, 2, 128, device=gpu, dtype=torch.bfloat16),
+                                 torch.empty(1, 2, 128, device=gpu, dtype=torch.bfloat16),
+                                 torch.empty(S, 2, 128, device=gpu, dtype=torch.bfloat16),
+                                 torch.empty(S, 2, 128, device=gpu, dtype=torch.bfloat16),
+                                 torch.zeros(1, 4, dtype=torch.int32, device=gpu), torch.zeros(1, dtype=torch.int32, device=gpu),
+                                 torch.ones(1, dtype=torch.int32, device=gpu), torch.zeros(1, dtype=torch.int32, device=gpu),
+                                 1, 0.1)
