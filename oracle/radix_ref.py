@@ -105,3 +105,80 @@ class RadixRef:
 
     def num_free(self) -> int:
         return len(self.free)
+
+
+class PagedRadixRef:
+    """The same bookkeeping at page granularity ("Prompt Caching" glossary, the
+    serving-engine paragraph: KV kept in fixed-size blocks, the blocks of the
+    longest matching prefix reused).  Readings where the pages are silent:
+      * only full pages are stored and shared: a prefix matches in whole pages,
+        the tokens of a partly matching page are computed again (the hit lost
+        at page boundaries);
+      * the cap keeps at least one token computed: at most (n - 1) // page_size
+        pages of an n-token request are reused;
+      * a request gets pages for its n + reserve tokens: the matched ones, then
+        fresh ones, first-in first-out, all or nothing in request order;
+      * inserting keeps the stored page where a page is already stored (first
+        writer wins) and frees the caller's, in ascending page order.
+    Like RadixRef it keeps no tree: stored sequences of full pages, each page a
+    tuple of token ids."""
+
+    def __init__(self, n_pages: int, page_size: int, free_order: Optional[Sequence[int]] = None):
+        self.ps = page_size
+        order = range(n_pages) if free_order is None else [int(x) for x in free_order]
+        self.free = deque(order)
+        self.seqs: List[Tuple[Tuple[Tuple[int, ...], ...], List[int]]] = []
+
+    def pages(self, tokens: Sequence[int]) -> Tuple[Tuple[int, ...], ...]:
+        t = [int(x) for x in tokens]
+        return tuple(tuple(t[i * self.ps:(i + 1) * self.ps]) for i in range(len(t) // self.ps))
+
+    def _longest(self, pg) -> Tuple[int, List[int]]:
+        best, ids = 0, []
+        for seq, pids in self.seqs:
+            m = _lcp(seq, pg)
+            if m > best:
+                best, ids = m, pids[:m]
+        return best, ids
+
+    def match(self, tokens: Sequence[int]) -> Tuple[int, List[int]]:
+        """(matched tokens, their page ids)."""
+        m, ids = self._longest(self.pages(tokens))
+        cap = (len(tokens) - 1) // self.ps if len(tokens) else 0
+        m = min(m, cap)
+        return m * self.ps, ids[:m]
+
+    def alloc(self, n: int) -> List[int]:
+        if n > len(self.free):
+            raise OutOfSlots(n)
+        return [self.free.popleft() for _ in range(n)]
+
+    def free_pages(self, pids: Sequence[int]) -> None:
+        self.free.extend(int(p) for p in pids)
+
+    def insert(self, tokens: Sequence[int], pids: Sequence[int]) -> Tuple[List[int], int]:
+        """Store the full pages of tokens with page ids pids[0 : len(tokens) // page_size].
+        Returns (the page ids now backing those pages, number of pages newly stored)."""
+        pg = self.pages(tokens)
+        pids = [int(p) for p in pids[:len(pg)]]
+        m, stored = self._longest(pg)
+        dups = [pids[i] for i in range(m) if pids[i] != stored[i]]
+        canon = stored[:m] + pids[m:]
+        self.free_pages(dups)
+        if m < len(pg):
+            self.seqs.append((pg, canon))
+        return canon, len(pg) - m
+
+    def emit_rows(self, batch: Sequence[Sequence[int]], reserve: int = 0):
+        """Rows of page ids [matched | fresh] per request.  Returns (rows, prefix_lens, extend_lens) in tokens."""
+        matches = [self.match(t) for t in batch]
+        npg = [(len(t) + reserve + self.ps - 1) // self.ps for t in batch]
+        need = sum(k - P // self.ps for k, (P, _) in zip(npg, matches))
+        if need > len(self.free):
+            raise OutOfSlots(need)
+        rows, plens, elens = [], [], []
+        for t, k, (P, ids) in zip(batch, npg, matches):
+            rows.append(list(ids) + self.alloc(k - P // self.ps))
+            plens.append(P)
+            elens.append(len(t) - P)
+        return rows, plens, elens
