@@ -244,6 +244,29 @@ typedef struct rc_radix_stats {
 /* free_order (host, nullable): the initial order in which slots are handed   */
 /* out, a permutation of [0, pool_slots); NULL means 0, 1, 2, ...            */
 rc_status rc_radix_create(int64_t pool_slots, const int32_t* free_order, rc_radix** out);
+
+/* A paged tree ("Prompt Caching" glossary, serving engines: KV kept in       */
+/* fixed-size blocks, the blocks of the longest matching prefix reused): the  */
+/* pool is n_pages pages of page_size (a power of two up to 1024) consecutive */
+/* slots, the same page size as rc_shape.page_size.  Every call below takes   */
+/* token ids as usual, but the tree stores, matches and shares whole pages:   */
+/* only the full pages of a sequence are inserted, a prefix matches in whole  */
+/* pages (a partly matching page is computed again), and "slots" are page ids */
+/* everywhere (alloc, free, evict, the rows of req_to_token, whose stride     */
+/* counts pages).  In detail:                                                 */
+/*   match      at most (n - 1) / page_size pages; *matched in tokens;        */
+/*              out_slots gets the matched page ids.                           */
+/*   insert     stores the n / page_size full pages; slots_inout holds their  */
+/*              page ids; n_new counts pages.                                  */
+/*   emit_rows  row b gets ceil((n_b + reserve) / page_size) page ids:        */
+/*              [matched pages | fresh pages]; prefix_lens = matched pages x  */
+/*              page_size, extend_lens = n_b - prefix_lens (tokens).          */
+/*   insert_rows, fork, lock: whole pages of the given tokens; lock's         */
+/*              *locked in tokens.                                             */
+/*   plan_decode, plan_extend: positions in tokens, as for unpaged trees.     */
+/*   stats      token counts are in pages.                                     */
+/* free_order (nullable) is a permutation of [0, n_pages).                     */
+rc_status rc_radix_create_paged(int64_t n_pages, int32_t page_size, const int32_t* free_order, rc_radix** out);
 void rc_radix_destroy(rc_radix* tree);
 
 /* Longest cached prefix of tokens[0..n), capped at n-1 (a request always     */

@@ -66,6 +66,7 @@ _SIGS = {
     "rc_extend_attention_shared": (i32, [C.POINTER(RcShape), P, P, P, P, P, i32, i64, P, i32, P,
                                          C.POINTER(RcPlanInfo), f32, P, i64, P]),
     "rc_radix_create": (i32, [i64, P, C.POINTER(P)]),
+    "rc_radix_create_paged": (i32, [i64, i32, P, C.POINTER(P)]),
     "rc_radix_destroy": (None, [P]),
     "rc_radix_match": (i32, [P, P, i64, P, I64P]),
     "rc_radix_alloc": (i32, [P, i64, P]),

@@ -305,13 +305,19 @@ def _lens(tb: TokenBatch, lengths) -> Optional[np.ndarray]:
 class RadixTree:
     """Host radix tree over token ids with the pool's slot allocator (rc_radix_*)."""
 
-    def __init__(self, pool_slots: int, free_order: Optional[np.ndarray] = None):
+    def __init__(self, pool_slots: int, free_order: Optional[np.ndarray] = None, page_size: int = 1):
+        """pool_slots: slots, or with page_size > 1 pages (of page_size slots) of the pool; the tree's
+        slots are then page ids and it stores and shares whole pages (rc_radix_create_paged)."""
         self._h = C.c_void_p()
         fo = None if free_order is None else np.ascontiguousarray(free_order, np.int32)
         if fo is not None and fo.size != pool_slots:
             raise ValueError("free_order must have pool_slots entries")
-        check(lib.rc_radix_create(pool_slots, _np_ptr(fo), C.byref(self._h)))
+        if page_size == 1:
+            check(lib.rc_radix_create(pool_slots, _np_ptr(fo), C.byref(self._h)))
+        else:
+            check(lib.rc_radix_create_paged(pool_slots, page_size, _np_ptr(fo), C.byref(self._h)))
         self.pool_slots = pool_slots
+        self.page_size = page_size
 
     def __del__(self):
         h = getattr(self, "_h", None)
@@ -320,11 +326,12 @@ class RadixTree:
             self._h = None
 
     def match(self, tokens) -> Tuple[int, np.ndarray]:
+        """(matched tokens, the matched slots, or page ids in a paged tree)."""
         t = np.ascontiguousarray(tokens, np.int32)
         out = np.zeros(max(t.size, 1), np.int32)
         m = C.c_int64()
         check(lib.rc_radix_match(self._h, _np_ptr(t), t.size, _np_ptr(out), C.byref(m)))
-        return m.value, out[:m.value].copy()
+        return m.value, out[:m.value // self.page_size].copy()
 
     def alloc(self, n: int) -> np.ndarray:
         out = np.zeros(max(n, 1), np.int32)
@@ -336,10 +343,12 @@ class RadixTree:
         check(lib.rc_radix_free(self._h, _np_ptr(s), s.size))
 
     def insert(self, tokens, slots) -> Tuple[np.ndarray, int]:
+        """Store tokens with their slots (paged tree: their len(tokens) // page_size full pages with
+        those pages' ids).  Returns (the slots now backing them, units newly stored)."""
         t = np.ascontiguousarray(tokens, np.int32)
         s = np.array(slots, np.int32, copy=True)
-        if s.size != t.size:
-            raise ValueError("tokens and slots differ in length")
+        if s.size != t.size // self.page_size:
+            raise ValueError("need one slot per token (one page id per full page in a paged tree)")
         n_new = C.c_int64()
         check(lib.rc_radix_insert(self._h, _np_ptr(t), _np_ptr(s), t.size, C.byref(n_new)))
         return s, n_new.value

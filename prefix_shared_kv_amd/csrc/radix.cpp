@@ -38,6 +38,41 @@ struct Node {
   bool alive = true;
 };
 
+// Pages of a paged tree as symbols: every distinct run of page_size token ids
+// gets a number, so the tree stores, matches and shares whole pages exactly as
+// it handles single tokens in an unpaged tree (its "slots" are then page ids).
+struct PageDict {
+  int32_t ps = 1;
+  std::vector<int32_t> arena;                 // tokens of symbol s at [s * ps, (s + 1) * ps)
+  std::unordered_map<uint64_t, int32_t> head;  // hash -> most recent symbol with that hash
+  std::vector<int32_t> next;                  // older symbol with the same hash, or -1
+
+  uint64_t hash(const int32_t* t) const {
+    uint64_t h = 1469598103934665603ull;
+    for (int32_t i = 0; i < ps; ++i) h = (h ^ (uint32_t)t[i]) * 1099511628211ull;
+    return h;
+  }
+  // the page's symbol, or -1 if it was never stored (read only: safe on several threads)
+  int32_t find(const int32_t* t) const {
+    auto it = head.find(hash(t));
+    if (it == head.end()) return -1;
+    for (int32_t s = it->second; s >= 0; s = next[s])
+      if (std::memcmp(arena.data() + (int64_t)s * ps, t, (size_t)ps * sizeof(int32_t)) == 0) return s;
+    return -1;
+  }
+  int32_t intern(const int32_t* t) {
+    int32_t s = find(t);
+    if (s >= 0) return s;
+    s = (int32_t)next.size();
+    const uint64_t h = hash(t);
+    auto it = head.find(h);
+    next.push_back(it == head.end() ? -1 : it->second);
+    head[h] = s;
+    arena.insert(arena.end(), t, t + ps);
+    return s;
+  }
+};
+
 }  // namespace
 
 struct rc_radix {
@@ -48,6 +83,8 @@ struct rc_radix {
   std::vector<uint8_t> in_tree;  // slot is owned by a tree node
   int64_t pool = 0;
   int64_t clock = 0;
+  int32_t page = 1;  // tokens per page; > 1: the tree's units are pages (symbols of PageDict)
+  PageDict dict;
   rc_radix_stats st{};
 };
 
@@ -130,6 +167,45 @@ bool rows_repeat(int32_t batch, const int32_t* rows) {
   std::vector<int32_t> v(rows, rows + batch);
   std::sort(v.begin(), v.end());
   return std::adjacent_find(v.begin(), v.end()) != v.end();
+}
+
+// A batch in the tree's units: the tokens themselves (unpaged tree), or the
+// symbols of each request's whole pages (paged tree: the first len(b) / page
+// tokens become len(b) / page symbols; a page never stored becomes -1, which
+// no edge starts with).  create: store unseen pages in the dictionary.
+struct Units {
+  const int32_t* data = nullptr;
+  const int64_t* off = nullptr;
+  std::vector<int32_t> sym;
+  std::vector<int64_t> own_off;
+  int64_t len(int32_t b) const { return off[b + 1] - off[b]; }
+  const int32_t* at(int32_t b) const { return data + off[b]; }
+};
+
+template <class LenF>
+Units units_of(rc_radix& t, int32_t batch, const int32_t* tokens, const int64_t* tok_off, LenF&& len, bool create) {
+  Units u;
+  if (t.page == 1 && batch > 0) {
+    // tokens as they are, each request cut to its first len(b)
+    bool whole = true;
+    for (int32_t b = 0; b < batch && whole; ++b) whole = len(b) == tok_off[b + 1] - tok_off[b];
+    if (whole) {
+      u.data = tokens;
+      u.off = tok_off;
+      return u;
+    }
+  }
+  u.own_off.assign(batch + 1, 0);
+  for (int32_t b = 0; b < batch; ++b) u.own_off[b + 1] = u.own_off[b] + len(b) / t.page;
+  u.sym.resize((size_t)u.own_off[batch]);
+  for (int32_t b = 0; b < batch; ++b) {
+    const int32_t* src = tokens ? tokens + tok_off[b] : nullptr;
+    for (int64_t i = 0; i < u.own_off[b + 1] - u.own_off[b]; ++i)
+      u.sym[u.own_off[b] + i] = t.page == 1 ? src[i] : create ? t.dict.intern(src + i * t.page) : t.dict.find(src + i * t.page);
+  }
+  u.data = u.sym.data();
+  u.off = u.own_off.data();
+  return u;
 }
 
 // f(b) for b in [0, n), on several host threads when the batch holds enough
@@ -261,20 +337,32 @@ rc_status rc_radix_create(int64_t pool_slots, const int32_t* free_order, rc_radi
   return RC_OK;
 }
 
+rc_status rc_radix_create_paged(int64_t n_pages, int32_t page_size, const int32_t* free_order, rc_radix** out) {
+  if (page_size < 1 || page_size > 1024 || (page_size & (page_size - 1)))
+    return fail(RC_ERR_ARG, "page_size %d is not a power of two up to 1024", page_size);
+  rc_status st = rc_radix_create(n_pages, free_order, out);
+  if (st != RC_OK) return st;
+  (*out)->page = page_size;
+  (*out)->dict.ps = page_size;
+  return RC_OK;
+}
+
 void rc_radix_destroy(rc_radix* tree) { delete tree; }
 
 rc_status rc_radix_match(rc_radix* t, const int32_t* tokens, int64_t n, int32_t* out_slots, int64_t* matched) {
   if (!t || !matched || n < 0 || (n > 0 && !tokens)) return fail(RC_ERR_ARG, "bad argument to rc_radix_match");
+  const int64_t off[2] = {0, n};
+  const Units u = units_of(*t, 1, tokens, off, [&](int32_t) { return n; }, false);
   std::vector<int32_t> touched;
   int64_t w = 0;
-  const int64_t cap = n > 0 ? n - 1 : 0;
-  walk(*t, tokens, n, [&](int32_t id, int64_t k) {
+  const int64_t cap = n > 0 ? (n - 1) / t->page : 0;  // at least one token is computed
+  walk(*t, u.at(0), u.len(0), [&](int32_t id, int64_t k) {
     touched.push_back(id);
     const Node& c = t->nodes[id];
     for (int64_t i = 0; i < k && w < cap; ++i, ++w)
       if (out_slots) out_slots[w] = c.slot[i];
   });
-  *matched = w;
+  *matched = w * t->page;
   int64_t now = ++t->clock;
   for (int32_t id : touched) t->nodes[id].last_use = now;
   t->st.matches++;
@@ -317,8 +405,8 @@ rc_status rc_radix_free(rc_radix* t, const int32_t* slots, int64_t n) {
   return RC_OK;
 }
 
-rc_status rc_radix_insert(rc_radix* t, const int32_t* tokens, int32_t* slots, int64_t n, int64_t* n_new) {
-  if (!t || n < 0 || (n > 0 && (!tokens || !slots))) return fail(RC_ERR_ARG, "bad argument to rc_radix_insert");
+// Insert n units (tokens, or page symbols) with their slots (or page ids).
+static rc_status insert_units(rc_radix* t, const int32_t* tokens, int32_t* slots, int64_t n, int64_t* n_new) {
   // pass 1 (read only): how much is stored already, and validate every slot
   std::vector<int32_t> stored;
   const int64_t m = walk(*t, tokens, n, [&](int32_t id, int64_t k) {
@@ -397,6 +485,18 @@ rc_status rc_radix_insert(rc_radix* t, const int32_t* tokens, int32_t* slots, in
   return RC_OK;
 }
 
+rc_status rc_radix_insert(rc_radix* t, const int32_t* tokens, int32_t* slots, int64_t n, int64_t* n_new) {
+  if (!t || n < 0 || (n > 0 && (!tokens || !slots))) return fail(RC_ERR_ARG, "bad argument to rc_radix_insert");
+  if (t->page == 1) return insert_units(t, tokens, slots, n, n_new);
+  try {
+    const int64_t off[2] = {0, n};
+    const Units u = units_of(*t, 1, tokens, off, [&](int32_t) { return n; }, true);  // whole pages only
+    return insert_units(t, u.at(0), slots, u.len(0), n_new);
+  } catch (const std::bad_alloc&) {
+    return fail(RC_ERR_NOMEM, "host allocation failed");
+  }
+}
+
 rc_status rc_radix_insert_rows(rc_radix* t, int32_t batch, const int32_t* tokens, const int64_t* tok_off,
                                const int64_t* tok_len, const int32_t* rows, int32_t* table, int32_t table_rows,
                                int64_t stride, int32_t* changed) {
@@ -407,13 +507,13 @@ rc_status rc_radix_insert_rows(rc_radix* t, int32_t batch, const int32_t* tokens
   for (int32_t b = 0; b < batch; ++b) {
     const int64_t n = len_of(b);
     if (rows[b] < 0 || rows[b] >= table_rows) return fail(RC_ERR_RANGE, "row %d of request %d outside [0, %d)", rows[b], b, table_rows);
-    if (n > stride) return fail(RC_ERR_RANGE, "request %d has %lld tokens, stride is %lld", b, (long long)n, (long long)stride);
+    if (n / t->page > stride) return fail(RC_ERR_RANGE, "request %d has %lld tokens, stride is %lld", b, (long long)n, (long long)stride);
   }
   std::vector<int32_t> before;
   for (int32_t b = 0; b < batch; ++b) {
-    const int64_t n = len_of(b);
+    const int64_t n = len_of(b), ne = n / t->page;  // table entries inserted: one per token, or per whole page
     int32_t* row = table + (int64_t)rows[b] * stride;
-    if (changed) before.assign(row, row + n);
+    if (changed) before.assign(row, row + ne);
     rc_status st = rc_radix_insert(t, tokens + tok_off[b], row, n, nullptr);
     if (st != RC_OK) return st;
     if (changed) changed[b] = !std::equal(before.begin(), before.end(), row);
@@ -428,6 +528,12 @@ rc_status rc_radix_emit_rows(rc_radix* t, int32_t batch, const int32_t* tokens, 
   if (!t || batch < 0 || reserve < 0 || stride <= 0 || table_rows < 0) return fail(RC_ERR_ARG, "bad argument to rc_radix_emit_rows");
   if (batch > 0 && (!tok_off || !rows || !table || !prefix_lens || !extend_lens)) return fail(RC_ERR_ARG, "NULL array in rc_radix_emit_rows");
   if (rc_status st = check_lens(batch, tok_off, nullptr); st != RC_OK) return st;
+  // In units of the tree: tokens, or pages.  Request b gets entries for its
+  // n + reserve tokens (ceil((n + reserve) / page) pages); at most (n - 1) /
+  // page units of its prefix are reused, so at least one token is computed.
+  const int64_t pg = t->page;
+  auto entries = [&](int32_t b) { return (tok_off[b + 1] - tok_off[b] + reserve + pg - 1) / pg; };
+  auto cap_of = [&](int32_t b) { const int64_t n = tok_off[b + 1] - tok_off[b]; return n > 0 ? (n - 1) / pg : 0; };
   // pass 1 (read only): matched length and the edges entered, per request
   struct Visit { int32_t node; int64_t k; };
   std::vector<int64_t> P(batch);
@@ -437,15 +543,15 @@ rc_status rc_radix_emit_rows(rc_radix* t, int32_t batch, const int32_t* tokens, 
     const int64_t n = tok_off[b + 1] - tok_off[b];
     if (n > 0 && !tokens) return fail(RC_ERR_ARG, "tokens is NULL");
     if (rows[b] < 0 || rows[b] >= table_rows) return fail(RC_ERR_RANGE, "row %d of request %d outside [0, %d)", rows[b], b, table_rows);
-    if (n + reserve > stride) return fail(RC_ERR_RANGE, "request %d needs %lld table entries, stride is %lld", b, (long long)(n + reserve), (long long)stride);
+    if (entries(b) > stride) return fail(RC_ERR_RANGE, "request %d needs %lld table entries, stride is %lld", b, (long long)entries(b), (long long)stride);
   }
+  const Units u = units_of(*t, batch, tokens, tok_off, [&](int32_t b) { return tok_off[b + 1] - tok_off[b]; }, false);
   const int64_t total = batch > 0 ? tok_off[batch] - tok_off[0] : 0;
   for_requests(batch, total, [&](int32_t b) {
-    const int64_t n = tok_off[b + 1] - tok_off[b];
-    const int64_t m = walk(*t, tokens + tok_off[b], n, [&](int32_t id, int64_t k) { visits[b].push_back({id, k}); });
-    P[b] = std::min(m, n > 0 ? n - 1 : 0);  // at least one token is always computed
+    const int64_t m = walk(*t, u.at(b), u.len(b), [&](int32_t id, int64_t k) { visits[b].push_back({id, k}); });
+    P[b] = std::min(m, cap_of(b));
   });
-  for (int32_t b = 0; b < batch; ++b) need += tok_off[b + 1] - tok_off[b] - P[b] + reserve;
+  for (int32_t b = 0; b < batch; ++b) need += entries(b) - P[b];
   if (rows_repeat(batch, rows)) return fail(RC_ERR_ARG, "two requests of the batch share a table row");
   const int64_t free0 = (int64_t)t->free_q.size();
   if (need > free0 && !evict)
@@ -483,14 +589,14 @@ rc_status rc_radix_emit_rows(rc_radix* t, int32_t batch, const int32_t* tokens, 
   for (int32_t b = 0; b < batch; ++b) {
     const int64_t n = tok_off[b + 1] - tok_off[b];
     int32_t* row = table + (int64_t)rows[b] * stride;
-    for (int64_t i = P[b]; i < n + reserve; ++i) {
+    for (int64_t i = P[b]; i < entries(b); ++i) {
       int32_t s = t->free_q.front();
       t->free_q.pop_front();
       t->is_free[s] = 0;
       row[i] = s;
     }
-    prefix_lens[b] = (int32_t)P[b];
-    extend_lens[b] = (int32_t)(n - P[b]);
+    prefix_lens[b] = (int32_t)(P[b] * pg);
+    extend_lens[b] = (int32_t)(n - P[b] * pg);
     t->st.matches++;
     t->st.matched_tokens += P[b];
   }
@@ -517,11 +623,12 @@ rc_status rc_radix_emit_rows(rc_radix* t, int32_t batch, const int32_t* tokens, 
 rc_status rc_radix_fork(rc_radix* t, const int32_t* tokens, const int32_t* parent_slots, int64_t n, int32_t n_children,
                         const int32_t* child_rows, int32_t* table, int32_t table_rows, int64_t stride) {
   if (!t || n < 0 || n_children < 0 || stride <= 0) return fail(RC_ERR_ARG, "bad argument to rc_radix_fork");
-  if (n > stride) return fail(RC_ERR_RANGE, "prefix of %lld tokens exceeds stride %lld", (long long)n, (long long)stride);
+  const int64_t ne = n / t->page;  // table entries shared: one per token, or per whole page
+  if (ne > stride) return fail(RC_ERR_RANGE, "prefix of %lld tokens exceeds stride %lld", (long long)n, (long long)stride);
   if (n_children > 0 && (!child_rows || !table)) return fail(RC_ERR_ARG, "NULL child rows or table");
   for (int32_t c = 0; c < n_children; ++c)
     if (child_rows[c] < 0 || child_rows[c] >= table_rows) return fail(RC_ERR_RANGE, "child row %d outside [0, %d)", child_rows[c], table_rows);
-  std::vector<int32_t> s(parent_slots, parent_slots + n);
+  std::vector<int32_t> s(parent_slots, parent_slots + ne);
   rc_status st = rc_radix_insert(t, tokens, s.data(), n, nullptr);
   if (st != RC_OK) return st;
   for (int32_t c = 0; c < n_children; ++c) std::copy(s.begin(), s.end(), table + (int64_t)child_rows[c] * stride);
@@ -541,15 +648,16 @@ rc_status rc_radix_lock(rc_radix* t, int32_t batch, const int32_t* tokens, const
   }
   std::vector<int32_t> end(batch, 0);
   std::vector<int64_t> m(batch, 0);
+  const Units u = units_of(*t, batch, tokens, tok_off, len_of, false);
   for_requests(batch, total, [&](int32_t b) {
     int32_t last = 0;
-    m[b] = walk(*t, tokens + tok_off[b], len_of(b), [&](int32_t id, int64_t) { last = id; });
+    m[b] = walk(*t, u.at(b), u.len(b), [&](int32_t id, int64_t) { last = id; });
     end[b] = last;
   });
   for (int32_t b = 0; b < batch; ++b) {
     pin(*t, end[b], +1);
     handles[b] = handle_of(*t, end[b]);
-    if (locked) locked[b] = m[b];
+    if (locked) locked[b] = m[b] * t->page;
   }
   return RC_OK;
 }
@@ -778,7 +886,7 @@ rc_status plan_from_walks(const rc_radix* t, int32_t n_mem, const std::vector<in
   for (auto& kv : by_node) {
     auto v = kv.second;
     std::sort(v.begin(), v.end());
-    int64_t prev = t->nodes[kv.first].start;
+    int64_t prev = t->nodes[kv.first].start * t->page;
     size_t i = 0;
     auto& out = subs[kv.first];
     while (i < v.size()) {
@@ -829,6 +937,7 @@ rc_status plan_from_walks(const rc_radix* t, int32_t n_mem, const std::vector<in
 
 // Walk request b's first len(b) tokens through the tree (several threads
 // for large batches).
+// Positions are in tokens: a paged tree walks whole pages, page tokens each.
 template <class LenF>
 void walk_requests(const rc_radix* t, int32_t batch, const int32_t* tokens, const int64_t* tok_off, LenF&& len,
                    std::vector<std::vector<Visit>>& walks, std::vector<int64_t>& walked) {
@@ -836,9 +945,11 @@ void walk_requests(const rc_radix* t, int32_t batch, const int32_t* tokens, cons
   walked.assign(batch, 0);
   int64_t total = 0;
   for (int32_t b = 0; b < batch; ++b) total += len(b);
+  const Units u = units_of(const_cast<rc_radix&>(*t), batch, tokens, tok_off, len, false);  // reads only
+  const int64_t pg = t->page;
   for_requests(batch, total, [&](int32_t b) {
-    walked[b] = walk(*t, tokens + tok_off[b], len(b), [&](int32_t id, int64_t k) {
-      walks[b].push_back({id, t->nodes[id].start + k});
+    walked[b] = pg * walk(*t, u.at(b), u.len(b), [&](int32_t id, int64_t k) {
+      walks[b].push_back({id, (t->nodes[id].start + k) * pg});
     });
   });
 }
