@@ -48,7 +48,7 @@ def test_paged_tree_matches_the_model(sc):
     n_pages = 48
     order = np.random.default_rng(ps).permutation(n_pages).astype(np.int32) if perm else None
     tree, ref = RadixTree(n_pages, order, page_size=ps), PagedRadixRef(n_pages, ps, order)
-    table = np.full((3, 16), -1, np.int32)
+    table = np.full((3, 64), -1, np.int32)  # wide enough for any request of the stream
     running = []  # (tokens, model rows, committed)
     for op in ops:
         if op[0] == "batch":
