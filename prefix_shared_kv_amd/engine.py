@@ -75,8 +75,15 @@ class Engine:
         S, H, D = shape.pool_slots, shape.num_kv_heads, shape.head_dim
         self.k_pool = k_pool if k_pool is not None else torch.zeros((S, H, D), dtype=shape.dtype, device=self.device)
         self.v_pool = v_pool if v_pool is not None else torch.zeros((S, H, D), dtype=shape.dtype, device=self.device)
-        self.tree = RadixTree(S, free_order)
-        self.stride = stride
+        # Paged pool (shape.page_size > 1): the tree hands out and shares whole
+        # pages, table rows hold page ids, and a position's slot is its page's
+        # first slot plus its offset in the page.  free_order is then over pages.
+        self.ps = shape.page_size
+        if S % self.ps:
+            raise ValueError("pool_slots must be a multiple of page_size")
+        self.tree = RadixTree(S // self.ps, free_order, page_size=self.ps)
+        self.stride = stride                     # most positions a row describes
+        self.width = -(-stride // self.ps)       # table entries per row
         # Rows are handed out oldest-free first.  With about two batches' worth
         # of rows, a batch never waits for rows whose upload is still queued
         # behind the GPU work of the batch before it.  (Row uploads stay on the
@@ -87,12 +94,12 @@ class Engine:
         # reaches it, so a row is rewritten on the host only after the last
         # upload that covered it has completed: each row remembers the number
         # of that upload, and the uploads' events complete in stream order.
-        self._table_pin = torch.full((max_rows, stride), -1, dtype=torch.int32, pin_memory=True)
+        self._table_pin = torch.full((max_rows, self.width), -1, dtype=torch.int32, pin_memory=True)
         self.table_h = self._table_pin.numpy()
         self._row_upload = np.zeros(max_rows, np.int64)  # number of the last upload reading each row
         self._uploads = collections.deque()              # (number, event) of uploads not known complete
         self._n_uploads = 0
-        self.table_d = torch.full((max_rows, stride), -1, dtype=torch.int32, device=self.device)
+        self.table_d = torch.full((max_rows, self.width), -1, dtype=torch.int32, device=self.device)
         self.free_rows = list(range(max_rows))
 
     # -- helpers ------------------------------------------------------------
@@ -167,6 +174,12 @@ class Engine:
         while self._uploads and self._uploads[0][1].query():
             self._uploads.popleft()
 
+    def slots_at(self, rows: np.ndarray, pos: np.ndarray) -> np.ndarray:
+        """Slots of positions pos in table rows rows (arrays of one shape)."""
+        if self.ps == 1:
+            return self.table_h[rows, pos]
+        return self.table_h[rows, pos // self.ps] * self.ps + pos % self.ps
+
     # -- cache population (a sequence whose K/V are already known) -----------
     def populate(self, tokens: Sequence[int], k: torch.Tensor, v: torch.Tensor, expect_cached: Optional[int] = None) -> int:
         """Store K/V for the uncached tail of `tokens` and insert the sequence.
@@ -181,13 +194,21 @@ class Engine:
             n_new = len(t) - m
             if k.shape[0] != n_new or v.shape[0] != n_new:
                 raise ValueError(f"need K/V for {n_new} uncached tokens, got {k.shape[0]}")
-            short = n_new - self.tree.stats()["free_slots"]
+            ps = self.ps
+            units = -(-len(t) // ps) - m // ps  # fresh slots, or pages
+            short = units - self.tree.stats()["free_slots"]
             if short > 0:
                 self.tree.evict(short)
-            new = self.tree.alloc(n_new)
+            new = self.tree.alloc(units)
             if n_new:
-                api.kv_store(self.shape, self.k_pool, self.v_pool, k, v, self._i32(new))
-            self.tree.insert(t, np.concatenate([pre, new]).astype(np.int32))
+                pos = np.arange(m, len(t))
+                ids = np.concatenate([pre, new]).astype(np.int64)
+                slots = ids[pos // ps] * ps + pos % ps
+                api.kv_store(self.shape, self.k_pool, self.v_pool, k, v, self._i32(slots.astype(np.int32)))
+            ids = np.concatenate([pre, new]).astype(np.int32)
+            self.tree.insert(t, ids[:len(t) // ps])
+            if len(t) % ps:  # a partial last page is not cached
+                self.tree.free(ids[len(t) // ps:])
         finally:
             self.tree.unlock(h)
         return m
@@ -215,8 +236,8 @@ class Engine:
         return b
 
     def new_token_slots(self, b: Batch) -> np.ndarray:
-        return np.concatenate([self.table_h[r, p:p + e] for r, p, e in zip(b.rows, b.prefix_lens, b.extend_lens)]
-                              ).astype(np.int32)
+        pos = [np.arange(p, p + e) for p, e in zip(b.prefix_lens, b.extend_lens)]
+        return np.concatenate([self.slots_at(np.full(len(x), r), x) for r, x in zip(b.rows, pos)]).astype(np.int32)
 
     def extend(self, b: Batch, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, sm_scale: float,
                o: Optional[torch.Tensor] = None, store: bool = True, cascade: bool = False,
@@ -254,7 +275,7 @@ class Engine:
         # The insert works on a copy of the batch's rows (the table's rows may
         # still be uploading); only rows the tree rewrote are written back.
         n = b.tb.lens() if lengths is None else np.asarray(lengths, np.int64)
-        width = max(int(n.max()) if b.size else 0, 1)
+        width = max(-(-int(n.max()) // self.ps) if b.size else 0, 1)
         work = np.ascontiguousarray(self.table_h[b.rows, :width])
         changed = self.tree.insert_rows(b.tb, work, np.arange(b.size, dtype=np.int32), lengths)
         if b.locks is not None:  # pin what is stored now, then drop the old pins
@@ -284,7 +305,7 @@ class Engine:
         plan.to(self.device, uploader=self._h2d)
         steps = np.arange(n_steps, dtype=np.int32)[:, None]
         pos = base[None, :] + steps                                    # [T, B]
-        slots = self.table_h[b.rows[None, :].repeat(n_steps, 0), pos]  # [T, B]
+        slots = self.slots_at(b.rows[None, :].repeat(n_steps, 0), pos)  # [T, B]
         seq = pos + 1
         ws = torch.empty(api.decode_workspace_bytes(self.shape, plan), dtype=torch.uint8, device=self.device)
         return DecodeState(plan, base, n_steps, self._i32(slots), self._i32(seq), ws)
@@ -312,7 +333,9 @@ class Engine:
             b.locks = None
         lens = b.tb.lens()
         keep = lens if keep is None else np.asarray(keep, np.int64)
-        tails = [self.table_h[r, k:n + b.reserve] for r, k, n in zip(b.rows, keep, lens)]
+        # entries past the kept tokens' whole units (tokens, or full pages) are the request's own
+        ps = self.ps
+        tails = [self.table_h[r, k // ps:-(-(n + b.reserve) // ps)] for r, k, n in zip(b.rows, keep, lens)]
         if tails:
             self.tree.free(np.concatenate(tails))
         # the rows' entries are left as they are: the next schedule rewrites

@@ -183,3 +183,120 @@ def test_rejects_bad_page_sizes(gpu):
                                  torch.zeros(1, 4, dtype=torch.int32, device=gpu), torch.zeros(1, dtype=torch.int32, device=gpu),
                                  torch.ones(1, dtype=torch.int32, device=gpu), torch.zeros(1, dtype=torch.int32, device=gpu),
                                  1, 0.1)
+
+
+# ------------------------------------------------------------- paged workloads
+from prefix_shared_kv_amd.engine import Engine  # noqa: E402
+from synth import drive  # noqa: E402
+
+
+def _path_kv(w, nid):
+    ids = []
+    while nid >= 0:
+        ids.append(nid)
+        nid = w.nodes[nid].parent
+    kv = [w.node_kv(i) for i in reversed(ids)]
+    return np.concatenate([k for k, _ in kv]), np.concatenate([v for _, v in kv])
+
+
+def _queries(w, start, own_q, P, tag):
+    """Query rows for positions [P, start + len(own_q)): keyed draws for the recomputed
+    tail of the prefix's last partial page, then the workload's own."""
+    extra = W.keyed_q(w.seed, w.shape, start - P, 777, tag) if start > P else own_q[:0]
+    return np.concatenate([extra, own_q])
+
+
+def _run_paged(gpu, w, ps, cascade=False, n_steps=None):
+    tol = TOL[w.shape.dtype]
+    S = (-(-w.pool_slots // ps) + 8 + len(w.requests) + 2 * len(w.nodes)) * ps
+    shape = KVShape(w.shape.num_q_heads, w.shape.num_kv_heads, w.shape.head_dim, DT[w.shape.dtype], S, ps)
+    longest = max(len(w.prompt_tokens(r)) + r.n_decode + 1 for r in w.requests)
+    longest = max([longest] + [w.node_start(n) + len(w.nodes[n].tokens) + 1 for n in range(len(w.nodes))])
+    eng = Engine(shape, longest + ps, len(w.requests) + len(w.prefill_nodes) + 2, gpu,
+                 free_order=np.random.default_rng(ps).permutation(S // ps).astype(np.int32))
+    up = lambda x: drive.up(x, w, gpu)
+    worst = 0.0
+    # cached nodes: prefill nodes through the extend, the rest stored directly
+    for nid in drive.node_order(w):
+        toks = drive.path_tokens(w, nid)
+        K, V = _path_kv(w, nid)
+        start = w.node_start(nid)
+        if nid in w.prefill_nodes:
+            b = eng.schedule([toks])
+            P = int(b.prefix_lens[0])
+            assert P % ps == 0 and P <= start
+            q = _queries(w, start, w.node_prefill_q(nid), P, nid)
+            o = host(eng.extend(b, up(q), up(K[P:]), up(V[P:]), w.sm_scale))
+            want = A.extend(q, K, V, P, w.sm_scale)
+            e = float(np.max(np.abs(o - want)))
+            assert e <= tol, f"prefill node {nid} (P={P}): max abs error {e:.3e}"
+            worst = max(worst, e)
+            eng.commit(b)
+            eng.release(b)
+        else:
+            m, _ = eng.tree.match(np.concatenate([toks, [-1]]).astype(np.int32))
+            assert m % ps == 0 and m <= start
+            eng.populate(toks, up(K[m:]), up(V[m:]), expect_cached=m)
+    # the requests: prompts extended over their page-rounded cached prefixes
+    reqs = w.requests
+    reserve = max(r.n_decode for r in reqs)
+    b = eng.schedule([w.prompt_tokens(r) for r in reqs], reserve=reserve)
+    P = b.prefix_lens
+    assert all(p % ps == 0 and p <= len(w.prefix_tokens(r)) for p, r in zip(P, reqs))
+    qs, ks, vs, ctx = [], [], [], []
+    for i, r in enumerate(reqs):
+        K, V = w.context_kv(i, 0)
+        pl = len(w.prefix_tokens(r))
+        own_q = w.ext_qkv(i)[0]
+        qs.append(_queries(w, pl, own_q, int(P[i]), 10000 + i))
+        ks.append(K[P[i]:])
+        vs.append(V[P[i]:])
+        ctx.append((K, V))
+    o = host(eng.extend(b, up(np.concatenate(qs)), up(np.concatenate(ks)), up(np.concatenate(vs)), w.sm_scale,
+                        cascade=cascade))
+    s = 0
+    for i in range(len(reqs)):
+        want = A.extend(qs[i], ctx[i][0], ctx[i][1], int(P[i]), w.sm_scale)
+        e = float(np.max(np.abs(o[s:s + len(qs[i])] - want)))
+        assert e <= tol, f"request {i} (P={P[i]}): max abs error {e:.3e}"
+        worst = max(worst, e)
+        s += len(qs[i])
+    eng.commit(b)
+    n_steps = reserve if n_steps is None else n_steps
+    if n_steps:
+        base = [len(w.prompt_tokens(r)) for r in reqs]
+        st = eng.prepare_decode(b, base, n_steps, chunk=256)
+        rids = list(range(len(reqs)))
+        for t in range(n_steps):
+            q, k, v = drive.decode_inputs(w, rids, t, device=gpu)
+            od = host(eng.decode_step(st, t, q, k, v, w.sm_scale))
+            sl = st.slots[t].long()
+            assert torch.equal(eng.k_pool[sl], k) and torch.equal(eng.v_pool[sl], v)
+            for j in rids:
+                K, V = w.context_kv(j, t + 1)
+                want = A.decode(w.dec_qkv(j, t)[0], K, V, w.sm_scale)
+                e = float(np.max(np.abs(od[j] - want)))
+                assert e <= tol, f"decode step {t} request {j}: max abs error {e:.3e}"
+                worst = max(worst, e)
+    eng.release(b)
+    return eng, b, worst
+
+
+@pytest.mark.parametrize("ps", [16, 64])
+def test_paged_gpt2_system_prompt(gpu, ps):
+    # 16-token pages: 25 whole pages of the 409-token prompt are shared; each
+    # branch recomputes the prompt's last 9 tokens with its own (17 of 417 and
+    # 16 of 416 computed, against 8 and 7 at one token per slot)
+    w = W.gpt2_system_prompt()
+    eng, b, _ = _run_paged(gpu, w, ps, n_steps=8)
+    full = (409 // ps) * ps
+    assert b.prefix_lens.tolist() == [full, full]
+    assert b.extend_lens.tolist() == [417 - full, 416 - full]
+
+
+@pytest.mark.parametrize("dtype,ps,cascade", [("bf16", 4, False), ("bf16", 16, True), ("f32", 16, False)])
+def test_paged_small_tree(gpu, dtype, ps, cascade):
+    w = W.multi_turn_tree(depth=3, fanout=3, seg_lo=5, seg_hi=90, ext=9, n_decode=3)
+    if dtype == "f32":
+        w.shape.dtype = "f32"
+    _run_paged(gpu, w, ps, cascade=cascade)
