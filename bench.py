@@ -130,6 +130,8 @@ def parse():
                     help="classify_heavy: label branches on the extend tiles instead of the shared-prefix plan")
     ap.add_argument("--decode-rows", type=int, default=0, help="narrow decode by groups of four kv heads (rc_set_tuning)")
     ap.add_argument("--host-phases", action="store_true", help="report host wall time per phase of the last step")
+    ap.add_argument("--page-size", type=int, default=1,
+                    help="classify_heavy: KV pool pages of this many positions (the table then holds page ids)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run kv_store into contiguous slots (a plain copy of known size) and print its bytes; "
                          "the scale for rocprofv3 FETCH_SIZE / WRITE_SIZE readings")
@@ -241,8 +243,12 @@ def bench_classify_heavy(args):
     # finds the pool short and evicts the least recently used unpinned nodes:
     # the previous step's branches and document (the decode contexts are
     # pinned by the batch that reads them).
-    pool = cached + (len(doc) + n_lab) + B * T + 1024
-    kvs = pk.KVShape(Hq, Hkv, D, torch.bfloat16, pool)
+    # With pages, every request also owns a partial page (a branch's label
+    # tokens, the decode steps' tokens), so each needs up to a page more.
+    ps = args.page_size
+    pool = cached + (len(doc) + n_lab) + B * T + 1024 + (len(labels) + B) * (ps - 1)
+    pool = -(-pool // ps) * ps
+    kvs = pk.KVShape(Hq, Hkv, D, torch.bfloat16, pool, ps)
     base = np.array([len(wh.prompt_tokens(r)) for r in wh.requests], np.int32)
     stride = int(base.max()) + T + 8
     # Table rows for two steps' batches: rows are handed out oldest-free first,
@@ -351,10 +357,10 @@ def bench_classify_heavy(args):
                         "1024 decode requests over 8192-token contexts (4096 shared per group of 16), 8 decode steps",
             "document_tokens": L, "branches": len(labels), "label_tokens": n_lab,
             "decode_batch": B, "decode_steps": T, "cached_positions": cached, "decode_chunk": args.chunk,
-            "tokens_per_step": tokens_per_step, "pool_slots": pool,
+            "tokens_per_step": tokens_per_step, "pool_slots": pool, "page_size": ps,
         },
         "cache": {"evicted_tokens_per_step": round(evicted / n_total, 1)},
-        "roofline": roofline("classify_heavy", dec_name, dec_bytes, dec_ms),
+        "roofline": roofline("classify_heavy" if ps == 1 else f"classify_heavy_page{ps}", dec_name, dec_bytes, dec_ms),
         "extend": {
             "prefill": extend_report("extend_bf16_d128@prefill", pre_flops, pre_ms, L),
             "branches": extend_report(br_name, br_flops, br_ms, n_lab),
@@ -598,6 +604,9 @@ def main():
     if args.copy_calibration:
         copy_calibration()
         return
+    if args.page_size != 1 and args.workload != "classify_heavy":
+        print("--page-size applies to the classify_heavy workload", file=sys.stderr)
+        sys.exit(2)
     res = bench_classify_heavy(args) if args.workload == "classify_heavy" else bench_multi_turn_tree(args)
     print(json.dumps(res))
 

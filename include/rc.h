@@ -239,6 +239,8 @@ typedef struct rc_radix_stats {
   int64_t evicted_tokens;  /* tokens removed by LRU eviction                   */
   int64_t evicted_nodes;
   int64_t locked_tokens;   /* tokens in nodes pinned by at least one lock       */
+  int64_t page_symbols;    /* paged tree: distinct page contents it holds (each */
+                           /* freed with its last holder); 0 when unpaged       */
 } rc_radix_stats;
 
 /* free_order (host, nullable): the initial order in which slots are handed   */

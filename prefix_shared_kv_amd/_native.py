@@ -34,7 +34,7 @@ class RcPlanInfo(C.Structure):
 class RcRadixStats(C.Structure):
     _fields_ = [(n, C.c_int64) for n in ("nodes", "cached_tokens", "free_slots", "pool_slots", "splits", "matches",
                                          "matched_tokens", "inserted_tokens", "duplicate_slots", "evicted_tokens",
-                                         "evicted_nodes", "locked_tokens")]
+                                         "evicted_nodes", "locked_tokens", "page_symbols")]
 
 
 class RcProfEntry(C.Structure):

@@ -39,37 +39,100 @@ struct Node {
 };
 
 // Pages of a paged tree as symbols: every distinct run of page_size token ids
-// gets a number, so the tree stores, matches and shares whole pages exactly as
-// it handles single tokens in an unpaged tree (its "slots" are then page ids).
+// held by the tree gets a number, so the tree stores, matches and shares whole
+// pages exactly as it handles single tokens in an unpaged tree (its "slots"
+// are then page ids).  A symbol lives while some tree edge holds it: refs
+// counts those edge positions, and a symbol whose count drops to zero (its
+// last holder evicted) is removed and its number reused.
 struct PageDict {
   int32_t ps = 1;
   std::vector<int32_t> arena;                 // tokens of symbol s at [s * ps, (s + 1) * ps)
   std::unordered_map<uint64_t, int32_t> head;  // hash -> most recent symbol with that hash
   std::vector<int32_t> next;                  // older symbol with the same hash, or -1
+  std::vector<int32_t> refs;                  // tree edge positions holding the symbol
+  std::vector<int32_t> spare;                 // numbers of removed symbols
+  int64_t live = 0;
 
+  // four independent multiply-xor chains over the page, then one mix; lookups
+  // compare the tokens themselves, so the hash only spreads the buckets
   uint64_t hash(const int32_t* t) const {
-    uint64_t h = 1469598103934665603ull;
-    for (int32_t i = 0; i < ps; ++i) h = (h ^ (uint32_t)t[i]) * 1099511628211ull;
-    return h;
+    constexpr uint64_t K = 0x9E3779B97F4A7C15ull;
+    uint64_t a = 1, b = 2, c = 3, d = 4;
+    int32_t i = 0;
+    for (; i + 4 <= ps; i += 4) {
+      a = (a ^ (uint32_t)t[i]) * K;
+      b = (b ^ (uint32_t)t[i + 1]) * K;
+      c = (c ^ (uint32_t)t[i + 2]) * K;
+      d = (d ^ (uint32_t)t[i + 3]) * K;
+    }
+    for (; i < ps; ++i) a = (a ^ (uint32_t)t[i]) * K;
+    uint64_t h = a ^ (b << 16 | b >> 48) ^ (c << 32 | c >> 32) ^ (d << 48 | d >> 16);
+    return (h ^ (h >> 29)) * K;
   }
-  // the page's symbol, or -1 if it was never stored (read only: safe on several threads)
+  bool same(int32_t s, const int32_t* t) const {
+    return std::memcmp(arena.data() + (int64_t)s * ps, t, (size_t)ps * sizeof(int32_t)) == 0;
+  }
+  // the page's symbol, or -1 if the tree holds no such page (read only: safe on several threads)
   int32_t find(const int32_t* t) const {
     auto it = head.find(hash(t));
     if (it == head.end()) return -1;
     for (int32_t s = it->second; s >= 0; s = next[s])
-      if (std::memcmp(arena.data() + (int64_t)s * ps, t, (size_t)ps * sizeof(int32_t)) == 0) return s;
+      if (same(s, t)) return s;
     return -1;
   }
-  int32_t intern(const int32_t* t) {
+  // the page's symbol, added (with no holders yet) if new; *fresh says which
+  int32_t intern(const int32_t* t, bool* fresh) {
     int32_t s = find(t);
+    *fresh = s < 0;
     if (s >= 0) return s;
-    s = (int32_t)next.size();
-    const uint64_t h = hash(t);
-    auto it = head.find(h);
-    next.push_back(it == head.end() ? -1 : it->second);
-    head[h] = s;
-    arena.insert(arena.end(), t, t + ps);
+    // every allocation first, so that a failure changes nothing
+    const bool reuse = !spare.empty();
+    if (!reuse) {
+      grow(arena, arena.size() + ps);
+      grow(next, next.size() + 1);
+      grow(refs, refs.size() + 1);
+      grow(spare, next.size() + 1);
+    }
+    s = reuse ? spare.back() : (int32_t)next.size();
+    auto [it, added] = head.try_emplace(hash(t), s);
+    const int32_t older = added ? -1 : it->second;
+    it->second = s;
+    if (reuse) {
+      spare.pop_back();
+      std::memcpy(arena.data() + (int64_t)s * ps, t, (size_t)ps * sizeof(int32_t));
+      next[s] = older;
+      refs[s] = 0;
+    } else {
+      arena.insert(arena.end(), t, t + ps);
+      next.push_back(older);
+      refs.push_back(0);
+    }
+    ++live;
     return s;
+  }
+  // capacity for at least `need` elements, growing geometrically
+  static void grow(std::vector<int32_t>& v, size_t need) {
+    if (v.capacity() < need) v.reserve(std::max(need, 2 * v.capacity()));
+  }
+  void remove(int32_t s) {
+    auto it = head.find(hash(arena.data() + (int64_t)s * ps));
+    if (it->second == s) {
+      if (next[s] < 0)
+        head.erase(it);
+      else
+        it->second = next[s];
+    } else {
+      int32_t p = it->second;
+      while (next[p] != s) p = next[p];
+      next[p] = next[s];
+    }
+    next[s] = -1;
+    spare.push_back(s);  // capacity reserved when s was added
+    --live;
+  }
+  void acquire(int32_t s) { ++refs[s]; }
+  void release(int32_t s) {
+    if (--refs[s] == 0) remove(s);
   }
 };
 
@@ -169,44 +232,18 @@ bool rows_repeat(int32_t batch, const int32_t* rows) {
   return std::adjacent_find(v.begin(), v.end()) != v.end();
 }
 
-// A batch in the tree's units: the tokens themselves (unpaged tree), or the
-// symbols of each request's whole pages (paged tree: the first len(b) / page
-// tokens become len(b) / page symbols; a page never stored becomes -1, which
-// no edge starts with).  create: store unseen pages in the dictionary.
+// A batch in the tree's units: the tokens themselves (unpaged tree), or page
+// symbols (paged tree; see units_of).
 struct Units {
-  const int32_t* data = nullptr;
+  const int32_t* data = nullptr;  // request b's units start at data + off[b]
   const int64_t* off = nullptr;
-  std::vector<int32_t> sym;
+  std::vector<int64_t> n;         // and number n[b]
+  std::vector<int32_t> sym;       // storage of a paged batch
   std::vector<int64_t> own_off;
-  int64_t len(int32_t b) const { return off[b + 1] - off[b]; }
+  std::vector<int32_t> created;   // symbols this conversion added to the dictionary
+  int64_t len(int32_t b) const { return n[b]; }
   const int32_t* at(int32_t b) const { return data + off[b]; }
 };
-
-template <class LenF>
-Units units_of(rc_radix& t, int32_t batch, const int32_t* tokens, const int64_t* tok_off, LenF&& len, bool create) {
-  Units u;
-  if (t.page == 1 && batch > 0) {
-    // tokens as they are, each request cut to its first len(b)
-    bool whole = true;
-    for (int32_t b = 0; b < batch && whole; ++b) whole = len(b) == tok_off[b + 1] - tok_off[b];
-    if (whole) {
-      u.data = tokens;
-      u.off = tok_off;
-      return u;
-    }
-  }
-  u.own_off.assign(batch + 1, 0);
-  for (int32_t b = 0; b < batch; ++b) u.own_off[b + 1] = u.own_off[b] + len(b) / t.page;
-  u.sym.resize((size_t)u.own_off[batch]);
-  for (int32_t b = 0; b < batch; ++b) {
-    const int32_t* src = tokens ? tokens + tok_off[b] : nullptr;
-    for (int64_t i = 0; i < u.own_off[b + 1] - u.own_off[b]; ++i)
-      u.sym[u.own_off[b] + i] = t.page == 1 ? src[i] : create ? t.dict.intern(src + i * t.page) : t.dict.find(src + i * t.page);
-  }
-  u.data = u.sym.data();
-  u.off = u.own_off.data();
-  return u;
-}
 
 // f(b) for b in [0, n), on several host threads when the batch holds enough
 // tokens to pay for them (f must only read shared state, or write to b's own
@@ -234,6 +271,85 @@ void for_requests(int32_t n, int64_t tokens, F&& f) {
     for (int32_t b = i; b < n; b += nt) f(b);
   for (int32_t b = 0; b < n; b += nt) f(b);
   for (auto& th : pool) th.join();
+}
+
+// The symbols of the stored prefix of a request's n whole pages, appended to
+// out; returns their number.  It follows the tree as walk() does, but looks a
+// page up in the dictionary only to pick the child edge at a node and
+// compares the rest of an edge page by page with the dictionary's copies.
+int64_t stored_pages(const rc_radix& t, const int32_t* tok, int64_t n, std::vector<int32_t>& out);
+
+// A batch in the tree's units, request b cut to its first len(b) tokens.
+// Unpaged: the tokens themselves.  Paged: the symbols of the request's whole
+// pages as far as the tree stores them (a lookup needs no more: the stored
+// prefix is all that a walk can match); with create, the remaining whole
+// pages follow, added to the dictionary where new (listed in created).
+template <class LenF>
+Units units_of(rc_radix& t, int32_t batch, const int32_t* tokens, const int64_t* tok_off, LenF&& len, bool create) {
+  Units u;
+  u.n.resize(batch);
+  if (t.page == 1) {
+    for (int32_t b = 0; b < batch; ++b) u.n[b] = len(b);
+    u.data = tokens;
+    u.off = tok_off;
+    return u;
+  }
+  const int64_t ps = t.page;
+  std::vector<std::vector<int32_t>> per(batch);
+  int64_t total = 0;
+  for (int32_t b = 0; b < batch; ++b) {
+    per[b].reserve((size_t)(len(b) / ps));  // no allocation on the worker threads
+    total += len(b);
+  }
+  if (!create) {
+    for_requests(batch, total, [&](int32_t b) {
+      if (len(b) >= ps) stored_pages(t, tokens + tok_off[b], len(b) / ps, per[b]);
+    });
+  } else {
+    for (int32_t b = 0; b < batch; ++b) {
+      const int64_t np = len(b) / ps;
+      if (np == 0) continue;
+      const int32_t* src = tokens + tok_off[b];
+      for (int64_t i = stored_pages(t, src, np, per[b]); i < np; ++i) {
+        bool fresh = false;
+        const int32_t s = t.dict.intern(src + i * ps, &fresh);
+        if (fresh) u.created.push_back(s);
+        per[b].push_back(s);
+      }
+    }
+  }
+  u.own_off.assign(batch + 1, 0);
+  for (int32_t b = 0; b < batch; ++b) u.own_off[b + 1] = u.own_off[b] + (int64_t)per[b].size();
+  u.sym.resize((size_t)u.own_off[batch]);
+  for (int32_t b = 0; b < batch; ++b) {
+    std::copy(per[b].begin(), per[b].end(), u.sym.begin() + u.own_off[b]);
+    u.n[b] = (int64_t)per[b].size();
+  }
+  u.data = u.sym.data();
+  u.off = u.own_off.data();
+  return u;
+}
+
+int64_t stored_pages(const rc_radix& t, const int32_t* tok, int64_t n, std::vector<int32_t>& out) {
+  const int64_t ps = t.page;
+  int32_t cur = 0;
+  int64_t pos = 0;
+  while (pos < n) {
+    const int32_t s = t.dict.find(tok + pos * ps);
+    if (s < 0) break;
+    auto it = t.nodes[cur].kids.find(s);
+    if (it == t.nodes[cur].kids.end()) break;
+    const Node& c = t.nodes[it->second];
+    const int64_t len = (int64_t)c.tok.size();
+    const int64_t lim = std::min(len, n - pos);
+    out.push_back(s);
+    int64_t k = 1;
+    while (k < lim && t.dict.same(c.tok[k], tok + (pos + k) * ps)) out.push_back(c.tok[k++]);
+    pos += k;
+    if (k < len) break;
+    cur = it->second;
+  }
+  return pos;
 }
 
 // Locks.  A lock pins the path from the root to one node (the deepest node
@@ -277,6 +393,8 @@ int64_t evict_lru(rc_radix& t, int64_t want) {
     const int32_t par = nd.parent;
     const int64_t len = (int64_t)nd.tok.size();
     t.nodes[par].kids.erase(nd.tok[0]);
+    if (t.page > 1)
+      for (int32_t s : nd.tok) t.dict.release(s);
     for (int32_t s : nd.slot) {
       t.in_tree[s] = 0;
       t.is_free[s] = 1;
@@ -442,6 +560,8 @@ static rc_status insert_units(rc_radix* t, const int32_t* tokens, int32_t* slots
         nn.slot.assign(slots + pos, slots + n);
         nn.last_use = now;
         for (int64_t i = pos; i < n; ++i) t->in_tree[slots[i]] = 1;
+        if (t->page > 1)
+          for (int64_t i = pos; i < n; ++i) t->dict.acquire(tokens[i]);
         t->nodes[cur].kids[tokens[pos]] = id;
         t->st.nodes++;
         t->st.cached_tokens += n - pos;
@@ -491,7 +611,10 @@ rc_status rc_radix_insert(rc_radix* t, const int32_t* tokens, int32_t* slots, in
   try {
     const int64_t off[2] = {0, n};
     const Units u = units_of(*t, 1, tokens, off, [&](int32_t) { return n; }, true);  // whole pages only
-    return insert_units(t, u.at(0), slots, u.len(0), n_new);
+    rc_status st = insert_units(t, u.at(0), slots, u.len(0), n_new);
+    for (int32_t s : u.created)  // pages a failed insert did not store
+      if (t->dict.refs[s] == 0) t->dict.remove(s);
+    return st;
   } catch (const std::bad_alloc&) {
     return fail(RC_ERR_NOMEM, "host allocation failed");
   }
@@ -697,6 +820,7 @@ rc_status rc_radix_stats_get(const rc_radix* t, rc_radix_stats* out) {
   if (!t || !out) return fail(RC_ERR_ARG, "NULL argument");
   *out = t->st;
   out->free_slots = (int64_t)t->free_q.size();
+  out->page_symbols = t->dict.live;
   out->locked_tokens = 0;
   for (size_t id = 1; id < t->nodes.size(); ++id)
     if (t->nodes[id].alive && t->nodes[id].lock > 0) out->locked_tokens += (int64_t)t->nodes[id].tok.size();

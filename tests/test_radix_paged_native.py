@@ -82,9 +82,14 @@ def test_paged_tree_matches_the_model(sc):
         elif op[0] == "match":
             m, ids = tree.match(op[1])
             assert (m, ids.tolist()) == ref.match(op[1])
-        assert tree.stats()["free_slots"] == len(ref.free)
+        st_ = tree.stats()
+        assert st_["free_slots"] == len(ref.free)
+        assert 0 < st_["page_symbols"] <= st_["cached_tokens"] or st_["page_symbols"] == st_["cached_tokens"] == 0
     n = len(ref.free)
     assert tree.alloc(n).tolist() == ref.alloc(n)
+    # nothing is locked: eviction empties the tree and its page dictionary
+    tree.evict(10 ** 6)
+    assert tree.stats()["cached_tokens"] == 0 and tree.stats()["page_symbols"] == 0
 
 
 def test_gpt2_example_at_page_size_16_native():
@@ -177,3 +182,65 @@ def test_paged_decode_and_extend_plans(ps):
     lens = np.array([len(x) for x in batch], np.int32)
     plan = t.plan_decode(batch, lens + reserve, group=4, chunk=128, rows=rows)
     _check_plan(plan, lens + reserve, rows, _expanded(table, ps), 4)
+
+
+def test_page_dictionary_holds_what_the_tree_holds():
+    ps = 4
+    A, B, C = [1, 2, 3, 4], [5, 6, 7, 8], [9, 9, 9, 9]
+    t = RadixTree(32, page_size=ps)
+    first = np.array(A + B + A + B + [3], np.int32)      # 4 full pages, 2 distinct contents
+    second = np.array(C + A, np.int32)
+    for seq in (first, second):
+        ids = t.alloc(len(seq) // ps)
+        t.insert(seq, ids)
+    st_ = t.stats()
+    assert st_["cached_tokens"] == 6 and st_["page_symbols"] == 3
+    h, _ = t.lock([second])                               # the older sequence goes first anyway
+    assert t.evict(1) == 4
+    assert t.stats()["page_symbols"] == 2                 # B had no other holder; A is still in `second`
+    m, _ = t.match(np.concatenate([first, [0]]).astype(np.int32))
+    assert m == 0
+    t.unlock(h)
+    assert t.evict(100) == 2 and t.stats()["page_symbols"] == 0
+    again = np.array(B + A + [0], np.int32)               # the numbers are reused after removal
+    t.insert(again, t.alloc(2))
+    assert t.stats()["page_symbols"] == 2
+    m, got = t.match(np.concatenate([again, [7]]).astype(np.int32))
+    assert m == 8 and len(got) == 2
+
+
+def test_failed_paged_insert_leaves_no_symbols():
+    t = RadixTree(8, page_size=2)
+    seq = np.arange(1, 9, dtype=np.int32)                 # 4 pages
+    with pytest.raises(RcError):
+        t.insert(seq, np.array([0, 1, 2, 3], np.int32))    # never allocated: refused
+    assert t.stats()["page_symbols"] == 0 and t.stats()["cached_tokens"] == 0
+    t.insert(seq, t.alloc(4))
+    assert t.stats()["page_symbols"] == 4
+
+
+def test_large_batches_walk_on_several_threads_like_single_requests():
+    # about a million tokens: the batch calls split their walks over host threads
+    ps, g = 16, np.random.default_rng(11)
+    stems = [g.integers(0, 50000, 2048 + 7 * i).astype(np.int32) for i in range(8)]
+    t = RadixTree(1 << 16, page_size=ps)
+    for x in stems:
+        t.insert(x, t.alloc(len(x) // ps))
+    batch = [np.concatenate([stems[i % 8][:g.integers(1000, len(stems[i % 8]) + 1)],
+                             g.integers(0, 50000, g.integers(1, 2200)).astype(np.int32)]) for i in range(512)]
+    assert sum(map(len, batch)) > 1 << 20
+    want = []
+    for x in batch:
+        m, ids = t.match(x)
+        want.append((m, ids))
+    table = np.full((len(batch), 512), -1, np.int32)
+    P, E = t.emit_rows(batch, table, reserve=3)
+    for b, (m, ids) in enumerate(want):
+        assert P[b] == m and (table[b, :m // ps] == ids).all()
+    h, locked = t.lock(batch)
+    assert locked.tolist() == [m for m, _ in want]
+    t.unlock(h)
+    rows = np.arange(len(batch), dtype=np.int32)
+    plan = t.plan_decode(batch, P.astype(np.int32) + 1, group=4, chunk=4096, rows=rows,
+                         lengths=P.astype(np.int64))
+    _check_plan(plan, P + 1, rows, _expanded(table, ps), 4)
