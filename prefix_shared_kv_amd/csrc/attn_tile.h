@@ -35,6 +35,7 @@
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -430,7 +431,7 @@ __device__ __forceinline__ void attn_bf16_body(const Args& a, const int mode, co
   };
   // Online softmax over the stage's 64 keys (masked on boundary stages only):
   // one maximum per column per stage, the cross-half exchange by a lane swap
-  auto softmax = [&](f32x16& s0, f32x16& s1, int kt, auto maskc) {
+  auto softmax = [&](f32x16& s0, f32x16& s1, int kt, auto maskc, bf16x8 (&pf)[4]) {
     constexpr bool MASK = decltype(maskc)::value;
     if constexpr (MASK) {
 #pragma unroll
@@ -442,7 +443,7 @@ __device__ __forceinline__ void attn_bf16_body(const Args& a, const int mode, co
     }
     float mx = -INFINITY;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) mx = fmaxf(mx, fmaxf(s0[v], s1[v]));
+    for (int v = 0; v < 16; ++v) mx = fmaxf(fmaxf(mx, s0[v]), s1[v]);  // one v_max3 per pair
     const auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, mx), __builtin_bit_cast(uint32_t, mx),
                                                      false, false);
     mx = fmaxf(__builtin_bit_cast(float, (uint32_t)sw[0]), __builtin_bit_cast(float, (uint32_t)sw[1])) * a.scale_log2;
@@ -456,29 +457,37 @@ __device__ __forceinline__ void attn_bf16_body(const Args& a, const int mode, co
       m_run = m_new;
     }
     const float m_use = m_run == -INFINITY ? 0.f : m_run;
-    float ps0 = 0.f, ps1 = 0.f;
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       s0[v] = __builtin_amdgcn_exp2f(fmaf(s0[v], a.scale_log2, -m_use));
-      ps0 += s0[v];
-    }
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
       s1[v] = __builtin_amdgcn_exp2f(fmaf(s1[v], a.scale_log2, -m_use));
-      ps1 += s1[v];
     }
-    l_run += ps0 + ps1;
+    // P rounded to bf16 once: the PV operands, and (two keys per v_dot2 with
+    // ones) the denominator, so numerator and denominator use the same weights
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      pf[0][i] = (__bf16)s0[i];
+      pf[1][i] = (__bf16)s0[8 + i];
+      pf[2][i] = (__bf16)s1[i];
+      pf[3][i] = (__bf16)s1[8 + i];
+    }
+    const bf16x2 one2 = {(__bf16)1.f, (__bf16)1.f};
+    float ps[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k2 = 0; k2 < 4; ++k2)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        ps[k2] = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pf[k2][2 * j], pf[k2][2 * j + 1]}, one2, ps[k2], false);
+    l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
   };
   // O^T += V^T P^T for half h (two 16-key steps); V^T by transposing reads
-  auto pv = [&](const f32x16& p, const uint16_t* tv, int h) {
+  auto pv = [&](const bf16x8 (&pfs)[4], const uint16_t* tv, int h) {
     const int g = lane >> 4, r = lane & 15;
     const int dsub = 16 * (g & 1) + 4 * (r & 3);
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
       const int k2 = 2 * h + hh;
-      bf16x8 pf;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) pf[i] = (__bf16)p[8 * hh + i];
+      const bf16x8 pf = pfs[k2];
       const int key0 = 16 * k2 + 4 * (g >> 1) + (r >> 2);
       const int key1 = key0 + 8;
       const int sw0 = swz<D>(key0), sw1 = swz<D>(key1);
@@ -494,10 +503,11 @@ __device__ __forceinline__ void attn_bf16_body(const Args& a, const int mode, co
   };
   auto compute = [&](const uint16_t* tk, const uint16_t* tv, int kt, auto maskc) {
     f32x16 s0, s1;
+    bf16x8 pf[4];
     qk(tk, s0, s1);
-    softmax(s0, s1, kt, maskc);
-    pv(s0, tv, 0);
-    pv(s1, tv, 1);
+    softmax(s0, s1, kt, maskc, pf);
+    pv(pf, tv, 0);
+    pv(pf, tv, 1);
   };
 
   // Pipeline: LDS double buffer.  At each stage's barrier the stage's tile has
