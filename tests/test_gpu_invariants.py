@@ -1,0 +1,75 @@
+"""GPU invariants that hold whatever the values, checked through the engine
+(every call through the C ABI) on whole workloads:
+
+- softmax weights sum to one: with V = 1 everywhere, every bf16 output of the
+  extend (tile and cascade), the prefill and every decode step is exactly 1.0
+  (P is rounded to bf16 once and the same rounded weights give numerator and
+  denominator, so the quotient is 1 to fp32 rounding, which bf16 cannot show);
+- slot numbering does not enter the arithmetic: the same workload over a pool
+  handed out in identity order and in a shuffled order gives bit-identical
+  outputs.
+"""
+import numpy as np
+import pytest
+import torch
+
+from synth import drive
+from synth import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+
+def _small_tree():
+    # depth 3, fanout 3: the root's children are shared by 9 requests (wide
+    # decode items at GQA 32/8), their children by 3 (narrow ones)
+    return W.multi_turn_tree(depth=3, fanout=3, seg_lo=5, seg_hi=90, ext=9, n_decode=3)
+
+
+def _ones_v(w):
+    orig = w._vals
+
+    def vals(shape, tag, *ids):
+        x = orig(shape, tag, *ids)
+        return np.ones_like(x) if tag in (W._T_NODE_V, W._T_EXT_V, W._T_DEC_V) else x
+
+    w._vals = vals
+    return w
+
+
+def _run(gpu, w, cascade, n_steps):
+    """Every output of the workload: prefill nodes, the requests' extend, n_steps decode steps."""
+    eng = drive.make_engine(w, gpu)
+    drive.populate(eng, w, [n for n in drive.node_order(w) if n not in w.prefill_nodes], device=gpu)
+    outs = [o.clone() for o in drive.prefill_nodes(eng, w, gpu).values()]
+    b, o = drive.extend_requests(eng, w, device=gpu, cascade=cascade)
+    outs.append(o.clone())
+    base = [len(w.prompt_tokens(r)) for r in w.requests]
+    st = eng.prepare_decode(b, base, n_steps, chunk=64)
+    rids = list(range(len(w.requests)))
+    for t in range(n_steps):
+        q, k, v = drive.decode_inputs(w, rids, t, device=gpu)
+        outs.append(eng.decode_step(st, t, q, k, v, w.sm_scale).clone())
+    eng.release(b)
+    torch.cuda.synchronize()
+    return outs
+
+
+@pytest.mark.parametrize("name,cascade", [("gpt2", False), ("gpt2", True), ("tree", False), ("tree", True)])
+def test_unit_values_give_exactly_one(gpu, name, cascade):
+    w = _ones_v(W.gpt2_system_prompt() if name == "gpt2" else _small_tree())
+    outs = _run(gpu, w, cascade, 3)
+    for i, o in enumerate(outs):
+        assert o.dtype == torch.bfloat16
+        bad = (o != 1).sum().item()
+        assert bad == 0, f"output {i}: {bad} of {o.numel()} elements differ from 1 (max |o-1| {(o.float() - 1).abs().max().item():.3e})"
+
+
+@pytest.mark.parametrize("name,cascade", [("gpt2", False), ("tree", True)])
+def test_slot_order_does_not_change_any_bit(gpu, name, cascade):
+    runs = []
+    for shuffled in (False, True):
+        w = W.gpt2_system_prompt() if name == "gpt2" else _small_tree()
+        w.shuffle_slots = shuffled
+        runs.append(_run(gpu, w, cascade, 3))
+    for i, (a, b) in enumerate(zip(*runs)):
+        assert torch.equal(a, b), f"output {i} differs between slot orders"

@@ -81,6 +81,16 @@ def test_single_key_gives_value_exactly():
         assert np.array_equal(got[0, h], v[0, h // 2])
 
 
+def test_weights_sum_to_one():
+    # V = 1 everywhere: every output is the sum of its softmax weights
+    P, E, D = 37, 9, 16
+    q, k = _rand(20, E, 4, D) * 3, _rand(21, P + E, 2, D) * 3
+    got = A.extend(q, k, np.ones((P + E, 2, D)), P, 0.7)
+    np.testing.assert_allclose(got, 1.0, rtol=0, atol=1e-14)
+    got = A.decode(q[0], k, np.ones((P + E, 2, D)), 0.7)
+    np.testing.assert_allclose(got, 1.0, rtol=0, atol=1e-14)
+
+
 def test_zero_query_gives_causal_running_mean():
     P, E, D = 6, 5, 8
     k, v = _rand(10, P + E, 1, D), _rand(11, P + E, 1, D)
