@@ -7,7 +7,10 @@
   denominator, so the quotient is 1 to fp32 rounding, which bf16 cannot show);
 - slot numbering does not enter the arithmetic: the same workload over a pool
   handed out in identity order and in a shuffled order gives bit-identical
-  outputs.
+  outputs;
+- node boundaries do not either: a sequence cut anywhere into cached prefix and
+  new tokens gives the tile extend's outputs bit for bit (its key stages are
+  aligned to absolute position 0).
 """
 import numpy as np
 import pytest
@@ -73,3 +76,45 @@ def test_slot_order_does_not_change_any_bit(gpu, name, cascade):
         runs.append(_run(gpu, w, cascade, 3))
     for i, (a, b) in enumerate(zip(*runs)):
         assert torch.equal(a, b), f"output {i} differs between slot orders"
+
+
+@pytest.mark.parametrize("dtype,Hq,Hkv,D", [("bf16", 32, 8, 128), ("bf16", 12, 12, 64), ("f32", 8, 2, 64)])
+def test_any_cached_length_gives_the_same_bits(gpu, dtype, Hq, Hkv, D):
+    # One logical sequence of N tokens, cut at P' cached + N - P' new tokens for
+    # several P' in one batch.  The tile walks keys in stages aligned to
+    # absolute position 0, so the outputs of positions >= P (every cut <= P)
+    # are bit-identical whatever P' is, and match the oracle.
+    from oracle import attention as A
+    from prefix_shared_kv_amd import KVShape, api
+    N, P = 300, 200
+    cuts = [0, 1, 63, 64, 65, 128, 199, 200]
+    dt = {"bf16": torch.bfloat16, "f32": torch.float32}[dtype]
+    g = np.random.default_rng(Hq * D)
+    rnd = lambda *s: (W.round_bf16 if dtype == "bf16" else (lambda x: x))(g.standard_normal(s).astype(np.float32))
+    q, k, v = rnd(N, Hq, D), rnd(N, Hkv, D), rnd(N, Hkv, D)
+    S = N + 64
+    slots = g.permutation(S)[:N].astype(np.int32)
+    kp = torch.zeros(S, Hkv, D, dtype=dt, device=gpu)
+    vp = torch.zeros_like(kp)
+    kp[torch.from_numpy(slots.astype(np.int64)).to(gpu)] = torch.from_numpy(k).to(gpu).to(dt)
+    vp[torch.from_numpy(slots.astype(np.int64)).to(gpu)] = torch.from_numpy(v).to(gpu).to(dt)
+    B = len(cuts)
+    table = np.tile(slots, (B, 1))
+    E = [N - c for c in cuts]
+    start = np.concatenate([[0], np.cumsum(E)[:-1]]).astype(np.int32)
+    to = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(gpu).to(dt)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(gpu)
+    qs = np.concatenate([q[c:] for c in cuts])
+    ks = np.concatenate([k[c:] for c in cuts])
+    vs = np.concatenate([v[c:] for c in cuts])
+    o = torch.empty(len(qs), Hq, D, dtype=dt, device=gpu)
+    shape = KVShape(Hq, Hkv, D, dt, S)
+    api.extend_attention(shape, o, to(qs), to(ks), to(vs), kp, vp, dev(table), dev(np.array(cuts, np.int32)),
+                         dev(np.array(E, np.int32)), dev(start), max(E), 1.0 / np.sqrt(D))
+    torch.cuda.synchronize()
+    tail = [o[start[b] + (P - cuts[b]):start[b] + E[b]] for b in range(B)]
+    for b in range(1, B):
+        assert torch.equal(tail[b], tail[0]), f"cut {cuts[b]} differs from cut {cuts[0]}"
+    want = A.extend(q[P:], k, v, P, 1.0 / np.sqrt(D))
+    err = float((tail[0].double().cpu() - torch.from_numpy(want)).abs().max())
+    assert err <= {"bf16": 2e-2, "f32": 1e-4}[dtype], err
