@@ -255,6 +255,10 @@ def bench_classify_heavy(args):
     # so a step's batches never reuse rows whose uploads are still queued
     # behind the previous step's decode launches, and the host runs ahead.
     eng = Engine(kvs, stride, 2 * (B + len(wc.requests) + 8), dev)
+    # The decode batch keeps its rows from step to step (two sets, used in
+    # turn), as running requests do: rescheduled on its own rows, a request's
+    # table row changes only in its last entries, and only those are uploaded.
+    dec_rows = [eng.take_rows(B), eng.take_rows(B)]
 
     # ---- cached contexts of the decode requests (untimed set-up) ----
     drive.populate(eng, wh, device=dev, device_values=True)
@@ -312,7 +316,7 @@ def bench_classify_heavy(args):
         eng.release(bb)
         ph.mark("branches")
         pk.prof_tag(None)
-        bh = eng.schedule(hd_tb, reserve=T - 1)
+        bh = eng.schedule(hd_tb, reserve=T - 1, rows=dec_rows[s % 2])
         ph.mark("decode_schedule")
         st = eng.prepare_decode(bh, base, T, chunk=args.chunk)
         plan_info.update(st.plan.summary)

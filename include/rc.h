@@ -98,6 +98,19 @@ const char* rc_version(void);
  * Process-wide; not thread-safe against concurrent GPU calls. */
 rc_status rc_set_error_word(int32_t* device_word);
 
+/* Copy a rectangle of a host req_to_token table to its device copy on       */
+/* `stream`: rows [row0, row0 + n_rows), entries [col0, col1) of each.  Both */
+/* tables are row-major int32 with host_stride / dev_stride entries a row.   */
+/* One asynchronous 2D copy: the host table should be pinned (else the copy */
+/* is staged and synchronous) and must not change until the stream has run */
+/* it.  Lets a caller upload only the entries rc_radix_emit_rows changed     */
+/* (its first_changed output) instead of whole rows.  Bad sizes or an empty  */
+/* rectangle's negative extents fail with RC_ERR_ARG; copy errors with       */
+/* RC_ERR_HIP.                                                                */
+rc_status rc_upload_table_rows(int32_t* dev_table, int64_t dev_stride, const int32_t* host_table,
+                               int64_t host_stride, int64_t row0, int64_t n_rows, int64_t col0, int64_t col1,
+                               void* stream);
+
 /* ------------------------------------------------------------------------ */
 /* KV-pool scatter  [PC] "How prompt caching works": K and V of every token   */
 /* are stored and kept for later use.                                         */
@@ -329,11 +342,16 @@ rc_status rc_radix_insert_rows(rc_radix* tree, int32_t batch, const int32_t* tok
 /*             rows still get them); if that is not enough the call fails    */
 /*             with RC_ERR_NOMEM, the rows and locks untouched, but what was */
 /*             evicted and the use marks stay.                                */
+/*   first_changed (host, nullable, batch entries): index of the first entry */
+/*             of row rows[b] whose value this call changed (the row's entry */
+/*             count if none did).  Entries before it hold what they held    */
+/*             before the call, so a caller that mirrors the table on the    */
+/*             device uploads only [first_changed[b], row entries).           */
 rc_status rc_radix_emit_rows(rc_radix* tree, int32_t batch, const int32_t* tokens,
                              const int64_t* tok_off, int32_t reserve, const int32_t* rows,
                              int32_t* req_to_token, int32_t table_rows, int64_t stride,
                              int32_t* prefix_lens, int32_t* extend_lens, int32_t evict,
-                             int64_t* handles);
+                             int64_t* handles, int64_t* first_changed);
 
 /* Locks and LRU eviction ([SG] RadixAttention bullet: an LRU cache of KV in */
 /* the radix tree; nine-step example, steps 5, 8 and 9: least recently used  */

@@ -56,6 +56,7 @@ _SIGS = {
     "rc_last_error": (C.c_char_p, []),
     "rc_version": (C.c_char_p, []),
     "rc_set_error_word": (i32, [P]),
+    "rc_upload_table_rows": (i32, [P, i64, P, i64, i64, i64, i64, i64, P]),
     "rc_kv_store": (i32, [C.POINTER(RcShape), P, P, P, P, P, i64, P]),
     "rc_label_distribution": (i32, [P, i32, i64, i64, i32, P, i32, P, P, P, P, P, P]),
     "rc_extend_attention": (i32, [C.POINTER(RcShape), P, P, P, P, P, P, P, i32, i64, P, P, P, P, i32, i64, i32, f32, P]),
@@ -72,7 +73,7 @@ _SIGS = {
     "rc_radix_alloc": (i32, [P, i64, P]),
     "rc_radix_free": (i32, [P, P, i64]),
     "rc_radix_insert": (i32, [P, P, P, i64, I64P]),
-    "rc_radix_emit_rows": (i32, [P, i32, P, P, i32, P, P, i32, i64, P, P, i32, P]),
+    "rc_radix_emit_rows": (i32, [P, i32, P, P, i32, P, P, i32, i64, P, P, i32, P, P]),
     "rc_radix_lock": (i32, [P, i32, P, P, P, P, P]),
     "rc_radix_unlock": (i32, [P, P, i32]),
     "rc_radix_evict": (i32, [P, i64, I64P]),

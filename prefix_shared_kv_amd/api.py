@@ -78,6 +78,21 @@ def set_error_word(word: Optional[torch.Tensor]) -> None:
     check(lib.rc_set_error_word(_vp(word)))
 
 
+def upload_table_rows(dev_table: torch.Tensor, host_table: torch.Tensor, row0: int, n_rows: int, col0: int, col1: int,
+                      stream=None) -> None:
+    """Copy rows [row0, row0 + n_rows) x entries [col0, col1) of a pinned host int32 table to the
+    device table (rc_upload_table_rows): one asynchronous 2D copy."""
+    _dev(dev_table, "dev_table", torch.int32)
+    if host_table.device.type != "cpu" or host_table.dtype != torch.int32 or host_table.dim() != 2:
+        raise ValueError("host_table must be a 2-D int32 CPU tensor")
+    if not (dev_table.is_contiguous() and host_table.is_contiguous()):
+        raise ValueError("tables must be contiguous")
+    if row0 + n_rows > min(dev_table.shape[0], host_table.shape[0]):
+        raise ValueError("rows outside the tables")
+    check(lib.rc_upload_table_rows(_vp(dev_table), dev_table.shape[1], C.c_void_p(host_table.data_ptr()),
+                                   host_table.shape[1], row0, n_rows, col0, col1, _stream(stream)))
+
+
 def kv_store(shape: KVShape, k_pool, v_pool, k_new, v_new, slots, stream=None) -> None:
     """pool[slots[i]] = new[i] for K and V (see rc_kv_store)."""
     H, D, S = shape.num_kv_heads, shape.head_dim, shape.pool_slots
@@ -354,11 +369,13 @@ class RadixTree:
         return s, n_new.value
 
     def emit_rows(self, batch: Sequence[Sequence[int]], table: np.ndarray, rows: Optional[Sequence[int]] = None,
-                  reserve: int = 0, evict: bool = False,
-                  handles: Optional[np.ndarray] = None) -> Tuple[np.ndarray, np.ndarray]:
+                  reserve: int = 0, evict: bool = False, handles: Optional[np.ndarray] = None,
+                  first_changed: Optional[np.ndarray] = None) -> Tuple[np.ndarray, np.ndarray]:
         """Fill rows of a host table [R, stride]; returns (prefix_lens, extend_lens).
         evict: evict least recently used unpinned nodes when the free slots fall short.
-        handles: an int64 array of one entry per request that receives locks on the matched prefixes."""
+        handles: an int64 array of one entry per request that receives locks on the matched prefixes.
+        first_changed: an int64 array of one entry per request that receives the first entry of its
+        row the call changed (the row's entry count if none)."""
         if table.dtype != np.int32 or table.ndim != 2 or not table.flags.c_contiguous:
             raise ValueError("table must be a C-contiguous int32 [rows, stride] array")
         tb = _tb(batch)
@@ -368,9 +385,12 @@ class RadixTree:
         E = np.zeros(B, np.int32)
         if handles is not None and (handles.dtype != np.int64 or handles.shape != (B,) or not handles.flags.c_contiguous):
             raise ValueError("handles must be a contiguous int64 array with one entry per request")
+        if first_changed is not None and (first_changed.dtype != np.int64 or first_changed.shape != (B,)
+                                          or not first_changed.flags.c_contiguous):
+            raise ValueError("first_changed must be a contiguous int64 array with one entry per request")
         check(lib.rc_radix_emit_rows(self._h, B, _np_ptr(tb.flat), _np_ptr(tb.off), reserve, _np_ptr(rw), _np_ptr(table),
                                      table.shape[0], table.shape[1], _np_ptr(P), _np_ptr(E), int(bool(evict)),
-                                     _np_ptr(handles)))
+                                     _np_ptr(handles), _np_ptr(first_changed)))
         return P, E
 
     def lock(self, batch, lengths: Optional[Sequence[int]] = None) -> Tuple[np.ndarray, np.ndarray]:

@@ -647,7 +647,7 @@ rc_status rc_radix_insert_rows(rc_radix* t, int32_t batch, const int32_t* tokens
 rc_status rc_radix_emit_rows(rc_radix* t, int32_t batch, const int32_t* tokens, const int64_t* tok_off,
                              int32_t reserve, const int32_t* rows, int32_t* table, int32_t table_rows,
                              int64_t stride, int32_t* prefix_lens, int32_t* extend_lens, int32_t evict,
-                             int64_t* handles) {
+                             int64_t* handles, int64_t* first_changed) {
   if (!t || batch < 0 || reserve < 0 || stride <= 0 || table_rows < 0) return fail(RC_ERR_ARG, "bad argument to rc_radix_emit_rows");
   if (batch > 0 && (!tok_off || !rows || !table || !prefix_lens || !extend_lens)) return fail(RC_ERR_ARG, "NULL array in rc_radix_emit_rows");
   if (rc_status st = check_lens(batch, tok_off, nullptr); st != RC_OK) return st;
@@ -709,15 +709,19 @@ rc_status rc_radix_emit_rows(rc_radix* t, int32_t batch, const int32_t* tokens, 
     }
   }
   // pass 2: allocate in request order, then copy the matched prefixes' slots
+  // (first_changed: the first entry whose value changes, per request)
   for (int32_t b = 0; b < batch; ++b) {
     const int64_t n = tok_off[b + 1] - tok_off[b];
     int32_t* row = table + (int64_t)rows[b] * stride;
+    int64_t fc = entries(b);
     for (int64_t i = P[b]; i < entries(b); ++i) {
       int32_t s = t->free_q.front();
       t->free_q.pop_front();
       t->is_free[s] = 0;
+      if (row[i] != s && fc == entries(b)) fc = i;
       row[i] = s;
     }
+    if (first_changed) first_changed[b] = fc;
     prefix_lens[b] = (int32_t)(P[b] * pg);
     extend_lens[b] = (int32_t)(n - P[b] * pg);
     t->st.matches++;
@@ -730,6 +734,10 @@ rc_status rc_radix_emit_rows(rc_radix* t, int32_t batch, const int32_t* tokens, 
       if (w >= P[b]) break;
       const Node& c = t->nodes[v.node];
       const int64_t k = std::min(v.k, P[b] - w);
+      if (first_changed && w < first_changed[b] &&
+          std::memcmp(row + w, c.slot.data(), (size_t)k * sizeof(int32_t)) != 0)
+        first_changed[b] = std::min(first_changed[b],
+                                    w + (std::mismatch(row + w, row + w + k, c.slot.data()).first - (row + w)));
       std::memcpy(row + w, c.slot.data(), (size_t)k * sizeof(int32_t));
       w += k;
     }

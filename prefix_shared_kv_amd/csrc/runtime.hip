@@ -62,6 +62,24 @@ extern "C" rc_status rc_set_error_word(int32_t* device_word) {
   return RC_OK;
 }
 
+extern "C" rc_status rc_upload_table_rows(int32_t* dev_table, int64_t dev_stride, const int32_t* host_table,
+                                          int64_t host_stride, int64_t row0, int64_t n_rows, int64_t col0,
+                                          int64_t col1, void* stream) {
+  if (n_rows < 0 || row0 < 0 || col0 < 0 || col1 < col0 || col1 > dev_stride || col1 > host_stride)
+    return rc::fail(RC_ERR_ARG, "bad table rectangle: rows %lld+%lld, entries [%lld, %lld), strides %lld/%lld",
+                    (long long)row0, (long long)n_rows, (long long)col0, (long long)col1, (long long)dev_stride,
+                    (long long)host_stride);
+  if (n_rows == 0 || col1 == col0) return RC_OK;
+  if (!dev_table || !host_table) return rc::fail(RC_ERR_ARG, "NULL table");
+  const size_t e = sizeof(int32_t);
+  hipError_t st = hipMemcpy2DAsync(dev_table + row0 * dev_stride + col0, (size_t)dev_stride * e,
+                                   host_table + row0 * host_stride + col0, (size_t)host_stride * e,
+                                   (size_t)(col1 - col0) * e, (size_t)n_rows, hipMemcpyHostToDevice,
+                                   (hipStream_t)stream);
+  if (st != hipSuccess) return rc::fail(RC_ERR_HIP, "table upload failed: %s", hipGetErrorString(st));
+  return RC_OK;
+}
+
 extern "C" rc_status rc_set_tuning(const char* name, int64_t value) {
   if (!name) return rc::fail(RC_ERR_ARG, "tuning name is NULL");
   if (!strcmp(name, "decode_rows")) {

@@ -42,6 +42,7 @@ class Batch:
     reserve: int
     locks: Optional[np.ndarray] = None  # lock handles pinning each request's cached tokens
     dev: dict = dataclasses.field(default_factory=dict)
+    own_rows: bool = True      # rows came from the engine's free list (returned at release)
 
     @property
     def size(self) -> int:
@@ -146,15 +147,26 @@ class Engine:
     def _i32(self, a) -> torch.Tensor:
         return self._h2d(np.asarray(a, np.int32))
 
-    def _upload_rows(self, rows: np.ndarray) -> None:
+    def _upload_rows(self, rows: np.ndarray, first: Optional[np.ndarray] = None,
+                     end: Optional[np.ndarray] = None) -> None:
+        """Upload entries [first[i], end[i]) of each row rows[i] (default: whole rows).  The
+        device table then equals the host table on those rows: entries before first[i] must
+        already be equal (emit_rows reports where a row starts to differ)."""
         if len(rows) == 0:
             return
-        # one copy per run of consecutive rows, straight from the pinned table
-        r = np.unique(np.asarray(rows, np.int64))
+        # one 2D copy per run of consecutive (distinct) rows, straight from the pinned table:
+        # the rectangle spanning the run's changed entries
+        r = np.asarray(rows, np.int64)
+        order = np.argsort(r, kind="stable")
+        r = r[order]
+        lo = np.zeros(len(r), np.int64) if first is None else np.asarray(first, np.int64)[order]
+        hi = np.full(len(r), self.width, np.int64) if end is None else np.asarray(end, np.int64)[order]
         cuts = np.flatnonzero(np.diff(r) != 1) + 1
-        for lo, hi in zip(np.concatenate([[0], cuts]), np.concatenate([cuts, [len(r)]])):
-            a, b = int(r[lo]), int(r[hi - 1]) + 1
-            self.table_d[a:b].copy_(self._table_pin[a:b], non_blocking=True)
+        for i0, i1 in zip(np.concatenate([[0], cuts]), np.concatenate([cuts, [len(r)]])):
+            a, b = int(r[i0]), int(r[i1 - 1]) + 1
+            c0, c1 = int(lo[i0:i1].min()), int(hi[i0:i1].max())
+            if c1 > c0:
+                api.upload_table_rows(self.table_d, self._table_pin, a, b - a, c0, c1)
         ev = torch.cuda.Event()
         ev.record(torch.cuda.current_stream(self.device))
         self._n_uploads += 1
@@ -214,21 +226,45 @@ class Engine:
         return m
 
     # -- a batch of requests --------------------------------------------------
-    def schedule(self, batch_tokens, reserve: int = 0, evict: bool = True) -> Batch:
+    def take_rows(self, n: int) -> np.ndarray:
+        """Hand n table rows to the caller, who schedules batches on them (schedule's `rows`) until
+        give_rows.  A request scheduled again on the row it had keeps that row's unchanged entries
+        on the device: only the entries that differ are uploaded."""
+        if n > len(self.free_rows):
+            raise RuntimeError("no free table rows")
+        rows = np.array(self.free_rows[:n], np.int32)
+        del self.free_rows[:n]
+        return rows
+
+    def give_rows(self, rows: np.ndarray) -> None:
+        self.free_rows.extend(int(r) for r in rows)
+
+    def schedule(self, batch_tokens, reserve: int = 0, evict: bool = True,
+                 rows: Optional[np.ndarray] = None) -> Batch:
         """batch_tokens: a list of token-id arrays or a TokenBatch.  Each request's cached prefix
         is pinned until release; with evict, least recently used unpinned nodes make room when
-        the free slots fall short."""
+        the free slots fall short.  rows: table rows from take_rows, one per request, not used by
+        another live batch (default: rows from the free list)."""
         tb = batch_tokens if isinstance(batch_tokens, TokenBatch) else TokenBatch(batch_tokens)
         B = len(tb)
-        if B > len(self.free_rows):
-            raise RuntimeError("no free table rows")
-        rows = np.array(self.free_rows[:B], np.int32)
+        own = rows is None
+        if own:
+            if B > len(self.free_rows):
+                raise RuntimeError("no free table rows")
+            rows = np.array(self.free_rows[:B], np.int32)
+        else:
+            rows = np.ascontiguousarray(rows, np.int32)
+            if rows.shape != (B,):
+                raise ValueError(f"{B} requests need {B} rows, got {rows.shape}")
         self._rows_writable(rows)
         locks = np.zeros(B, np.int64)
-        P, E = self.tree.emit_rows(tb, self.table_h, rows=rows, reserve=reserve, evict=evict, handles=locks)
-        del self.free_rows[:B]
-        self._upload_rows(rows)
-        b = Batch(tb, rows, P, E, reserve, locks)
+        first = np.zeros(B, np.int64)
+        P, E = self.tree.emit_rows(tb, self.table_h, rows=rows, reserve=reserve, evict=evict, handles=locks,
+                                   first_changed=first)
+        if own:
+            del self.free_rows[:B]
+        self._upload_rows(rows, first, -(-(tb.lens() + reserve) // self.ps))
+        b = Batch(tb, rows, P, E, reserve, locks, own_rows=own)
         start = np.zeros(B, np.int32)
         if B:
             start[1:] = np.cumsum(E)[:-1]
@@ -340,4 +376,5 @@ class Engine:
             self.tree.free(np.concatenate(tails))
         # the rows' entries are left as they are: the next schedule rewrites
         # every entry a request can read
-        self.free_rows.extend(int(r) for r in b.rows)
+        if b.own_rows:
+            self.free_rows.extend(int(r) for r in b.rows)

@@ -118,3 +118,32 @@ def test_any_cached_length_gives_the_same_bits(gpu, dtype, Hq, Hkv, D):
     want = A.extend(q[P:], k, v, P, 1.0 / np.sqrt(D))
     err = float((tail[0].double().cpu() - torch.from_numpy(want)).abs().max())
     assert err <= {"bf16": 2e-2, "f32": 1e-4}[dtype], err
+
+
+def test_batches_rescheduled_on_their_own_rows(gpu):
+    # caller-owned rows (take_rows): the same requests, then a permuted order
+    # (rows rewritten from their first entries), then the same again; only the
+    # entries a schedule changes are uploaded, and every extend still matches
+    # the oracle
+    from oracle import attention as A
+    w = _small_tree()
+    eng = drive.make_engine(w, gpu, max_rows=2 * len(w.requests) + 4)
+    drive.populate(eng, w, device=gpu)
+    n = len(w.requests)
+    rows = eng.take_rows(n)
+    for order in (np.arange(n), np.random.default_rng(0).permutation(n), np.arange(n)):
+        b = eng.schedule([w.prompt_tokens(w.requests[i]) for i in order], reserve=2, rows=rows)
+        assert b.prefix_lens.tolist() == [len(w.prefix_tokens(w.requests[i])) for i in order]
+        qs, ks, vs = zip(*(w.ext_qkv(int(i)) for i in order))
+        o = eng.extend(b, *(drive.up(np.concatenate(x), w, gpu) for x in (qs, ks, vs)), w.sm_scale)
+        got = o.float().cpu().numpy()
+        s = 0
+        for j, i in enumerate(order):
+            K, V = w.context_kv(int(i), 0)
+            want = A.extend(qs[j], K, V, int(b.prefix_lens[j]), w.sm_scale)
+            err = float(np.abs(got[s:s + len(qs[j])] - want).max())
+            assert err <= 2e-2, (j, err)
+            s += len(qs[j])
+        eng.release(b, keep=b.prefix_lens)
+    eng.give_rows(rows)
+    assert len(eng.free_rows) == 2 * len(w.requests) + 4

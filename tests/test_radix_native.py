@@ -180,3 +180,34 @@ def test_token_batch_lengths_equal_sliced_lists():
         t.plan_decode(tb, max_seq, 4, 64, lengths=[len(seqs[0]) + 1] + lengths[1:])
     with pytest.raises(RcError):
         t.insert_rows(tb, np.zeros((12, 400), np.int32), list(range(12)), lengths=[-1] + lengths[1:])
+
+
+@pytest.mark.parametrize("ps", [1, 4])
+def test_first_changed_marks_where_each_row_starts_to_differ(ps):
+    # rows reused by batch after batch: first_changed[b] is the first entry of
+    # row rows[b] that the call changed (its entry count if none), and no entry
+    # before it changed; later batches share prefixes with the rows' earlier
+    # contents, so the changes start anywhere from 0 to past the prefix
+    g = np.random.default_rng(ps)
+    stems = [g.integers(0, 40, g.integers(4, 60)).astype(np.int32) for _ in range(5)]
+    t = RadixTree(1 << 16, page_size=ps) if ps > 1 else RadixTree(1 << 16)
+    table = np.full((6, 80), -1, np.int32)
+    seen = set()
+    for it in range(60):
+        B = int(g.integers(1, 5))
+        rows = g.permutation(6)[:B].astype(np.int32)
+        batch = [np.concatenate([stems[g.integers(0, 5)][:g.integers(0, 60)],
+                                 g.integers(0, 40, g.integers(1, 8)).astype(np.int32)]) for _ in range(B)]
+        reserve = int(g.integers(0, 3))
+        before = table.copy()
+        first = np.zeros(B, np.int64)
+        t.emit_rows(batch, table, rows=rows, reserve=reserve, first_changed=first)
+        for b, r in enumerate(rows):
+            n = -(-(len(batch[b]) + reserve) // ps)
+            diff = np.flatnonzero(table[r, :n] != before[r, :n])
+            assert first[b] == (diff[0] if len(diff) else n), (it, b)
+            assert (table[r, n:] == before[r, n:]).all()
+            seen.add(min(int(first[b]), 3))
+        if it % 2 == 0:
+            t.insert_rows(batch, table, rows)
+    assert {0, 3} <= seen  # rows changed from their first entry, and from later ones
