@@ -147,6 +147,16 @@ class Engine:
     def _i32(self, a) -> torch.Tensor:
         return self._h2d(np.asarray(a, np.int32))
 
+    def _i32_many(self, *arrays) -> List[torch.Tensor]:
+        """Several int32 arrays in one upload: device views of one buffer, each in its array's shape."""
+        parts = [np.asarray(a, np.int32) for a in arrays]
+        flat = self._i32(np.concatenate([p.reshape(-1) for p in parts]) if parts else np.zeros(0, np.int32))
+        out, o = [], 0
+        for p in parts:
+            out.append(flat[o:o + p.size].view(p.shape))
+            o += p.size
+        return out
+
     def _upload_rows(self, rows: np.ndarray, first: Optional[np.ndarray] = None,
                      end: Optional[np.ndarray] = None) -> None:
         """Upload entries [first[i], end[i]) of each row rows[i] (default: whole rows).  The
@@ -268,12 +278,22 @@ class Engine:
         start = np.zeros(B, np.int32)
         if B:
             start[1:] = np.cumsum(E)[:-1]
-        b.dev = {"rows": self._i32(rows), "P": self._i32(P), "E": self._i32(E), "start": self._i32(start)}
+        # every integer array the batch's launches read, in one upload
+        names = ("rows", "P", "E", "start", "slots")
+        b.dev = dict(zip(names, self._i32_many(rows, P, E, start, self._new_slots(rows, P, E))))
         return b
 
     def new_token_slots(self, b: Batch) -> np.ndarray:
-        pos = [np.arange(p, p + e) for p, e in zip(b.prefix_lens, b.extend_lens)]
-        return np.concatenate([self.slots_at(np.full(len(x), r), x) for r, x in zip(b.rows, pos)]).astype(np.int32)
+        return self._new_slots(b.rows, b.prefix_lens, b.extend_lens)
+
+    def _new_slots(self, rows, P, E) -> np.ndarray:
+        """Slots of the new tokens, request after request (positions P_b .. P_b + E_b - 1 of row b)."""
+        n = int(np.sum(E))
+        if n == 0:
+            return np.zeros(0, np.int32)
+        r = np.repeat(np.asarray(rows, np.int64), E)
+        pos = np.arange(n, dtype=np.int64) - np.repeat(np.cumsum(E) - E, E) + np.repeat(np.asarray(P, np.int64), E)
+        return self.slots_at(r, pos).astype(np.int32)
 
     def extend(self, b: Batch, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, sm_scale: float,
                o: Optional[torch.Tensor] = None, store: bool = True, cascade: bool = False,
@@ -294,10 +314,10 @@ class Engine:
             return o
         if cascade:
             plan = self.tree.plan_extend(b.tb, b.prefix_lens, b.extend_lens, self.shape.group, chunk, rows=b.rows)
-            plan.to(self.device, uploader=self._h2d)
             seq = np.concatenate([p + np.arange(1, e + 1) for p, e in zip(b.prefix_lens, b.extend_lens)])
+            plan.dev, seq_d = self._i32_many(plan.host, seq)
             ws = torch.empty(api.decode_workspace_bytes(self.shape, plan), dtype=torch.uint8, device=self.device)
-            api.extend_attention_shared(self.shape, o, q, self.k_pool, self.v_pool, self.table_d, self._i32(seq),
+            api.extend_attention_shared(self.shape, o, q, self.k_pool, self.v_pool, self.table_d, seq_d,
                                         plan, sm_scale, ws)
             return o
         api.extend_attention(self.shape, o, q, k_new, v_new, self.k_pool, self.v_pool, self.table_d, b.dev["P"],
@@ -338,13 +358,13 @@ class Engine:
             plan = self.tree.plan_decode(b.tb, max_seq, g, chunk, rows=b.rows, lengths=com)
         else:
             plan = api.plan_decode_unshared(max_seq, g, chunk, rows=b.rows)
-        plan.to(self.device, uploader=self._h2d)
         steps = np.arange(n_steps, dtype=np.int32)[:, None]
         pos = base[None, :] + steps                                    # [T, B]
         slots = self.slots_at(b.rows[None, :].repeat(n_steps, 0), pos)  # [T, B]
         seq = pos + 1
+        plan.dev, slots_d, seq_d = self._i32_many(plan.host, slots, seq)
         ws = torch.empty(api.decode_workspace_bytes(self.shape, plan), dtype=torch.uint8, device=self.device)
-        return DecodeState(plan, base, n_steps, self._i32(slots), self._i32(seq), ws)
+        return DecodeState(plan, base, n_steps, slots_d, seq_d, ws)
 
     def decode_step(self, st: DecodeState, t: int, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                     sm_scale: float, o: Optional[torch.Tensor] = None, fused_store: bool = True) -> torch.Tensor:
