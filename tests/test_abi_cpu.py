@@ -129,3 +129,17 @@ def test_error_text_is_thread_local_and_set():
     sh = shape(d=96)
     N.lib.rc_kv_store(C.byref(sh), FAKE, FAKE, FAKE, FAKE, FAKE, 4, None)
     assert "head_dim" in N.last_error()
+
+
+def test_table_upload_argument_checks():
+    up = N.lib.rc_upload_table_rows
+    # (dev, dev_stride, host, host_stride, row0, n_rows, col0, col1, stream)
+    assert up(FAKE, 8, FAKE, 8, 0, 0, 0, 8, None) == N.RC_OK      # no rows: nothing to copy
+    assert up(FAKE, 8, FAKE, 8, 0, 4, 3, 3, None) == N.RC_OK      # empty column range
+    assert up(FAKE, 8, FAKE, 8, 0, 4, 0, 9, None) == N.RC_ERR_ARG  # past the device row
+    assert up(FAKE, 16, FAKE, 8, 0, 4, 0, 9, None) == N.RC_ERR_ARG  # past the host row
+    assert up(FAKE, 8, FAKE, 8, 0, 4, 5, 4, None) == N.RC_ERR_ARG  # reversed columns
+    assert up(FAKE, 8, FAKE, 8, -1, 4, 0, 8, None) == N.RC_ERR_ARG
+    assert up(FAKE, 8, FAKE, 8, 0, -1, 0, 8, None) == N.RC_ERR_ARG
+    assert up(None, 8, FAKE, 8, 0, 4, 0, 8, None) == N.RC_ERR_ARG
+    assert "rectangle" in N.last_error() or "NULL" in N.last_error()
