@@ -602,8 +602,8 @@ def cpu_baseline_tree(w, n_req, n_dec, tokens_per_step, T):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU: the path is a single-GPU kernel library and this build runs on "
-              "one MI355X; run it with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU: the path is a single-GPU kernel library measured on one MI355X; "
+              "run it with --gpus 1.", file=sys.stderr)
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
