@@ -342,6 +342,7 @@ __device__ __forceinline__ void attn_bf16_body(const Args& a, const int mode, co
   // are issued), so no wait for these loads lands before their use a stage
   // later.
   auto load_slots = [&](int (&sl)[KPT], int kt) {
+    if (kt >= w.ext_begin) return;  // (uniform) only new tokens: no table entries needed
 #pragma unroll
     for (int r = 0; r < KPT; ++r) {
       const int j = min(kt + lkey(r), w.key_end - 1);  // keys past the end repeat the last one
@@ -379,6 +380,16 @@ __device__ __forceinline__ void attn_bf16_body(const Args& a, const int mode, co
         const int blk = (NW * r + wave) * KPB * D;
         dma(kcol + off, dk + blk);
         dma(vcol + off, dv + blk);
+      }
+      return;
+    }
+    if (kt >= w.ext_begin) {  // every key of the stage is a new token
+#pragma unroll
+      for (int r = 0; r < KPT; ++r) {
+        const int blk = (NW * r + wave) * KPB * D;
+        const uint64_t off = (uint64_t)(w.ext_base + (min(kt + lkey(r), w.key_end - 1) - w.ext_begin)) * row_bytes;
+        dma(kncol + off, dk + blk);
+        dma(vncol + off, dv + blk);
       }
       return;
     }
