@@ -284,7 +284,9 @@ __device__ __forceinline__ i16x4 lds_read_tr(const uint16_t* p) {
 // are exact up to rounding for any reference maximum.
 constexpr float RESCALE_SLACK = 8.f;
 
-template <int D, int NW = 4>
+// STREAM: K/V loads are nontemporal (decode steps read each range once per
+// launch; extends re-read a prefix across tiles and keep it in L2).
+template <int D, int NW = 4, bool STREAM = false>
 __device__ __forceinline__ void attn_bf16_body(const Args& a, const int mode, const int L, uint16_t (&sK)[2][BN * D],
                                                uint16_t (&sV)[2][BN * D]) {
   constexpr int CH = D / 8;                 // 16-byte chunks per key row
@@ -360,7 +362,10 @@ __device__ __forceinline__ void attn_bf16_body(const Args& a, const int mode, co
   // separates its write from the load that reads it.
   auto dma = [&](const char* src, uint16_t* dst) {
     const uint32_t lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint16_t*)dst;
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(lds) : "memory", "m0");
+    if constexpr (STREAM)
+      asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt" : : "v"(src), "s"(lds) : "memory", "m0");
+    else
+      asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(lds) : "memory", "m0");
   };
   // Out-of-range slots are clamped (and reported), so every load stays in
   // the pool.  Keys past the range end are loaded as copies of the last key,
