@@ -187,7 +187,8 @@ typedef struct rc_plan_info {
   int32_t shared_items;/* items with more than one member                       */
   int32_t narrow_begin;/* items from here on have members*group <= 16 (the plan */
                        /* lists wider items first)                              */
-  int32_t reserved;
+  int32_t narrow_first;/* 1: the decode launch deals out the narrow items before */
+                       /* the wide ones (the longer-running class goes first)   */
   int64_t plan_ints;   /* length of the plan buffer in int32                    */
   int64_t unique_positions; /* sum over items of (pos_end - pos_begin)         */
   int64_t logical_positions;/* sum over requests of their context length       */

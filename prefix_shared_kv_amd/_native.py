@@ -28,7 +28,7 @@ class RcShape(C.Structure):
 class RcPlanInfo(C.Structure):
     _fields_ = [("n_items", C.c_int32), ("n_members", C.c_int32), ("max_splits", C.c_int32), ("batch", C.c_int32),
                 ("group", C.c_int32), ("chunk", C.c_int32), ("max_cols", C.c_int32), ("shared_items", C.c_int32),
-                ("narrow_begin", C.c_int32), ("reserved", C.c_int32), ("plan_ints", C.c_int64), ("unique_positions", C.c_int64), ("logical_positions", C.c_int64)]
+                ("narrow_begin", C.c_int32), ("narrow_first", C.c_int32), ("plan_ints", C.c_int64), ("unique_positions", C.c_int64), ("logical_positions", C.c_int64)]
 
 
 class RcRadixStats(C.Structure):

@@ -78,6 +78,7 @@ struct Args {
   const int32_t* new_slots;    // decode: pool slot of each request's current token (with k_new/v_new)
   int32_t n_items, n_members;  // from the planner's host summary
   int32_t narrow_begin;        // first item with members*group <= 16
+  int32_t narrow_first;        // workgroups run the narrow items first, then the wide ones
   int32_t n_wide_blocks;       // workgroups that run wide items
   int32_t n_narrow_units;      // (narrow item, kv head) pairs, one wave each
   int32_t rows_path;           // narrow items by groups of four kv heads (Hkv % 4 == 0)

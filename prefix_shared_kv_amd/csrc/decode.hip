@@ -401,12 +401,17 @@ __global__ __launch_bounds__(NT, 2) void decode_attn_bf16(Args a) {
   __shared__ __attribute__((aligned(16))) uint16_t sK[2][BN * D];
   __shared__ __attribute__((aligned(16))) uint16_t sV[2][BN * D];
   static_assert(2 * BN == 4 * BNN, "narrow tiles reuse the wide stage buffers");
-  if ((int)blockIdx.x < a.n_wide_blocks) {
-    attn_bf16_body<D, 4, ROLE == 0>(a, DECODE, blockIdx.x, sK, sV);
+  // the grid is [wide workgroups][narrow workgroups], or the other way round
+  // when the plan says the narrow class runs longer (workgroups start in order)
+  const int n_narrow_blocks = (a.n_narrow_units + 3) >> 2;
+  const int bid = (int)blockIdx.x;
+  const bool wide = a.narrow_first ? bid >= n_narrow_blocks : bid < a.n_wide_blocks;
+  if (wide) {
+    attn_bf16_body<D, 4, ROLE == 0>(a, DECODE, a.narrow_first ? bid - n_narrow_blocks : bid, sK, sV);
     return;
   }
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave
-  const int unit = ((int)blockIdx.x - a.n_wide_blocks) * 4 + wave;
+  const int unit = (a.narrow_first ? bid : bid - a.n_wide_blocks) * 4 + wave;
   if (unit >= a.n_narrow_units) return;
   decode_narrow_body<D, ROLE == 0>(a, unit, &sK[0][0] + wave * BNN * D, &sV[0][0] + wave * BNN * D);
 }
@@ -540,6 +545,7 @@ rc_status split_k_attention(const rc_shape* shape, void* o, const void* q, void*
   a.plan = plan_dev; a.seq_lens = seq_lens;
   a.n_items = info->n_items; a.n_members = info->n_members;
   a.narrow_begin = info->narrow_begin;
+  a.narrow_first = info->narrow_first != 0;
   a.ws_o = (float*)workspace;
   a.ws_ml = (float*)workspace + parts * shape->head_dim;
   a.max_splits = info->max_splits;

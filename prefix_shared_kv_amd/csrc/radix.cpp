@@ -862,6 +862,7 @@ struct PlanBuilder {
   std::vector<int32_t> nsplit;
   int32_t shared_items = 0;
   int32_t narrow_begin = 0;
+  int32_t narrow_first = 0;
   int64_t unique_pos = 0;
 
   int32_t row_of(int32_t b) const { return rows ? rows[b] : b; }
@@ -921,6 +922,14 @@ struct PlanBuilder {
     std::stable_sort(wide.begin(), wide.end(), by_cost);
     std::stable_sort(narrow.begin(), narrow.end(), by_cost);
     narrow_begin = (int32_t)wide.size();
+    // Which class the launch deals out first: the one holding the item that
+    // takes longest, so that no long item starts late.  A narrow item is one
+    // wave per kv head and streams its range at roughly half the rate of a
+    // wide item's four waves, so its length counts double.
+    int64_t long_wide = 0, long_narrow = 0;
+    for (const Item& it : wide) long_wide = std::max<int64_t>(long_wide, it.v[2] - it.v[1]);
+    for (const Item& it : narrow) long_narrow = std::max<int64_t>(long_narrow, it.v[2] - it.v[1]);
+    narrow_first = 2 * long_narrow > long_wide;
     item_rows.reserve((wide.size() + narrow.size()) * RC_PLAN_ITEM);
     for (auto* list : {&wide, &narrow})
       for (Item& it : *list) {
@@ -947,7 +956,7 @@ struct PlanBuilder {
     info->max_cols = max_m * group;
     info->shared_items = shared_items;
     info->narrow_begin = narrow_begin;
-    info->reserved = 0;
+    info->narrow_first = narrow_first;
     info->plan_ints = need;
     info->unique_positions = unique_pos;
     info->logical_positions = logical;

@@ -136,3 +136,24 @@ def test_plans_cover_every_context_with_shared_slots(case):
     lens = np.array([len(b) for b in batch])
     plan = t.plan_decode(batch, lens + reserve, group, chunk)
     check_plan(plan, lens + reserve, np.arange(len(batch)), table, group)
+
+
+def test_launch_order_puts_the_longer_running_class_first():
+    # a long shared prefix and short own tails: wide items first; short shared
+    # heads and long own tails: narrow items first (a narrow item's length counts
+    # double: one wave streams it against a wide item's four)
+    g = np.random.default_rng(3)
+    for shared, own, want in ((2048, 64, 0), (256, 2000, 1), (1000, 600, 1), (1000, 400, 0)):
+        stem = g.integers(0, 1000, shared).astype(np.int32)
+        batch = [np.concatenate([stem, g.integers(0, 1000, own).astype(np.int32)]) for _ in range(64)]
+        t = RadixTree(1 << 20)
+        table = np.full((64, shared + own + 8), -1, np.int32)
+        t.emit_rows(batch, table)
+        t.insert_rows(batch, table, np.arange(64, dtype=np.int32))
+        lens = np.array([len(x) for x in batch], np.int32)
+        plan = t.plan_decode(batch, lens, group=4, chunk=4096)
+        items = plan.items()
+        nb = plan.info.narrow_begin
+        lw = int((items[:nb, 2] - items[:nb, 1]).max())
+        ln = int((items[nb:, 2] - items[nb:, 1]).max())
+        assert (lw, ln) == (shared, own) and plan.info.narrow_first == want, (shared, own)
