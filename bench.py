@@ -116,7 +116,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", choices=["classify_heavy", "multi_turn_tree"], default="classify_heavy")
-    ap.add_argument("--chunk", type=int, default=4096, help="decode split size (nominal positions per work item)")
+    ap.add_argument("--chunk", type=int, default=None,
+                    help="decode split size, nominal positions per work item (default: 4096 for classify_heavy, "
+                         "1024 for multi_turn_tree)")
     ap.add_argument("--decode-steps", type=int, default=None,
                     help="decode steps per step (default 8 for classify_heavy, 256 for multi_turn_tree)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -225,6 +227,9 @@ def bench_classify_heavy(args):
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     pk.set_tuning("decode_rows", args.decode_rows)
+    # pieces of 4096 positions: 1024 long contexts give about two work units per
+    # resident wave, and longer pieces start up fewer times
+    args.chunk = args.chunk or 4096
     T = args.decode_steps or 8
     wc = W.classify64()
     wh = W.heavy_decode(n_decode=T)
@@ -457,6 +462,9 @@ def bench_multi_turn_tree(args):
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     pk.set_tuning("decode_rows", args.decode_rows)
+    # pieces of 1024 positions: the tree's 256 requests give only about 1.3 work
+    # units per resident wave at 4096, and the longest own ranges then end late
+    args.chunk = args.chunk or 1024
     T = args.decode_steps or 256
     w = W.multi_turn_tree(n_decode=T)
     sh = w.shape
