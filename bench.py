@@ -113,8 +113,8 @@ def log(msg):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=5)
-    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", choices=["classify_heavy", "multi_turn_tree"], default="classify_heavy")
     ap.add_argument("--chunk", type=int, default=None,
                     help="decode split size, nominal positions per work item (default: 4096 for classify_heavy, "
