@@ -182,3 +182,23 @@ def test_heavy_decode_full_size(gpu):
     drive.populate(eng, w, device=gpu, device_values=True)
     b = drive.schedule_decode_only(eng, w)
     run_decode(w, eng, b, ctx, sample(len(w.requests), 8, 4, always=(0, 15, 16, 1023)), {0, 3, 7}, gpu)
+
+
+def test_heavy_decode_full_size_paged(gpu):
+    # the same workload over a pool of 16-token pages: the table holds page ids,
+    # the tree shares whole pages, and each request's decode tokens take one
+    # page of their own (the pool grows by a page per request)
+    from prefix_shared_kv_amd import KVShape
+    from prefix_shared_kv_amd.engine import Engine
+    ps = 16
+    w = W.heavy_decode()
+    sh = w.shape
+    S = -(-(w.pool_slots + len(w.requests) * ps) // ps) * ps
+    shape = KVShape(sh.num_q_heads, sh.num_kv_heads, sh.head_dim, torch.bfloat16, S, ps)
+    longest = max(len(w.prompt_tokens(r)) + r.n_decode + 1 for r in w.requests)
+    eng = Engine(shape, longest + ps, len(w.requests) + 1, gpu)
+    ctx = Context(w, device=gpu)
+    drive.populate(eng, w, device=gpu, device_values=True)
+    b = drive.schedule_decode_only(eng, w)
+    assert (b.prefix_lens == 8192).all()
+    run_decode(w, eng, b, ctx, sample(len(w.requests), 8, 5, always=(0, 15, 16, 1023)), {0, 3, 7}, gpu)
