@@ -2,6 +2,11 @@ import os
 import sys
 
 import pytest
+from hypothesis import settings
+
+# property tests draw the same examples on every run (no example database)
+settings.register_profile("fixed", derandomize=True, database=None)
+settings.load_profile("fixed")
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 if ROOT not in sys.path:
