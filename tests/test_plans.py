@@ -157,3 +157,22 @@ def test_launch_order_puts_the_longer_running_class_first():
         lw = int((items[:nb, 2] - items[:nb, 1]).max())
         ln = int((items[nb:, 2] - items[nb:, 1]).max())
         assert (lw, ln) == (shared, own) and plan.info.narrow_first == want, (shared, own)
+
+
+def test_unshared_and_cascade_plans_choose_their_launch_order():
+    # an unshared plan has only narrow items (one member each): they go first;
+    # a cascade plan over a long document with short label branches keeps its
+    # wide document ranges first
+    from prefix_shared_kv_amd import api
+    plan = api.plan_decode_unshared(np.array([5000, 300, 1], np.int32), 4, 4096)
+    assert plan.info.narrow_begin == 0 and plan.info.narrow_first == 1
+    g = np.random.default_rng(5)
+    doc = g.integers(0, 1000, 4096).astype(np.int32)
+    batch = [np.concatenate([doc, g.integers(0, 1000, n).astype(np.int32)]) for n in (2, 9, 16, 5) * 16]
+    t = RadixTree(1 << 20)
+    table = np.full((len(batch), 4200), -1, np.int32)
+    t.emit_rows([doc], table[:1])
+    t.insert_rows([doc], table[:1], np.zeros(1, np.int32))
+    P, E = t.emit_rows(batch, table)
+    plan = t.plan_extend(batch, P, E, group=8, chunk=1024)
+    assert plan.info.narrow_begin > 0 and plan.info.narrow_first == 0
