@@ -244,3 +244,21 @@ def test_large_batches_walk_on_several_threads_like_single_requests():
     plan = t.plan_decode(batch, P.astype(np.int32) + 1, group=4, chunk=4096, rows=rows,
                          lengths=P.astype(np.int64))
     _check_plan(plan, P + 1, rows, _expanded(table, ps), 4)
+
+
+@pytest.mark.parametrize("ps", [0, -4, 3, 12, 2048])
+def test_paged_tree_rejects_bad_page_sizes(ps):
+    with pytest.raises((RcError, ValueError)):
+        RadixTree(64, page_size=ps)
+
+
+def test_paged_calls_reject_mismatched_page_rows():
+    t = RadixTree(16, page_size=4)
+    seq = np.arange(1, 10, dtype=np.int32)          # 2 full pages + 1 token
+    with pytest.raises((RcError, ValueError)):
+        t.insert(seq, t.alloc(3))                   # one page id per full page: 2, not 3
+    assert t.stats()["cached_tokens"] == 0 and t.stats()["page_symbols"] == 0
+    table = np.full((1, 2), -1, np.int32)           # 9 tokens + 0 reserve need 3 pages
+    with pytest.raises(RcError) as e:
+        t.emit_rows([seq], table)
+    assert e.value.status == N.RC_ERR_RANGE
