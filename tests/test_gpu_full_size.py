@@ -1,7 +1,7 @@
 """GPU parity at the workloads' full sizes, in the launch configuration the
-benchmark times (shared decode plan, 4096-position pieces, the step's K/V
-stored by the decode call).  Every phase runs in full on the GPU; the oracle
-recomputes a seeded sample of its outputs one request or one row at a time
+benchmark times (shared decode plan, pieces of 4096 positions, 1024 for the
+multi-turn tree, the step's K/V stored by the decode call).  Every phase runs
+in full on the GPU; the oracle recomputes a seeded sample of its outputs one request or one row at a time
 (all heads of each sampled row), within max-abs 2e-2 for bf16 inputs.
 
 Pools too large to draw on the host (the heavy-decode workload's 9 GB, the
@@ -107,11 +107,11 @@ def check_extend(w, ctx, o, rids):
     return worst
 
 
-def run_decode(w, eng, b, ctx, rids_checked, steps_checked, device):
+def run_decode(w, eng, b, ctx, rids_checked, steps_checked, device, chunk=CHUNK):
     B = len(w.requests)
     n_steps = max(r.n_decode for r in w.requests)
     base = [len(w.prompt_tokens(r)) for r in w.requests]
-    st = eng.prepare_decode(b, base, n_steps, chunk=CHUNK)
+    st = eng.prepare_decode(b, base, n_steps, chunk=chunk)
     worst = 0.0
     for t in range(n_steps):
         q, k, v = drive.decode_inputs(w, range(B), t, device=device)
@@ -149,7 +149,8 @@ def test_multi_turn_tree_full_size(gpu):
     drive.populate(eng, w, device=gpu, device_values=True)
     b, o = drive.extend_requests(eng, w, device=gpu)
     check_extend(w, ctx, o, sample(len(w.requests), 16, 2, always=(0, 255)))
-    run_decode(w, eng, b, ctx, sample(len(w.requests), 8, 3, always=(0, 255)), {0, 128, 255}, gpu)
+    # the benchmark runs this workload's decode in pieces of 1024 positions
+    run_decode(w, eng, b, ctx, sample(len(w.requests), 8, 3, always=(0, 255)), {0, 128, 255}, gpu, chunk=1024)
 
 
 def test_classify64_full_size(gpu):
