@@ -130,7 +130,6 @@ def parse():
                     help="classify_heavy: split size of the shared-prefix plan of the label branches")
     ap.add_argument("--branch-tiles", action="store_true",
                     help="classify_heavy: label branches on the extend tiles instead of the shared-prefix plan")
-    ap.add_argument("--decode-rows", type=int, default=0, help="narrow decode by groups of four kv heads (rc_set_tuning)")
     ap.add_argument("--host-phases", action="store_true", help="report host wall time per phase of the last step")
     ap.add_argument("--page-size", type=int, default=1,
                     help="classify_heavy: KV pool pages of this many positions (the table then holds page ids)")
@@ -226,7 +225,6 @@ def bench_classify_heavy(args):
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    pk.set_tuning("decode_rows", args.decode_rows)
     # pieces of 4096 positions: 1024 long contexts give about two work units per
     # resident wave, and longer pieces start up fewer times
     args.chunk = args.chunk or 4096
@@ -461,7 +459,6 @@ def bench_multi_turn_tree(args):
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    pk.set_tuning("decode_rows", args.decode_rows)
     # pieces of 1024 positions: the tree's 256 requests give only about 1.3 work
     # units per resident wave at 4096, and the longest own ranges then end late
     args.chunk = args.chunk or 1024

@@ -36,6 +36,8 @@
  *              req_to_token    [rows, stride] int32   (slot of position j of a
  *                                                      request's context)
  *   - Grouped-query attention: query head h reads kv head h / (Hq / Hkv).
+ *   - sm_scale (the softmax scale, usually 1/sqrt(head_dim)) must be finite
+ *     and positive, else RC_ERR_ARG.
  *   - Causal alignment is by absolute position: new token i of a request with
  *     a cached prefix of P tokens is at position P+i and sees keys 0..P+i.
  */
@@ -164,9 +166,13 @@ rc_status rc_extend_attention(const rc_shape* shape, void* o, const void* q, con
 /*   [0..8)      header {RC_PLAN_MAGIC, n_items, n_members, max_splits,        */
 /*                        batch, group, chunk, max_cols}                      */
 /*   items       n_items x 8 {rep_row, pos_begin, pos_end, split, member_off, */
-/*                            member_cnt, 0, 0}                               */
+/*                            member_cnt, flags, 0}                           */
 /*   members     n_members batch indices                                       */
 /*   n_splits    batch entries: partial results per request                    */
+/* flags: RC_PLAN_ITEM_OWN marks a piece of its one member's own positions   */
+/* (the part of its context no other request of the batch reads); only such  */
+/* an item stores the current token (rc_decode_attention with k_new), so a   */
+/* position other requests read is never written.                            */
 /* Items with members*group > 16 come first, then the narrow ones.           */
 /* The kernel clamps pos_end to seq_lens[first member]; the planners only    */
 /* put a range in a shared item when it lies inside every member's context.  */
@@ -174,6 +180,7 @@ rc_status rc_extend_attention(const rc_shape* shape, void* o, const void* q, con
 #define RC_PLAN_MAGIC 0x52435031 /* "RCP1" */
 #define RC_PLAN_HEADER 8
 #define RC_PLAN_ITEM 8
+#define RC_PLAN_ITEM_OWN 1 /* item flag: the range holds its member's own positions */
 
 typedef struct rc_plan_info {
   int32_t n_items;
@@ -214,6 +221,9 @@ int64_t rc_decode_workspace_bytes(const rc_shape* shape, const rc_plan_info* inf
 /* pool already (k_new = v_new = new_slots = NULL), or are passed in k_new / */
 /* v_new [batch, Hkv, D]: then the call also stores them at pool slot        */
 /* new_slots[b] (what rc_kv_store would do) and uses them as key L_b - 1.    */
+/* That key is taken from k_new / v_new by the RC_PLAN_ITEM_OWN item holding */
+/* position L_b - 1; a plan whose request has no such item (position L_b - 1 */
+/* inside a shared range) reads the key from the pool and stores nothing.    */
 /* Split-K: each item writes fp32 partial (max, sum, unnormalised output)    */
 /* per member and head; a merge kernel combines each request's partials in   */
 /* split order (deterministic, no float atomics).                             */
@@ -477,13 +487,6 @@ rc_status rc_label_distribution(const void* logits, int32_t dtype, int64_t row_s
                                 int32_t n_rows, const int32_t* label_ids, int32_t n_labels,
                                 const int32_t* counts, float* probs, int32_t* choice, float* expected,
                                 float* confidence, void* stream);
-
-/* Tuning switches (process-wide, take effect on the next call):             */
-/*   "decode_rows" 0|1: narrow decode items are computed by groups of four kv */
-/*                 heads per workgroup, each load covering whole slot-row    */
-/*                 segments (1) instead of one wave per kv head (0, default). */
-/* Unknown names return RC_ERR_ARG.                                          */
-rc_status rc_set_tuning(const char* name, int64_t value);
 
 /* ------------------------------------------------------------------------ */
 /* Kernel timing.  While enabled, every kernel the library launches is       */

@@ -7,5 +7,5 @@ include/rc.h for the C ABI.
 """
 from .api import (DecodePlan, KVShape, RadixTree, TokenBatch, decode_attention,  # noqa: F401
                   decode_workspace_bytes, extend_attention, extend_attention_shared, kv_store, label_distribution,
-                  plan_decode_unshared, prof_collect, prof_enable, prof_tag, set_error_word, set_tuning, version)
+                  plan_decode_unshared, prof_collect, prof_enable, prof_tag, set_error_word, version)
 from ._native import RcError  # noqa: F401

@@ -1,6 +1,7 @@
 """ctypes declarations for librcattn.so (the C ABI in include/rc.h).
 
-The library is built in-tree by ``python -m prefix_shared_kv_amd.build``.  There
+The library is built in-tree by ``python prefix_shared_kv_amd/build.py`` (run by path:
+importing the package would load the library being rebuilt).  There
 is no fallback: if it is missing or does not load, importing raises.
 """
 from __future__ import annotations
@@ -13,7 +14,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "librcattn.s
 RC_OK, RC_ERR_ARG, RC_ERR_SHAPE, RC_ERR_DTYPE, RC_ERR_RANGE, RC_ERR_NOMEM, RC_ERR_HIP, RC_ERR_INTERNAL = range(8)
 RC_F32, RC_BF16 = 0, 1
 RC_DEVERR_SLOT, RC_DEVERR_TABLE, RC_DEVERR_LENGTH, RC_DEVERR_PLAN = 1, 2, 4, 8
-RC_PLAN_MAGIC, RC_PLAN_HEADER, RC_PLAN_ITEM = 0x52435031, 8, 8
+RC_PLAN_MAGIC, RC_PLAN_HEADER, RC_PLAN_ITEM, RC_PLAN_ITEM_OWN = 0x52435031, 8, 8, 1
 
 STATUS_NAMES = {0: "RC_OK", 1: "RC_ERR_ARG", 2: "RC_ERR_SHAPE", 3: "RC_ERR_DTYPE", 4: "RC_ERR_RANGE",
                 5: "RC_ERR_NOMEM", 6: "RC_ERR_HIP", 7: "RC_ERR_INTERNAL"}
@@ -82,7 +83,6 @@ _SIGS = {
     "rc_radix_plan_decode": (i32, [P, i32, P, P, P, P, P, i32, i32, P, i64, C.POINTER(RcPlanInfo)]),
     "rc_radix_plan_extend": (i32, [P, i32, P, P, P, P, P, i32, i32, P, i64, C.POINTER(RcPlanInfo)]),
     "rc_radix_stats_get": (i32, [P, C.POINTER(RcRadixStats)]),
-    "rc_set_tuning": (i32, [C.c_char_p, i64]),
     "rc_prof_enable": (i32, [i32]),
     "rc_prof_tag": (i32, [C.c_char_p]),
     "rc_prof_collect": (i32, [C.POINTER(RcProfEntry), i32, I32P]),

@@ -468,11 +468,6 @@ class RadixTree:
         return {f: getattr(st, f) for f, _ in RcRadixStats._fields_}
 
 
-def set_tuning(name: str, value: int) -> None:
-    """Library-wide tuning switch (rc_set_tuning)."""
-    check(lib.rc_set_tuning(name.encode(), int(value)))
-
-
 def prof_enable(on: bool = True) -> None:
     check(lib.rc_prof_enable(1 if on else 0))
 

@@ -81,7 +81,6 @@ struct Args {
   int32_t narrow_first;        // workgroups run the narrow items first, then the wide ones
   int32_t n_wide_blocks;       // workgroups that run wide items
   int32_t n_narrow_units;      // (narrow item, kv head) pairs, one wave each
-  int32_t rows_path;           // narrow items by groups of four kv heads (Hkv % 4 == 0)
   const int32_t* seq_lens;
   float* ws_o;
   float* ws_ml;
@@ -189,9 +188,10 @@ __device__ Work resolve(const Args& a, int mode, int L, bool leader) {
     w.ext_begin = INT_MAX;
     w.ext_base = 0;
     w.store_b = -1;
-    // The item holding a request's last position (its own range) takes the
-    // current token's K/V from k_new/v_new and writes them to the pool.
-    if (a.k_new && w.mcnt == 1 && sl >= 1 && pb <= sl - 1 && pe >= sl) {
+    // The piece of a request's own range (marked by the planner) holding its
+    // last position takes the current token's K/V from k_new/v_new and writes
+    // them to the pool; a shared range is never written.
+    if (a.k_new && (it[6] & RC_PLAN_ITEM_OWN) && w.mcnt == 1 && sl >= 1 && pb <= sl - 1 && pe >= sl) {
       w.ext_begin = sl - 1;
       w.ext_base = mem[0];
       w.store_b = mem[0];
@@ -287,15 +287,27 @@ constexpr float RESCALE_SLACK = 8.f;
 
 // STREAM: K/V loads are nontemporal (decode steps read each range once per
 // launch; extends re-read a prefix across tiles and keep it in L2).
-template <int D, int NW = 4, bool STREAM = false>
-__device__ __forceinline__ void attn_bf16_body(const Args& a, const int mode, const int L, uint16_t (&sK)[2][BN * D],
+//
+// Keys whose table entry gives no valid pool slot are absent from the
+// softmax.  The usual pass loads such a key from a clamped slot (every load
+// stays inside the pool) and only notes it; if any lane of the workgroup met
+// one, it writes nothing and returns true, and the caller runs the item again
+// with CAREFUL set: that pass loads zeros for those keys and gives them a -inf
+// score by reading each key's table entry beside its score.  The check costs
+// the usual pass one workgroup-wide OR per item.
+template <int D, int NW = 4, bool STREAM = false, bool CAREFUL = false>
+__device__ __forceinline__ bool attn_bf16_body(const Args& a, const int mode, const int L, uint16_t (&sK)[2][BN * D],
                                                uint16_t (&sV)[2][BN * D]) {
   constexpr int CH = D / 8;                 // 16-byte chunks per key row
   constexpr int KPT = BN * CH / (64 * NW);  // keys per thread per stage
   constexpr int NKS = D / 16;        // MFMA k-steps over D
   constexpr int NDB = D / 32;        // 32-row blocks of O^T
   const Work w = resolve(a, mode, L, threadIdx.x == 0);
-  if (!w.valid) return;  // uniform over the workgroup
+  if (!w.valid) return false;  // uniform over the workgroup
+  // set by lanes that met an invalid slot; cleared before the first stage
+  // barrier, so no lane can set it earlier
+  __shared__ int32_t s_absent;
+  if (!CAREFUL && threadIdx.x == 0) s_absent = 0;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: LDS block addresses stay scalar
@@ -333,6 +345,9 @@ __device__ __forceinline__ void attn_bf16_body(const Args& a, const int mode, co
   const char* vcol = (const char*)a.v_pool + coff;
   const char* kncol = (const char*)a.k_new + coff;
   const char* vncol = (const char*)a.v_new + coff;
+  // k_new / v_new relative to the pools (offsets, not a choice between pointers,
+  // keep the address arithmetic in registers)
+  const uint64_t knew_off = (uint64_t)kncol - (uint64_t)kcol, vnew_off = (uint64_t)vncol - (uint64_t)vcol;
   const int32_t* trow = a.table + w.row * a.stride;
   const int sh = a.page_shift;
   const uint32_t npages = (uint32_t)(a.pool_slots >> sh);
@@ -368,9 +383,12 @@ __device__ __forceinline__ void attn_bf16_body(const Args& a, const int mode, co
     else
       asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(lds) : "memory", "m0");
   };
+  // this lane's 16 bytes of a 1 KiB block, as a load would have written them
+  auto zero16 = [&](uint16_t* dst) { *(u32x4*)(dst + lane * 8) = u32x4{0, 0, 0, 0}; };
   // Out-of-range slots are clamped (and reported), so every load stays in
-  // the pool.  Keys past the range end are loaded as copies of the last key,
-  // so the tile holds finite values where p = 0 multiplies them.
+  // the pool; the careful pass stores zeros for them instead.  Keys past the
+  // range end are loaded as copies of the last key, so the tile holds finite
+  // values where p = 0 multiplies them.
   auto issue = [&](uint16_t* dk, uint16_t* dv, const int (&sl)[KPT], int kt) {
     if (kt + BN <= plain_end) {  // every key of the stage is a cached prefix key
       uint32_t s[KPT], mx = 0;
@@ -384,8 +402,13 @@ __device__ __forceinline__ void attn_bf16_body(const Args& a, const int mode, co
       for (int r = 0; r < KPT; ++r) {
         const uint64_t off = (uint64_t)min(s[r], nslots - 1) * row_bytes;
         const int blk = (NW * r + wave) * KPB * D;
-        dma(kcol + off, dk + blk);
-        dma(vcol + off, dv + blk);
+        if (CAREFUL && s[r] >= nslots) {
+          zero16(dk + blk);
+          zero16(dv + blk);
+        } else {
+          dma(kcol + off, dk + blk);
+          dma(vcol + off, dv + blk);
+        }
       }
       return;
     }
@@ -399,7 +422,6 @@ __device__ __forceinline__ void attn_bf16_body(const Args& a, const int mode, co
       }
       return;
     }
-    // (integer selects, not a choice between pointers, keep this in registers)
 #pragma unroll
     for (int r = 0; r < KPT; ++r) {
       const int blk = (NW * r + wave) * KPB * D;
@@ -408,11 +430,20 @@ __device__ __forceinline__ void attn_bf16_body(const Args& a, const int mode, co
       const uint32_t sr = (uint32_t)page_slot(sl[r], j, sh, npages);
       bad_slot |= !is_new && sr >= nslots;
       const uint64_t idx = is_new ? (uint64_t)(w.ext_base + (j - w.ext_begin)) : (uint64_t)min(sr, nslots - 1);
-      const uint64_t kb_ = is_new ? (uint64_t)kncol : (uint64_t)kcol;
-      const uint64_t vb_ = is_new ? (uint64_t)vncol : (uint64_t)vcol;
-      dma((const char*)(kb_ + idx * row_bytes), dk + blk);
-      dma((const char*)(vb_ + idx * row_bytes), dv + blk);
+      const uint64_t kb_ = (uint64_t)kcol + (is_new ? knew_off : 0);
+      const uint64_t vb_ = (uint64_t)vcol + (is_new ? vnew_off : 0);
+      if (CAREFUL && !is_new && sr >= nslots) {
+        zero16(dk + blk);
+        zero16(dv + blk);
+      } else {
+        dma((const char*)(kb_ + idx * row_bytes), dk + blk);
+        dma((const char*)(vb_ + idx * row_bytes), dv + blk);
+      }
     }
+  };
+  // careful pass: is key j (a pool key below the range end) without a valid slot?
+  auto absent = [&](int j) {
+    return j < plain_end && (uint32_t)page_slot(trow[j >> sh], j, sh, npages) >= nslots;
   };
 
   // S^T for the two 32-key halves of the stage in LDS.  The halves' MFMA
@@ -456,6 +487,10 @@ __device__ __forceinline__ void attn_bf16_body(const Args& a, const int mode, co
         const int key = kt + (v >> 2) * 8 + hi * 4 + (v & 3);
         s0[v] = (key >= w.key_end || key > col.limit) ? -INFINITY : s0[v];
         s1[v] = (key + 32 >= w.key_end || key + 32 > col.limit) ? -INFINITY : s1[v];
+        if constexpr (CAREFUL) {
+          s0[v] = absent(key) ? -INFINITY : s0[v];
+          s1[v] = absent(key + 32) ? -INFINITY : s1[v];
+        }
       }
     }
     float mx = -INFINITY;
@@ -551,7 +586,7 @@ __device__ __forceinline__ void attn_bf16_body(const Args& a, const int mode, co
   };
   // stages before n_plain need no mask: every key is below the range end and
   // at or below every column's causal limit; the rest (a tail) are masked
-  int n_plain = (w.key_end - kb) / BN;
+  int n_plain = CAREFUL ? 0 : (w.key_end - kb) / BN;
   if (w.min_limit != INT_MAX) n_plain = min(n_plain, max(0, (w.min_limit + 1 - kb) / BN));
   const auto B0 = std::integral_constant<int, 0>{};
   const auto B1 = std::integral_constant<int, 1>{};
@@ -573,8 +608,15 @@ __device__ __forceinline__ void attn_bf16_body(const Args& a, const int mode, co
     if (i + 1 < n_st) step(B1, i + 1, std::true_type{});
   }
 
-  if (bad_slot) flag(a.err, RC_DEVERR_SLOT);
-  if (!active || !col.real) return;
+  if constexpr (!CAREFUL) {
+    if (bad_slot) s_absent = 1;
+    __syncthreads();
+    if (s_absent) {  // some key is absent: the careful pass computes the item
+      if (threadIdx.x == 0) flag(a.err, RC_DEVERR_SLOT);
+      return true;
+    }
+  }
+  if (!active || !col.real) return false;
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   if (mode == EXTEND) {
     const float inv = 1.f / l_tot;
@@ -605,6 +647,14 @@ __device__ __forceinline__ void attn_bf16_body(const Args& a, const int mode, co
       }
     if (hi == 0) *(float2*)(a.ws_ml + pidx * 2) = make_float2(m_run, l_tot);
   }
+  return false;
+}
+
+// One MFMA work item: the usual pass, then the careful one if a key was absent.
+template <int D, int NW, bool STREAM>
+__device__ __forceinline__ void attn_bf16_tile(const Args& a, const int mode, const int L, uint16_t (&sK)[2][BN * D],
+                                               uint16_t (&sV)[2][BN * D]) {
+  if (attn_bf16_body<D, NW, STREAM, false>(a, mode, L, sK, sV)) attn_bf16_body<D, NW, STREAM, true>(a, mode, L, sK, sV);
 }
 
 // fp32 path: one wave per column, lanes over head dims, keys one at a time.
@@ -681,7 +731,10 @@ __device__ __forceinline__ void attn_f32_body(const Args& a, const int mode) {
 rc_status check_common(const rc_shape* shape, float sm_scale) {
   rc_status st = rc::check_shape(shape);
   if (st != RC_OK) return st;
-  if (!std::isfinite(sm_scale)) return rc::fail(RC_ERR_ARG, "sm_scale is not finite");
+  // the kernels take each column's maximum over raw scores and scale it after
+  // (exact for a positive scale), and masked keys hold -inf scores
+  if (!std::isfinite(sm_scale) || !(sm_scale > 0.f))
+    return rc::fail(RC_ERR_ARG, "sm_scale %g is not a finite positive number", (double)sm_scale);
   return RC_OK;
 }
 

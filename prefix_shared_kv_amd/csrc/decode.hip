@@ -18,9 +18,12 @@ namespace {
 // 16-key block, so the softmax reductions cross the 4 lane groups (2 steps).
 constexpr int BNN = 32;  // keys per narrow stage
 
-// STREAM: nontemporal K/V loads (see attn_bf16_body)
-template <int D, bool STREAM = false>
-__device__ __forceinline__ void decode_narrow_body(const Args& a, const int unit, uint16_t* sk, uint16_t* sv) {
+// STREAM: nontemporal K/V loads (see attn_bf16_body).  CAREFUL: the second
+// pass over an item that met a key without a valid slot (as in attn_bf16_body):
+// the usual pass returns true without writing, the careful one loads zeros for
+// such keys and gives them a -inf score.
+template <int D, bool STREAM = false, bool CAREFUL = false>
+__device__ __forceinline__ bool decode_narrow_body(const Args& a, const int unit, uint16_t* sk, uint16_t* sv) {
   constexpr int NKS = D / 32;         // k-steps of 32 over D
   constexpr int NDB = D / 16;         // 16-row blocks of O^T
   constexpr int CH = D / 8;           // 16-byte chunks per key row
@@ -30,7 +33,7 @@ __device__ __forceinline__ void decode_narrow_body(const Args& a, const int unit
   const int grp = lane >> 4, r16 = lane & 15;
   const int L = (a.narrow_begin + unit / a.Hkv) * a.Hkv + unit % a.Hkv;
   const Work w = resolve(a, DECODE, L, lane == 0);
-  if (!w.valid) return;  // uniform over the wave
+  if (!w.valid) return false;  // uniform over the wave
   const Col col = column(a, DECODE, w, r16);
 
   const uint16_t* q = (const uint16_t*)a.q;
@@ -62,13 +65,22 @@ __device__ __forceinline__ void decode_narrow_body(const Args& a, const int unit
       sl[t] = key < w.key_end ? (key >= w.ext_begin ? NEWTOK : trow[key >> sh]) : INT_MIN;
     }
   };
+  // careful pass: bit k of the stage's mask marks key kt + k as absent (set
+  // when the stage is loaded, from a ballot of the lanes that load the key)
+  uint32_t absent_next = 0, absent_cur = 0;
   auto load_kv = [&](u32x4 (&kr)[NI], u32x4 (&vr)[NI], const int (&sl)[NI], int kt, bool partial) {
+    if constexpr (CAREFUL) absent_next = 0;
 #pragma unroll
     for (int t = 0; t < NI; ++t) {
       const bool special = sl[t] == INT_MIN || sl[t] == NEWTOK;
       const int32_t st = special ? sl[t] : page_slot(sl[t], kt + t * KPI + lk, sh, npages);
       const bool ok = (uint32_t)st < (uint32_t)a.pool_slots;
       bad_slot |= !ok & !special;
+      if constexpr (CAREFUL) {
+        const uint64_t bl = __ballot(!ok & !special);  // lane lk * CH loads key t * KPI + lk's first chunk
+#pragma unroll
+        for (int k = 0; k < KPI; ++k) absent_next |= (uint32_t)((bl >> (k * CH)) & 1) << (t * KPI + k);
+      }
       const int64_t off = (int64_t)(ok ? st : 0) * rowHD;
       if constexpr (STREAM) {
         kr[t] = __builtin_nontemporal_load((const u32x4*)(kbase + off));
@@ -88,13 +100,17 @@ __device__ __forceinline__ void decode_narrow_body(const Args& a, const int unit
       }
     }
   };
+  // (the careful pass stores zeros for absent keys: they were loaded from a
+  // stand-in slot, and p = 0 multiplies them)
   auto store = [&](const u32x4 (&kr)[NI], const u32x4 (&vr)[NI]) {
+    if constexpr (CAREFUL) absent_cur = absent_next;
 #pragma unroll
     for (int t = 0; t < NI; ++t) {
       const int key = t * KPI + lk;
       const int o = key * D + ((lc ^ swz<D>(key)) << 3);
-      *(u32x4*)(sk + o) = kr[t];
-      *(u32x4*)(sv + o) = vr[t];
+      const bool z = CAREFUL && ((absent_cur >> key) & 1);
+      *(u32x4*)(sk + o) = z ? u32x4{0, 0, 0, 0} : kr[t];
+      *(u32x4*)(sv + o) = z ? u32x4{0, 0, 0, 0} : vr[t];
     }
   };
   auto compute = [&](int kt) {
@@ -116,8 +132,10 @@ __device__ __forceinline__ void decode_narrow_body(const Args& a, const int unit
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
+        const int key = kt + 16 * j + 4 * grp + v;
         float x = s[j][v];
-        if (need_mask && kt + 16 * j + 4 * grp + v >= w.key_end) x = -INFINITY;
+        if (need_mask && key >= w.key_end) x = -INFINITY;
+        if (CAREFUL && ((absent_cur >> (key - kt)) & 1)) x = -INFINITY;  // a key without a valid slot
         s[j][v] = x;
         mx = fmaxf(mx, x);
       }
@@ -167,13 +185,23 @@ __device__ __forceinline__ void decode_narrow_body(const Args& a, const int unit
   const int plain_end = min(w.key_end, w.ext_begin);  // stages ending after this take the careful path
   int slA[NI], slB[NI];
   u32x4 kr[NI], vr[NI];
-  if (n_st > 0) load_slots(slA, kb);
-  if (n_st > 1) load_slots(slB, kb + BNN);
-  if (n_st > 0) load_kv(kr, vr, slA, kb, kb + BNN > plain_end);
-  if (n_st > 2) load_slots(slA, kb + 2 * BNN);
+  if constexpr (CAREFUL) {
+    // the careful pass runs its stages one after the other (no prefetch)
+    for (int i = 0; i < n_st; ++i) {
+      const int kt = kb + i * BNN;
+      load_slots(slA, kt);
+      load_kv(kr, vr, slA, kt, true);
+      store(kr, vr);
+      compute(kt);
+    }
+  }
+  if (!CAREFUL && n_st > 0) load_slots(slA, kb);
+  if (!CAREFUL && n_st > 1) load_slots(slB, kb + BNN);
+  if (!CAREFUL && n_st > 0) load_kv(kr, vr, slA, kb, kb + BNN > plain_end);
+  if (!CAREFUL && n_st > 2) load_slots(slA, kb + 2 * BNN);
   // The LDS tile is private to the wave and LDS operations of a wave complete
   // in order, so the next stage may overwrite it right after this stage's reads.
-  for (int i = 0; i < n_st; i += 2) {
+  for (int i = 0; !CAREFUL && i < n_st; i += 2) {
     int kt = kb + i * BNN;
     store(kr, vr);
     if (i + 1 < n_st) {
@@ -191,199 +219,22 @@ __device__ __forceinline__ void decode_narrow_body(const Args& a, const int unit
     compute(kt);
   }
 
-  if (bad_slot) flag(a.err, RC_DEVERR_SLOT);
-  float l_tot = l_run + __shfl_xor(l_run, 16);
-  l_tot += __shfl_xor(l_tot, 32);
-  if (!col.real) return;
-  const int64_t pidx = ((int64_t)col.b * a.Hq + col.head) * a.max_splits + w.split;
-  float* wo = a.ws_o + pidx * D;
-#pragma unroll
-  for (int db = 0; db < NDB; ++db)
-    *(float4*)(wo + db * 16 + 4 * grp) = make_float4(acc[db][0], acc[db][1], acc[db][2], acc[db][3]);
-  if (grp == 0) *(float2*)(a.ws_ml + pidx * 2) = make_float2(m_run, l_tot);
-}
-
-// Narrow decode items, kv heads in groups of four: one workgroup per (item,
-// head group).  The gather is the bandwidth limiter for decode, and scattered
-// 256-byte reads (one head of one slot) reach far less HBM bandwidth than
-// whole slot rows, so here every load instruction covers one key's four heads
-// (1 KiB contiguous for D = 128): each wave loads 8 keys of a 32-key stage
-// into registers, the stage goes to LDS as [key][head][D] (chunk-swizzled per
-// key), and wave w computes head w from it with the narrow kernel's
-// 16x16x32 tiles (K operand by ds_read_b128, V^T by transposing reads).
-constexpr int HG = 4;     // kv heads per workgroup
-constexpr int BNR = 32;   // keys per stage
-
-template <int D>
-__device__ __forceinline__ void decode_rows_body(const Args& a, const int unit, uint16_t* sk, uint16_t* sv) {
-  constexpr int NKS = D / 32;          // k-steps of 32 over D
-  constexpr int NDB = D / 16;          // 16-row blocks of O^T
-  constexpr int CHH = D / 8;           // 16-byte chunks per (key, head)
-  constexpr int LPK = HG * CHH;        // lanes covering one key's heads (64 for D=128, 32 for D=64)
-  constexpr int KPI = 64 / LPK;        // keys per load instruction
-  constexpr int NI = BNR / 4 / KPI;    // load instructions per lane per stage and array
-  constexpr int RS = HG * D;           // LDS elements per key
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int grp = lane >> 4, r16 = lane & 15;
-  const int groups = a.Hkv / HG;
-  const int L = (a.narrow_begin + unit / groups) * a.Hkv + (unit % groups) * HG;
-  Work w = resolve(a, DECODE, L, tid == 0);
-  if (!w.valid) return;  // uniform over the workgroup
-  const int hk0 = w.hk;
-  w.hk = hk0 + wave;     // this wave's kv head
-  const Col col = column(a, DECODE, w, r16);
-
-  const uint16_t* q = (const uint16_t*)a.q;
-  bf16x8 qf[NKS];
-#pragma unroll
-  for (int ks = 0; ks < NKS; ++ks) qf[ks] = *(const bf16x8*)(q + col.qoff * D + ks * 32 + 8 * grp);
-  f32x4 acc[NDB];
-#pragma unroll
-  for (int i = 0; i < NDB; ++i) acc[i] = f32x4{};
-  float m_run = -INFINITY, l_run = 0.f;
-
-  // loader: lane -> (key k0 + lane / LPK, head, chunk) of each instruction
-  const int lk = lane / LPK;                  // key within an instruction
-  const int lh = (lane % LPK) / CHH;          // head within the group
-  const int lc = lane % CHH;                  // chunk within the head's row
-  const int64_t rowHD = (int64_t)a.Hkv * D;
-  const uint16_t* kbase = (const uint16_t*)a.k_pool + (int64_t)hk0 * D + lh * D + lc * 8;
-  const uint16_t* vbase = (const uint16_t*)a.v_pool + (int64_t)hk0 * D + lh * D + lc * 8;
-  const int32_t* trow = a.table + w.row * a.stride;
-  const int sh = a.page_shift;
-  const uint32_t npages = (uint32_t)(a.pool_slots >> sh);
-  int bad_slot = 0;
-  int sl[2][NI];
-  u32x4 kr[NI], vr[NI];
-
-  auto key_of = [&](int t) { return wave * (BNR / 4) + t * KPI + lk; };  // key within the stage
-  auto load_slots = [&](int (&s)[NI], int kt) {
-#pragma unroll
-    for (int t = 0; t < NI; ++t) {
-      const int j = kt + key_of(t);
-      s[t] = j < w.key_end ? trow[j >> sh] : INT_MIN;  // INT_MIN: past the range end; raw entries
+  if constexpr (!CAREFUL) {
+    if (__any(bad_slot)) {  // some key is absent: the careful pass computes the item
+      if (lane == 0) flag(a.err, RC_DEVERR_SLOT);
+      return true;
     }
-  };
-  auto load_kv = [&](const int (&s)[NI], int kt, bool partial) {
-#pragma unroll
-    for (int t = 0; t < NI; ++t) {
-      const int32_t sv_ = s[t] == INT_MIN ? INT_MIN : page_slot(s[t], kt + key_of(t), sh, npages);
-      const bool ok = (uint32_t)sv_ < (uint32_t)a.pool_slots;
-      bad_slot |= !ok & (sv_ != INT_MIN);
-      const int64_t off = (int64_t)(ok ? sv_ : 0) * rowHD;
-      kr[t] = *(const u32x4*)(kbase + off);
-      vr[t] = *(const u32x4*)(vbase + off);
-      if (partial && !ok) {  // keys past the end must hold finite values: p = 0 multiplies them
-        kr[t] = u32x4{0, 0, 0, 0};
-        vr[t] = u32x4{0, 0, 0, 0};
-      }
-    }
-  };
-  auto store = [&]() {
-#pragma unroll
-    for (int t = 0; t < NI; ++t) {
-      const int key = key_of(t);
-      const int o = key * RS + lh * D + ((lc ^ swz<D>(key)) << 3);
-      *(u32x4*)(sk + o) = kr[t];
-      *(u32x4*)(sv + o) = vr[t];
-    }
-  };
-  auto compute = [&](int kt) {
-    const uint16_t* hk_ = sk + wave * D;
-    const uint16_t* hv_ = sv + wave * D;
-    f32x4 s[2];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      s[j] = f32x4{};
-      const int key = 16 * j + r16;
-      const int sw = swz<D>(key);
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        const bf16x8 kf = *(const bf16x8*)(hk_ + key * RS + (((4 * ks + grp) ^ sw) << 3));
-        s[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[ks], s[j], 0, 0, 0);
-      }
-    }
-    const bool need_mask = kt + BNR > w.key_end;
-    float mx = -INFINITY;
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        float x = s[j][v];
-        if (need_mask && kt + 16 * j + 4 * grp + v >= w.key_end) x = -INFINITY;
-        s[j][v] = x;
-        mx = fmaxf(mx, x);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32)) * a.scale_log2;
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    float psum = 0.f;
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(s[j][v], a.scale_log2, -m_use));
-        s[j][v] = p;
-        psum += p;
-      }
-    if (__any(m_new != m_run)) {
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-      l_run *= alpha;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) acc[db] *= alpha;
-    }
-    l_run += psum;
-    m_run = m_new;
-    bf16x8 pf;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      pf[i] = (__bf16)s[0][i];
-      pf[4 + i] = (__bf16)s[1][i];
-    }
-    const int key0 = 4 * grp + (r16 >> 2), key1 = key0 + 16;
-    const int sw0 = swz<D>(key0), sw1 = swz<D>(key1);
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-      const int d = db * 16 + 4 * (r16 & 3);
-      const i16x4 lo = lds_read_tr(hv_ + key0 * RS + (((d >> 3) ^ sw0) << 3) + (d & 7));
-      const i16x4 up = lds_read_tr(hv_ + key1 * RS + (((d >> 3) ^ sw1) << 3) + (d & 7));
-      const i16x8 both = __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7);
-      acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, both), pf, acc[db], 0, 0, 0);
-    }
-  };
-
-  const int kb = w.key_begin;
-  const int n_st = (w.key_end - kb + BNR - 1) / BNR;
-  if (n_st > 0) load_slots(sl[0], kb);
-  if (n_st > 1) load_slots(sl[1], kb + BNR);
-  if (n_st > 0) load_kv(sl[0], kb, kb + BNR > w.key_end);
-  auto step = [&](auto bufc, int i) {
-    constexpr int b = decltype(bufc)::value;
-    const int kt = kb + i * BNR;
-    __syncthreads();  // the previous stage's reads are done
-    store();
-    __syncthreads();
-    if (i + 1 < n_st) load_kv(sl[b ^ 1], kt + BNR, kt + 2 * BNR > w.key_end);
-    if (i + 2 < n_st) load_slots(sl[b], kt + 2 * BNR);
-    compute(kt);
-  };
-  for (int i = 0; i < n_st; i += 2) {
-    step(std::integral_constant<int, 0>{}, i);
-    if (i + 1 < n_st) step(std::integral_constant<int, 1>{}, i + 1);
   }
-
-  if (bad_slot) flag(a.err, RC_DEVERR_SLOT);
   float l_tot = l_run + __shfl_xor(l_run, 16);
   l_tot += __shfl_xor(l_tot, 32);
-  if (!col.real) return;
+  if (!col.real) return false;
   const int64_t pidx = ((int64_t)col.b * a.Hq + col.head) * a.max_splits + w.split;
   float* wo = a.ws_o + pidx * D;
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
     *(float4*)(wo + db * 16 + 4 * grp) = make_float4(acc[db][0], acc[db][1], acc[db][2], acc[db][3]);
   if (grp == 0) *(float2*)(a.ws_ml + pidx * 2) = make_float2(m_run, l_tot);
+  return false;
 }
 
 // Decode, one launch: the plan lists wide items (workgroup-cooperative tiles,
@@ -407,21 +258,15 @@ __global__ __launch_bounds__(NT, 2) void decode_attn_bf16(Args a) {
   const int bid = (int)blockIdx.x;
   const bool wide = a.narrow_first ? bid >= n_narrow_blocks : bid < a.n_wide_blocks;
   if (wide) {
-    attn_bf16_body<D, 4, ROLE == 0>(a, DECODE, a.narrow_first ? bid - n_narrow_blocks : bid, sK, sV);
+    attn_bf16_tile<D, 4, ROLE == 0>(a, DECODE, a.narrow_first ? bid - n_narrow_blocks : bid, sK, sV);
     return;
   }
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave
   const int unit = (a.narrow_first ? bid : bid - a.n_wide_blocks) * 4 + wave;
   if (unit >= a.n_narrow_units) return;
-  decode_narrow_body<D, ROLE == 0>(a, unit, &sK[0][0] + wave * BNN * D, &sV[0][0] + wave * BNN * D);
-}
-
-// Narrow decode items, one workgroup per group of four kv heads.
-template <int D>
-__global__ __launch_bounds__(NT) void decode_rows_bf16(Args a) {
-  __shared__ __attribute__((aligned(16))) uint16_t sK[HG * BNR * D];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[HG * BNR * D];
-  decode_rows_body<D>(a, (int)blockIdx.x, sK, sV);
+  uint16_t* sk = &sK[0][0] + wave * BNN * D;
+  uint16_t* sv = &sV[0][0] + wave * BNN * D;
+  if (decode_narrow_body<D, ROLE == 0, false>(a, unit, sk, sv)) decode_narrow_body<D, ROLE == 0, true>(a, unit, sk, sv);
 }
 
 template <int D>
@@ -567,41 +412,15 @@ rc_status split_k_attention(const rc_shape* shape, void* o, const void* q, void*
   } else {
     // wide items: one workgroup per (item, kv head)
     const int64_t n_wide = (int64_t)info->narrow_begin * a.Hkv;
-    // narrow items: one wave per (item, kv head), or one workgroup per four kv heads
+    // narrow items: one wave per (item, kv head), four waves per workgroup
     const int64_t units = (int64_t)(info->n_items - info->narrow_begin) * a.Hkv;
+    const int64_t n_narrow = (units + 3) / 4;
+    const int64_t grid = n_wide + n_narrow;
+    if (grid > INT32_MAX) return fail(RC_ERR_RANGE, "grid too large");
     a.n_narrow_units = (int32_t)units;
-    a.rows_path = rc::tuning().decode_rows && a.Hkv % HG == 0;
-    const int64_t n_narrow = a.rows_path ? units / HG : (units + 3) / 4;
-    if (n_wide > INT32_MAX || n_narrow > INT32_MAX) return fail(RC_ERR_RANGE, "grid too large");
-    if (a.rows_path && a.k_new) {
-      // the grouped-heads variant reads every key from the pool: store first
-      st = rc_kv_store(shape, k_pool, v_pool, k_new, v_new, new_slots, batch, stream);
-      if (st != RC_OK) return st;
-      a.k_new = a.v_new = nullptr;
-      a.new_slots = nullptr;
-    }
-    ProfScope p(attn_name, s);
-    if (a.rows_path) {
-      // grouped-heads variant: wide items, then narrow items, two launches
-      if (n_wide > 0) {
-        Args aw = a;
-        aw.n_wide_blocks = (int32_t)n_wide;
-        aw.n_narrow_units = 0;
-        if (shape->head_dim == 128)
-          hipLaunchKernelGGL((decode_attn_bf16<128, ROLE>), dim3((unsigned)n_wide), dim3(NT), 0, s, aw);
-        else
-          hipLaunchKernelGGL((decode_attn_bf16<64, ROLE>), dim3((unsigned)n_wide), dim3(NT), 0, s, aw);
-      }
-      if (n_narrow > 0) {
-        if (shape->head_dim == 128)
-          hipLaunchKernelGGL(decode_rows_bf16<128>, dim3((unsigned)n_narrow), dim3(NT), 0, s, a);
-        else
-          hipLaunchKernelGGL(decode_rows_bf16<64>, dim3((unsigned)n_narrow), dim3(NT), 0, s, a);
-      }
-    } else if (n_wide + n_narrow > 0) {
-      a.n_wide_blocks = (int32_t)n_wide;
-      const int64_t grid = n_wide + n_narrow;
-      if (grid > INT32_MAX) return fail(RC_ERR_RANGE, "grid too large");
+    a.n_wide_blocks = (int32_t)n_wide;
+    if (grid > 0) {
+      ProfScope p(attn_name, s);
       if (shape->head_dim == 128)
         hipLaunchKernelGGL((decode_attn_bf16<128, ROLE>), dim3((unsigned)grid), dim3(NT), 0, s, a);
       else

@@ -32,7 +32,7 @@ __global__ __launch_bounds__(64 * EXT_WAVES, 1) void extend_attn_bf16(Args a, in
   __shared__ __attribute__((aligned(16))) uint16_t sV[2][BN * D];
   const int L = extend_order(blockIdx.x, n_bh, a.tiles, ck);
   if (L < 0) return;
-  attn_bf16_body<D, EXT_WAVES>(a, EXTEND, L, sK, sV);
+  attn_bf16_tile<D, EXT_WAVES, false>(a, EXTEND, L, sK, sV);
 }
 
 template <int D>

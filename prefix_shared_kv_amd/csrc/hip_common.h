@@ -21,12 +21,6 @@ class ProfScope {
   hipStream_t stream_;
 };
 
-// Library-wide tuning switches (rc_set_tuning).
-struct Tuning {
-  int decode_rows = 0;  // narrow decode items by groups of four kv heads per workgroup
-};
-Tuning& tuning();
-
 // Check the launch that just happened.
 rc_status check_launch(const char* what);
 

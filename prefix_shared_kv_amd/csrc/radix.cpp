@@ -850,6 +850,7 @@ namespace {
 struct Range {
   int64_t begin, end;
   std::vector<int32_t> members;
+  bool own = false;  // the positions of its one member alone (its items carry RC_PLAN_ITEM_OWN)
 };
 
 struct PlanBuilder {
@@ -911,7 +912,8 @@ struct PlanBuilder {
         const int64_t pe = std::min<int64_t>(p + pl, R.end);
         for (size_t g0 = 0; g0 < R.members.size(); g0 += max_m) {
           const size_t cnt = std::min<size_t>(max_m, R.members.size() - g0);
-          const Item it{(int64_t)cnt * (pe - p), {row_of(R.members[g0]), (int32_t)p, (int32_t)pe, sp, 0, (int32_t)cnt, 0, 0},
+          const Item it{(int64_t)cnt * (pe - p),
+                        {row_of(R.members[g0]), (int32_t)p, (int32_t)pe, sp, 0, (int32_t)cnt, R.own ? RC_PLAN_ITEM_OWN : 0, 0},
                         r, (int32_t)g0};
           ((int64_t)cnt * group <= 16 ? narrow : wide).push_back(it);
           if (R.members.size() > 1) shared_items++;
@@ -990,7 +992,7 @@ extern "C" rc_status rc_plan_decode_unshared(int32_t batch, const int32_t* rows,
   pb.path.resize(batch);
   int64_t logical = 0;
   for (int32_t b = 0; b < batch; ++b) {
-    pb.ranges.push_back(Range{0, max_seq[b], {b}});
+    pb.ranges.push_back(Range{0, max_seq[b], {b}, true});
     pb.path[b].push_back((int32_t)pb.ranges.size() - 1);
     logical += max_seq[b];
   }
@@ -1065,7 +1067,7 @@ rc_status plan_from_walks(const rc_radix* t, int32_t n_mem, const std::vector<in
       if (own) break;
     }
     if (max_seq[m] > own_begin) {
-      pb.ranges.push_back(Range{own_begin, max_seq[m], {m}});
+      pb.ranges.push_back(Range{own_begin, max_seq[m], {m}, true});
       pb.path[m].push_back((int32_t)pb.ranges.size() - 1);
     }
   }

@@ -10,9 +10,6 @@ namespace rc {
 static int32_t* g_err_word = nullptr;
 int32_t* error_word() { return g_err_word; }
 
-static Tuning g_tuning;
-Tuning& tuning() { return g_tuning; }
-
 namespace {
 struct Rec {
   std::string name;
@@ -78,15 +75,6 @@ extern "C" rc_status rc_upload_table_rows(int32_t* dev_table, int64_t dev_stride
                                    (hipStream_t)stream);
   if (st != hipSuccess) return rc::fail(RC_ERR_HIP, "table upload failed: %s", hipGetErrorString(st));
   return RC_OK;
-}
-
-extern "C" rc_status rc_set_tuning(const char* name, int64_t value) {
-  if (!name) return rc::fail(RC_ERR_ARG, "tuning name is NULL");
-  if (!strcmp(name, "decode_rows")) {
-    rc::g_tuning.decode_rows = value != 0;
-    return RC_OK;
-  }
-  return rc::fail(RC_ERR_ARG, "unknown tuning switch '%s'", name);
 }
 
 extern "C" rc_status rc_prof_enable(int32_t on) {

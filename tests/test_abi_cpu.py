@@ -64,6 +64,11 @@ def test_extend_argument_checks():
     args = [C.byref(sh), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 64, None, FAKE, FAKE, FAKE]
     assert N.lib.rc_extend_attention(*args, -1, 10, 8, 0.1, None) == N.RC_ERR_ARG
     assert N.lib.rc_extend_attention(*args, 2, 10, 8, float("nan"), None) == N.RC_ERR_ARG
+    # the softmax scale must be positive: the kernels scale each column's
+    # maximum after taking it, and masked keys carry -inf scores
+    for bad_scale in (0.0, -0.125, -0.0, float("inf"), float("-inf")):
+        assert N.lib.rc_extend_attention(*args, 2, 10, 8, bad_scale, None) == N.RC_ERR_ARG
+        assert "sm_scale" in N.last_error()
     assert N.lib.rc_extend_attention(*args, 0, 0, 0, 0.1, None) == N.RC_OK
     bad = list(args)
     bad[1] = None
@@ -98,6 +103,13 @@ def test_decode_argument_checks():
     assert call(sh, 3, need) == N.RC_ERR_ARG  # plan built for batch 2
     assert call(shape(hq=8, hkv=8), 2, need) == N.RC_ERR_SHAPE  # plan built for group 4
     assert call(sh, 0, need) == N.RC_OK
+    for bad_scale in (0.0, -1.0, float("nan")):
+        st = N.lib.rc_decode_attention(C.byref(sh), FAKE, FAKE, FAKE, FAKE, None, None, None, FAKE, 2, 128, FAKE,
+                                       2, FAKE, C.byref(info), bad_scale, FAKE, need, None)
+        assert st == N.RC_ERR_ARG
+        st = N.lib.rc_extend_attention_shared(C.byref(sh), FAKE, FAKE, FAKE, FAKE, FAKE, 2, 128, FAKE, 2, FAKE,
+                                              C.byref(info), bad_scale, FAKE, need, None)
+        assert st == N.RC_ERR_ARG
     # the current token's K/V come as a triple
     st = N.lib.rc_decode_attention(C.byref(sh), FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, 2, 128, FAKE, 2, FAKE,
                                    C.byref(info), 0.1, FAKE, need, None)
@@ -113,8 +125,8 @@ def test_unshared_plan_layout():
     assert info.max_splits == 3
     items = buf[8:8 + 8 * info.n_items].reshape(-1, 8)
     cover = {}
-    for rep, pb, pe, sp, mo, mc, _, _ in items:
-        assert mc == 1
+    for rep, pb, pe, sp, mo, mc, flags, _ in items:
+        assert mc == 1 and flags == N.RC_PLAN_ITEM_OWN  # no sharing: every item is its request's own
         b = buf[8 + 8 * info.n_items + mo]
         cover.setdefault(int(b), []).append((int(pb), int(pe), int(sp)))
     assert sorted(cover[0]) == [(0, 50, 0), (50, 100, 1)]

@@ -49,7 +49,7 @@ def fill_pool(g, S, Hkv, D, dtype):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-@pytest.mark.parametrize("ps", [4, 16, 64])
+@pytest.mark.parametrize("ps", [4, 16, 64, 256, 1024])
 def test_paged_extend_equals_expanded_table(gpu, dtype, ps):
     g = np.random.default_rng(ps)
     Hq, Hkv, D = HEADS[dtype]
@@ -97,7 +97,7 @@ def test_paged_extend_equals_expanded_table(gpu, dtype, ps):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-@pytest.mark.parametrize("ps", [4, 16, 64])
+@pytest.mark.parametrize("ps", [4, 16, 64, 256, 1024])
 def test_paged_decode_with_store_equals_expanded_table(gpu, dtype, ps):
     g = np.random.default_rng(100 + ps)
     Hq, Hkv, D = HEADS[dtype]
@@ -141,33 +141,79 @@ def test_paged_decode_with_store_equals_expanded_table(gpu, dtype, ps):
         assert e <= TOL[dtype], f"request {b} (L={L[b]}): max abs error {e:.3e}"
 
 
-def test_page_ids_outside_the_pool_are_flagged(gpu):
-    ps, Hq, Hkv, D = 16, 8, 2, 128
-    n_pages = 8
-    S = n_pages * ps
-    shape = KVShape(Hq, Hkv, D, torch.bfloat16, S, ps)
-    kp = torch.randn(S, Hkv, D, device=gpu).to(torch.bfloat16)
-    vp = torch.randn(S, Hkv, D, device=gpu).to(torch.bfloat16)
-    tab = np.array([[0, 1, n_pages + 3, 2, -5]], np.int32)  # the third and fifth pages are invalid
-    L = [5 * ps]
-    plan = api.plan_decode_unshared(L, Hq // Hkv, 256)
-    plan.to(gpu)
-    o = torch.empty(1, Hq, D, device=gpu, dtype=torch.bfloat16)
-    ws = torch.empty(api.decode_workspace_bytes(shape, plan), dtype=torch.uint8, device=gpu)
+@pytest.mark.parametrize("dtype,Hq,Hkv,D", [("bf16", 8, 2, 128), ("bf16", 32, 1, 128), ("bf16", 16, 4, 64),
+                                             ("f32", 8, 2, 64)])
+@pytest.mark.parametrize("ps", [1, 16])
+def test_keys_without_a_valid_slot_are_absent(gpu, dtype, Hq, Hkv, D, ps):
+    # table entries outside the pool (page ids, or slots at page size 1) are
+    # flagged, never dereferenced, and their keys drop out of the softmax: the
+    # outputs equal the oracle over the remaining keys.  Narrow (8/2, 16/4) and
+    # wide (32/1) decode items; the extend with invalid keys in stages of pool
+    # keys only and in a stage that also holds new tokens.
+    g = np.random.default_rng(7 * ps + Hq)
+    U = 16  # positions per group below (whole pages when ps = 16)
+    S = 8 * U
+    n_pages = S // ps
+    shape = KVShape(Hq, Hkv, D, DT[dtype], S, ps)
+    rnd = lambda *s: (W.round_bf16 if dtype == "bf16" else (lambda x: x))(g.standard_normal(s).astype(np.float32))
+    to = lambda a: torch.from_numpy(a).to(gpu).to(DT[dtype])
+    kpool, vpool = rnd(S, Hkv, D), rnd(S, Hkv, D)
+    # groups of 16 positions: pages (ps = 16) or runs of 16 slots (ps = 1); groups 2 and 4 invalid
+    group_ids = [0, 1, n_pages + 3, 2, -5]
+    valid = [True, True, False, True, False]
+    if ps == 1:
+        row = np.concatenate([np.arange(u * U, (u + 1) * U) if ok else np.full(U, x if x < 0 else S + 7)
+                              for u, (x, ok) in enumerate(zip(group_ids, valid))]).astype(np.int32)
+        slot_of = lambda p: int(row[p])
+    else:
+        row = np.array(group_ids, np.int32)
+        slot_of = lambda p: int(row[p // ps]) * ps + p % ps
+    ok_pos = lambda p: valid[p // U]
+    tab = np.stack([row, row])
+    scale = 1.0 / np.sqrt(D)
+
+    def kv_of(positions):
+        sl = [slot_of(p) for p in positions if ok_pos(p)]
+        return kpool[sl], vpool[sl]
+
     err = torch.zeros(1, dtype=torch.int32, device=gpu)
     api.set_error_word(err)
     try:
-        api.decode_attention(shape, o, torch.randn(1, Hq, D, device=gpu).to(torch.bfloat16), kp, vp, dev(tab, gpu),
-                             dev(np.array(L, np.int32), gpu), plan, 0.1, ws)
-        q = torch.randn(8, Hq, D, device=gpu).to(torch.bfloat16)
-        kn = torch.randn(8, Hkv, D, device=gpu).to(torch.bfloat16)
-        ext_o = torch.empty_like(q)
-        api.extend_attention(shape, ext_o, q, kn, kn, kp, vp, dev(tab, gpu), dev(np.array([4 * ps], np.int32), gpu),
-                             dev(np.array([8], np.int32), gpu), dev(np.array([0], np.int32), gpu), 8, 0.1)
+        # decode: one request over all 80 positions (groups 0..4)
+        L = [5 * U]
+        q = rnd(1, Hq, D)
+        plan = api.plan_decode_unshared(L, Hq // Hkv, 256)
+        plan.to(gpu)
+        o = torch.empty(1, Hq, D, device=gpu, dtype=DT[dtype])
+        ws = torch.empty(api.decode_workspace_bytes(shape, plan), dtype=torch.uint8, device=gpu)
+        api.decode_attention(shape, o, to(q), to(kpool), to(vpool), dev(tab, gpu), dev(np.array(L, np.int32), gpu),
+                             plan, scale, ws)
+        # extend: P = 64 (pool stages only) and P = 40 (its first stage mixes pool keys and new tokens)
+        P_list, E_list = [64, 40], [8, 30]
+        T = sum(E_list)
+        qe, kn, vn = rnd(T, Hq, D), rnd(T, Hkv, D), rnd(T, Hkv, D)
+        start = np.array([0, E_list[0]], np.int32)
+        ext_o = torch.empty(T, Hq, D, device=gpu, dtype=DT[dtype])
+        api.extend_attention(shape, ext_o, to(qe), to(kn), to(vn), to(kpool), to(vpool), dev(tab, gpu),
+                             dev(np.array(P_list, np.int32), gpu), dev(np.array(E_list, np.int32), gpu), dev(start, gpu),
+                             max(E_list), scale)
         torch.cuda.synchronize()
     finally:
         api.set_error_word(None)
     assert int(err.item()) & 1  # RC_DEVERR_SLOT
+    tol = TOL[dtype]
+    K, V = kv_of(range(L[0]))
+    assert len(K) == 48
+    e = float(np.max(np.abs(host(o)[0] - A.decode(q[0], K, V, scale))))
+    assert e <= tol, f"decode: max abs error {e:.3e}"
+    got = host(ext_o)
+    for b, (P, E) in enumerate(zip(P_list, E_list)):
+        s0 = int(start[b])
+        Kp, Vp = kv_of(range(P))
+        want = A.extend(qe[s0:s0 + E], np.concatenate([Kp, kn[s0:s0 + E]]), np.concatenate([Vp, vn[s0:s0 + E]]),
+                        len(Kp), scale)
+        e = float(np.max(np.abs(got[s0:s0 + E] - want)))
+        assert e <= tol, f"extend request {b} (P={P}): max abs error {e:.3e}"
 
 
 def test_rejects_bad_page_sizes(gpu):

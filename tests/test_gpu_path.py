@@ -123,8 +123,14 @@ def _extend_case(gpu, dtype, Hq, Hkv, D, P_list, E_list, seed=0, shuffled=True):
     return worst
 
 
+# group sizes 1 to 128 (the largest the library accepts): with 32 and more
+# query heads per kv head an extend tile holds 256 / group tokens
+HEAD_LAYOUTS = [(4, 4, 64), (8, 2, 128), (32, 8, 128), (16, 1, 64), (12, 4, 128), (24, 3, 64),
+                (32, 1, 128), (64, 1, 128), (128, 1, 64), (64, 2, 64)]
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-@pytest.mark.parametrize("Hq,Hkv,D", [(4, 4, 64), (8, 2, 128), (32, 8, 128), (16, 1, 64), (12, 4, 128), (24, 3, 64)])
+@pytest.mark.parametrize("Hq,Hkv,D", HEAD_LAYOUTS)
 def test_extend_ragged_against_oracle(gpu, dtype, Hq, Hkv, D):
     P_list = [0, 1, 63, 64, 130, 300, 5]
     E_list = [70, 1, 65, 0, 33, 129, 8]
@@ -215,6 +221,19 @@ def test_cascade_extend_matches_the_oracle(gpu, dtype):
         _run_workload(gpu, w, cascade=True, decode_steps=0)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("Hq,Hkv,D", [(32, 1, 128), (64, 1, 128), (128, 1, 64)])
+def test_cascade_extend_large_groups(gpu, dtype, Hq, Hkv, D):
+    # branches over one document through the shared-prefix plan with 32 to 128
+    # query heads per kv head (4 to 1 new tokens per member group)
+    w = W.classify64(prefix=300, n_branch=12)
+    w.shape.num_q_heads, w.shape.num_kv_heads, w.shape.head_dim = Hq, Hkv, D
+    w.sm_scale = 1.0 / np.sqrt(D)
+    if dtype == "f32":
+        w.shape.dtype = "f32"
+    _run_workload(gpu, w, cascade=True, decode_steps=0)
+
+
 def test_decode_is_deterministic(gpu):
     w = W.few_shot(n_req=6, prefix=200, ext=5, n_decode=2)
     outs = []
@@ -247,20 +266,16 @@ def test_unused_pool_slots_holding_nan_do_not_leak(gpu):
             check(d[i], A.decode(w.dec_qkv(i, t)[0], K, V, w.sm_scale), TOL["bf16"], f"decode step {t} request {i}")
 
 
-@pytest.mark.parametrize("rows", [0, 1])
-@pytest.mark.parametrize("Hq,Hkv,D", [(12, 3, 128), (16, 2, 64), (8, 8, 128), (48, 12, 64)])
-def test_decode_head_layouts(gpu, Hq, Hkv, D, rows):
-    # both narrow decode paths (one wave per kv head; groups of four kv heads per
-    # workgroup, used when Hkv % 4 == 0 and the switch is on)
+@pytest.mark.parametrize("Hq,Hkv,D", [(12, 3, 128), (16, 2, 64), (8, 8, 128), (48, 12, 64),
+                                      (32, 1, 128), (64, 1, 128), (128, 1, 64), (64, 2, 64)])
+def test_decode_head_layouts(gpu, Hq, Hkv, D):
+    # wide and narrow decode items over shared and unshared plans (groups of 32
+    # and more make every item wide: 128 / group members per item)
     w = W.multi_turn_tree(depth=3, fanout=2, seg_lo=20, seg_hi=150, ext=6, n_decode=2)
     w.shape.num_q_heads, w.shape.num_kv_heads, w.shape.head_dim = Hq, Hkv, D
     w.sm_scale = 1.0 / np.sqrt(D)
-    api.set_tuning("decode_rows", rows)
-    try:
-        for shared, chunk in [(True, 64), (False, 100)]:
-            _run_workload(gpu, w, shared=shared, chunk=chunk)
-    finally:
-        api.set_tuning("decode_rows", 0)
+    for shared, chunk in [(True, 64), (False, 100)]:
+        _run_workload(gpu, w, shared=shared, chunk=chunk)
 
 
 def test_decode_merge_of_many_splits(gpu):

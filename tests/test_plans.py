@@ -6,7 +6,11 @@ built by the tree itself:
     distinct split indices below its split count;
   * an item's positions hold the same slots in every member's table row as
     in the representative row the kernel reads them through;
-  * members per item stay within max(1, 128 / group).
+  * members per item stay within max(1, 128 / group);
+  * items flagged as a request's own positions (the only items the decode
+    kernel lets store the current token) have one member and cover a suffix
+    of its positions, every position past its committed tokens included,
+    never a range that another request reads.
 """
 import numpy as np
 import pytest
@@ -26,17 +30,36 @@ def parse(plan):
     return items, mem, nsplit
 
 
-def check_plan(plan, max_seq, rows, table, group):
+def check_plan(plan, max_seq, rows, table, group, own_from=None):
     items, mem, nsplit = parse(plan)
     max_m = max(1, 128 // group)
     cover = {m: [] for m in range(len(max_seq))}
-    for rep, pb, pe, sp, mo, mc, _, _ in items:
+    own = {m: [] for m in range(len(max_seq))}
+    for rep, pb, pe, sp, mo, mc, flags, _ in items:
         assert 1 <= mc <= max_m and pb < pe
+        assert flags & ~N.RC_PLAN_ITEM_OWN == 0
+        if flags & N.RC_PLAN_ITEM_OWN:
+            assert mc == 1
+            own[int(mem[mo])].append((int(pb), int(pe)))
         for m in mem[mo:mo + mc]:
             m = int(m)
             cover[m].append((int(pb), int(pe), int(sp)))
             # the kernel reads the range through rep's row for every member
             assert np.array_equal(table[rep, pb:pe], table[rows[m], pb:pe]), (m, pb, pe)
+    for m, rs in own.items():
+        if not rs:
+            assert own_from is None or own_from[m] >= max_seq[m]
+            continue
+        rs.sort()
+        assert rs[-1][1] == max_seq[m], (m, rs)  # a suffix of the member's positions ...
+        assert all(a[1] == b[0] for a, b in zip(rs, rs[1:])), (m, rs)
+        assert all(pe <= rs[0][0] for pb, pe, _ in cover[m] if (pb, pe) not in rs), (m, rs)
+        if own_from is not None:  # ... holding every position past its committed tokens
+            assert rs[0][0] <= own_from[m], (m, rs, own_from[m])
+            # members are requests: no other request reads a slot of these positions
+            others = np.concatenate([table[rows[x], :max_seq[x]] for x in own if x != m] or [np.zeros(0, np.int32)])
+            mine = np.concatenate([table[rows[m], pb:pe] for pb, pe in rs])
+            assert not np.isin(mine, others).any(), (m, rs)
     for m, ranges in cover.items():
         ranges.sort()
         pos = 0
@@ -135,7 +158,11 @@ def test_plans_cover_every_context_with_shared_slots(case):
     t.insert_rows(batch, table, np.arange(len(batch), dtype=np.int32))
     lens = np.array([len(b) for b in batch])
     plan = t.plan_decode(batch, lens + reserve, group, chunk)
-    check_plan(plan, lens + reserve, np.arange(len(batch)), table, group)
+    check_plan(plan, lens + reserve, np.arange(len(batch)), table, group, own_from=lens)
+    # the shared (cached) part of a context is never flagged as a request's own
+    for rep, pb, pe, sp, mo, mc, flags, _ in plan.items():
+        if mc > 1:
+            assert flags == 0
 
 
 def test_launch_order_puts_the_longer_running_class_first():
