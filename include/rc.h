@@ -242,6 +242,28 @@ rc_status rc_decode_attention(const rc_shape* shape, void* o, const void* q, voi
                               const rc_plan_info* info, float sm_scale, void* workspace,
                               int64_t ws_bytes, void* stream);
 
+/* rc_decode_attention without a workspace argument, for callers that cannot */
+/* allocate device memory (code under HIP graph capture, tight serving       */
+/* loops, harnesses that forbid hipMalloc).  The partials go to a static     */
+/* workspace inside the library: one array of                                */
+/* RC_DECODE_STATIC_WORKSPACE_BYTES per GPU, created with the library's code */
+/* on that GPU and held until the process ends.  A plan whose               */
+/* rc_decode_workspace_bytes exceeds it fails with RC_ERR_RANGE before       */
+/* anything is launched.  The call allocates nothing (no hipMalloc, no       */
+/* events: kernel timing skips it); the first call on a device looks up the  */
+/* array's address there (RC_ERR_HIP if that fails).  All calls on one GPU   */
+/* share the array, whose contents persist from call to call (every partial  */
+/* is written before it is read, so nothing needs clearing): calls that may  */
+/* overlap on one GPU (other streams, other threads) race and give wrong     */
+/* results; serialise them.  Arguments, outputs and errors otherwise as      */
+/* rc_decode_attention.                                                      */
+#define RC_DECODE_STATIC_WORKSPACE_BYTES (64ll << 20)
+rc_status rc_decode_attention_static(const rc_shape* shape, void* o, const void* q, void* k_pool, void* v_pool,
+                                     const void* k_new, const void* v_new, const int32_t* new_slots,
+                                     const int32_t* req_to_token, int32_t table_rows, int64_t stride,
+                                     const int32_t* seq_lens, int32_t batch, const int32_t* plan_dev,
+                                     const rc_plan_info* info, float sm_scale, void* stream);
+
 /* ------------------------------------------------------------------------ */
 /* Radix tree over token ids, with the KV-pool slot allocator  ([SG]         */
 /* RadixAttention bullet and nine-step example; [PC] exact-prefix reuse).    */

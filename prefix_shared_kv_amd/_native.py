@@ -15,6 +15,7 @@ RC_OK, RC_ERR_ARG, RC_ERR_SHAPE, RC_ERR_DTYPE, RC_ERR_RANGE, RC_ERR_NOMEM, RC_ER
 RC_F32, RC_BF16 = 0, 1
 RC_DEVERR_SLOT, RC_DEVERR_TABLE, RC_DEVERR_LENGTH, RC_DEVERR_PLAN = 1, 2, 4, 8
 RC_PLAN_MAGIC, RC_PLAN_HEADER, RC_PLAN_ITEM, RC_PLAN_ITEM_OWN = 0x52435031, 8, 8, 1
+RC_DECODE_STATIC_WORKSPACE_BYTES = 64 << 20
 
 STATUS_NAMES = {0: "RC_OK", 1: "RC_ERR_ARG", 2: "RC_ERR_SHAPE", 3: "RC_ERR_DTYPE", 4: "RC_ERR_RANGE",
                 5: "RC_ERR_NOMEM", 6: "RC_ERR_HIP", 7: "RC_ERR_INTERNAL"}
@@ -65,6 +66,8 @@ _SIGS = {
     "rc_decode_workspace_bytes": (i64, [C.POINTER(RcShape), C.POINTER(RcPlanInfo)]),
     "rc_decode_attention": (i32, [C.POINTER(RcShape), P, P, P, P, P, P, P, P, i32, i64, P, i32, P,
                                   C.POINTER(RcPlanInfo), f32, P, i64, P]),
+    "rc_decode_attention_static": (i32, [C.POINTER(RcShape), P, P, P, P, P, P, P, P, i32, i64, P, i32, P,
+                                         C.POINTER(RcPlanInfo), f32, P]),
     "rc_extend_attention_shared": (i32, [C.POINTER(RcShape), P, P, P, P, P, i32, i64, P, i32, P,
                                          C.POINTER(RcPlanInfo), f32, P, i64, P]),
     "rc_radix_create": (i32, [i64, P, C.POINTER(P)]),

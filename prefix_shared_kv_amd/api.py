@@ -259,6 +259,34 @@ def decode_attention(shape: KVShape, o, q, k_pool, v_pool, req_to_token, seq_len
                                   _vp(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
+def decode_attention_static(shape: KVShape, o, q, k_pool, v_pool, req_to_token, seq_lens, plan: DecodePlan,
+                            sm_scale: float, k_new=None, v_new=None, new_slots=None, stream=None) -> None:
+    """decode_attention without a workspace (rc_decode_attention_static): the partials go to the
+    library's static per-GPU workspace, so the call allocates nothing.  Calls that may overlap on
+    one GPU race on that workspace."""
+    Hq, Hkv, D, S = shape.num_q_heads, shape.num_kv_heads, shape.head_dim, shape.pool_slots
+    B = q.shape[0]
+    _dev(q, "q", shape.dtype, (B, Hq, D))
+    _dev(o, "o", shape.dtype, (B, Hq, D))
+    _dev(k_pool, "k_pool", shape.dtype, (S, Hkv, D))
+    _dev(v_pool, "v_pool", shape.dtype, (S, Hkv, D))
+    _dev(req_to_token, "req_to_token", torch.int32)
+    _dev(seq_lens, "seq_lens", torch.int32, (B,))
+    if (k_new is None) != (v_new is None) or (k_new is None) != (new_slots is None):
+        raise ValueError("k_new, v_new and new_slots go together")
+    if k_new is not None:
+        _dev(k_new, "k_new", shape.dtype, (B, Hkv, D))
+        _dev(v_new, "v_new", shape.dtype, (B, Hkv, D))
+        _dev(new_slots, "new_slots", torch.int32, (B,))
+    if plan.dev is None:
+        raise ValueError("plan has no device copy; call plan.to(device)")
+    sh = shape.c()
+    check(lib.rc_decode_attention_static(C.byref(sh), _vp(o), _vp(q), _vp(k_pool), _vp(v_pool), _vp(k_new),
+                                         _vp(v_new), _vp(new_slots), _vp(req_to_token), req_to_token.shape[0],
+                                         req_to_token.shape[1], _vp(seq_lens), B, _vp(plan.dev), C.byref(plan.info),
+                                         float(sm_scale), _stream(stream)))
+
+
 def extend_attention_shared(shape: KVShape, o, q, k_pool, v_pool, req_to_token, seq_lens, plan: DecodePlan,
                             sm_scale: float, workspace, stream=None) -> None:
     """Extend attention over a shared-prefix plan (rc_extend_attention_shared): row m of q/o is new

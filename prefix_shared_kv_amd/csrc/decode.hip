@@ -1,6 +1,8 @@
 // Split-K decode attention over a shared plan: one query token per request
 // attends over its whole context; shared tree ranges are read once for all
 // the requests that pass through them.
+#include <mutex>
+
 #include "attn_tile.h"
 
 namespace {
@@ -332,8 +334,8 @@ __global__ __launch_bounds__(256) void merge_kernel(void* out, const float* __re
 }
 
 template <int D>
-void launch_decode_f32(const Args& a, int n_work, hipStream_t s, const char* name) {
-  rc::ProfScope p(name, s);
+void launch_decode_f32(const Args& a, int n_work, hipStream_t s, const char* name, bool timed) {
+  rc::ProfScope p(name, s, timed);
   hipLaunchKernelGGL(decode_attn_f32<D>, dim3(n_work), dim3(NT), 0, s, a);
 }
 
@@ -347,14 +349,16 @@ extern "C" int64_t rc_decode_workspace_bytes(const rc_shape* shape, const rc_pla
 
 namespace {
 
-// Split-K attention over a plan, then the merge: the body of both
-// rc_decode_attention (role 0) and rc_extend_attention_shared (role 1).
+// Split-K attention over a plan, then the merge: the body of
+// rc_decode_attention and rc_decode_attention_static (role 0) and of
+// rc_extend_attention_shared (role 1).  timed = false: no kernel timing (the
+// allocation-free entry point creates no events).
 template <int ROLE>
 rc_status split_k_attention(const rc_shape* shape, void* o, const void* q, void* k_pool, void* v_pool,
                             const void* k_new, const void* v_new, const int32_t* new_slots,
                             const int32_t* req_to_token, int32_t table_rows, int64_t stride, const int32_t* seq_lens,
                             int32_t batch, const int32_t* plan_dev, const rc_plan_info* info, float sm_scale,
-                            void* workspace, int64_t ws_bytes, void* stream) {
+                            void* workspace, int64_t ws_bytes, void* stream, bool timed = true) {
   using namespace rc;
   const bool d128 = shape && shape->head_dim == 128;
   const char* attn_name = ROLE == 0 ? (d128 ? "decode_attention_d128" : "decode_attention_d64")
@@ -403,9 +407,9 @@ rc_status split_k_attention(const rc_shape* shape, void* o, const void* q, void*
     a.n_work = (int32_t)n_work;
     if (n_work > 0) {
       if (shape->head_dim == 128)
-        launch_decode_f32<128>(a, a.n_work, s, "decode_f32_d128");
+        launch_decode_f32<128>(a, a.n_work, s, "decode_f32_d128", timed);
       else
-        launch_decode_f32<64>(a, a.n_work, s, "decode_f32_d64");
+        launch_decode_f32<64>(a, a.n_work, s, "decode_f32_d64", timed);
       st = check_launch("decode attention");
       if (st != RC_OK) return st;
     }
@@ -420,7 +424,7 @@ rc_status split_k_attention(const rc_shape* shape, void* o, const void* q, void*
     a.n_narrow_units = (int32_t)units;
     a.n_wide_blocks = (int32_t)n_wide;
     if (grid > 0) {
-      ProfScope p(attn_name, s);
+      ProfScope p(attn_name, s, timed);
       if (shape->head_dim == 128)
         hipLaunchKernelGGL((decode_attn_bf16<128, ROLE>), dim3((unsigned)grid), dim3(NT), 0, s, a);
       else
@@ -433,7 +437,7 @@ rc_status split_k_attention(const rc_shape* shape, void* o, const void* q, void*
   const int pairs = batch * shape->num_q_heads;
   const dim3 grid((pairs + 3) / 4);
   {
-    ProfScope p(merge_name, s);
+    ProfScope p(merge_name, s, timed);
     if (shape->head_dim == 128) {
       if (bf16)
         hipLaunchKernelGGL((merge_kernel<128, true>), grid, dim3(256), 0, s, o, a.ws_o, a.ws_ml, nsplit, batch, a.Hq, a.max_splits);
@@ -459,6 +463,60 @@ extern "C" rc_status rc_decode_attention(const rc_shape* shape, void* o, const v
                                          int64_t ws_bytes, void* stream) {
   return split_k_attention<0>(shape, o, q, k_pool, v_pool, k_new, v_new, new_slots, req_to_token, table_rows, stride,
                               seq_lens, batch, plan_dev, info, sm_scale, workspace, ws_bytes, stream);
+}
+
+// Workspace of rc_decode_attention_static: a file-scope device array, one copy
+// per GPU, which the process holds until it ends.  Host code never uses the
+// array's name as an address (on the host it is only a stand-in for the
+// symbol): each device's address comes from hipGetSymbolAddress, taken once
+// per device with that device current, and goes to the kernels as the
+// workspace pointer.
+static __device__ __align__(256) unsigned char scratch[RC_DECODE_STATIC_WORKSPACE_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The scratch array's address on the current device.
+rc_status scratch_on_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return rc::fail(RC_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return rc::fail(RC_ERR_HIP, "device %d beyond the %d this library serves", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return rc::fail(RC_ERR_HIP, "hipGetSymbolAddress(scratch) failed on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return RC_OK;
+}
+
+}  // namespace
+
+extern "C" rc_status rc_decode_attention_static(const rc_shape* shape, void* o, const void* q, void* k_pool,
+                                                void* v_pool, const void* k_new, const void* v_new,
+                                                const int32_t* new_slots, const int32_t* req_to_token,
+                                                int32_t table_rows, int64_t stride, const int32_t* seq_lens,
+                                                int32_t batch, const int32_t* plan_dev, const rc_plan_info* info,
+                                                float sm_scale, void* stream) {
+  if (!shape || !info) return rc::fail(RC_ERR_ARG, "shape or plan info is NULL");
+  if (batch == 0) return RC_OK;
+  const int64_t need = rc_decode_workspace_bytes(shape, info);
+  if (need < 0 || need > RC_DECODE_STATIC_WORKSPACE_BYTES)
+    return rc::fail(RC_ERR_RANGE, "the plan needs %lld bytes of workspace, above the %lld of the static workspace",
+                    (long long)need, (long long)RC_DECODE_STATIC_WORKSPACE_BYTES);
+  void* ws = nullptr;
+  rc_status st = scratch_on_current_device(&ws);
+  if (st != RC_OK) return st;
+  return split_k_attention<0>(shape, o, q, k_pool, v_pool, k_new, v_new, new_slots, req_to_token, table_rows, stride,
+                              seq_lens, batch, plan_dev, info, sm_scale, ws, RC_DECODE_STATIC_WORKSPACE_BYTES, stream,
+                              false);
 }
 
 extern "C" rc_status rc_extend_attention_shared(const rc_shape* shape, void* o, const void* q, const void* k_pool,

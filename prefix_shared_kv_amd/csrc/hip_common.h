@@ -10,10 +10,11 @@ namespace rc {
 // Device error word registered through rc_set_error_word (nullptr = off).
 int32_t* error_word();
 
-// Times one launch with HIP events on `stream` while timing is enabled.
+// Times one launch with HIP events on `stream` while timing is enabled
+// (and `timed`: calls that must allocate nothing pass false).
 class ProfScope {
  public:
-  ProfScope(const char* name, hipStream_t stream);
+  ProfScope(const char* name, hipStream_t stream, bool timed = true);
   ~ProfScope();
 
  private:

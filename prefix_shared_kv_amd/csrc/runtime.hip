@@ -32,8 +32,8 @@ hipEvent_t get_event() {
 }
 }  // namespace
 
-ProfScope::ProfScope(const char* name, hipStream_t stream) : stream_(stream) {
-  if (!g_on) return;
+ProfScope::ProfScope(const char* name, hipStream_t stream, bool timed) : stream_(stream) {
+  if (!g_on || !timed) return;
   hipEvent_t a = get_event(), b = get_event();
   if (!a || !b) return;
   if (hipEventRecord(a, stream) != hipSuccess) return;  // not timed

@@ -116,6 +116,21 @@ def test_decode_argument_checks():
     assert st == N.RC_ERR_ARG
 
 
+def test_static_decode_argument_checks():
+    # the allocation-free decode rejects a plan whose workspace exceeds the
+    # static one before it touches the device
+    sh = shape()  # group 4, Hq 8, head_dim 128
+    buf, info = _plan([640] * 2048, 4)  # 2048 x 8 heads x 9 splits x 130 x 4 B = 76.7 MB
+    need = N.lib.rc_decode_workspace_bytes(C.byref(sh), C.byref(info))
+    assert need > N.RC_DECODE_STATIC_WORKSPACE_BYTES
+    call = N.lib.rc_decode_attention_static
+    st = call(C.byref(sh), FAKE, FAKE, FAKE, FAKE, None, None, None, FAKE, 2048, 640, FAKE, 2048, FAKE,
+              C.byref(info), 0.1, None)
+    assert st == N.RC_ERR_RANGE and "static workspace" in N.last_error()
+    assert call(None, FAKE, FAKE, FAKE, FAKE, None, None, None, FAKE, 2, 128, FAKE, 2, FAKE, C.byref(info), 0.1,
+                None) == N.RC_ERR_ARG
+
+
 def test_unshared_plan_layout():
     # chunk 64: ranges up to 72 (chunk + chunk/8) stay whole, longer ones are
     # cut into the fewest near-equal pieces of at most 72
