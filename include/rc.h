@@ -209,6 +209,23 @@ rc_status rc_plan_decode_unshared(int32_t batch, const int32_t* rows, const int3
                                   int32_t group, int32_t chunk, int32_t* plan, int64_t capacity,
                                   rc_plan_info* info);
 
+/* Per-step inputs of decode steps t = 0..n_steps-1 ("Prompt Caching"       */
+/* glossary: each decoded token's K/V are stored and it attends over every   */
+/* cached position): request b's step-t token sits at position              */
+/* p = base_lens[b] + t of table row rows[b] (NULL rows: b), so             */
+/*   slots[t * batch + b]    = the pool slot of position p (row[p], or       */
+/*                             row[p / page_size] * page_size +              */
+/*                             p % page_size with page_size > 1)             */
+/*   seq_lens[t * batch + b] = p + 1 (it attends over positions [0, p])      */
+/* the new_slots and seq_lens of rc_decode_attention for step t.  Host call; */
+/* req_to_token is the host table [table_rows, stride].  row_entries         */
+/* (nullable, batch entries): the entries each row holds (from               */
+/* rc_radix_emit_rows); positions past them, or entries below 0, fail with  */
+/* RC_ERR_RANGE before anything is written.                                  */
+rc_status rc_decode_steps(const int32_t* req_to_token, int32_t table_rows, int64_t stride, int32_t page_size,
+                          int32_t batch, const int32_t* rows, const int64_t* row_entries, const int32_t* base_lens,
+                          int32_t n_steps, int32_t* slots, int32_t* seq_lens);
+
 /* Workspace bytes rc_decode_attention needs for a plan (fp32 partials).     */
 int64_t rc_decode_workspace_bytes(const rc_shape* shape, const rc_plan_info* info);
 
@@ -366,25 +383,52 @@ rc_status rc_radix_insert_rows(rc_radix* tree, int32_t batch, const int32_t* tok
 /* stride (n_b + reserve <= stride) or the call fails with RC_ERR_RANGE.     */
 /* Every node the requests' tokens enter is marked as used now (one time     */
 /* for the whole batch).                                                     */
+/*   flags     RC_EMIT_EVICT: when too few slots are free, first free the    */
+/*             missing ones by rc_radix_evict (the batch's matched prefixes  */
+/*             are pinned meanwhile, so the rows still get them); if that is */
+/*             not enough the call fails with RC_ERR_NOMEM, the rows and     */
+/*             locks untouched, but what was evicted and the use marks stay. */
+/*             Without it too few free slots fail with RC_ERR_NOMEM and      */
+/*             change nothing.                                               */
+/*             RC_EMIT_FULL_MATCH: the match is not capped at n_b - 1, so a  */
+/*             fully cached request gets E_b = 0 (for storing K/V computed  */
+/*             elsewhere, not for running the request).  Other bits:         */
+/*             RC_ERR_ARG.                                                    */
 /*   handles (host, nullable, batch entries): also lock each request's       */
 /*             matched prefix (as rc_radix_lock of its first P_b tokens) and */
 /*             return the handles; release them with rc_radix_unlock.        */
-/*   evict     0: too few free slots fail with RC_ERR_NOMEM and change       */
-/*             nothing.  1: first free the missing slots by rc_radix_evict   */
-/*             (the batch's matched prefixes are pinned meanwhile, so the    */
-/*             rows still get them); if that is not enough the call fails    */
-/*             with RC_ERR_NOMEM, the rows and locks untouched, but what was */
-/*             evicted and the use marks stay.                                */
 /*   first_changed (host, nullable, batch entries): index of the first entry */
 /*             of row rows[b] whose value this call changed (the row's entry */
 /*             count if none did).  Entries before it hold what they held    */
 /*             before the call, so a caller that mirrors the table on the    */
 /*             device uploads only [first_changed[b], row entries).           */
+/*   row_entries (host, nullable, batch entries): the entries row rows[b]    */
+/*             now uses, n_b + reserve (tokens) or ceil((n_b + reserve) /    */
+/*             page_size) (paged tree).                                      */
+/*   new_slots (host, nullable, room for sum_b n_b entries): the pool slots  */
+/*             of the new tokens, request after request: positions P_b ..    */
+/*             n_b - 1 of request b at offset sum_{c<b} E_c; in a paged tree */
+/*             position p's slot is page(p / page_size) * page_size +        */
+/*             p % page_size.  These are the slots rc_kv_store fills.         */
+#define RC_EMIT_EVICT 1
+#define RC_EMIT_FULL_MATCH 2
 rc_status rc_radix_emit_rows(rc_radix* tree, int32_t batch, const int32_t* tokens,
                              const int64_t* tok_off, int32_t reserve, const int32_t* rows,
                              int32_t* req_to_token, int32_t table_rows, int64_t stride,
-                             int32_t* prefix_lens, int32_t* extend_lens, int32_t evict,
-                             int64_t* handles, int64_t* first_changed);
+                             int32_t* prefix_lens, int32_t* extend_lens, int32_t flags,
+                             int64_t* handles, int64_t* first_changed, int64_t* row_entries,
+                             int32_t* new_slots);
+
+/* Return a batch's own slots when its requests end: for each request b,    */
+/* the units (slots, or pages in a paged tree) of row rows[b] of the host    */
+/* table from entry keep_lens[b] / page_size up to row_entries[b]: the       */
+/* positions from its first token not kept in the tree (a partly kept page   */
+/* is never in the tree) to the end of its row.  keep_lens in tokens,        */
+/* row_entries as rc_radix_emit_rows reported them.  All or nothing, with   */
+/* rc_radix_free's checks (a unit already free or given twice: RC_ERR_ARG).  */
+rc_status rc_radix_free_rows(rc_radix* tree, int32_t batch, const int32_t* rows, const int32_t* req_to_token,
+                             int32_t table_rows, int64_t stride, const int64_t* keep_lens,
+                             const int64_t* row_entries);
 
 /* Locks and LRU eviction ([SG] RadixAttention bullet: an LRU cache of KV in */
 /* the radix tree; nine-step example, steps 5, 8 and 9: least recently used  */
@@ -451,11 +495,13 @@ rc_status rc_radix_plan_decode(rc_radix* tree, int32_t batch, const int32_t* tok
 /* each token reads its own request's new tokens up to itself alone.        */
 /* Run it with rc_extend_attention_shared.  Output and sizing as            */
 /* rc_plan_decode_unshared; RC_ERR_RANGE also when a request's prefix +      */
-/* extend exceed its tokens.                                                 */
+/* extend exceed its tokens.  seq_lens (host, nullable, one entry per new    */
+/* token) receives each token's context length prefix_lens[b] + i + 1, the  */
+/* seq_lens rc_extend_attention_shared takes (written on success only).     */
 rc_status rc_radix_plan_extend(rc_radix* tree, int32_t batch, const int32_t* tokens, const int64_t* tok_off,
                                const int32_t* prefix_lens, const int32_t* extend_lens, const int32_t* rows,
                                int32_t group, int32_t chunk, int32_t* plan, int64_t capacity,
-                               rc_plan_info* info);
+                               rc_plan_info* info, int32_t* seq_lens);
 
 /* Extend attention over a shared-prefix plan (rc_radix_plan_extend): the    */
 /* same outputs as rc_extend_attention, o[m] for new token m (token i of     */

@@ -16,6 +16,7 @@ RC_F32, RC_BF16 = 0, 1
 RC_DEVERR_SLOT, RC_DEVERR_TABLE, RC_DEVERR_LENGTH, RC_DEVERR_PLAN = 1, 2, 4, 8
 RC_PLAN_MAGIC, RC_PLAN_HEADER, RC_PLAN_ITEM, RC_PLAN_ITEM_OWN = 0x52435031, 8, 8, 1
 RC_DECODE_STATIC_WORKSPACE_BYTES = 64 << 20
+RC_EMIT_EVICT, RC_EMIT_FULL_MATCH = 1, 2
 
 STATUS_NAMES = {0: "RC_OK", 1: "RC_ERR_ARG", 2: "RC_ERR_SHAPE", 3: "RC_ERR_DTYPE", 4: "RC_ERR_RANGE",
                 5: "RC_ERR_NOMEM", 6: "RC_ERR_HIP", 7: "RC_ERR_INTERNAL"}
@@ -77,14 +78,16 @@ _SIGS = {
     "rc_radix_alloc": (i32, [P, i64, P]),
     "rc_radix_free": (i32, [P, P, i64]),
     "rc_radix_insert": (i32, [P, P, P, i64, I64P]),
-    "rc_radix_emit_rows": (i32, [P, i32, P, P, i32, P, P, i32, i64, P, P, i32, P, P]),
+    "rc_radix_emit_rows": (i32, [P, i32, P, P, i32, P, P, i32, i64, P, P, i32, P, P, P, P]),
+    "rc_radix_free_rows": (i32, [P, i32, P, P, i32, i64, P, P]),
+    "rc_decode_steps": (i32, [P, i32, i64, i32, i32, P, P, P, i32, P, P]),
     "rc_radix_lock": (i32, [P, i32, P, P, P, P, P]),
     "rc_radix_unlock": (i32, [P, P, i32]),
     "rc_radix_evict": (i32, [P, i64, I64P]),
     "rc_radix_insert_rows": (i32, [P, i32, P, P, P, P, P, i32, i64, P]),
     "rc_radix_fork": (i32, [P, P, P, i64, i32, P, P, i32, i64]),
     "rc_radix_plan_decode": (i32, [P, i32, P, P, P, P, P, i32, i32, P, i64, C.POINTER(RcPlanInfo)]),
-    "rc_radix_plan_extend": (i32, [P, i32, P, P, P, P, P, i32, i32, P, i64, C.POINTER(RcPlanInfo)]),
+    "rc_radix_plan_extend": (i32, [P, i32, P, P, P, P, P, i32, i32, P, i64, C.POINTER(RcPlanInfo), P]),
     "rc_radix_stats_get": (i32, [P, C.POINTER(RcRadixStats)]),
     "rc_prof_enable": (i32, [i32]),
     "rc_prof_tag": (i32, [C.c_char_p]),

@@ -173,6 +173,7 @@ class DecodePlan:
         self.host = buf
         self.info = info
         self.dev: Optional[torch.Tensor] = None
+        self.seq_lens: Optional[np.ndarray] = None  # cascade extend plans: each new token's context length
 
     def to(self, device, uploader=None) -> "DecodePlan":
         """Device copy of the plan; `uploader(array) -> tensor` may supply an asynchronous copy."""
@@ -224,6 +225,25 @@ def plan_decode_unshared(max_seq_lens: Sequence[int], group: int, chunk: int = 5
     rw = None if rows is None else np.ascontiguousarray(rows, np.int32)
     return _run_planner(lambda p, cap, info: lib.rc_plan_decode_unshared(
         ms.size, _np_ptr(rw), _np_ptr(ms), group, chunk, p, cap, C.byref(info)), _plan_guess(ms, group, chunk))
+
+
+def decode_steps(table: np.ndarray, rows: Sequence[int], base_lens: Sequence[int], n_steps: int, page_size: int = 1,
+                 row_entries: Optional[Sequence[int]] = None) -> Tuple[np.ndarray, np.ndarray]:
+    """(slots, seq_lens), both int32 [n_steps, batch]: the pool slot of request b's step-t token,
+    at position base_lens[b] + t of host table row rows[b], and the number of positions it attends
+    over (rc_decode_steps)."""
+    if table.dtype != np.int32 or table.ndim != 2 or not table.flags.c_contiguous:
+        raise ValueError("table must be a C-contiguous int32 [rows, stride] array")
+    rw = np.ascontiguousarray(rows, np.int32)
+    base = np.ascontiguousarray(base_lens, np.int32)
+    re = None if row_entries is None else np.ascontiguousarray(row_entries, np.int64)
+    if base.shape != rw.shape or (re is not None and re.shape != rw.shape):
+        raise ValueError("one base length (and row entry count) per row")
+    slots = np.zeros((n_steps, rw.size), np.int32)
+    seq = np.zeros((n_steps, rw.size), np.int32)
+    check(lib.rc_decode_steps(_np_ptr(table), table.shape[0], table.shape[1], page_size, rw.size, _np_ptr(rw),
+                              _np_ptr(re), _np_ptr(base), n_steps, _np_ptr(slots), _np_ptr(seq)))
+    return slots, seq
 
 
 def decode_workspace_bytes(shape: KVShape, plan: DecodePlan) -> int:
@@ -398,12 +418,18 @@ class RadixTree:
 
     def emit_rows(self, batch: Sequence[Sequence[int]], table: np.ndarray, rows: Optional[Sequence[int]] = None,
                   reserve: int = 0, evict: bool = False, handles: Optional[np.ndarray] = None,
-                  first_changed: Optional[np.ndarray] = None) -> Tuple[np.ndarray, np.ndarray]:
+                  first_changed: Optional[np.ndarray] = None, full_match: bool = False,
+                  row_entries: Optional[np.ndarray] = None,
+                  new_slots: Optional[np.ndarray] = None) -> Tuple[np.ndarray, np.ndarray]:
         """Fill rows of a host table [R, stride]; returns (prefix_lens, extend_lens).
         evict: evict least recently used unpinned nodes when the free slots fall short.
+        full_match: do not cap the match at n - 1 tokens (storing K/V computed elsewhere).
         handles: an int64 array of one entry per request that receives locks on the matched prefixes.
         first_changed: an int64 array of one entry per request that receives the first entry of its
-        row the call changed (the row's entry count if none)."""
+        row the call changed (the row's entry count if none).
+        row_entries: an int64 array of one entry per request that receives the entries its row uses.
+        new_slots: an int32 array with room for every token of the batch; its first sum(extend_lens)
+        entries receive the new tokens' pool slots, request after request."""
         if table.dtype != np.int32 or table.ndim != 2 or not table.flags.c_contiguous:
             raise ValueError("table must be a C-contiguous int32 [rows, stride] array")
         tb = _tb(batch)
@@ -411,15 +437,31 @@ class RadixTree:
         rw = np.arange(B, dtype=np.int32) if rows is None else np.ascontiguousarray(rows, np.int32)
         P = np.zeros(B, np.int32)
         E = np.zeros(B, np.int32)
-        if handles is not None and (handles.dtype != np.int64 or handles.shape != (B,) or not handles.flags.c_contiguous):
-            raise ValueError("handles must be a contiguous int64 array with one entry per request")
-        if first_changed is not None and (first_changed.dtype != np.int64 or first_changed.shape != (B,)
-                                          or not first_changed.flags.c_contiguous):
-            raise ValueError("first_changed must be a contiguous int64 array with one entry per request")
+        for arr, nm in ((handles, "handles"), (first_changed, "first_changed"), (row_entries, "row_entries")):
+            if arr is not None and (arr.dtype != np.int64 or arr.shape != (B,) or not arr.flags.c_contiguous):
+                raise ValueError(f"{nm} must be a contiguous int64 array with one entry per request")
+        if new_slots is not None and (new_slots.dtype != np.int32 or new_slots.ndim != 1 or new_slots.size < tb.flat.size
+                                      or not new_slots.flags.c_contiguous):
+            raise ValueError("new_slots must be a contiguous int32 array with room for every token of the batch")
+        flags = (N.RC_EMIT_EVICT if evict else 0) | (N.RC_EMIT_FULL_MATCH if full_match else 0)
         check(lib.rc_radix_emit_rows(self._h, B, _np_ptr(tb.flat), _np_ptr(tb.off), reserve, _np_ptr(rw), _np_ptr(table),
-                                     table.shape[0], table.shape[1], _np_ptr(P), _np_ptr(E), int(bool(evict)),
-                                     _np_ptr(handles), _np_ptr(first_changed)))
+                                     table.shape[0], table.shape[1], _np_ptr(P), _np_ptr(E), flags,
+                                     _np_ptr(handles), _np_ptr(first_changed), _np_ptr(row_entries), _np_ptr(new_slots)))
         return P, E
+
+    def free_rows(self, rows: Sequence[int], table: np.ndarray, keep_lens: Sequence[int],
+                  row_entries: Sequence[int]) -> None:
+        """Return each row's units from the first position not kept (keep_lens, tokens) to its end
+        (row_entries, as emit_rows reported them) to the pool (rc_radix_free_rows)."""
+        if table.dtype != np.int32 or table.ndim != 2 or not table.flags.c_contiguous:
+            raise ValueError("table must be a C-contiguous int32 [rows, stride] array")
+        rw = np.ascontiguousarray(rows, np.int32)
+        kp = np.ascontiguousarray(keep_lens, np.int64)
+        re = np.ascontiguousarray(row_entries, np.int64)
+        if kp.shape != rw.shape or re.shape != rw.shape:
+            raise ValueError("one keep length and one row entry count per row")
+        check(lib.rc_radix_free_rows(self._h, rw.size, _np_ptr(rw), _np_ptr(table), table.shape[0], table.shape[1],
+                                     _np_ptr(kp), _np_ptr(re)))
 
     def lock(self, batch, lengths: Optional[Sequence[int]] = None) -> Tuple[np.ndarray, np.ndarray]:
         """Pin the cached prefix of each request's first lengths[b] tokens (default: all) against
@@ -477,7 +519,8 @@ class RadixTree:
 
     def plan_extend(self, batch, prefix_lens: Sequence[int], extend_lens: Sequence[int], group: int,
                     chunk: int = 4096, rows: Optional[Sequence[int]] = None) -> DecodePlan:
-        """Cascade extend plan: members are the batch's new tokens (rc_radix_plan_extend)."""
+        """Cascade extend plan: members are the batch's new tokens (rc_radix_plan_extend).  The plan's
+        seq_lens holds each new token's context length (the seq_lens of extend_attention_shared)."""
         tb = _tb(batch)
         B = len(tb)
         P = np.ascontiguousarray(prefix_lens, np.int32)
@@ -485,10 +528,16 @@ class RadixTree:
         if P.shape != (B,) or E.shape != (B,):
             raise ValueError("one prefix and one extend length per request")
         rw = np.arange(B, dtype=np.int32) if rows is None else np.ascontiguousarray(rows, np.int32)
-        seq = np.concatenate([p + np.arange(1, e + 1) for p, e in zip(P, E)]) if B else np.zeros(0, np.int64)
-        return _run_planner(lambda p, cap, info: lib.rc_radix_plan_extend(
+        seq = np.zeros(int(E.sum()), np.int32)
+        # buffer guess: every new token reads its request's context in pieces of chunk, plus a few shared ranges
+        n_tok = int(E.sum())
+        longest = int((P.astype(np.int64) + E).max()) if B else 0
+        guess = N.RC_PLAN_HEADER + n_tok * (longest // max(chunk, 1) + 4) * (N.RC_PLAN_ITEM + 2) + n_tok
+        plan = _run_planner(lambda p, cap, info: lib.rc_radix_plan_extend(
             self._h, B, _np_ptr(tb.flat), _np_ptr(tb.off), _np_ptr(P), _np_ptr(E), _np_ptr(rw), group, chunk, p, cap,
-            C.byref(info)), _plan_guess(np.asarray(seq, np.int32), group, chunk))
+            C.byref(info), _np_ptr(seq)), guess)
+        plan.seq_lens = seq
+        return plan
 
     def stats(self) -> dict:
         st = RcRadixStats()

@@ -646,17 +646,24 @@ rc_status rc_radix_insert_rows(rc_radix* t, int32_t batch, const int32_t* tokens
 
 rc_status rc_radix_emit_rows(rc_radix* t, int32_t batch, const int32_t* tokens, const int64_t* tok_off,
                              int32_t reserve, const int32_t* rows, int32_t* table, int32_t table_rows,
-                             int64_t stride, int32_t* prefix_lens, int32_t* extend_lens, int32_t evict,
-                             int64_t* handles, int64_t* first_changed) {
+                             int64_t stride, int32_t* prefix_lens, int32_t* extend_lens, int32_t flags,
+                             int64_t* handles, int64_t* first_changed, int64_t* row_entries, int32_t* new_slots) {
   if (!t || batch < 0 || reserve < 0 || stride <= 0 || table_rows < 0) return fail(RC_ERR_ARG, "bad argument to rc_radix_emit_rows");
   if (batch > 0 && (!tok_off || !rows || !table || !prefix_lens || !extend_lens)) return fail(RC_ERR_ARG, "NULL array in rc_radix_emit_rows");
+  if (flags & ~(RC_EMIT_EVICT | RC_EMIT_FULL_MATCH)) return fail(RC_ERR_ARG, "unknown emit_rows flags 0x%x", (unsigned)flags);
   if (rc_status st = check_lens(batch, tok_off, nullptr); st != RC_OK) return st;
+  const bool evict = flags & RC_EMIT_EVICT;
   // In units of the tree: tokens, or pages.  Request b gets entries for its
   // n + reserve tokens (ceil((n + reserve) / page) pages); at most (n - 1) /
-  // page units of its prefix are reused, so at least one token is computed.
+  // page units of its prefix are reused, so at least one token is computed
+  // (with RC_EMIT_FULL_MATCH all n / page whole units of it).
   const int64_t pg = t->page;
+  const bool full = flags & RC_EMIT_FULL_MATCH;
   auto entries = [&](int32_t b) { return (tok_off[b + 1] - tok_off[b] + reserve + pg - 1) / pg; };
-  auto cap_of = [&](int32_t b) { const int64_t n = tok_off[b + 1] - tok_off[b]; return n > 0 ? (n - 1) / pg : 0; };
+  auto cap_of = [&](int32_t b) {
+    const int64_t n = tok_off[b + 1] - tok_off[b];
+    return full ? n / pg : (n > 0 ? (n - 1) / pg : 0);
+  };
   // pass 1 (read only): matched length and the edges entered, per request
   struct Visit { int32_t node; int64_t k; };
   std::vector<int64_t> P(batch);
@@ -722,6 +729,7 @@ rc_status rc_radix_emit_rows(rc_radix* t, int32_t batch, const int32_t* tokens, 
       row[i] = s;
     }
     if (first_changed) first_changed[b] = fc;
+    if (row_entries) row_entries[b] = entries(b);
     prefix_lens[b] = (int32_t)(P[b] * pg);
     extend_lens[b] = (int32_t)(n - P[b] * pg);
     t->st.matches++;
@@ -747,6 +755,65 @@ rc_status rc_radix_emit_rows(rc_radix* t, int32_t batch, const int32_t* tokens, 
       handles[b] = handle_of(*t, end[b]);
     else if (pinning)
       pin(*t, end[b], -1);
+  }
+  // pool slots of the new tokens, request after request: position p of a row
+  // is slot row[p] (unpaged) or row[p / page] * page + p % page
+  if (new_slots) {
+    int64_t o = 0;
+    for (int32_t b = 0; b < batch; ++b) {
+      const int32_t* row = table + (int64_t)rows[b] * stride;
+      for (int64_t p = prefix_lens[b]; p < prefix_lens[b] + extend_lens[b]; ++p)
+        new_slots[o++] = (int32_t)((int64_t)row[p / pg] * pg + p % pg);
+    }
+  }
+  return RC_OK;
+}
+
+rc_status rc_radix_free_rows(rc_radix* t, int32_t batch, const int32_t* rows, const int32_t* table, int32_t table_rows,
+                             int64_t stride, const int64_t* keep_lens, const int64_t* row_entries) {
+  if (!t || batch < 0 || stride <= 0 || table_rows < 0) return fail(RC_ERR_ARG, "bad argument to rc_radix_free_rows");
+  if (batch > 0 && (!rows || !table || !keep_lens || !row_entries)) return fail(RC_ERR_ARG, "NULL array in rc_radix_free_rows");
+  // units [keep / page, entries) of each row: the request's own positions
+  // from its first position not kept (a partly kept page is not in the tree)
+  std::vector<int32_t> units;
+  for (int32_t b = 0; b < batch; ++b) {
+    if (rows[b] < 0 || rows[b] >= table_rows) return fail(RC_ERR_RANGE, "row %d of request %d outside [0, %d)", rows[b], b, table_rows);
+    if (keep_lens[b] < 0 || row_entries[b] < 0 || row_entries[b] > stride)
+      return fail(RC_ERR_RANGE, "request %d: kept %lld tokens, %lld row entries (stride %lld)", b, (long long)keep_lens[b],
+                  (long long)row_entries[b], (long long)stride);
+    const int32_t* row = table + (int64_t)rows[b] * stride;
+    for (int64_t i = keep_lens[b] / t->page; i < row_entries[b]; ++i) units.push_back(row[i]);
+  }
+  return rc_radix_free(t, units.data(), (int64_t)units.size());
+}
+
+rc_status rc_decode_steps(const int32_t* table, int32_t table_rows, int64_t stride, int32_t page_size, int32_t batch,
+                          const int32_t* rows, const int64_t* row_entries, const int32_t* base_lens, int32_t n_steps,
+                          int32_t* slots, int32_t* seq_lens) {
+  if (batch < 0 || n_steps < 0 || stride <= 0 || table_rows < 0) return fail(RC_ERR_ARG, "bad argument to rc_decode_steps");
+  if (page_size < 1 || page_size > 1024 || (page_size & (page_size - 1)))
+    return fail(RC_ERR_SHAPE, "page_size %d is not a power of two up to 1024", page_size);
+  if (batch > 0 && n_steps > 0 && (!table || !base_lens || !slots || !seq_lens)) return fail(RC_ERR_ARG, "NULL array in rc_decode_steps");
+  for (int32_t b = 0; b < batch && n_steps > 0; ++b) {
+    const int32_t r = rows ? rows[b] : b;
+    if (r < 0 || r >= table_rows) return fail(RC_ERR_RANGE, "row %d of request %d outside [0, %d)", r, b, table_rows);
+    const int64_t ent = row_entries ? row_entries[b] : stride;
+    if (base_lens[b] < 0 || ent > stride || (int64_t)base_lens[b] + n_steps > ent * page_size)
+      return fail(RC_ERR_RANGE, "request %d: decode positions [%d, %lld) past its %lld row entries", b, base_lens[b],
+                  (long long)base_lens[b] + n_steps, (long long)ent);
+    const int32_t* row = table + (int64_t)r * stride;
+    for (int32_t s = 0; s < n_steps; ++s) {
+      const int64_t p = (int64_t)base_lens[b] + s;
+      if (row[p / page_size] < 0) return fail(RC_ERR_RANGE, "request %d: position %lld of row %d holds no slot", b, (long long)p, r);
+    }
+  }
+  for (int32_t b = 0; b < batch; ++b) {
+    const int32_t* row = table + (int64_t)(rows ? rows[b] : b) * stride;
+    for (int32_t s = 0; s < n_steps; ++s) {
+      const int64_t p = (int64_t)base_lens[b] + s;  // the token of step s sits at position p ...
+      slots[(int64_t)s * batch + b] = (int32_t)((int64_t)row[p / page_size] * page_size + p % page_size);
+      seq_lens[(int64_t)s * batch + b] = (int32_t)(p + 1);  // ... and attends over positions [0, p]
+    }
   }
   return RC_OK;
 }
@@ -1125,7 +1192,7 @@ extern "C" rc_status rc_radix_plan_decode(rc_radix* t, int32_t batch, const int3
 extern "C" rc_status rc_radix_plan_extend(rc_radix* t, int32_t batch, const int32_t* tokens, const int64_t* tok_off,
                                           const int32_t* prefix_lens, const int32_t* extend_lens, const int32_t* rows,
                                           int32_t group, int32_t chunk, int32_t* plan, int64_t cap,
-                                          rc_plan_info* info) {
+                                          rc_plan_info* info, int32_t* seq_lens) {
   if (!t || !info) return fail(RC_ERR_ARG, "tree or info is NULL");
   if (batch < 0) return fail(RC_ERR_ARG, "batch < 0");
   if (batch > 0 && (!tok_off || !prefix_lens || !extend_lens)) return fail(RC_ERR_ARG, "NULL array in rc_radix_plan_extend");
@@ -1155,6 +1222,7 @@ extern "C" rc_status rc_radix_plan_extend(rc_radix* t, int32_t batch, const int3
   std::vector<std::vector<Visit>> walks;
   std::vector<int64_t> walked;
   walk_requests(t, batch, tokens, tok_off, [&](int32_t b) { return (int64_t)prefix_lens[b]; }, walks, walked);
-  return plan_from_walks(t, (int32_t)n_tok, req_of, walks, walked, rows_of, max_seq.data(), group, chunk, plan, cap,
-                         info);
+  st = plan_from_walks(t, (int32_t)n_tok, req_of, walks, walked, rows_of, max_seq.data(), group, chunk, plan, cap, info);
+  if (st == RC_OK && seq_lens) std::copy(max_seq.begin(), max_seq.end(), seq_lens);
+  return st;
 }

@@ -40,6 +40,8 @@ class Batch:
     prefix_lens: np.ndarray    # P_b
     extend_lens: np.ndarray    # E_b
     reserve: int
+    entries: np.ndarray        # table entries each row uses (tokens, or pages)
+    new_slots: np.ndarray      # pool slots of the new tokens, request after request
     locks: Optional[np.ndarray] = None  # lock handles pinning each request's cached tokens
     dev: dict = dataclasses.field(default_factory=dict)
     own_rows: bool = True      # rows came from the engine's free list (returned at release)
@@ -196,43 +198,28 @@ class Engine:
         while self._uploads and self._uploads[0][1].query():
             self._uploads.popleft()
 
-    def slots_at(self, rows: np.ndarray, pos: np.ndarray) -> np.ndarray:
-        """Slots of positions pos in table rows rows (arrays of one shape)."""
-        if self.ps == 1:
-            return self.table_h[rows, pos]
-        return self.table_h[rows, pos // self.ps] * self.ps + pos % self.ps
-
     # -- cache population (a sequence whose K/V are already known) -----------
     def populate(self, tokens: Sequence[int], k: torch.Tensor, v: torch.Tensor, expect_cached: Optional[int] = None) -> int:
-        """Store K/V for the uncached tail of `tokens` and insert the sequence.
-        k, v hold rows for positions [cached, n).  Returns the cached length found."""
+        """Store K/V for the uncached tail of `tokens` and insert the sequence (K/V computed
+        elsewhere, e.g. a prefix loaded from storage).  k, v hold rows for positions [cached, n),
+        cached being the whole cached prefix (whole pages in a paged pool).  Returns it."""
         t = np.ascontiguousarray(tokens, np.int32)
-        h, _ = self.tree.lock([t])  # the cached part stays while room is made for the rest
+        b = self.schedule(TokenBatch([t]), full_match=True)
+        stored = False
         try:
-            probe = np.concatenate([t, np.array([-1], np.int32)])  # no stored edge starts with -1: full match allowed
-            m, pre = self.tree.match(probe)
+            m, n_new = int(b.prefix_lens[0]), int(b.extend_lens[0])
             if expect_cached is not None and m != expect_cached:
                 raise RuntimeError(f"expected {expect_cached} cached tokens, found {m}")
-            n_new = len(t) - m
             if k.shape[0] != n_new or v.shape[0] != n_new:
                 raise ValueError(f"need K/V for {n_new} uncached tokens, got {k.shape[0]}")
-            ps = self.ps
-            units = -(-len(t) // ps) - m // ps  # fresh slots, or pages
-            short = units - self.tree.stats()["free_slots"]
-            if short > 0:
-                self.tree.evict(short)
-            new = self.tree.alloc(units)
             if n_new:
-                pos = np.arange(m, len(t))
-                ids = np.concatenate([pre, new]).astype(np.int64)
-                slots = ids[pos // ps] * ps + pos % ps
-                api.kv_store(self.shape, self.k_pool, self.v_pool, k, v, self._i32(slots.astype(np.int32)))
-            ids = np.concatenate([pre, new]).astype(np.int32)
-            self.tree.insert(t, ids[:len(t) // ps])
-            if len(t) % ps:  # a partial last page is not cached
-                self.tree.free(ids[len(t) // ps:])
+                api.kv_store(self.shape, self.k_pool, self.v_pool, k, v, b.dev["slots"])
+            self.commit(b)
+            stored = True
         finally:
-            self.tree.unlock(h)
+            # stored: slots past the tree's whole units (a partial last page) go back;
+            # otherwise every slot the call took
+            self.release(b, keep=None if stored else b.prefix_lens)
         return m
 
     # -- a batch of requests --------------------------------------------------
@@ -250,11 +237,12 @@ class Engine:
         self.free_rows.extend(int(r) for r in rows)
 
     def schedule(self, batch_tokens, reserve: int = 0, evict: bool = True,
-                 rows: Optional[np.ndarray] = None) -> Batch:
+                 rows: Optional[np.ndarray] = None, full_match: bool = False) -> Batch:
         """batch_tokens: a list of token-id arrays or a TokenBatch.  Each request's cached prefix
         is pinned until release; with evict, least recently used unpinned nodes make room when
         the free slots fall short.  rows: table rows from take_rows, one per request, not used by
-        another live batch (default: rows from the free list)."""
+        another live batch (default: rows from the free list).  full_match: a fully cached request
+        gets no new tokens (populate), instead of recomputing its last one."""
         tb = batch_tokens if isinstance(batch_tokens, TokenBatch) else TokenBatch(batch_tokens)
         B = len(tb)
         own = rows is None
@@ -269,31 +257,22 @@ class Engine:
         self._rows_writable(rows)
         locks = np.zeros(B, np.int64)
         first = np.zeros(B, np.int64)
+        entries = np.zeros(B, np.int64)
+        slots = np.zeros(max(tb.flat.size, 1), np.int32)
         P, E = self.tree.emit_rows(tb, self.table_h, rows=rows, reserve=reserve, evict=evict, handles=locks,
-                                   first_changed=first)
+                                   first_changed=first, full_match=full_match, row_entries=entries, new_slots=slots)
         if own:
             del self.free_rows[:B]
-        self._upload_rows(rows, first, -(-(tb.lens() + reserve) // self.ps))
-        b = Batch(tb, rows, P, E, reserve, locks, own_rows=own)
+        self._upload_rows(rows, first, entries)
+        b = Batch(tb, rows, P, E, reserve, entries, slots[:int(E.sum())], locks, own_rows=own)
+        # requests' new tokens are packed one after the other in q, k_new, v_new and o
         start = np.zeros(B, np.int32)
         if B:
             start[1:] = np.cumsum(E)[:-1]
         # every integer array the batch's launches read, in one upload
         names = ("rows", "P", "E", "start", "slots")
-        b.dev = dict(zip(names, self._i32_many(rows, P, E, start, self._new_slots(rows, P, E))))
+        b.dev = dict(zip(names, self._i32_many(rows, P, E, start, b.new_slots)))
         return b
-
-    def new_token_slots(self, b: Batch) -> np.ndarray:
-        return self._new_slots(b.rows, b.prefix_lens, b.extend_lens)
-
-    def _new_slots(self, rows, P, E) -> np.ndarray:
-        """Slots of the new tokens, request after request (positions P_b .. P_b + E_b - 1 of row b)."""
-        n = int(np.sum(E))
-        if n == 0:
-            return np.zeros(0, np.int32)
-        r = np.repeat(np.asarray(rows, np.int64), E)
-        pos = np.arange(n, dtype=np.int64) - np.repeat(np.cumsum(E) - E, E) + np.repeat(np.asarray(P, np.int64), E)
-        return self.slots_at(r, pos).astype(np.int32)
 
     def extend(self, b: Batch, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, sm_scale: float,
                o: Optional[torch.Tensor] = None, store: bool = True, cascade: bool = False,
@@ -304,8 +283,6 @@ class Engine:
         T = b.total_extend
         if q.shape[0] != T:
             raise ValueError(f"q has {q.shape[0]} rows, the batch has {T} new tokens")
-        if (store or cascade) and "slots" not in b.dev:
-            b.dev["slots"] = self._i32(self.new_token_slots(b))
         if store or cascade:  # the cascade path reads every key, the new ones too, from the pool
             api.kv_store(self.shape, self.k_pool, self.v_pool, k_new, v_new, b.dev["slots"])
         if o is None:
@@ -314,8 +291,7 @@ class Engine:
             return o
         if cascade:
             plan = self.tree.plan_extend(b.tb, b.prefix_lens, b.extend_lens, self.shape.group, chunk, rows=b.rows)
-            seq = np.concatenate([p + np.arange(1, e + 1) for p, e in zip(b.prefix_lens, b.extend_lens)])
-            plan.dev, seq_d = self._i32_many(plan.host, seq)
+            plan.dev, seq_d = self._i32_many(plan.host, plan.seq_lens)
             ws = torch.empty(api.decode_workspace_bytes(self.shape, plan), dtype=torch.uint8, device=self.device)
             api.extend_attention_shared(self.shape, o, q, self.k_pool, self.v_pool, self.table_d, seq_d,
                                         plan, sm_scale, ws)
@@ -330,8 +306,7 @@ class Engine:
         Where the tree already held them, the row is rewritten to the tree's slots."""
         # The insert works on a copy of the batch's rows (the table's rows may
         # still be uploading); only rows the tree rewrote are written back.
-        n = b.tb.lens() if lengths is None else np.asarray(lengths, np.int64)
-        width = max(-(-int(n.max()) // self.ps) if b.size else 0, 1)
+        width = max(int(b.entries.max()) if b.size else 0, 1)
         work = np.ascontiguousarray(self.table_h[b.rows, :width])
         changed = self.tree.insert_rows(b.tb, work, np.arange(b.size, dtype=np.int32), lengths)
         if b.locks is not None:  # pin what is stored now, then drop the old pins
@@ -349,19 +324,20 @@ class Engine:
         """Plan decode steps t = 0..n_steps-1; step t's token sits at position base_lens[i] + t.
         `committed[i]` tokens of request i are in the tree (default: base_lens)."""
         base = np.asarray(base_lens, np.int32)
-        if np.any(base + n_steps > b.tb.lens() + b.reserve):
-            raise ValueError("decode steps run past the reserved slots")
-        max_seq = base + n_steps
-        g = self.shape.group
         com = base if committed is None else np.asarray(committed, np.int32)
+        if np.any(com > base):
+            # the plan would share positions the decode steps overwrite
+            raise ValueError("committed tokens reach past a request's first decode position")
+        if n_steps < 1:
+            raise ValueError("n_steps must be at least 1")
+        # each step's token slot and context length, from the table rows (positions past a row's
+        # reserved entries are rejected)
+        slots, seq = api.decode_steps(self.table_h, b.rows, base, n_steps, self.ps, row_entries=b.entries)
+        g = self.shape.group
         if shared:
-            plan = self.tree.plan_decode(b.tb, max_seq, g, chunk, rows=b.rows, lengths=com)
+            plan = self.tree.plan_decode(b.tb, seq[-1], g, chunk, rows=b.rows, lengths=com)
         else:
-            plan = api.plan_decode_unshared(max_seq, g, chunk, rows=b.rows)
-        steps = np.arange(n_steps, dtype=np.int32)[:, None]
-        pos = base[None, :] + steps                                    # [T, B]
-        slots = self.slots_at(b.rows[None, :].repeat(n_steps, 0), pos)  # [T, B]
-        seq = pos + 1
+            plan = api.plan_decode_unshared(seq[-1], g, chunk, rows=b.rows)
         plan.dev, slots_d, seq_d = self._i32_many(plan.host, slots, seq)
         ws = torch.empty(api.decode_workspace_bytes(self.shape, plan), dtype=torch.uint8, device=self.device)
         return DecodeState(plan, base, n_steps, slots_d, seq_d, ws)
@@ -387,13 +363,9 @@ class Engine:
         if b.locks is not None:
             self.tree.unlock(b.locks)
             b.locks = None
-        lens = b.tb.lens()
-        keep = lens if keep is None else np.asarray(keep, np.int64)
-        # entries past the kept tokens' whole units (tokens, or full pages) are the request's own
-        ps = self.ps
-        tails = [self.table_h[r, k // ps:-(-(n + b.reserve) // ps)] for r, k, n in zip(b.rows, keep, lens)]
-        if tails:
-            self.tree.free(np.concatenate(tails))
+        keep = b.tb.lens() if keep is None else np.asarray(keep, np.int64)
+        # the units past the kept tokens (a partly kept page included) are the request's own
+        self.tree.free_rows(b.rows, self.table_h, keep, b.entries)
         # the rows' entries are left as they are: the next schedule rewrites
         # every entry a request can read
         if b.own_rows:

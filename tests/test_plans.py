@@ -154,6 +154,8 @@ def test_plans_cover_every_context_with_shared_slots(case):
     rows = np.repeat(np.arange(len(batch)), E)
     max_seq = np.concatenate([p + np.arange(1, e + 1) for p, e in zip(P, E)])
     check_plan(plan, max_seq, rows, table, group)
+    # token i of request b attends over positions [0, P_b + i]
+    assert plan.seq_lens.tolist() == max_seq.tolist()
     # decode plan after commit: contexts up to the reserved slots
     t.insert_rows(batch, table, np.arange(len(batch), dtype=np.int32))
     lens = np.array([len(b) for b in batch])

@@ -2,6 +2,8 @@
 oracle/radix_ref.py: matched lengths, slot lists, table rows and the free
 list must agree exactly on random operation sequences.  Tree shapes may
 differ; only observable outputs are compared."""
+import ctypes as C
+
 import numpy as np
 import pytest
 from hypothesis import HealthCheck, given, settings
@@ -77,11 +79,19 @@ def test_tree_matches_bruteforce(sc):
                 assert ei.value.status == N.RC_ERR_NOMEM
                 assert tree.stats()["free_slots"] == before
                 continue
-            P, E = tree.emit_rows(batch, table, reserve=reserve)
+            entries = np.zeros(len(batch), np.int64)
+            new_slots = np.full(sum(len(x) for x in batch) + 1, -7, np.int32)
+            P, E = tree.emit_rows(batch, table, reserve=reserve, row_entries=entries, new_slots=new_slots)
             assert P.tolist() == P_w and E.tolist() == E_w
+            o = 0
             for b, toks in enumerate(batch):
                 n = len(toks) + reserve
                 assert table[b, :n].tolist() == rows_w[b]
+                assert entries[b] == n
+                # the new tokens' slots: positions P_b .. n_b - 1 of the model's row
+                assert new_slots[o:o + E_w[b]].tolist() == rows_w[b][P_w[b]:P_w[b] + E_w[b]]
+                o += E_w[b]
+            assert (new_slots[o:] == -7).all()
             # commit each request's prompt; rows get the tree's slots back
             if len(ops) % 2:
                 for b, toks in enumerate(batch):
@@ -96,9 +106,10 @@ def test_tree_matches_bruteforce(sc):
                     assert table[b, :len(toks)].tolist() == canon_w
                     assert bool(changed[b]) == (before[b, :len(toks)].tolist() != canon_w)
                 # reserved decode slots are not used here: give them back
+            # the reserved decode slots go back (free_rows from each prompt's end to its row's end)
+            tree.free_rows(np.arange(len(batch)), table, [len(x) for x in batch], entries)
             for b, toks in enumerate(batch):
                 if reserve:
-                    tree.free(table[b, len(toks):len(toks) + reserve])
                     ref.free_slots(rows_w[b][len(toks):len(toks) + reserve])
         assert tree.stats()["free_slots"] == ref.num_free()
     assert list(ref.free)[:5] == tree.alloc(min(5, ref.num_free())).tolist()
@@ -211,3 +222,56 @@ def test_first_changed_marks_where_each_row_starts_to_differ(ps):
         if it % 2 == 0:
             t.insert_rows(batch, table, rows)
     assert {0, 3} <= seen  # rows changed from their first entry, and from later ones
+
+
+def test_full_match_flag_stores_a_fully_cached_sequence_without_new_tokens():
+    # the usual match keeps at least one token to run; with RC_EMIT_FULL_MATCH a
+    # sequence already cached gets no new tokens (storing K/V computed elsewhere)
+    t, ref = RadixTree(64), RadixRef(64)
+    seq = [5, 6, 7, 8, 9]
+    table = np.full((2, 16), -1, np.int32)
+    P, E = t.emit_rows([seq], table)
+    rows_w, P_w, E_w = ref.emit_rows([seq], 0)
+    assert (P.tolist(), E.tolist()) == (P_w, E_w) == ([0], [5])
+    t.insert(seq, table[0, :5])
+    ref.insert(seq, rows_w[0])
+    P, E = t.emit_rows([seq], table, rows=[1])
+    assert (P.tolist(), E.tolist()) == ([4], [1])  # capped at n - 1
+    t.free(table[1, 4:5])
+    new = np.zeros(6, np.int32)
+    P, E = t.emit_rows([seq], table, rows=[1], full_match=True, new_slots=new)
+    m, slots = ref.match(seq + [-1])  # the model's uncapped match: a probe one token longer
+    assert (P.tolist(), E.tolist()) == ([m], [0]) and table[1, :5].tolist() == slots
+    with pytest.raises(RcError) as e:  # unknown flag bits
+        N.check(N.lib.rc_radix_emit_rows(t._h, 0, None, np.zeros(1, np.int64).ctypes.data_as(C.c_void_p), 0, None,
+                                         None, 0, 16, None, None, 4, None, None, None, None))
+    assert e.value.status == N.RC_ERR_ARG
+
+
+@pytest.mark.parametrize("ps", [1, 4, 16])
+def test_decode_steps_follow_the_table_rows(ps):
+    # step t of request b: the token at position base_b + t, its slot read from the row
+    # (row[p], or row[p // ps] * ps + p % ps for pages) and its context p + 1 positions
+    from prefix_shared_kv_amd import api
+    g = np.random.default_rng(ps)
+    rows = np.array([2, 0, 3], np.int32)
+    base = np.array([0, 17, 40], np.int32)
+    T = 9
+    entries = np.array([-(-(int(x) + T) // ps) for x in base], np.int64)
+    table = np.full((4, 64), -1, np.int32)
+    for r, e in zip(rows, entries):
+        table[r, :e] = g.permutation(1000)[:e]
+    slots, seq = api.decode_steps(table, rows, base, T, ps, row_entries=entries)
+    for t in range(T):
+        for b in range(3):
+            p = int(base[b]) + t
+            assert slots[t, b] == table[rows[b], p // ps] * ps + p % ps
+            assert seq[t, b] == p + 1
+    with pytest.raises(RcError):  # one step past the first request's reserved entries
+        api.decode_steps(table, rows, base, int(entries[0]) * ps + 1, ps, row_entries=entries)
+    short = table.copy()
+    short[rows[2], entries[2] - 1] = -1
+    with pytest.raises(RcError):  # a position whose entry holds no slot
+        api.decode_steps(short, rows, base, T, ps, row_entries=entries)
+    with pytest.raises(RcError):
+        api.decode_steps(table, rows, base, T, 3)

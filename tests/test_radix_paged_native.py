@@ -60,10 +60,19 @@ def test_paged_tree_matches_the_model(sc):
                     tree.emit_rows(batch, table, reserve=reserve)
                 assert e.value.status == N.RC_ERR_NOMEM
                 continue
-            Pn, En = tree.emit_rows(batch, table, reserve=reserve)
+            entries = np.zeros(len(batch), np.int64)
+            new_slots = np.full(sum(len(t) for t in batch) + 1, -7, np.int32)
+            Pn, En = tree.emit_rows(batch, table, reserve=reserve, row_entries=entries, new_slots=new_slots)
             assert Pn.tolist() == P and En.tolist() == E
+            o = 0
             for b, r in enumerate(rows):
                 assert table[b, :len(r)].tolist() == r
+                assert entries[b] == len(r)
+                # new token at position p: slot = page(p // page_size) * page_size + p % page_size
+                want = [r[p // ps] * ps + p % ps for p in range(P[b], P[b] + E[b])]
+                assert new_slots[o:o + E[b]].tolist() == want
+                o += E[b]
+            assert (new_slots[o:] == -7).all()
             if commit:
                 for b, t in enumerate(batch):
                     canon, _ = ref.insert(t, rows[b])
@@ -71,14 +80,15 @@ def test_paged_tree_matches_the_model(sc):
                 tree.insert_rows(batch, table, np.arange(len(batch), dtype=np.int32))
                 for b, r in enumerate(rows):
                     assert table[b, :len(r)].tolist() == r
-            running.append((batch, rows, commit, P))
+            running.append((batch, rows, commit, P, table[:len(batch)].copy(), entries))
         elif op[0] == "release" and running:
-            batch, rows, commit, P = running.pop(op[1] % len(running))
+            batch, rows, commit, P, tab, entries = running.pop(op[1] % len(running))
             own = []
             for t, r, p in zip(batch, rows, P):
                 own += r[(len(t) // ps if commit else p // ps):]  # pages the tree does not hold
             ref.free_pages(own)
-            tree.free(np.array(own, np.int32))
+            keep = [len(t) for t in batch] if commit else P
+            tree.free_rows(np.arange(len(batch)), tab, keep, entries)
         elif op[0] == "match":
             m, ids = tree.match(op[1])
             assert (m, ids.tolist()) == ref.match(op[1])
@@ -262,3 +272,25 @@ def test_paged_calls_reject_mismatched_page_rows():
     with pytest.raises(RcError) as e:
         t.emit_rows([seq], table)
     assert e.value.status == N.RC_ERR_RANGE
+
+
+def test_full_match_flag_in_pages():
+    # RC_EMIT_FULL_MATCH reuses every whole cached page: the model's match of a
+    # probe one token longer; the partial last page is new
+    ps = 4
+    t, ref = RadixTree(32, page_size=ps), PagedRadixRef(32, ps)
+    seq = list(range(100, 110))  # 2 whole pages + 2 tokens
+    table = np.full((2, 8), -1, np.int32)
+    rows, P, E = ref.emit_rows([seq])
+    t.emit_rows([seq], table)
+    ref.insert(seq, rows[0])
+    t.insert_rows([seq], table, np.zeros(1, np.int32))
+    t.free(table[0, 2:3])
+    ref.free_pages(rows[0][2:3])
+    m, ids = ref.match(seq + [-1])
+    new = np.zeros(len(seq), np.int32)
+    entries = np.zeros(1, np.int64)
+    Pn, En = t.emit_rows([seq], table, rows=[1], full_match=True, row_entries=entries, new_slots=new)
+    assert (int(Pn[0]), int(En[0])) == (m, len(seq) - m) == (8, 2)
+    assert table[1, :2].tolist() == ids and entries[0] == 3
+    assert new[:2].tolist() == [table[1, 2] * ps + 0, table[1, 2] * ps + 1]
