@@ -9,7 +9,10 @@ from __future__ import annotations
 import ctypes as C
 import os
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "librcattn.so")
+_HERE = os.path.dirname(os.path.abspath(__file__))
+# RC_SANITIZED=1: the build with AddressSanitizer / UndefinedBehaviorSanitizer on
+# its host code (prefix_shared_kv_amd/build_host_sanitized.py), for CPU test runs
+LIB_PATH = os.path.join(_HERE, "librcattn_san.so" if os.environ.get("RC_SANITIZED") == "1" else "librcattn.so")
 
 RC_OK, RC_ERR_ARG, RC_ERR_SHAPE, RC_ERR_DTYPE, RC_ERR_RANGE, RC_ERR_NOMEM, RC_ERR_HIP, RC_ERR_INTERNAL = range(8)
 RC_F32, RC_BF16 = 0, 1

@@ -170,3 +170,12 @@ def test_table_upload_argument_checks():
     assert up(FAKE, 8, FAKE, 8, 0, -1, 0, 8, None) == N.RC_ERR_ARG
     assert up(None, 8, FAKE, 8, 0, 4, 0, 8, None) == N.RC_ERR_ARG
     assert "rectangle" in N.last_error() or "NULL" in N.last_error()
+
+
+def test_sanitized_build_is_the_one_loaded_when_asked():
+    # RC_SANITIZED=1 runs the CPU tests against the build with AddressSanitizer and
+    # UndefinedBehaviorSanitizer on its host code; make sure that library is the one in use
+    if os.environ.get("RC_SANITIZED") != "1":
+        pytest.skip("plain build")
+    assert N.LIB_PATH.endswith("librcattn_san.so")
+    assert "librcattn_san.so" in open("/proc/self/maps").read()
