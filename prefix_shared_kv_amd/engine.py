@@ -274,12 +274,29 @@ class Engine:
         b.dev = dict(zip(names, self._i32_many(rows, P, E, start, b.new_slots)))
         return b
 
+    # workgroups of the split-K launch resident at once: two 4-wave workgroups per CU
+    def _resident_workgroups(self) -> int:
+        if not hasattr(self, "_resident"):
+            self._resident = 2 * torch.cuda.get_device_properties(self.device).multi_processor_count
+        return self._resident
+
+    def _cascade_chunk(self, b: Batch) -> int:
+        """Piece length for the shared ranges of a cascade extend: as many pieces as keep every
+        workgroup of the launch resident at once (one round, no tail), no more.  Each piece of
+        a shared range becomes ceil(new tokens / tokens per group) workgroups per kv head."""
+        per_group = max(1, 128 // self.shape.group)
+        groups = -(-b.total_extend // per_group) * self.shape.num_kv_heads
+        pieces = max(1, self._resident_workgroups() // max(groups, 1))
+        longest = int(b.prefix_lens.max()) if b.size else 0
+        return max(64, -(-longest // pieces))
+
     def extend(self, b: Batch, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, sm_scale: float,
                o: Optional[torch.Tensor] = None, store: bool = True, cascade: bool = False,
-               chunk: int = 4096) -> torch.Tensor:
+               chunk: Optional[int] = None) -> torch.Tensor:
         """Store the new tokens' K/V in their slots, then attend (new tokens over prefix + themselves).
         cascade: compute it from a shared-prefix plan (rc_radix_plan_extend) with the split-K
-        kernel, so a prefix shared by many requests is read once for all their new tokens."""
+        kernel, so a prefix shared by many requests is read once for all their new tokens; chunk
+        (default: sized from the launch) is the plan's piece length."""
         T = b.total_extend
         if q.shape[0] != T:
             raise ValueError(f"q has {q.shape[0]} rows, the batch has {T} new tokens")
@@ -290,6 +307,7 @@ class Engine:
         if T == 0:
             return o
         if cascade:
+            chunk = chunk or self._cascade_chunk(b)
             plan = self.tree.plan_extend(b.tb, b.prefix_lens, b.extend_lens, self.shape.group, chunk, rows=b.rows)
             plan.dev, seq_d = self._i32_many(plan.host, plan.seq_lens)
             ws = torch.empty(api.decode_workspace_bytes(self.shape, plan), dtype=torch.uint8, device=self.device)
