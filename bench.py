@@ -123,6 +123,72 @@ def copy_calibration():
                       "read_bytes_per_launch": 2 * n * row + 4 * n, "write_bytes_per_launch": 2 * n * row}))
 
 
+def ceilings():
+    """Measured ceilings beside the datasheet peaks (libceilings.so): a streaming
+    read of 8 GiB with plain and with nontemporal 16-byte loads, the K/V scatter
+    as a copy of 2 x 4.3 GB into contiguous slots, and a dense loop of
+    v_mfma_f32_32x32x16_bf16 (four independent chains per wave, two waves per SIMD)."""
+    import ctypes as C
+
+    import torch
+
+    import prefix_shared_kv_amd as pk
+    lib = C.CDLL(os.path.join(ROOT, "prefix_shared_kv_amd", "libceilings.so"))
+    lib.ceil_stream_read_ms.restype = C.c_double
+    lib.ceil_stream_read_ms.argtypes = [C.c_void_p, C.c_int64, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p]
+    lib.ceil_mfma_ms.restype = C.c_double
+    lib.ceil_mfma_ms.argtypes = [C.c_int32, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p]
+    dev = torch.device("cuda:0")
+    stream = C.c_void_p(torch.cuda.current_stream().cuda_stream)
+    word = torch.zeros(4, dtype=torch.int32, device=dev)
+    out = {"peaks": {"hbm_gbs": HBM_PEAK_GBS, "mfma_bf16_tflops": MFMA_BF16_PEAK_TFLOPS}}
+    n = 8 << 30
+    buf = torch.full((n,), 1, dtype=torch.uint8, device=dev)
+    for nt in (0, 1):
+        ms = lib.ceil_stream_read_ms(C.c_void_p(buf.data_ptr()), n, nt, 5, C.c_void_p(word.data_ptr()), stream)
+        if ms <= 0:
+            raise RuntimeError(f"stream read failed ({ms})")
+        out["stream_read_nontemporal" if nt else "stream_read"] = {
+            "bytes": n, "avg_ms": round(ms, 4), "gbs": round(n / (ms * 1e-3) / 1e9, 1),
+            "frac_of_peak": round(n / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    del buf
+    torch.cuda.empty_cache()
+    # the scatter as a plain copy: 2.1M rows of 8 x 128 bf16 (K and V) into contiguous slots
+    rows, h, d = 1 << 21, 8, 128
+    kvs = pk.KVShape(32, h, d, torch.bfloat16, rows)
+    pool_k = torch.empty((rows, h, d), dtype=torch.bfloat16, device=dev)
+    pool_v = torch.empty_like(pool_k)
+    src_k = torch.ones_like(pool_k)
+    src_v = torch.ones_like(pool_k)
+    slots = torch.arange(rows, dtype=torch.int32, device=dev)
+    pk.kv_store(kvs, pool_k, pool_v, src_k, src_v, slots)
+    torch.cuda.synchronize()
+    pk.prof_collect()
+    pk.prof_enable(True)
+    for _ in range(5):
+        pk.kv_store(kvs, pool_k, pool_v, src_k, src_v, slots)
+    torch.cuda.synchronize()
+    prof = pk.prof_collect()
+    pk.prof_enable(False)
+    ms = avg_ms(prof, "kv_store")
+    nbytes = 2 * (2 * rows * h * d * 2) + 4 * rows
+    out["copy_kv_store"] = {"bytes_moved": nbytes, "avg_ms": round(ms, 4), "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                            "frac_of_peak": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    del pool_k, pool_v, src_k, src_v, slots
+    torch.cuda.empty_cache()
+    cu = torch.cuda.get_device_properties(dev).multi_processor_count
+    blocks, iters = 2 * cu, 8192
+    ms = lib.ceil_mfma_ms(blocks, iters, 5, C.c_void_p(word.data_ptr()), stream)
+    if ms <= 0:
+        raise RuntimeError(f"mfma loop failed ({ms})")
+    flops = blocks * 4 * 4 * iters * 32768.0
+    tf = flops / (ms * 1e-3) / 1e12
+    out["mfma_bf16_32x32x16"] = {"workgroups": blocks, "waves_per_simd": 2, "flops": flops, "avg_ms": round(ms, 4),
+                                 "tflops": round(tf, 1), "frac_of_peak": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                                 "implied_clock_ghz_at_full_rate": round(tf * 1e12 / (cu * 4 * 1024) / 1e9, 3)}
+    print(json.dumps({"ceilings": out}))
+
+
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
@@ -134,8 +200,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", choices=WORKLOADS, default="classify_heavy")
     ap.add_argument("--chunk", type=int, default=None,
-                    help="decode split size, nominal positions per work item (default: 4096; 1024 for "
-                         "multi_turn_tree)")
+                    help="decode split size, nominal positions per work item (default: 4096 for classify_heavy, "
+                         "1024 for multi_turn_tree, sized from the step for the small workloads)")
     ap.add_argument("--decode-steps", type=int, default=None, help="decode steps per step (default: the workload's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -153,6 +219,8 @@ def parse():
     ap.add_argument("--host-phases", action="store_true", help="report host wall time per phase of the last step")
     ap.add_argument("--page-size", type=int, default=1,
                     help="classify_heavy: KV pool pages of this many positions (the table then holds page ids)")
+    ap.add_argument("--ceilings", action="store_true",
+                    help="only measure the streaming-read, copy and MFMA-loop ceilings and print them")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run kv_store into contiguous slots (a plain copy of known size) and print its bytes; "
                          "the scale for rocprofv3 FETCH_SIZE / WRITE_SIZE readings")
@@ -563,15 +631,15 @@ TREE_SPECS = {
              "segments, 256 leaf requests), segments U[256,1024], 128 new tokens per leaf then 256 decode steps, "
              "shuffled pool slots"),
     "few_shot": dict(
-        make=lambda W, T: W.few_shot(n_decode=T), decode_steps=128, chunk=4096,
+        make=lambda W, T: W.few_shot(n_decode=T), decode_steps=128, chunk=None,
         text="few-shot batch: GQA 32/8, head_dim 128, bf16; a fresh 2048-token prefix prefilled each step, "
              "64 requests x 64 new tokens extended over it, then 128 decode steps"),
     "gpt2_system_prompt": dict(
-        make=lambda W, T: W.gpt2_system_prompt(), decode_steps=32, chunk=4096,
+        make=lambda W, T: W.gpt2_system_prompt(), decode_steps=32, chunk=None,
         text="GPT-2-small-shaped layer: 12/12 heads, head_dim 64, bf16, inputs N(0,1)/8; a fresh 409-token system "
              "prompt prefilled each step, branches of 8 and 7 tokens, 32 decode steps each"),
     "tiny_fp32": dict(
-        make=lambda W, T: W.tiny_fp32(), decode_steps=4, chunk=4096,
+        make=lambda W, T: W.tiny_fp32(), decode_steps=4, chunk=None,
         text="tiny single-layer attention, fp32: 4/4 heads, head_dim 64; a fresh 128-token prefix prefilled each "
              "step, 2 requests x 8 new tokens, 4 decode steps"),
 }
@@ -699,6 +767,7 @@ def bench_tree(args):
         pk.prof_tag(None)
         st = eng.prepare_decode(b, prompt_len, T, chunk=args.chunk)
         plan_info.update(st.plan.summary)
+        plan_info["chunk"] = st.plan.info.chunk
         ph.mark("prepare_decode")
         for t in range(T):
             eng.decode_step(st, t, q_dec[t], k_dec[t], v_dec[t], scale, o=o_dec[t])
@@ -741,7 +810,8 @@ def bench_tree(args):
         "config": {
             "workload": spec["text"],
             "batch": B, "new_tokens": n_ext, "prefill_tokens": pre_tokens, "decode_steps": T,
-            "cached_tokens": cached, "mean_prefix": round(float(P_expect.mean()), 1), "decode_chunk": args.chunk,
+            "cached_tokens": cached, "mean_prefix": round(float(P_expect.mean()), 1),
+            "decode_chunk": args.chunk or f"{plan_info['chunk']} (sized from the step)",
             "extend_path": "shared-prefix plan" if args.cascade else "tiles",
             "slot_order": "shuffled" if order is not None else "in order", "tokens_per_step": tokens_per_step,
         },
@@ -881,6 +951,9 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.ceilings:
+        ceilings()
         return
     if args.page_size != 1 and args.workload != "classify_heavy":
         print("--page-size applies to the classify_heavy workload", file=sys.stderr)

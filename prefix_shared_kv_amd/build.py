@@ -15,6 +15,10 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "librcattn.so")
+# measured ceilings (streaming read, MFMA loop) for the roofline figures: a
+# library of its own, not part of the attention library
+CEIL_SRC = os.path.join(CSRC, "ceilings", "ceilings.hip")
+CEIL_LIB = os.path.join(PKG, "libceilings.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -65,6 +69,9 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
     tmp = LIB + ".tmp"
     _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-pthread", "-o", tmp, *[o for _, o in jobs_list]])
     shutil.move(tmp, LIB)
+    tmp = CEIL_LIB + ".tmp"
+    _run([HIPCC, *HIP_FLAGS, "-shared", "-o", tmp, CEIL_SRC])
+    shutil.move(tmp, CEIL_LIB)
     return LIB
 
 

@@ -337,10 +337,27 @@ class Engine:
             self.table_h[rows, :width] = work[changed]
             self._upload_rows(np.sort(rows))
 
-    def prepare_decode(self, b: Batch, base_lens: Sequence[int], n_steps: int, chunk: int = 4096,
+    # Decode piece length when the caller gives none.  A step that reads much
+    # (more than fits the Infinity Cache) streams HBM, where long pieces start
+    # up fewest times; a small step is latency-bound and wants many short items.
+    _STREAM_BYTES = 128 << 20
+
+    def _decode_chunk(self, unique_positions: int) -> int:
+        """Pieces of 4096 positions when the step's unique K/V bytes exceed _STREAM_BYTES; below
+        that, the power of two nearest unique_positions * kv_heads / 512 (within [64, 4096]), so
+        a small step spreads over many short work items."""
+        el = 4 if self.shape.dtype == torch.float32 else 2
+        row = 2 * self.shape.num_kv_heads * self.shape.head_dim * el
+        if unique_positions * row >= self._STREAM_BYTES:
+            return 4096
+        x = max(unique_positions * self.shape.num_kv_heads / 512.0, 1.0)
+        return int(min(4096, max(64, 2 ** round(np.log2(x)))))
+
+    def prepare_decode(self, b: Batch, base_lens: Sequence[int], n_steps: int, chunk: Optional[int] = None,
                        shared: bool = True, committed: Optional[Sequence[int]] = None) -> DecodeState:
         """Plan decode steps t = 0..n_steps-1; step t's token sits at position base_lens[i] + t.
-        `committed[i]` tokens of request i are in the tree (default: base_lens)."""
+        `committed[i]` tokens of request i are in the tree (default: base_lens).  chunk: the
+        plan's piece length (default: from the step's size, _decode_chunk)."""
         base = np.asarray(base_lens, np.int32)
         com = base if committed is None else np.asarray(committed, np.int32)
         if np.any(com > base):
@@ -352,10 +369,17 @@ class Engine:
         # reserved entries are rejected)
         slots, seq = api.decode_steps(self.table_h, b.rows, base, n_steps, self.ps, row_entries=b.entries)
         g = self.shape.group
-        if shared:
-            plan = self.tree.plan_decode(b.tb, seq[-1], g, chunk, rows=b.rows, lengths=com)
-        else:
-            plan = api.plan_decode_unshared(seq[-1], g, chunk, rows=b.rows)
+
+        def make(c):
+            if shared:
+                return self.tree.plan_decode(b.tb, seq[-1], g, c, rows=b.rows, lengths=com)
+            return api.plan_decode_unshared(seq[-1], g, c, rows=b.rows)
+
+        plan = make(chunk or 4096)
+        if chunk is None:
+            auto = self._decode_chunk(plan.info.unique_positions)
+            if auto != 4096:
+                plan = make(auto)
         plan.dev, slots_d, seq_d = self._i32_many(plan.host, slots, seq)
         ws = torch.empty(api.decode_workspace_bytes(self.shape, plan), dtype=torch.uint8, device=self.device)
         return DecodeState(plan, base, n_steps, slots_d, seq_d, ws)
