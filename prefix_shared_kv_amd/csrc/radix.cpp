@@ -966,8 +966,8 @@ struct PlanBuilder {
       return ranges[a].members.size() > ranges[b].members.size();
     });
     // wide items (members*group > 16) first, then narrow ones; within each
-    // class the longest first (members x positions), so the last workgroups
-    // to start are the short ones
+    // class the longest running first (wide: members x positions, narrow:
+    // positions), so the last workgroups to start are the short ones
     struct Item { int64_t cost; int32_t v[RC_PLAN_ITEM]; int32_t range, first; };
     std::vector<Item> wide, narrow;
     for (int32_t r : order) {
@@ -979,10 +979,13 @@ struct PlanBuilder {
         const int64_t pe = std::min<int64_t>(p + pl, R.end);
         for (size_t g0 = 0; g0 < R.members.size(); g0 += max_m) {
           const size_t cnt = std::min<size_t>(max_m, R.members.size() - g0);
-          const Item it{(int64_t)cnt * (pe - p),
+          const bool is_narrow = (int64_t)cnt * group <= 16;
+          // a narrow item's time is its range (one wave streams it; its columns
+          // fit one tile whatever their number), a wide item's grows with its members
+          const Item it{is_narrow ? pe - p : (int64_t)cnt * (pe - p),
                         {row_of(R.members[g0]), (int32_t)p, (int32_t)pe, sp, 0, (int32_t)cnt, R.own ? RC_PLAN_ITEM_OWN : 0, 0},
                         r, (int32_t)g0};
-          ((int64_t)cnt * group <= 16 ? narrow : wide).push_back(it);
+          (is_narrow ? narrow : wide).push_back(it);
           if (R.members.size() > 1) shared_items++;
         }
       }

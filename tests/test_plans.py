@@ -205,3 +205,27 @@ def test_unshared_and_cascade_plans_choose_their_launch_order():
     P, E = t.emit_rows(batch, table)
     plan = t.plan_extend(batch, P, E, group=8, chunk=1024)
     assert plan.info.narrow_begin > 0 and plan.info.narrow_first == 0
+
+
+def test_items_run_longest_first_within_each_class():
+    # without bins: wide items by members x positions, narrow items by
+    # positions alone (one wave streams a narrow range whatever its members)
+    g = np.random.default_rng(21)
+    stems = [g.integers(0, 1000, n).astype(np.int32) for n in (700, 300)]
+    batch = []
+    for k, stem in enumerate(stems):
+        for i in range(4 if k else 6):  # 6 and 4 members: wide with group 4 past 4 members
+            batch.append(np.concatenate([stem, g.integers(2000, 3000, int(g.integers(50, 900))).astype(np.int32)]))
+    t = RadixTree(1 << 20)
+    table = np.full((len(batch), 2000), -1, np.int32)
+    t.emit_rows(batch, table)
+    t.insert_rows(batch, table, np.arange(len(batch), dtype=np.int32))
+    lens = np.array([len(x) for x in batch], np.int32)
+    plan = t.plan_decode(batch, lens, group=4, chunk=4096)
+    items, _ = check_plan(plan, lens, np.arange(len(batch)), table, 4, own_from=lens)
+    nb = plan.info.narrow_begin
+    wide_cost = (items[:nb, 2] - items[:nb, 1]) * items[:nb, 5]
+    narrow_len = items[nb:, 2] - items[nb:, 1]
+    assert nb >= 1 and np.all(np.diff(wide_cost) <= 0) and np.all(np.diff(narrow_len) <= 0)
+    # the 4-member stem is narrow (16 columns) and sorts among the own ranges by its length
+    assert any(it[5] == 4 for it in items[nb:])
