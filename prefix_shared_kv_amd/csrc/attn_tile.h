@@ -657,15 +657,21 @@ __device__ __forceinline__ void attn_bf16_tile(const Args& a, const int mode, co
   if (attn_bf16_body<D, NW, STREAM, false>(a, mode, L, sK, sV)) attn_bf16_body<D, NW, STREAM, true>(a, mode, L, sK, sV);
 }
 
-// fp32 path: one wave per column, lanes over head dims, keys one at a time.
-// Same work decomposition and outputs as the MFMA kernel; used for fp32 data.
+// fp32 path: one wave per column; its 64 lanes are 16 keys x 4 groups of
+// D/4 head dims, so a wave takes 16 keys at a time: each lane dots its key's
+// group with the query's (two shuffles finish the score), the online softmax
+// moves once per 16 keys, and each lane accumulates p x V for its key and
+// group; the 16 key lanes of each group are summed once, at the end.  Same
+// work decomposition and outputs as the MFMA kernel; used for fp32 data.
 template <int D>
 __device__ __forceinline__ void attn_f32_body(const Args& a, const int mode) {
-  constexpr int PER = D / 64;
+  constexpr int DG = D / 4;     // head dims per lane group
+  constexpr int NV = DG / 4;    // float4 per lane and row
   const int L = xcd_remap(blockIdx.x, a.n_work);
   const Work w = resolve(a, mode, L, threadIdx.x == 0);
   if (!w.valid) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int kk = lane >> 2, grp = lane & 3;  // key within the 16, head-dim group
   if (w.store_b >= 0) store_new_token<float, D>(a, w.store_b, w.hk, threadIdx.x);
   const float* q = (const float*)a.q;
   const float* kpool = (const float*)a.k_pool;
@@ -673,57 +679,91 @@ __device__ __forceinline__ void attn_f32_body(const Args& a, const int mode) {
   const float* knew = (const float*)a.k_new;
   const float* vnew = (const float*)a.v_new;
   const int64_t rowHD = (int64_t)a.Hkv * D;
+  const int64_t head_off = (int64_t)w.hk * D + grp * DG;
+  const uint32_t npages = (uint32_t)(a.pool_slots >> a.page_shift);
+  // row offset (in floats, from the pool or from k_new/v_new) of key j; -1: no key
+  auto row_of = [&](int j, int end, bool& from_new) -> int64_t {
+    from_new = false;
+    if (j >= end) return -1;
+    if (j >= w.ext_begin) {
+      from_new = true;
+      return (w.ext_base + (j - w.ext_begin)) * rowHD + head_off;
+    }
+    const int32_t sl = page_slot(a.table[w.row * a.stride + (j >> a.page_shift)], j, a.page_shift, npages);
+    if (sl < 0 || (int64_t)sl >= a.pool_slots) {
+      if (grp == 0) flag(a.err, RC_DEVERR_SLOT);  // an absent key
+      return -1;
+    }
+    return (int64_t)sl * rowHD + head_off;
+  };
   for (int c = wave; c < w.ncols; c += NT / 64) {
     const Col col = column(a, mode, w, c);
-    float qv[PER], ov[PER];
+    float4 qv[NV];
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      qv[i] = q[col.qoff * D + lane + 64 * i];
-      ov[i] = 0.f;
-    }
+    for (int i = 0; i < NV; ++i) qv[i] = *(const float4*)(q + col.qoff * D + grp * DG + 4 * i);
+    float4 ov[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) ov[i] = make_float4(0.f, 0.f, 0.f, 0.f);
     float m_run = -INFINITY, l_run = 0.f;
     const int end = min(w.key_end, col.limit == INT_MAX ? w.key_end : col.limit + 1);
-    for (int j = w.key_begin; j < end; ++j) {
-      const float *kp, *vp;
-      if (j >= w.ext_begin) {
-        const int64_t off = (w.ext_base + (j - w.ext_begin)) * rowHD + (int64_t)w.hk * D;
-        kp = knew + off;
-        vp = vnew + off;
-      } else {
-        const int32_t s = page_slot(a.table[w.row * a.stride + (j >> a.page_shift)], j, a.page_shift,
-                                    (uint32_t)(a.pool_slots >> a.page_shift));
-        if (s < 0 || (int64_t)s >= a.pool_slots) {
-          if (lane == 0) flag(a.err, RC_DEVERR_SLOT);
-          continue;
-        }
-        const int64_t off = (int64_t)s * rowHD + (int64_t)w.hk * D;
-        kp = kpool + off;
-        vp = vpool + off;
+    for (int j0 = w.key_begin; j0 < end; j0 += 16) {
+      bool from_new;
+      const int64_t off = row_of(j0 + kk, end, from_new);
+      const bool has = off >= 0;
+      const float* kp = (from_new ? knew : kpool) + (has ? off : 0);
+      const float* vp = (from_new ? vnew : vpool) + (has ? off : 0);
+      float4 kv[NV], vv[NV];
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        kv[i] = has ? *(const float4*)(kp + 4 * i) : make_float4(0.f, 0.f, 0.f, 0.f);
+        vv[i] = has ? *(const float4*)(vp + 4 * i) : make_float4(0.f, 0.f, 0.f, 0.f);
       }
       float dot = 0.f;
 #pragma unroll
-      for (int i = 0; i < PER; ++i) dot += qv[i] * kp[lane + 64 * i];
+      for (int i = 0; i < NV; ++i) dot += qv[i].x * kv[i].x + qv[i].y * kv[i].y + qv[i].z * kv[i].z + qv[i].w * kv[i].w;
+      dot += __shfl_xor(dot, 1);
+      dot += __shfl_xor(dot, 2);
+      const float x = has ? dot * a.scale_log2 : -INFINITY;
+      float mx = x;
 #pragma unroll
-      for (int sh = 32; sh >= 1; sh >>= 1) dot += __shfl_xor(dot, sh);
-      const float x = dot * a.scale_log2;
-      const float m_new = fmaxf(m_run, x);
-      const float alpha = exp2f(m_run - m_new);
-      const float p = exp2f(x - m_new);
-      l_run = l_run * alpha + p;
+      for (int sh = 4; sh <= 32; sh <<= 1) mx = fmaxf(mx, __shfl_xor(mx, sh));
+      const float m_new = fmaxf(m_run, mx);
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      const float alpha = exp2f(m_run - m_use);
+      const float pr = has ? exp2f(x - m_use) : 0.f;
+      l_run = l_run * alpha + pr;
 #pragma unroll
-      for (int i = 0; i < PER; ++i) ov[i] = ov[i] * alpha + p * vp[lane + 64 * i];
+      for (int i = 0; i < NV; ++i) {
+        ov[i].x = ov[i].x * alpha + pr * vv[i].x;
+        ov[i].y = ov[i].y * alpha + pr * vv[i].y;
+        ov[i].z = ov[i].z * alpha + pr * vv[i].z;
+        ov[i].w = ov[i].w * alpha + pr * vv[i].w;
+      }
       m_run = m_new;
     }
-    if (!col.real) continue;
-    if (mode == EXTEND) {
-      float* o = (float*)a.o + col.qoff * D;
+    // sum over the 16 key lanes of each head-dim group
 #pragma unroll
-      for (int i = 0; i < PER; ++i) o[lane + 64 * i] = ov[i] / l_run;
+    for (int sh = 4; sh <= 32; sh <<= 1) {
+      l_run += __shfl_xor(l_run, sh);
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        ov[i].x += __shfl_xor(ov[i].x, sh);
+        ov[i].y += __shfl_xor(ov[i].y, sh);
+        ov[i].z += __shfl_xor(ov[i].z, sh);
+        ov[i].w += __shfl_xor(ov[i].w, sh);
+      }
+    }
+    if (!col.real || kk != 0) continue;
+    if (mode == EXTEND) {
+      float* o = (float*)a.o + col.qoff * D + grp * DG;
+      const float inv = 1.f / l_run;
+#pragma unroll
+      for (int i = 0; i < NV; ++i) *(float4*)(o + 4 * i) = make_float4(ov[i].x * inv, ov[i].y * inv, ov[i].z * inv, ov[i].w * inv);
     } else {
       const int64_t pidx = ((int64_t)col.b * a.Hq + col.head) * a.max_splits + w.split;
 #pragma unroll
-      for (int i = 0; i < PER; ++i) a.ws_o[pidx * D + lane + 64 * i] = ov[i];
-      if (lane == 0) *(float2*)(a.ws_ml + pidx * 2) = make_float2(m_run, l_run);
+      for (int i = 0; i < NV; ++i) *(float4*)(a.ws_o + pidx * D + grp * DG + 4 * i) = ov[i];
+      if (grp == 0) *(float2*)(a.ws_ml + pidx * 2) = make_float2(m_run, l_run);
     }
   }
 }

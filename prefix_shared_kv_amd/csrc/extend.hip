@@ -82,7 +82,8 @@ extern "C" rc_status rc_extend_attention(const rc_shape* shape, void* o, const v
   a.total_extend = total_extend;
   a.rows = rows; a.prefix_lens = prefix_lens; a.extend_lens = extend_lens; a.extend_start = extend_start;
   a.batch = batch; a.max_extend = max_extend;
-  a.tok_per_tile = (shape->dtype == RC_BF16 ? 32 * EXT_WAVES : NCOL) / g;
+  // bf16: 32 columns per wave of the MFMA tile; fp32: one column per wave
+  a.tok_per_tile = shape->dtype == RC_BF16 ? 32 * EXT_WAVES / g : (g < NT / 64 ? NT / 64 / g : 1);
   a.tiles = (max_extend + a.tok_per_tile - 1) / a.tok_per_tile;
   const int64_t n_work = (int64_t)batch * a.Hkv * a.tiles;
   if (n_work > INT32_MAX / 8) return fail(RC_ERR_RANGE, "grid of %lld workgroups too large", (long long)n_work);
