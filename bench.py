@@ -40,9 +40,13 @@ step, or a cached tree) -> the requests' new tokens extended over it -> commit
       128-token prefix, 2 requests x 8 new tokens, 4 decode steps (latency).
 
 Inputs (q, k, v and the token batches) are made before timing; q, k and v
-are drawn on the GPU and stay resident in HBM.  The cpu_baseline leg runs the
-float64 oracle on host copies of those same inputs, times it, and compares the
-outputs of the last timed step with it (error histogram).
+are drawn on the GPU and stay resident in HBM.  The K timed steps run without
+kernel timing; K more steps then bracket every library kernel with HIP events
+for the per-kernel durations (the roofline figures), since recording events
+costs each launch a few microseconds that would count in the step time of the
+launch-bound workloads.  The cpu_baseline leg runs the float64 oracle on host
+copies of those same inputs, times it, and compares the outputs of the last
+step with it (error histogram).
 """
 from __future__ import annotations
 
@@ -243,8 +247,11 @@ class Phases:
 
 
 def run_steps(args, one_step):
-    """W untimed warm-up steps, then exactly K timed steps between device syncs;
-    kernel times from the library's HIP events over the timed steps."""
+    """W untimed warm-up steps, then exactly K timed steps between device syncs,
+    whose wall time is the step time; then K more steps with every library
+    kernel bracketed by HIP events on its stream, for the per-kernel durations.
+    Recording the events costs each launch a few microseconds of host and GPU
+    time, which the step time of a launch-bound workload must not include."""
     import torch
 
     import prefix_shared_kv_amd as pk
@@ -253,15 +260,19 @@ def run_steps(args, one_step):
     torch.cuda.synchronize()
     log(f"{args.warmup} warm-up steps done")
     pk.prof_collect()
-    pk.prof_enable(True)
     t0 = time.perf_counter()
     for s in range(args.steps):
         one_step(args.warmup + s)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    log(f"{args.steps} timed steps done: {elapsed / args.steps * 1e3:.2f} ms/step")
+    pk.prof_enable(True)
+    for s in range(args.steps):
+        one_step(args.warmup + args.steps + s)
+    torch.cuda.synchronize()
     prof = pk.prof_collect()
     pk.prof_enable(False)
-    log(f"{args.steps} timed steps done: {elapsed / args.steps * 1e3:.2f} ms/step")
+    log(f"{args.steps} steps with kernel timing done")
     return elapsed, prof
 
 
@@ -347,7 +358,7 @@ def bench_classify_heavy(args):
                                                                                 sh.head_dim)
     Hq, Hkv, D = sh.num_q_heads, sh.num_kv_heads, sh.head_dim
     B = len(wh.requests)
-    n_total = args.warmup + args.steps
+    n_total = args.warmup + 2 * args.steps  # the timed steps, then as many with kernel timing
     doc = wc.prefix_tokens(wc.requests[0])
     labels = [r.ext_tokens for r in wc.requests]
     n_lab = sum(len(x) for x in labels)
@@ -551,7 +562,7 @@ def cpu_baseline_classify_heavy(wc, wh, gpu, budget, n_dec, tokens_per_step, T, 
     branch extends in full, then the decode of requests (in a seeded order) at
     `n_dec` of the T steps, their contexts regenerated from the seeded node
     draws, until `budget` seconds of oracle time are spent; the per-token decode
-    time is scaled to the whole batch.  The last timed step's GPU outputs for
+    time is scaled to the whole batch.  The last step's GPU outputs for
     the same items give the error histogram."""
     from threadpoolctl import threadpool_limits
 
@@ -616,7 +627,7 @@ def cpu_baseline_classify_heavy(wc, wh, gpu, budget, n_dec, tokens_per_step, T, 
                      f"steps); the decode time per token scaled to {B}x{T}: one step = {est:.1f} s",
            "sample_seconds": round(t_pre + t_br + n_tok * t_dec, 2)}
     err = {k: v.report() for k, v in hist.items()}
-    err["compared"] = "the last timed step's outputs of the oracle's sample, element-wise"
+    err["compared"] = "the last step's outputs (the last step with kernel timing) over the oracle's sample, element-wise"
     return cpu, err
 
 
@@ -668,7 +679,7 @@ def bench_tree(args):
     reqs = w.requests
     B = len(reqs)
     E = np.array([len(r.ext_tokens) for r in reqs], np.int64)
-    n_total = args.warmup + args.steps
+    n_total = args.warmup + 2 * args.steps  # the timed steps, then as many with kernel timing
     prefill = list(w.prefill_nodes)          # prefilled fresh every step
     fresh = bool(prefill)
     cached_nodes = [n for n in drive.node_order(w) if n not in prefill]
@@ -851,7 +862,7 @@ def cpu_baseline_tree(w, gpu, budget, n_dec, tokens_per_step, T, dev):
     prefilled prefix, then requests in a seeded order (their extend and their
     decode at `n_dec` evenly spaced steps, contexts from the seeded node draws)
     until `budget` seconds of oracle time are spent; the per-row, per-request
-    and per-token times are scaled to one step.  The last timed step's GPU
+    and per-token times are scaled to one step.  The last step's GPU
     outputs for the same items give the error histogram."""
     from threadpoolctl import threadpool_limits
 
@@ -939,7 +950,7 @@ def cpu_baseline_tree(w, gpu, budget, n_dec, tokens_per_step, T, dev):
                      f"step = {est:.3g} s",
            "sample_seconds": round(sampled, 2)}
     err = {k: v.report() for k, v in hist.items() if v.n}
-    err["compared"] = "the last timed step's outputs of the oracle's sample, element-wise"
+    err["compared"] = "the last step's outputs (the last step with kernel timing) over the oracle's sample, element-wise"
     return cpu, err
 
 

@@ -559,7 +559,9 @@ rc_status rc_label_distribution(const void* logits, int32_t dtype, int64_t row_s
 /* ------------------------------------------------------------------------ */
 /* Kernel timing.  While enabled, every kernel the library launches is       */
 /* bracketed by HIP events on its own stream.  rc_prof_collect waits for the */
-/* recorded events, returns per-kernel totals and clears them.               */
+/* recorded events, returns per-kernel totals and clears them.  Enabling     */
+/* creates a pool of events up front (16384 with those already recorded), so*/
+/* timed launches only record them; RC_ERR_HIP if creating one fails.       */
 /* ------------------------------------------------------------------------ */
 typedef struct rc_prof_entry {
   char name[48];

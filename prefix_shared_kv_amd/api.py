@@ -279,6 +279,60 @@ def decode_attention(shape: KVShape, o, q, k_pool, v_pool, req_to_token, seq_len
                                   _vp(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
+class DecodeLauncher:
+    """rc_decode_attention for the steps of one decode batch: the arguments that stay fixed over
+    the steps (pools, table, plan, workspace, scale, stream) are checked once here, and each call
+    checks only the step's own tensors, so a step costs little host time.  The stream is the one
+    current at construction unless given."""
+
+    def __init__(self, shape: KVShape, k_pool, v_pool, req_to_token, plan: DecodePlan, workspace, sm_scale: float,
+                 batch: int, stream=None):
+        Hq, Hkv, D, S = shape.num_q_heads, shape.num_kv_heads, shape.head_dim, shape.pool_slots
+        _dev(k_pool, "k_pool", shape.dtype, (S, Hkv, D))
+        _dev(v_pool, "v_pool", shape.dtype, (S, Hkv, D))
+        _dev(req_to_token, "req_to_token", torch.int32)
+        _dev(workspace, "workspace")
+        if plan.dev is None:
+            raise ValueError("plan has no device copy; call plan.to(device)")
+        if plan.info.batch != batch:
+            raise ValueError(f"plan built for batch {plan.info.batch}, launcher for {batch}")
+        self._sh = shape.c()
+        self._info = plan.info
+        self._dtype = shape.dtype
+        self._q_shape = (batch, Hq, D)
+        self._kv_shape = (batch, Hkv, D)
+        self.batch = batch
+        self._keep = (k_pool, v_pool, req_to_token, plan, workspace)  # alive while the launcher is
+        self._pools = (k_pool.data_ptr(), v_pool.data_ptr())
+        self._table = (req_to_token.data_ptr(), req_to_token.shape[0], req_to_token.shape[1])
+        self._plan = plan.dev.data_ptr()
+        self._ws = (workspace.data_ptr(), workspace.numel() * workspace.element_size())
+        self._scale = float(sm_scale)
+        self._stream = _stream(stream)
+
+    def _check(self, t, name, dtype, shape):
+        if not (isinstance(t, torch.Tensor) and t.is_cuda and t.dtype == dtype and tuple(t.shape) == shape
+                and t.is_contiguous()):
+            raise ValueError(f"{name}: expected a contiguous device tensor {dtype} {shape}")
+
+    def __call__(self, o, q, seq_lens_ptr: int, k_new=None, v_new=None, new_slots_ptr: Optional[int] = None) -> None:
+        """o, q: [batch, Hq, D]; k_new/v_new: [batch, Hkv, D] or None; seq_lens_ptr / new_slots_ptr:
+        device addresses of batch int32 each (the caller's tensors, kept alive by it)."""
+        self._check(o, "o", self._dtype, self._q_shape)
+        self._check(q, "q", self._dtype, self._q_shape)
+        if (k_new is None) != (v_new is None) or (k_new is None) != (new_slots_ptr is None):
+            raise ValueError("k_new, v_new and new_slots go together")
+        kn = vn = None
+        if k_new is not None:
+            self._check(k_new, "k_new", self._dtype, self._kv_shape)
+            self._check(v_new, "v_new", self._dtype, self._kv_shape)
+            kn, vn = k_new.data_ptr(), v_new.data_ptr()
+        check(lib.rc_decode_attention(C.byref(self._sh), o.data_ptr(), q.data_ptr(), self._pools[0], self._pools[1],
+                                      kn, vn, new_slots_ptr, self._table[0], self._table[1], self._table[2],
+                                      seq_lens_ptr, self.batch, self._plan, C.byref(self._info), self._scale,
+                                      self._ws[0], self._ws[1], self._stream))
+
+
 def decode_attention_static(shape: KVShape, o, q, k_pool, v_pool, req_to_token, seq_lens, plan: DecodePlan,
                             sm_scale: float, k_new=None, v_new=None, new_slots=None, stream=None) -> None:
     """decode_attention without a workspace (rc_decode_attention_static): the partials go to the

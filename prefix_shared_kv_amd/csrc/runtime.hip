@@ -79,6 +79,14 @@ extern "C" rc_status rc_upload_table_rows(int32_t* dev_table, int64_t dev_stride
 
 extern "C" rc_status rc_prof_enable(int32_t on) {
   rc::g_on = on != 0;
+  // events are created here, not at the launches, so a timed region pays
+  // only for the records (creating an event takes far longer)
+  constexpr size_t kPool = 16384;
+  while (rc::g_on && rc::g_pool.size() + rc::g_recs.size() * 2 < kPool) {
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return rc::fail(RC_ERR_HIP, "hipEventCreate failed");
+    rc::g_pool.push_back(e);
+  }
   return RC_OK;
 }
 

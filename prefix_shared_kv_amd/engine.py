@@ -67,6 +67,7 @@ class DecodeState:
     slots: torch.Tensor        # [n_steps, B] int32: slot of each step's token
     seq_lens: torch.Tensor     # [n_steps, B] int32: keys attended at each step
     workspace: torch.Tensor
+    launcher: Optional[api.DecodeLauncher] = None  # built at the first fused step
 
 
 class Engine:
@@ -390,9 +391,15 @@ class Engine:
         (one call with fused_store, else a scatter then the attention)."""
         if o is None:
             o = torch.empty_like(q)
+        if not 0 <= t < st.n_steps:
+            raise IndexError(f"step {t} outside the {st.n_steps} planned")
         if fused_store:
-            api.decode_attention(self.shape, o, q, self.k_pool, self.v_pool, self.table_d, st.seq_lens[t], st.plan,
-                                 sm_scale, st.workspace, k_new=k, v_new=v, new_slots=st.slots[t])
+            ln = st.launcher
+            if ln is None or ln._scale != float(sm_scale):
+                ln = st.launcher = api.DecodeLauncher(self.shape, self.k_pool, self.v_pool, self.table_d, st.plan,
+                                                      st.workspace, sm_scale, st.seq_lens.shape[1])
+            B4 = 4 * st.seq_lens.shape[1]  # int32 rows of seq_lens and slots
+            ln(o, q, st.seq_lens.data_ptr() + t * B4, k_new=k, v_new=v, new_slots_ptr=st.slots.data_ptr() + t * B4)
         else:
             api.kv_store(self.shape, self.k_pool, self.v_pool, k, v, st.slots[t])
             api.decode_attention(self.shape, o, q, self.k_pool, self.v_pool, self.table_d, st.seq_lens[t], st.plan,
