@@ -129,7 +129,8 @@ def copy_calibration():
 
 def ceilings():
     """Measured ceilings beside the datasheet peaks (libceilings.so): a streaming
-    read of 8 GiB with plain and with nontemporal 16-byte loads, the K/V scatter
+    read of 8 GiB with plain and with nontemporal 16-byte loads, 1024 and 2048
+    waves each streaming its own contiguous 512 KiB, the K/V scatter
     as a copy of 2 x 4.3 GB into contiguous slots, and a dense loop of
     v_mfma_f32_32x32x16_bf16 (four independent chains per wave, two waves per SIMD)."""
     import ctypes as C
@@ -155,6 +156,21 @@ def ceilings():
         out["stream_read_nontemporal" if nt else "stream_read"] = {
             "bytes": n, "avg_ms": round(ms, 4), "gbs": round(n / (ms * 1e-3) / 1e9, 1),
             "frac_of_peak": round(n / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    # each wave streaming its own contiguous 512 KiB (16 KiB per wave in flight)
+    word2 = torch.zeros(4, dtype=torch.int32, device=dev)
+    lib.ceil_wave_stream_ms.restype = C.c_double
+    lib.ceil_wave_stream_ms.argtypes = [C.c_void_p, C.c_int32, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p]
+    per_wave = 512 << 10
+    for waves in (1024, 2048):
+        assert waves * per_wave <= n
+        ms = lib.ceil_wave_stream_ms(C.c_void_p(buf.data_ptr()), waves, per_wave // 16384, 5,
+                                     C.c_void_p(word2.data_ptr()), stream)
+        if ms <= 0:
+            raise RuntimeError(f"wave stream failed ({ms})")
+        nb = waves * per_wave
+        out[f"wave_stream_{waves}"] = {
+            "bytes": nb, "waves": waves, "avg_ms": round(ms, 4), "gbs": round(nb / (ms * 1e-3) / 1e9, 1),
+            "frac_of_peak": round(nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
     del buf
     torch.cuda.empty_cache()
     # the scatter as a plain copy: 2.1M rows of 8 x 128 bf16 (K and V) into contiguous slots
