@@ -62,6 +62,22 @@ import numpy as np
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
 FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X fp32 vector, TFLOP/s
+# the path's targets: extend at half the dense bf16 MFMA peak, decode at 0.7 of the HBM peak
+TARGET_EXTEND_MFMA_FRAC = 0.50
+TARGET_DECODE_HBM_FRAC = 0.70
+
+
+def targets(extend_fracs, decode_frac, decode_hbm=True):
+    """Each target beside what this run measured and whether it is met."""
+    out = {"extend_bf16_mfma_frac": {"target": TARGET_EXTEND_MFMA_FRAC, "measured": extend_fracs,
+                                     "met": all(f >= TARGET_EXTEND_MFMA_FRAC for f in extend_fracs.values())}}
+    if decode_hbm:
+        out["decode_hbm_frac"] = {"target": TARGET_DECODE_HBM_FRAC, "measured": decode_frac,
+                                  "met": decode_frac >= TARGET_DECODE_HBM_FRAC}
+    else:
+        out["decode_hbm_frac"] = {"target": TARGET_DECODE_HBM_FRAC, "measured": None, "met": None,
+                                  "note": "the decode working set fits the Infinity Cache: not an HBM-bound figure"}
+    return out
 ROOT = os.path.dirname(os.path.abspath(__file__))
 # what the decode kernel's code depends on: its sources and the build flags;
 # a traffic figure stands only while these are unchanged
@@ -528,6 +544,8 @@ def bench_classify_heavy(args):
         "pool_fill": fill,
         "kernel_ms_per_step": {k: round(v[1] / args.steps, 4) for k, v in prof.items()},
     }
+    res["targets"] = targets({"prefill": res["extend"]["prefill"]["frac"], "branches": res["extend"]["branches"]["frac"]},
+                             res["roofline"]["frac"])
     if args.host_phases:
         res["host_phase_ms"] = ph.ms
     if not args.no_cpu_baseline:
@@ -862,6 +880,11 @@ def bench_tree(args):
     if dec_bytes < 256e6:  # the decode working set fits the 256 MB Infinity Cache
         res["roofline"]["note"] = ("decode working set below the 256 MB Infinity Cache: served from it across "
                                    "steps, so GB/s here is not HBM evidence")
+    if not f32:  # the targets are for the bf16 path
+        fr = {"extend": res["extend"]["frac"]}
+        if prefill:
+            fr["prefill"] = res["prefill"]["frac"]
+        res["targets"] = targets(fr, res["roofline"]["frac"], decode_hbm=dec_bytes >= 256e6)
     if args.host_phases:
         res["host_phase_ms"] = ph.ms
     if not args.no_cpu_baseline:
