@@ -248,6 +248,41 @@ def test_decode_is_deterministic(gpu):
     assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
 
 
+def test_decode_launcher_equals_the_plain_call(gpu):
+    # the engine's per-batch launcher (fixed arguments checked once) gives the
+    # bits of rc_decode_attention called through api.decode_attention, pool
+    # writes included, and rejects a step tensor of the wrong shape or dtype
+    w = W.few_shot(n_req=6, prefix=200, ext=5, n_decode=3)
+    res = []
+    for plain in (False, True):
+        eng = drive.make_engine(w, device=gpu)
+        drive.prefill_nodes(eng, w, device=gpu)
+        b, _ = drive.extend_requests(eng, w, device=gpu)
+        st = eng.prepare_decode(b, [len(w.prompt_tokens(r)) for r in w.requests], 3, chunk=64)
+        outs = []
+        for t in range(3):
+            q, k, v = drive.decode_inputs(w, range(6), t, device=gpu)
+            if plain:
+                o = torch.empty_like(q)
+                api.decode_attention(eng.shape, o, q, eng.k_pool, eng.v_pool, eng.table_d, st.seq_lens[t], st.plan,
+                                     w.sm_scale, st.workspace, k_new=k, v_new=v, new_slots=st.slots[t])
+            else:
+                o = eng.decode_step(st, t, q, k, v, w.sm_scale)
+            outs.append(o.view(torch.int16).cpu())
+        sl = st.slots.long().reshape(-1)
+        res.append((outs, eng.k_pool[sl].view(torch.int16).cpu(), eng.v_pool[sl].view(torch.int16).cpu()))
+        if not plain:
+            q, k, v = drive.decode_inputs(w, range(6), 0, device=gpu)
+            with pytest.raises(ValueError):
+                eng.decode_step(st, 0, q[:5], k, v, w.sm_scale)
+            with pytest.raises(ValueError):
+                eng.decode_step(st, 0, q.float(), k, v, w.sm_scale)
+            with pytest.raises(IndexError):
+                eng.decode_step(st, 3, q, k, v, w.sm_scale)
+    assert all(torch.equal(x, y) for x, y in zip(res[0][0], res[1][0]))
+    assert torch.equal(res[0][1], res[1][1]) and torch.equal(res[0][2], res[1][2])
+
+
 def test_unused_pool_slots_holding_nan_do_not_leak(gpu):
     # past-the-end keys of a stage read some pool row; its contents must never reach the output
     w = W.multi_turn_tree(depth=2, fanout=3, seg_lo=7, seg_hi=70, ext=5, n_decode=2)
