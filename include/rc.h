@@ -181,6 +181,11 @@ rc_status rc_extend_attention(const rc_shape* shape, void* o, const void* q, con
 #define RC_PLAN_HEADER 8
 #define RC_PLAN_ITEM 8
 #define RC_PLAN_ITEM_OWN 1 /* item flag: the range holds its member's own positions */
+/* Query columns (members x group) per item: a decode plan's items fill a    */
+/* four-wave tile, a cascade extend plan's (rc_radix_plan_extend) an         */
+/* eight-wave one (when the group alone is wider, an item has one member).   */
+#define RC_DECODE_COLS 128
+#define RC_EXTEND_SHARED_COLS 256
 
 typedef struct rc_plan_info {
   int32_t n_items;
@@ -190,7 +195,9 @@ typedef struct rc_plan_info {
   int32_t group;       /* Hq / Hkv the plan was built for                       */
   int32_t chunk;       /* nominal positions per item (pieces are balanced and */
                        /* at most chunk + chunk/8 long)                        */
-  int32_t max_cols;    /* max members*group per item                           */
+  int32_t max_cols;    /* max members*group per item (at most RC_DECODE_COLS   */
+                       /* for decode plans, RC_EXTEND_SHARED_COLS for cascade  */
+                       /* extend plans)                                        */
   int32_t shared_items;/* items with more than one member                       */
   int32_t narrow_begin;/* items from here on have members*group <= 16 (the plan */
                        /* lists wider items first)                              */
@@ -249,7 +256,8 @@ int64_t rc_decode_workspace_bytes(const rc_shape* shape, const rc_plan_info* inf
 /*   req_to_token  : device int32 [table_rows, stride]                        */
 /*   seq_lens      : device int32 [batch]                                     */
 /*   plan_dev      : device copy of the plan buffer (info->plan_ints int32);  */
-/*                   info: the summary the planner returned with it          */
+/*                   info: the summary the planner returned with it (a plan  */
+/*                   with info->max_cols > RC_DECODE_COLS: RC_ERR_ARG)        */
 /*   workspace     : device, >= rc_decode_workspace_bytes() bytes             */
 /* ------------------------------------------------------------------------ */
 rc_status rc_decode_attention(const rc_shape* shape, void* o, const void* q, void* k_pool, void* v_pool,
@@ -491,7 +499,8 @@ rc_status rc_radix_plan_decode(rc_radix* tree, int32_t batch, const int32_t* tok
 /* tokens over the cached prefix) computed as split-K decode over the plan:  */
 /* every tree range on the prefixes is read once for all the new tokens      */
 /* that pass through it (e.g. 64 label branches of one document read the     */
-/* document once per group of 128 / group tokens, not once per branch), and  */
+/* document once per group of RC_EXTEND_SHARED_COLS / group tokens, not      */
+/* once per branch), and                                                     */
 /* each token reads its own request's new tokens up to itself alone.        */
 /* Run it with rc_extend_attention_shared.  Output and sizing as            */
 /* rc_plan_decode_unshared; RC_ERR_RANGE also when a request's prefix +      */

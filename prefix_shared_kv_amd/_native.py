@@ -18,6 +18,7 @@ RC_OK, RC_ERR_ARG, RC_ERR_SHAPE, RC_ERR_DTYPE, RC_ERR_RANGE, RC_ERR_NOMEM, RC_ER
 RC_F32, RC_BF16 = 0, 1
 RC_DEVERR_SLOT, RC_DEVERR_TABLE, RC_DEVERR_LENGTH, RC_DEVERR_PLAN = 1, 2, 4, 8
 RC_PLAN_MAGIC, RC_PLAN_HEADER, RC_PLAN_ITEM, RC_PLAN_ITEM_OWN = 0x52435031, 8, 8, 1
+RC_DECODE_COLS, RC_EXTEND_SHARED_COLS = 128, 256
 RC_DECODE_STATIC_WORKSPACE_BYTES = 64 << 20
 RC_EMIT_EVICT, RC_EMIT_FULL_MATCH = 1, 2
 

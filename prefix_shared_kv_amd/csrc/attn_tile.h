@@ -41,7 +41,6 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int BN = 64;     // keys per stage
-constexpr int NCOL = 128;  // query columns per workgroup (4 waves x 32)
 constexpr int NT = 256;
 constexpr float LOG2E = 1.4426950408889634f;
 
@@ -81,6 +80,7 @@ struct Args {
   int32_t narrow_first;        // workgroups run the narrow items first, then the wide ones
   int32_t n_wide_blocks;       // workgroups that run wide items
   int32_t n_narrow_units;      // (narrow item, kv head) pairs, one wave each
+  int32_t max_cols;            // query columns of the launch's tile (32 per wave)
   const int32_t* seq_lens;
   float* ws_o;
   float* ws_ml;
@@ -170,7 +170,7 @@ __device__ Work resolve(const Args& a, int mode, int L, bool leader) {
     if (rep < 0 || rep >= a.table_rows || pb < 0 || pe < pb || (int64_t)pe > (a.stride << a.page_shift) ||
         a.pool_slots < 1 ||
         w.split < 0 || w.split >= a.max_splits ||
-        w.moff < 0 || w.mcnt < 1 || w.mcnt * a.g > NCOL || w.moff + w.mcnt > n_members) {
+        w.moff < 0 || w.mcnt < 1 || w.mcnt * a.g > a.max_cols || w.moff + w.mcnt > n_members) {
       if (leader) flag(a.err, RC_DEVERR_PLAN);
       return w;
     }

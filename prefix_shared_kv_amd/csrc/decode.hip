@@ -249,22 +249,37 @@ __device__ __forceinline__ bool decode_narrow_body(const Args& a, const int unit
 // on the heavy-decode workload); ROLE 1: extends run over a shared-prefix plan
 // (the members are new tokens), whose member groups re-read a prompt and keep
 // it in L2.  The two instantiations also tell the paths apart in profiles.
+// Decode steps take four-wave workgroups (two per CU); the cascade extend
+// takes eight-wave ones (one per CU), whose wide items carry up to
+// RC_EXTEND_SHARED_COLS query columns, so each K/V stage loaded into LDS feeds
+// twice the columns, as in the extend tile.
+template <int ROLE>
+constexpr int role_waves() {
+  return ROLE == 0 ? 4 : 8;
+}
+
 template <int D, int ROLE>
-__global__ __launch_bounds__(NT, 2) void decode_attn_bf16(Args a) {
-  __shared__ __attribute__((aligned(16))) uint16_t sK[2][BN * D];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[2][BN * D];
-  static_assert(2 * BN == 4 * BNN, "narrow tiles reuse the wide stage buffers");
+__global__ __launch_bounds__(64 * role_waves<ROLE>(), ROLE == 0 ? 2 : 1) void decode_attn_bf16(Args a) {
+  constexpr int NWK = role_waves<ROLE>();
+  // 64-key blocks: the wide tile's two K and two V stages use the first two,
+  // the narrow waves' 32-key tiles all of them
+  constexpr int NB = NWK * BNN / BN;
+  static_assert(NB >= 2 && NB * BN == NWK * BNN, "narrow tiles and wide stages share the buffers");
+  __shared__ __attribute__((aligned(16))) uint16_t sK[NB][BN * D];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[NB][BN * D];
   // the grid is [wide workgroups][narrow workgroups], or the other way round
   // when the plan says the narrow class runs longer (workgroups start in order)
-  const int n_narrow_blocks = (a.n_narrow_units + 3) >> 2;
+  const int n_narrow_blocks = (a.n_narrow_units + NWK - 1) / NWK;
   const int bid = (int)blockIdx.x;
   const bool wide = a.narrow_first ? bid >= n_narrow_blocks : bid < a.n_wide_blocks;
   if (wide) {
-    attn_bf16_tile<D, 4, ROLE == 0>(a, DECODE, a.narrow_first ? bid - n_narrow_blocks : bid, sK, sV);
+    typedef uint16_t Stages[2][BN * D];
+    attn_bf16_tile<D, NWK, ROLE == 0>(a, DECODE, a.narrow_first ? bid - n_narrow_blocks : bid,
+                                      *reinterpret_cast<Stages*>(&sK[0][0]), *reinterpret_cast<Stages*>(&sV[0][0]));
     return;
   }
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave
-  const int unit = (a.narrow_first ? bid : bid - a.n_wide_blocks) * 4 + wave;
+  const int unit = (a.narrow_first ? bid : bid - a.n_wide_blocks) * NWK + wave;
   if (unit >= a.n_narrow_units) return;
   uint16_t* sk = &sK[0][0] + wave * BNN * D;
   uint16_t* sv = &sV[0][0] + wave * BNN * D;
@@ -376,7 +391,8 @@ rc_status split_k_attention(const rc_shape* shape, void* o, const void* q, void*
   const int g = shape->num_q_heads / shape->num_kv_heads;
   if (info->batch != batch) return fail(RC_ERR_ARG, "plan built for batch %d, called with %d", info->batch, batch);
   if (info->group != g) return fail(RC_ERR_SHAPE, "plan built for group %d, shape has %d", info->group, g);
-  if (info->max_cols > NCOL || info->n_items < 0 || info->n_members < 0 || info->max_splits < 1 ||
+  constexpr int NWK = role_waves<ROLE>();
+  if (info->max_cols > 32 * NWK || info->n_items < 0 || info->n_members < 0 || info->max_splits < 1 ||
       info->plan_ints != RC_PLAN_HEADER + (int64_t)info->n_items * RC_PLAN_ITEM + info->n_members + batch)
     return fail(RC_ERR_ARG, "plan summary out of range");
   const int64_t need = rc_decode_workspace_bytes(shape, info);
@@ -398,6 +414,7 @@ rc_status split_k_attention(const rc_shape* shape, void* o, const void* q, void*
   a.ws_o = (float*)workspace;
   a.ws_ml = (float*)workspace + parts * shape->head_dim;
   a.max_splits = info->max_splits;
+  a.max_cols = 32 * NWK;
   if (info->narrow_begin < 0 || info->narrow_begin > info->n_items) return fail(RC_ERR_ARG, "plan summary out of range");
   hipStream_t s = (hipStream_t)stream;
   const bool bf16 = shape->dtype == RC_BF16;
@@ -416,9 +433,9 @@ rc_status split_k_attention(const rc_shape* shape, void* o, const void* q, void*
   } else {
     // wide items: one workgroup per (item, kv head)
     const int64_t n_wide = (int64_t)info->narrow_begin * a.Hkv;
-    // narrow items: one wave per (item, kv head), four waves per workgroup
+    // narrow items: one wave per (item, kv head), NWK waves per workgroup
     const int64_t units = (int64_t)(info->n_items - info->narrow_begin) * a.Hkv;
-    const int64_t n_narrow = (units + 3) / 4;
+    const int64_t n_narrow = (units + NWK - 1) / NWK;
     const int64_t grid = n_wide + n_narrow;
     if (grid > INT32_MAX) return fail(RC_ERR_RANGE, "grid too large");
     a.n_narrow_units = (int32_t)units;
@@ -426,9 +443,9 @@ rc_status split_k_attention(const rc_shape* shape, void* o, const void* q, void*
     if (grid > 0) {
       ProfScope p(attn_name, s, timed);
       if (shape->head_dim == 128)
-        hipLaunchKernelGGL((decode_attn_bf16<128, ROLE>), dim3((unsigned)grid), dim3(NT), 0, s, a);
+        hipLaunchKernelGGL((decode_attn_bf16<128, ROLE>), dim3((unsigned)grid), dim3(64 * NWK), 0, s, a);
       else
-        hipLaunchKernelGGL((decode_attn_bf16<64, ROLE>), dim3((unsigned)grid), dim3(NT), 0, s, a);
+        hipLaunchKernelGGL((decode_attn_bf16<64, ROLE>), dim3((unsigned)grid), dim3(64 * NWK), 0, s, a);
     }
     st = check_launch("decode attention");
     if (st != RC_OK) return st;

@@ -1058,7 +1058,7 @@ extern "C" rc_status rc_plan_decode_unshared(int32_t batch, const int32_t* rows,
                                              int32_t chunk, int32_t* plan, int64_t cap, rc_plan_info* info) {
   rc_status st = plan_args(batch, max_seq, group, chunk, info);
   if (st != RC_OK) return st;
-  PlanBuilder pb{batch, group, chunk, std::max(1, 128 / group), rows, {}, {}, {}, {}, {}};
+  PlanBuilder pb{batch, group, chunk, std::max(1, RC_DECODE_COLS / group), rows, {}, {}, {}, {}, {}};
   pb.path.resize(batch);
   int64_t logical = 0;
   for (int32_t b = 0; b < batch; ++b) {
@@ -1085,14 +1085,14 @@ struct Visit {
 rc_status plan_from_walks(const rc_radix* t, int32_t n_mem, const std::vector<int32_t>& req_of,
                           const std::vector<std::vector<Visit>>& walks, const std::vector<int64_t>& walked,
                           const std::vector<int32_t>& rows_of, const int32_t* max_seq, int32_t group, int32_t chunk,
-                          int32_t* plan, int64_t cap, rc_plan_info* info) {
+                          int32_t max_cols, int32_t* plan, int64_t cap, rc_plan_info* info) {
   std::unordered_map<int32_t, std::vector<std::pair<int64_t, int32_t>>> by_node;  // node -> (end, member)
   for (int32_t m = 0; m < n_mem; ++m) {
     const int32_t r = req_of[m];
     if (max_seq[m] < walked[r]) return fail(RC_ERR_RANGE, "max_seq_lens[%d] = %d shorter than its cached prefix %lld", m, max_seq[m], (long long)walked[r]);
     for (const Visit& v : walks[r]) by_node[v.node].push_back({v.end, m});
   }
-  PlanBuilder pb{n_mem, group, chunk, std::max(1, 128 / group), rows_of.data(), {}, {}, {}, {}, {}};
+  PlanBuilder pb{n_mem, group, chunk, std::max(1, max_cols / group), rows_of.data(), {}, {}, {}, {}, {}};
   pb.path.resize(n_mem);
   // node -> list of (sub-range id, sub-range end); members of a sub-range reach at least its end
   std::unordered_map<int32_t, std::vector<std::pair<int32_t, int64_t>>> subs;
@@ -1189,7 +1189,8 @@ extern "C" rc_status rc_radix_plan_decode(rc_radix* t, int32_t batch, const int3
     req_of[b] = b;
     rows_of[b] = rows ? rows[b] : b;
   }
-  return plan_from_walks(t, batch, req_of, walks, walked, rows_of, max_seq, group, chunk, plan, cap, info);
+  return plan_from_walks(t, batch, req_of, walks, walked, rows_of, max_seq, group, chunk, RC_DECODE_COLS, plan, cap,
+                         info);
 }
 
 extern "C" rc_status rc_radix_plan_extend(rc_radix* t, int32_t batch, const int32_t* tokens, const int64_t* tok_off,
@@ -1225,7 +1226,8 @@ extern "C" rc_status rc_radix_plan_extend(rc_radix* t, int32_t batch, const int3
   std::vector<std::vector<Visit>> walks;
   std::vector<int64_t> walked;
   walk_requests(t, batch, tokens, tok_off, [&](int32_t b) { return (int64_t)prefix_lens[b]; }, walks, walked);
-  st = plan_from_walks(t, (int32_t)n_tok, req_of, walks, walked, rows_of, max_seq.data(), group, chunk, plan, cap, info);
+  st = plan_from_walks(t, (int32_t)n_tok, req_of, walks, walked, rows_of, max_seq.data(), group, chunk,
+                       RC_EXTEND_SHARED_COLS, plan, cap, info);
   if (st == RC_OK && seq_lens) std::copy(max_seq.begin(), max_seq.end(), seq_lens);
   return st;
 }

@@ -29,6 +29,7 @@ from typing import List, Optional, Sequence
 import numpy as np
 import torch
 
+from . import _native as N
 from . import api
 from .api import DecodePlan, KVShape, RadixTree, TokenBatch
 
@@ -275,17 +276,17 @@ class Engine:
         b.dev = dict(zip(names, self._i32_many(rows, P, E, start, b.new_slots)))
         return b
 
-    # workgroups of the split-K launch resident at once: two 4-wave workgroups per CU
+    # workgroups of the cascade's split-K launch resident at once: one 8-wave workgroup per CU
     def _resident_workgroups(self) -> int:
         if not hasattr(self, "_resident"):
-            self._resident = 2 * torch.cuda.get_device_properties(self.device).multi_processor_count
+            self._resident = torch.cuda.get_device_properties(self.device).multi_processor_count
         return self._resident
 
     def _cascade_chunk(self, b: Batch) -> int:
         """Piece length for the shared ranges of a cascade extend: as many pieces as keep every
         workgroup of the launch resident at once (one round, no tail), no more.  Each piece of
         a shared range becomes ceil(new tokens / tokens per group) workgroups per kv head."""
-        per_group = max(1, 128 // self.shape.group)
+        per_group = max(1, N.RC_EXTEND_SHARED_COLS // self.shape.group)
         groups = -(-b.total_extend // per_group) * self.shape.num_kv_heads
         pieces = max(1, self._resident_workgroups() // max(groups, 1))
         longest = int(b.prefix_lens.max()) if b.size else 0

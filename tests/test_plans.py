@@ -6,7 +6,8 @@ built by the tree itself:
     distinct split indices below its split count;
   * an item's positions hold the same slots in every member's table row as
     in the representative row the kernel reads them through;
-  * members per item stay within max(1, 128 / group);
+  * members per item stay within max(1, cols / group), cols = 128 columns for
+    decode plans and 256 for cascade extend plans;
   * items flagged as a request's own positions (the only items the decode
     kernel lets store the current token) have one member and cover a suffix
     of its positions, every position past its committed tokens included,
@@ -30,9 +31,10 @@ def parse(plan):
     return items, mem, nsplit
 
 
-def check_plan(plan, max_seq, rows, table, group, own_from=None):
+def check_plan(plan, max_seq, rows, table, group, own_from=None, cols=N.RC_DECODE_COLS):
     items, mem, nsplit = parse(plan)
-    max_m = max(1, 128 // group)
+    max_m = max(1, cols // group)
+    assert plan.info.max_cols == max_m * group
     cover = {m: [] for m in range(len(max_seq))}
     own = {m: [] for m in range(len(max_seq))}
     for rep, pb, pe, sp, mo, mc, flags, _ in items:
@@ -96,10 +98,10 @@ def test_extend_plan_reads_a_shared_document_once_per_token_group():
     plan = t.plan_extend(batch, P, E, group)
     rows = np.repeat(np.arange(5), E)
     max_seq = np.concatenate([p + np.arange(1, e + 1) for p, e in zip(P, E)])
-    items, mem = check_plan(plan, max_seq, rows, table, group)
+    items, mem = check_plan(plan, max_seq, rows, table, group, cols=N.RC_EXTEND_SHARED_COLS)
     doc_items = [it for it in items if it[1] == 0 and it[2] == 300]
-    # 33 new tokens in groups of 128 / 8 = 16: the document is read by 3 items, not 5 or 33
-    assert sorted(int(it[5]) for it in doc_items) == [1, 16, 16]
+    # 33 new tokens in groups of 256 / 8 = 32: the document is read by 2 items, not 5 or 33
+    assert sorted(int(it[5]) for it in doc_items) == [1, 32]
     own = [it for it in items if it[1] >= 300]
     assert len(own) == 33 and all(it[5] == 1 for it in own)
     assert plan.info.batch == 33 and plan.info.max_splits == 2
@@ -112,7 +114,8 @@ def test_extend_plan_without_a_cached_prefix():
     P, E = t.emit_rows(batch, table)
     assert P.tolist() == [0, 0]
     plan = t.plan_extend(batch, P, E, 4)
-    check_plan(plan, np.concatenate([np.arange(1, 21), np.arange(1, 8)]), np.repeat([0, 1], E), table, 4)
+    check_plan(plan, np.concatenate([np.arange(1, 21), np.arange(1, 8)]), np.repeat([0, 1], E), table, 4,
+               cols=N.RC_EXTEND_SHARED_COLS)
     assert plan.info.shared_items == 0
 
 
@@ -153,7 +156,7 @@ def test_plans_cover_every_context_with_shared_slots(case):
     plan = t.plan_extend(batch, P, E, group, chunk)
     rows = np.repeat(np.arange(len(batch)), E)
     max_seq = np.concatenate([p + np.arange(1, e + 1) for p, e in zip(P, E)])
-    check_plan(plan, max_seq, rows, table, group)
+    check_plan(plan, max_seq, rows, table, group, cols=N.RC_EXTEND_SHARED_COLS)
     # token i of request b attends over positions [0, P_b + i]
     assert plan.seq_lens.tolist() == max_seq.tolist()
     # decode plan after commit: contexts up to the reserved slots

@@ -146,14 +146,14 @@ def _expanded(table, ps):
     return out
 
 
-def _check_plan(plan, max_seq, rows, slots, group):
+def _check_plan(plan, max_seq, rows, slots, group, cols=N.RC_DECODE_COLS):
     buf, info = plan.host, plan.info
     H, I = N.RC_PLAN_HEADER, N.RC_PLAN_ITEM
     items = buf[H:H + I * info.n_items].reshape(-1, I)
     mem = buf[H + I * info.n_items:H + I * info.n_items + info.n_members]
     cover = {m: [] for m in range(len(max_seq))}
     for rep, pb, pe, sp, mo, mc, _, _ in items:
-        assert 1 <= mc <= max(1, 128 // group) and pb < pe
+        assert 1 <= mc <= max(1, cols // group) and pb < pe
         for m in mem[mo:mo + mc]:
             cover[int(m)].append((int(pb), int(pe)))
             assert np.array_equal(slots[rep, pb:pe], slots[rows[int(m)], pb:pe])
@@ -185,7 +185,7 @@ def test_paged_decode_and_extend_plans(ps):
     plan = t.plan_extend(batch, P, E, group=4, chunk=128, rows=rows)
     seq = np.concatenate([p + np.arange(1, e + 1) for p, e in zip(P, E)])
     rows_of = np.repeat(rows, E)
-    items, mem = _check_plan(plan, seq, rows_of, _expanded(table, ps), 4)
+    items, mem = _check_plan(plan, seq, rows_of, _expanded(table, ps), 4, cols=N.RC_EXTEND_SHARED_COLS)
     assert any(mc > 1 for *_, mc, _, _ in items)  # the shared pages are read for several tokens at once
     # decode after committing the batch
     t.insert_rows(batch, table, rows)
