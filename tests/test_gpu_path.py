@@ -225,7 +225,7 @@ def test_cascade_extend_matches_the_oracle(gpu, dtype):
 @pytest.mark.parametrize("Hq,Hkv,D", [(32, 1, 128), (64, 1, 128), (128, 1, 64)])
 def test_cascade_extend_large_groups(gpu, dtype, Hq, Hkv, D):
     # branches over one document through the shared-prefix plan with 32 to 128
-    # query heads per kv head (4 to 1 new tokens per member group)
+    # query heads per kv head (8 to 2 new tokens per 256-column member group)
     w = W.classify64(prefix=300, n_branch=12)
     w.shape.num_q_heads, w.shape.num_kv_heads, w.shape.head_dim = Hq, Hkv, D
     w.sm_scale = 1.0 / np.sqrt(D)
