@@ -116,6 +116,30 @@ def test_decode_argument_checks():
     assert st == N.RC_ERR_ARG
 
 
+def test_plan_columns_are_checked_against_the_launch():
+    # a cascade extend plan fills eight-wave tiles (256 columns per item); the
+    # decode launch runs four-wave tiles and rejects it before touching the
+    # device, while the cascade launch accepts both kinds of plan
+    from prefix_shared_kv_amd import RadixTree
+    sh = shape()  # group 4
+    t = RadixTree(4096)
+    doc = np.arange(100, 400, dtype=np.int32)
+    batch = [np.concatenate([doc, np.arange(1000 + 40 * k, 1000 + 40 * k + 40, dtype=np.int32)]) for k in range(2)]
+    table = np.full((2, 400), -1, np.int32)
+    t.emit_rows([doc], table[:1])
+    t.insert_rows([doc], table[:1], np.zeros(1, np.int32))
+    P, E = t.emit_rows(batch, table)
+    plan = t.plan_extend(batch, P, E, 4, 4096)
+    info = plan.info
+    assert info.max_cols == N.RC_EXTEND_SHARED_COLS > N.RC_DECODE_COLS
+    need = N.lib.rc_decode_workspace_bytes(C.byref(sh), C.byref(info))
+    st = N.lib.rc_decode_attention(C.byref(sh), FAKE, FAKE, FAKE, FAKE, None, None, None, FAKE, 2, 400, FAKE,
+                                   info.batch, FAKE, C.byref(info), 0.1, FAKE, need, None)
+    assert st == N.RC_ERR_ARG and "plan summary" in N.last_error()
+    _, dinfo = _plan([100, 70], 4)
+    assert dinfo.max_cols == N.RC_DECODE_COLS
+
+
 def test_static_decode_argument_checks():
     # the allocation-free decode rejects a plan whose workspace exceeds the
     # static one before it touches the device
