@@ -476,7 +476,8 @@ rc_status rc_radix_fork(rc_radix* tree, const int32_t* tokens, const int32_t* pa
 /* Shared decode plan from the tree: request b's committed tokens (its      */
 /* tok_len[b] first, or all) are walked through the tree; every node         */
 /* range is one item whose members are all batch requests passing through    */
-/* it (split into items of at most max(1, 128 / group) members); positions   */
+/* it (split into items of at most max(1, RC_DECODE_COLS / group) members);*/
+/* positions                                                                 */
 /* past the walked prefix up to max_seq_lens[b] form the request's own tail. */
 /* A range is cut into the fewest near-equal pieces of at most chunk +      */
 /* chunk/8 positions.  Table rows must                                        */

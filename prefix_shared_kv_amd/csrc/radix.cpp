@@ -997,7 +997,8 @@ struct PlanBuilder {
     // Which class the launch deals out first: the one holding the item that
     // takes longest, so that no long item starts late.  A narrow item is one
     // wave per kv head and streams its range at roughly half the rate of a
-    // wide item's four waves, so its length counts double.
+    // wide item's workgroup (four waves, eight in a cascade extend), so its
+    // length counts double.
     int64_t long_wide = 0, long_narrow = 0;
     for (const Item& it : wide) long_wide = std::max<int64_t>(long_wide, it.v[2] - it.v[1]);
     for (const Item& it : narrow) long_narrow = std::max<int64_t>(long_narrow, it.v[2] - it.v[1]);
