@@ -233,7 +233,9 @@ rc_status rc_decode_steps(const int32_t* req_to_token, int32_t table_rows, int64
                           int32_t batch, const int32_t* rows, const int64_t* row_entries, const int32_t* base_lens,
                           int32_t n_steps, int32_t* slots, int32_t* seq_lens);
 
-/* Workspace bytes rc_decode_attention needs for a plan (fp32 partials).     */
+/* Workspace bytes rc_decode_attention needs for a plan: per member, head   */
+/* and split, a partial output row in the shape's dtype (bf16 or fp32) and   */
+/* an fp32 (max, sum) pair.                                                  */
 int64_t rc_decode_workspace_bytes(const rc_shape* shape, const rc_plan_info* info);
 
 /* ------------------------------------------------------------------------ */
@@ -248,9 +250,11 @@ int64_t rc_decode_workspace_bytes(const rc_shape* shape, const rc_plan_info* inf
 /* That key is taken from k_new / v_new by the RC_PLAN_ITEM_OWN item holding */
 /* position L_b - 1; a plan whose request has no such item (position L_b - 1 */
 /* inside a shared range) reads the key from the pool and stores nothing.    */
-/* Split-K: each item writes fp32 partial (max, sum, unnormalised output)    */
-/* per member and head; a merge kernel combines each request's partials in   */
-/* split order (deterministic, no float atomics).                             */
+/* Split-K: each item writes a partial (fp32 max and sum, and the output   */
+/* row: for bf16 data normalised by its sum and rounded to bf16 once, for   */
+/* fp32 data unnormalised fp32) per member and head; a merge kernel          */
+/* combines each request's partials in fp32 in split order (deterministic,  */
+/* no float atomics).                                                        */
 /*   o, q          : device [batch, Hq, D]                                    */
 /*   k_pool, v_pool: device [pool_slots, Hkv, D] (written only with k_new)    */
 /*   req_to_token  : device int32 [table_rows, stride]                        */

@@ -82,7 +82,7 @@ struct Args {
   int32_t n_narrow_units;      // (narrow item, kv head) pairs, one wave each
   int32_t max_cols;            // query columns of the launch's tile (32 per wave)
   const int32_t* seq_lens;
-  float* ws_o;
+  void* ws_o;    // partial outputs: bf16 rows for bf16 data, fp32 rows for fp32
   float* ws_ml;
   int32_t max_splits;
 };
@@ -636,14 +636,22 @@ __device__ __forceinline__ bool attn_bf16_body(const Args& a, const int mode, co
         }
     }
   } else {
+    // the partial row normalised by its own sum and rounded to bf16 once; the
+    // merge weighs the rows by their (max, sum) pairs in fp32
     const int64_t pidx = ((int64_t)col.b * a.Hq + col.head) * a.max_splits + w.split;
-    float* wo = a.ws_o + pidx * D;
+    uint16_t* wo = (uint16_t*)a.ws_o + pidx * D;
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         const int d = db * 32 + g4 * 8 + hi * 4;
-        *(float4*)(wo + d) = make_float4(acc[db][4 * g4], acc[db][4 * g4 + 1], acc[db][4 * g4 + 2], acc[db][4 * g4 + 3]);
+        const __bf16 b0 = (__bf16)(acc[db][4 * g4 + 0] * inv), b1 = (__bf16)(acc[db][4 * g4 + 1] * inv);
+        const __bf16 b2 = (__bf16)(acc[db][4 * g4 + 2] * inv), b3 = (__bf16)(acc[db][4 * g4 + 3] * inv);
+        uint2 pk;
+        pk.x = pack2(__builtin_bit_cast(uint16_t, b0), __builtin_bit_cast(uint16_t, b1));
+        pk.y = pack2(__builtin_bit_cast(uint16_t, b2), __builtin_bit_cast(uint16_t, b3));
+        *(uint2*)(wo + d) = pk;
       }
     if (hi == 0) *(float2*)(a.ws_ml + pidx * 2) = make_float2(m_run, l_tot);
   }
@@ -762,7 +770,7 @@ __device__ __forceinline__ void attn_f32_body(const Args& a, const int mode) {
     } else {
       const int64_t pidx = ((int64_t)col.b * a.Hq + col.head) * a.max_splits + w.split;
 #pragma unroll
-      for (int i = 0; i < NV; ++i) *(float4*)(a.ws_o + pidx * D + grp * DG + 4 * i) = ov[i];
+      for (int i = 0; i < NV; ++i) *(float4*)((float*)a.ws_o + pidx * D + grp * DG + 4 * i) = ov[i];
       if (grp == 0) *(float2*)(a.ws_ml + pidx * 2) = make_float2(m_run, l_run);
     }
   }

@@ -231,10 +231,15 @@ __device__ __forceinline__ bool decode_narrow_body(const Args& a, const int unit
   l_tot += __shfl_xor(l_tot, 32);
   if (!col.real) return false;
   const int64_t pidx = ((int64_t)col.b * a.Hq + col.head) * a.max_splits + w.split;
-  float* wo = a.ws_o + pidx * D;
+  uint16_t* wo = (uint16_t*)a.ws_o + pidx * D;  // the normalised partial row in bf16, as in the wide tile
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
 #pragma unroll
-  for (int db = 0; db < NDB; ++db)
-    *(float4*)(wo + db * 16 + 4 * grp) = make_float4(acc[db][0], acc[db][1], acc[db][2], acc[db][3]);
+  for (int db = 0; db < NDB; ++db) {
+    uint2 pk;
+    pk.x = pack2(__builtin_bit_cast(uint16_t, (__bf16)(acc[db][0] * inv)), __builtin_bit_cast(uint16_t, (__bf16)(acc[db][1] * inv)));
+    pk.y = pack2(__builtin_bit_cast(uint16_t, (__bf16)(acc[db][2] * inv)), __builtin_bit_cast(uint16_t, (__bf16)(acc[db][3] * inv)));
+    *(uint2*)(wo + db * 16 + 4 * grp) = pk;
+  }
   if (grp == 0) *(float2*)(a.ws_ml + pidx * 2) = make_float2(m_run, l_tot);
   return false;
 }
@@ -296,9 +301,13 @@ __global__ __launch_bounds__(NT) void decode_attn_f32(Args a) {
 // One wave per (request, head).  The (max, sum) pairs of 64 splits at a time
 // are loaded at once (one per lane) and reduced across the wave, then the
 // partial outputs are read with all those splits' loads in flight together.
-// Beyond 64 splits the blocks are combined with the usual rescaling.
+// Beyond 64 splits the blocks are combined with the usual rescaling.  BF16:
+// bf16 data, whose partial rows come normalised (o_k / l_k) in bf16, so each
+// row is weighed by u_k = l_k 2^(m_k - M) and the same u_k sum to l (with V = 1
+// the output is exactly 1); fp32 data: unnormalised fp32 rows weighed by
+// 2^(m_k - M).  Lane l handles the PER consecutive elements from l * PER of a row.
 template <int D, bool BF16>
-__global__ __launch_bounds__(256) void merge_kernel(void* out, const float* __restrict__ ws_o,
+__global__ __launch_bounds__(256) void merge_kernel(void* out, const void* __restrict__ ws_o,
                                                     const float* __restrict__ ws_ml, const int32_t* nsplit,
                                                     int32_t batch, int32_t Hq, int32_t max_splits) {
   constexpr int PER = D / 64;
@@ -309,7 +318,14 @@ __global__ __launch_bounds__(256) void merge_kernel(void* out, const float* __re
   int ns = nsplit[b];
   ns = ns < 0 ? 0 : (ns < max_splits ? ns : max_splits);
   const float* ml = ws_ml + (int64_t)pair * max_splits * 2;
-  const float* po = ws_o + (int64_t)pair * max_splits * D;
+  const int64_t row0 = (int64_t)pair * max_splits * D + lane * PER;
+  // element i of this lane in partial k, in fp32
+  auto part = [&](int k, int i) -> float {
+    if constexpr (BF16)
+      return (float)((const __bf16*)ws_o)[row0 + (int64_t)k * D + i];
+    else
+      return ((const float*)ws_o)[row0 + (int64_t)k * D + i];
+  };
   float acc[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) acc[i] = 0.f;
@@ -332,9 +348,10 @@ __global__ __launch_bounds__(256) void merge_kernel(void* out, const float* __re
     const int n = min(64, ns - k0);
     for (int j = 0; j < n; ++j) {
       const float wj = __shfl(wk, j);
-      l += __shfl(mine.y, j) * wj;
+      const float uj = __shfl(mine.y, j) * wj;
+      l += uj;
 #pragma unroll
-      for (int i = 0; i < PER; ++i) acc[i] += po[(int64_t)(k0 + j) * D + lane + 64 * i] * wj;
+      for (int i = 0; i < PER; ++i) acc[i] += part(k0 + j, i) * (BF16 ? uj : wj);
     }
   }
   const float inv = l > 0.f ? 1.f / l : 0.f;
@@ -342,9 +359,9 @@ __global__ __launch_bounds__(256) void merge_kernel(void* out, const float* __re
   for (int i = 0; i < PER; ++i) {
     const float r = acc[i] * inv;
     if (BF16)
-      ((__bf16*)out)[(int64_t)pair * D + lane + 64 * i] = (__bf16)r;
+      ((__bf16*)out)[(int64_t)pair * D + lane * PER + i] = (__bf16)r;
     else
-      ((float*)out)[(int64_t)pair * D + lane + 64 * i] = r;
+      ((float*)out)[(int64_t)pair * D + lane * PER + i] = r;
   }
 }
 
@@ -359,7 +376,9 @@ void launch_decode_f32(const Args& a, int n_work, hipStream_t s, const char* nam
 extern "C" int64_t rc_decode_workspace_bytes(const rc_shape* shape, const rc_plan_info* info) {
   if (!shape || !info || shape->head_dim <= 0) return -1;
   const int64_t parts = (int64_t)info->batch * shape->num_q_heads * (info->max_splits > 0 ? info->max_splits : 1);
-  return parts * shape->head_dim * 4 + parts * 2 * 4;
+  // partial rows in the data type (bf16 or fp32), then fp32 (max, sum) pairs
+  const int64_t row_bytes = shape->head_dim * (shape->dtype == RC_BF16 ? 2 : 4);
+  return parts * row_bytes + parts * 2 * 4;
 }
 
 namespace {
@@ -411,8 +430,8 @@ rc_status split_k_attention(const rc_shape* shape, void* o, const void* q, void*
   a.n_items = info->n_items; a.n_members = info->n_members;
   a.narrow_begin = info->narrow_begin;
   a.narrow_first = info->narrow_first != 0;
-  a.ws_o = (float*)workspace;
-  a.ws_ml = (float*)workspace + parts * shape->head_dim;
+  a.ws_o = workspace;
+  a.ws_ml = (float*)((char*)workspace + parts * shape->head_dim * (shape->dtype == RC_BF16 ? 2 : 4));
   a.max_splits = info->max_splits;
   a.max_cols = 32 * NWK;
   if (info->narrow_begin < 0 || info->narrow_begin > info->n_items) return fail(RC_ERR_ARG, "plan summary out of range");

@@ -93,7 +93,10 @@ def test_decode_argument_checks():
     sh = shape()  # group 4
     buf, info = _plan([100, 70], 4)
     need = N.lib.rc_decode_workspace_bytes(C.byref(sh), C.byref(info))
-    assert need == 2 * 8 * info.max_splits * (128 + 2) * 4
+    # bf16 partial rows (128 x 2 bytes) and fp32 (max, sum) pairs; fp32 data keeps fp32 rows
+    assert need == 2 * 8 * info.max_splits * (128 * 2 + 2 * 4)
+    assert N.lib.rc_decode_workspace_bytes(C.byref(shape(dtype=N.RC_F32)), C.byref(info)) == \
+        2 * 8 * info.max_splits * (128 * 4 + 2 * 4)
 
     def call(sh_, batch, ws):
         return N.lib.rc_decode_attention(C.byref(sh_), FAKE, FAKE, FAKE, FAKE, None, None, None, FAKE, 2, 128, FAKE,
@@ -144,11 +147,11 @@ def test_static_decode_argument_checks():
     # the allocation-free decode rejects a plan whose workspace exceeds the
     # static one before it touches the device
     sh = shape()  # group 4, Hq 8, head_dim 128
-    buf, info = _plan([640] * 2048, 4)  # 2048 x 8 heads x 9 splits x 130 x 4 B = 76.7 MB
+    buf, info = _plan([640] * 4096, 4)  # 4096 x 8 heads x 9 splits x (256 + 8) B = 77.9 MB
     need = N.lib.rc_decode_workspace_bytes(C.byref(sh), C.byref(info))
     assert need > N.RC_DECODE_STATIC_WORKSPACE_BYTES
     call = N.lib.rc_decode_attention_static
-    st = call(C.byref(sh), FAKE, FAKE, FAKE, FAKE, None, None, None, FAKE, 2048, 640, FAKE, 2048, FAKE,
+    st = call(C.byref(sh), FAKE, FAKE, FAKE, FAKE, None, None, None, FAKE, 4096, 640, FAKE, 4096, FAKE,
               C.byref(info), 0.1, None)
     assert st == N.RC_ERR_RANGE and "static workspace" in N.last_error()
     assert call(None, FAKE, FAKE, FAKE, FAKE, None, None, None, FAKE, 2, 128, FAKE, 2, FAKE, C.byref(info), 0.1,

@@ -74,8 +74,8 @@ def test_static_workspace_decode_twice_second_smaller(gpu, dtype):
 
 
 def test_static_workspace_rejects_plans_too_large(gpu):
-    # 512 requests x 32 heads x 9 splits x (128 + 2) fp32 = 76.7 MB > 64 MiB
-    B, Hq, Hkv, D = 512, 32, 8, 128
+    # 1024 requests x 32 heads x 9 splits x (128 bf16 + 2 fp32) = 77.9 MB > 64 MiB
+    B, Hq, Hkv, D = 1024, 32, 8, 128
     shape = KVShape(Hq, Hkv, D, torch.bfloat16, 64)
     plan = api.plan_decode_unshared(np.full(B, 640, np.int32), Hq // Hkv, 64)
     assert api.decode_workspace_bytes(shape, plan) > N.RC_DECODE_STATIC_WORKSPACE_BYTES
