@@ -298,46 +298,43 @@ __global__ __launch_bounds__(NT) void decode_attn_f32(Args a) {
 
 // Split merge: for each (request, q head), combine its partials k = 0..n-1 in
 // order: M = max m_k, l = sum l_k 2^(m_k - M), o = sum o_k 2^(m_k - M) / l.
-// One wave per (request, head).  The (max, sum) pairs of 64 splits at a time
-// are loaded at once (one per lane) and reduced across the wave, then the
-// partial outputs are read with all those splits' loads in flight together.
-// Beyond 64 splits the blocks are combined with the usual rescaling.  BF16:
-// bf16 data, whose partial rows come normalised (o_k / l_k) in bf16, so each
-// row is weighed by u_k = l_k 2^(m_k - M) and the same u_k sum to l (with V = 1
-// the output is exactly 1); fp32 data: unnormalised fp32 rows weighed by
-// 2^(m_k - M).  Lane l handles the PER consecutive elements from l * PER of a row.
+// 16 lanes per (request, head), four pairs per wave; a lane handles D/16
+// consecutive elements of a row (one 16-byte load per partial row for bf16
+// data at D = 128).  The (max, sum) pairs of 16 splits at a time are loaded
+// at once (one per lane) and reduced across the 16 lanes; the partial rows are
+// then read four at a time with their loads in flight together.  Beyond 16
+// splits the blocks are combined with the usual rescaling.  BF16: bf16 data,
+// whose partial rows come normalised (o_k / l_k) in bf16, so each row is
+// weighed by u_k = l_k 2^(m_k - M) and the same u_k sum to l (with V = 1 the
+// output is exactly 1); fp32 data: unnormalised fp32 rows weighed by
+// 2^(m_k - M).
 template <int D, bool BF16>
 __global__ __launch_bounds__(256) void merge_kernel(void* out, const void* __restrict__ ws_o,
                                                     const float* __restrict__ ws_ml, const int32_t* nsplit,
                                                     int32_t batch, int32_t Hq, int32_t max_splits) {
-  constexpr int PER = D / 64;
-  const int pair = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (pair >= batch * Hq) return;
+  constexpr int PER = D / 16;
+  constexpr int MU = 4;  // partial rows in flight per lane
+  typedef __bf16 bvec __attribute__((ext_vector_type(PER)));  // one lane's elements of a bf16 row
   const int lane = threadIdx.x & 63;
-  const int b = pair / Hq;
-  int ns = nsplit[b];
+  const int sub = lane & 15, gbase = lane & 48;
+  const int pair = (int)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const bool live = pair < batch * Hq;
+  int ns = live ? nsplit[pair / Hq] : 0;
   ns = ns < 0 ? 0 : (ns < max_splits ? ns : max_splits);
   const float* ml = ws_ml + (int64_t)pair * max_splits * 2;
-  const int64_t row0 = (int64_t)pair * max_splits * D + lane * PER;
-  // element i of this lane in partial k, in fp32
-  auto part = [&](int k, int i) -> float {
-    if constexpr (BF16)
-      return (float)((const __bf16*)ws_o)[row0 + (int64_t)k * D + i];
-    else
-      return ((const float*)ws_o)[row0 + (int64_t)k * D + i];
-  };
+  const int64_t row0 = (int64_t)pair * max_splits * D + sub * PER;
   float acc[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) acc[i] = 0.f;
   float l = 0.f, M_run = -INFINITY;
-  for (int k0 = 0; k0 < ns; k0 += 64) {
-    const int k = k0 + lane;
+  for (int k0 = 0; k0 < ns; k0 += 16) {
+    const int k = k0 + sub;
     const float2 mine = k < ns ? *(const float2*)(ml + 2 * k) : make_float2(-INFINITY, 0.f);
     float Mb = mine.x;
 #pragma unroll
-    for (int sh = 32; sh >= 1; sh >>= 1) Mb = fmaxf(Mb, __shfl_xor(Mb, sh));
+    for (int sh = 8; sh >= 1; sh >>= 1) Mb = fmaxf(Mb, __shfl_xor(Mb, sh));
     const float M = fmaxf(M_run, Mb);
-    if (k0 > 0 && M_run != M) {  // earlier blocks were weighted against an older maximum
+    if (k0 > 0 && M_run != M) {
       const float r = M_run == -INFINITY ? 0.f : exp2f(M_run - M);
       l *= r;
 #pragma unroll
@@ -345,23 +342,63 @@ __global__ __launch_bounds__(256) void merge_kernel(void* out, const void* __res
     }
     M_run = M;
     const float wk = mine.x == -INFINITY ? 0.f : exp2f(mine.x - M);
-    const int n = min(64, ns - k0);
-    for (int j = 0; j < n; ++j) {
-      const float wj = __shfl(wk, j);
-      const float uj = __shfl(mine.y, j) * wj;
-      l += uj;
+    const int n = min(16, ns - k0);
+    // MU partial rows at a time, their loads issued together (a split past n
+    // re-reads the block's last row and gets weight 0)
+    for (int j0 = 0; j0 < n; j0 += MU) {
+      float wq[MU], uq[MU];
+      int64_t eq[MU];
 #pragma unroll
-      for (int i = 0; i < PER; ++i) acc[i] += part(k0 + j, i) * (BF16 ? uj : wj);
+      for (int t = 0; t < MU; ++t) {
+        const int j = min(j0 + t, n - 1);
+        const float wj = __shfl(wk, gbase + j);
+        const float uj = __shfl(mine.y, gbase + j) * wj;
+        wq[t] = j0 + t < n ? wj : 0.f;
+        uq[t] = j0 + t < n ? uj : 0.f;
+        eq[t] = row0 + (int64_t)(k0 + j) * D;
+      }
+      if constexpr (BF16) {
+        bvec v[MU];
+#pragma unroll
+        for (int t = 0; t < MU; ++t) v[t] = *(const bvec*)((const __bf16*)ws_o + eq[t]);
+#pragma unroll
+        for (int t = 0; t < MU; ++t) {
+          l += uq[t];
+#pragma unroll
+          for (int i = 0; i < PER; ++i) acc[i] += (float)v[t][i] * uq[t];
+        }
+      } else {
+        float4 v[MU][PER / 4];
+#pragma unroll
+        for (int t = 0; t < MU; ++t)
+#pragma unroll
+          for (int i = 0; i < PER / 4; ++i) v[t][i] = *(const float4*)((const float*)ws_o + eq[t] + 4 * i);
+#pragma unroll
+        for (int t = 0; t < MU; ++t) {
+          l += uq[t];
+#pragma unroll
+          for (int i = 0; i < PER / 4; ++i) {
+            acc[4 * i] += v[t][i].x * wq[t];
+            acc[4 * i + 1] += v[t][i].y * wq[t];
+            acc[4 * i + 2] += v[t][i].z * wq[t];
+            acc[4 * i + 3] += v[t][i].w * wq[t];
+          }
+        }
+      }
     }
   }
+  if (!live) return;
   const float inv = l > 0.f ? 1.f / l : 0.f;
+  const int64_t o0 = (int64_t)pair * D + sub * PER;
+  if constexpr (BF16) {
+    bvec r;
 #pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const float r = acc[i] * inv;
-    if (BF16)
-      ((__bf16*)out)[(int64_t)pair * D + lane * PER + i] = (__bf16)r;
-    else
-      ((float*)out)[(int64_t)pair * D + lane * PER + i] = r;
+    for (int i = 0; i < PER; ++i) r[i] = (__bf16)(acc[i] * inv);
+    *(bvec*)((__bf16*)out + o0) = r;
+  } else {
+#pragma unroll
+    for (int i = 0; i < PER; i += 4)
+      *(float4*)((float*)out + o0 + i) = make_float4(acc[i] * inv, acc[i + 1] * inv, acc[i + 2] * inv, acc[i + 3] * inv);
   }
 }
 
@@ -471,7 +508,7 @@ rc_status split_k_attention(const rc_shape* shape, void* o, const void* q, void*
   }
   const int32_t* nsplit = plan_dev + RC_PLAN_HEADER + (int64_t)info->n_items * RC_PLAN_ITEM + info->n_members;
   const int pairs = batch * shape->num_q_heads;
-  const dim3 grid((pairs + 3) / 4);
+  const dim3 grid((pairs + 15) / 16);
   {
     ProfScope p(merge_name, s, timed);
     if (shape->head_dim == 128) {
