@@ -313,7 +313,15 @@ def test_decode_head_layouts(gpu, Hq, Hkv, D):
         _run_workload(gpu, w, shared=shared, chunk=chunk)
 
 
-def test_decode_merge_of_many_splits(gpu):
-    # more than 64 partials per request: the merge combines blocks of 64 splits
-    w = W.few_shot(n_req=3, prefix=1500, ext=5, n_decode=1)
+@pytest.mark.parametrize("prefix,dtype,D", [(1500, "bf16", 128), (256, "bf16", 128), (272, "bf16", 128),
+                                             (272, "f32", 64), (272, "bf16", 64)])
+def test_decode_merge_of_many_splits(gpu, prefix, dtype, D):
+    # the merge combines the partials 16 splits at a time: 85 splits over a
+    # 1500-token prefix (six blocks, each rescaled against the next), and 16
+    # and 17 splits (the shared prefix in 15 or 16 pieces of at most 18
+    # positions, plus each request's own range) on both sides of one block;
+    # fp32 partial rows and head_dim 64 take their own loads
+    w = W.few_shot(n_req=3, prefix=prefix, ext=5, n_decode=1)
+    w.shape.dtype, w.shape.head_dim = dtype, D
+    w.sm_scale = 1.0 / np.sqrt(D)
     _run_workload(gpu, w, shared=True, chunk=16)
